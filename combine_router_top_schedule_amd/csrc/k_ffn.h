@@ -1,0 +1,185 @@
+// Expert FFN tiles: gate/up GEMM with the SwiGLU epilogue, and the down GEMM with the push
+// epilogue that writes each result row into its token's receive slot. Used by the staged
+// kernels (k_ffn.hip) and by the fused persistent forward.
+#pragma once
+
+#include "k_gemm.h"
+
+namespace mok {
+
+struct FfnWeights {
+  const uint8_t* wg;    // BF16 [El][I][H] or E4M3 codes
+  const uint8_t* wu;
+  const uint8_t* wd;    // BF16 [El][H][I] or codes
+  const uint8_t* wg_s;  // MXFP8 scales [El][I][H/32]
+  const uint8_t* wu_s;
+  const uint8_t* wd_s;  // [El][H][I/32]
+};
+
+struct FfnShape {
+  int H, I;
+};
+
+// g|u = x [Wg;Wu]^T over the 128 h-columns [i0, i0+128) of expert e; SwiGLU h = silu(g) u.
+// B tile rows interleave 64-row blocks of Wg and Wu (block q even: Wg, odd: Wu, both for
+// i = i0 + (q/2)*64 + row%64), so wave (wm, wn) holds g in column blocks 0,1 and the matching
+// u in column blocks 2,3, lane for lane.
+template <bool MX>
+__device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
+                                            const ActPlanes& pl, int64_t prow0, int nrows, int e,
+                                            int i0) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int eb = MX ? 1 : 2;                              // bytes per element
+  const int xrow = s.H * eb;
+  Operand A, B;
+  A.interleave = 0;
+  A.stride = xrow;
+  A.sstride = s.H / 32;
+  A.r0 = A.r1 = make_rsrc(pl.x + prow0 * xrow, int64_t(nrows) * xrow);
+  B.interleave = 1;
+  B.stride = xrow;
+  B.sstride = s.H / 32;
+  const int64_t wrow0 = int64_t(e) * s.I + i0;
+  B.r0 = make_rsrc(w.wg + wrow0 * xrow, int64_t(128) * xrow);
+  B.r1 = make_rsrc(w.wu + wrow0 * xrow, int64_t(128) * xrow);
+  if (MX) {
+    A.s0 = A.s1 = make_rsrc(pl.xs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
+    B.s0 = make_rsrc(w.wg_s + wrow0 * B.sstride, int64_t(128) * B.sstride);
+    B.s1 = make_rsrc(w.wu_s + wrow0 * B.sstride, int64_t(128) * B.sstride);
+  }
+  f32x16 acc[4][4];
+  gemm_tile<MX>(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
+
+  // SwiGLU epilogue. Column blocks (jg, jg+2) = (g, u) of h-column i0 + wn*64 + jg*32 + lane%32.
+  // The K loop ended on a barrier, so the whole 128 KB of stage buffers is free: stage the
+  // BF16 g|u tile as [256 rows][g 128 | u 128], write it out row by row with 16-byte stores,
+  // then do the same for h.
+  uint16_t* t = reinterpret_cast<uint16_t*>(sm.a[0]);
+  {
+    // lane-dependent part of the staging address; the rest are immediate offsets
+    uint16_t* tl = t + opaque((wm * 128 + 4 * (lane >> 5)) * 256 + wn * 64 + (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jg = 0; jg < 2; ++jg)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int ro = (i * 32 + 8 * (v >> 2) + (v & 3)) * 256 + jg * 32;
+          tl[ro] = f2bf(acc[i][jg][v]);
+          tl[ro + 128] = f2bf(acc[i][jg + 2][v]);
+        }
+  }
+  __syncthreads();
+  {
+    // 32 lanes per row (512 B), two rows per wave per step.
+    const int half = lane >> 5, c = lane & 31;
+    for (int r = wave * 2 + half; r < nrows; r += 8) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(t + r * 256 + c * 8);
+      uint16_t* dst = pl.gu + (prow0 + r) * 2 * s.I + (c < 16 ? i0 + c * 8 : s.I + i0 + (c - 16) * 8);
+      *reinterpret_cast<u32x4*>(dst) = val;
+    }
+  }
+  __syncthreads();
+  uint8_t* tb = sm.a[0];
+  uint32_t* ts = reinterpret_cast<uint32_t*>(sm.b[0]);   // MXFP8 scales, one word per row
+  const int rl = opaque(wm * 128 + 4 * (lane >> 5));
+  const int cl = opaque(wn * 64 + (lane & 31));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jg = 0; jg < 2; ++jg) {
+      const int col = cl + jg * 32;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = rl + i * 32 + 8 * (v >> 2) + (v & 3);
+        const float g = acc[i][jg][v];
+        const float u = acc[i][jg + 2][v];
+        const float h = g / (1.f + expf(-g)) * u;
+        if (MX) {
+          // Quantise h along I: the 32 lanes of this half-wave hold one MX block of row r.
+          float amax = fabsf(h);
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+          const int ex = mx_block_exp(amax);
+          tb[r * 128 + col] = uint8_t(e4m3x2(h * exp2i(-ex), 0.f) & 0xFFu);
+          if ((lane & 31) == 0) reinterpret_cast<uint8_t*>(ts)[r * 4 + (col >> 5)] = uint8_t(ex + 127);
+        } else {
+          t[r * 128 + col] = f2bf(h);
+        }
+      }
+    }
+  __syncthreads();
+  if (MX) {
+    // 8 lanes per row (128 B of codes); the row's 4 scale bytes by lane 0 of the group.
+    const int sub = lane >> 3, c = lane & 7;
+    for (int r = wave * 8 + sub; r < nrows; r += 32) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(tb + r * 128 + c * 16);
+      *reinterpret_cast<u32x4*>(pl.h + (prow0 + r) * s.I + i0 + c * 16) = val;
+      if (c == 0)
+        *reinterpret_cast<uint32_t*>(pl.hs + (prow0 + r) * (s.I / 32) + i0 / 32) = ts[r];
+    }
+  } else {
+    // 16 lanes per row (256 B).
+    const int sub = lane >> 4, c = lane & 15;
+    for (int r = wave * 4 + sub; r < nrows; r += 16) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(t + r * 128 + c * 8);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(pl.h) + (prow0 + r) * s.I + i0 + c * 8) = val;
+    }
+  }
+  __syncthreads();
+}
+
+// y = h Wd^T over the 256 output columns [c0, c0+256) of expert e; the epilogue pushes each
+// row to its token's receive slot: slots[perm[row]][c] = bf16(y).
+template <bool MX>
+__device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
+                                          const ActPlanes& pl, int64_t prow0, int64_t row0,
+                                          int nrows, int e, int c0, const int32_t* perm,
+                                          uint16_t* slots) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int eb = MX ? 1 : 2;
+  const int hrow = s.I * eb;
+  Operand A, B;
+  A.interleave = B.interleave = 0;
+  A.stride = B.stride = hrow;
+  A.sstride = B.sstride = s.I / 32;
+  A.r0 = A.r1 = make_rsrc(pl.h + prow0 * hrow, int64_t(nrows) * hrow);
+  const int ncols = min(kTileN, s.H - c0);
+  const int64_t wrow0 = int64_t(e) * s.H + c0;
+  B.r0 = B.r1 = make_rsrc(w.wd + wrow0 * hrow, int64_t(ncols) * hrow);
+  if (MX) {
+    A.s0 = A.s1 = make_rsrc(pl.hs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
+    B.s0 = B.s1 = make_rsrc(w.wd_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
+  }
+  f32x16 acc[4][4];
+  gemm_tile<MX>(sm, A, B, hrow / kStageRowBytes, acc, wm, wn, lane);
+
+  // Push epilogue: stage the BF16 tile in LDS, then write whole rows (512 B, 16 B per lane)
+  // to the receive slot of each row's pair.
+  uint16_t* t = reinterpret_cast<uint16_t*>(sm.a[0]);
+  {
+    uint16_t* tl = t + opaque((wm * 128 + 4 * (lane >> 5)) * 256 + wn * 128 + (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          tl[(i * 32 + 8 * (v >> 2) + (v & 3)) * 256 + j * 32] = f2bf(acc[i][j][v]);
+  }
+  __syncthreads();
+  {
+    const int half = lane >> 5, c = lane & 31;
+    const bool colok = c0 + c * 8 < s.H;
+    for (int r = wave * 2 + half; r < nrows; r += 8) {
+      const int32_t pair = perm[row0 + r];
+      const u32x4 val = *reinterpret_cast<const u32x4*>(t + r * 256 + c * 8);
+      if (colok) *reinterpret_cast<u32x4*>(slots + int64_t(pair) * s.H + c0 + c * 8) = val;
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace mok

@@ -1,0 +1,98 @@
+// Staged grouped SwiGLU expert FFN: a persistent gate/up kernel over all m-tiles x h-column
+// tiles, then a persistent down kernel over all m-tiles x output-column tiles. Workgroups walk
+// the tile list with a static stride (no atomics, so the assignment is deterministic).
+#include "k_ffn.h"
+
+namespace mok {
+namespace {
+
+struct FfnStagedArgs {
+  const MTile* tiles;
+  const int32_t* ntiles;
+  const int32_t* perm;
+  FfnShape s;
+  FfnWeights w;
+  ActPlanes pl;
+  uint16_t* slots;
+};
+
+template <bool MX>
+__global__ __launch_bounds__(256, 1) void k_gateup_staged(FfnStagedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  const int mtiles = *a.ntiles;
+  const int ntn = a.s.I / 128;
+  const int total = mtiles * ntn;
+  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
+    int mt, nt;
+    tile_coords(t, mtiles, ntn, mt, nt);
+    const MTile tl = a.tiles[mt];
+    gateup_tile<MX>(sm, a.s, a.w, a.pl, tl.row0, tl.nrows, tl.e, nt * 128);
+  }
+}
+
+template <bool MX>
+__global__ __launch_bounds__(256, 1) void k_down_staged(FfnStagedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  const int mtiles = *a.ntiles;
+  const int ntn = (a.s.H + kTileN - 1) / kTileN;
+  const int total = mtiles * ntn;
+  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
+    int mt, nt;
+    tile_coords(t, mtiles, ntn, mt, nt);
+    const MTile tl = a.tiles[mt];
+    down_tile<MX>(sm, a.s, a.w, a.pl, tl.row0, tl.row0, tl.nrows, tl.e, nt * kTileN, a.perm,
+                  a.slots);
+  }
+}
+
+template <class F>
+hipError_t allow_big_lds(F* f) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(f),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kGemmLdsBytes));
+}
+
+}  // namespace
+
+hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                             const mok_weights& w, uint8_t* act, uint16_t* slots, uint8_t* ws,
+                             hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e;
+    if ((e = allow_big_lds(k_gateup_staged<false>)) != hipSuccess) return e;
+    if ((e = allow_big_lds(k_gateup_staged<true>)) != hipSuccess) return e;
+    if ((e = allow_big_lds(k_down_staged<false>)) != hipSuccess) return e;
+    if ((e = allow_big_lds(k_down_staged<true>)) != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipError_t err = launch_tiles(L, int(L.rows_max), saved, ws, s);
+  if (err != hipSuccess) return err;
+  const bool mx = L.dtype == MOK_MXFP8;
+  FfnStagedArgs a{};
+  a.tiles = reinterpret_cast<const MTile*>(ws + L.ws_tiles);
+  a.ntiles = reinterpret_cast<const int32_t*>(ws) + kWsNumTiles;
+  a.perm = reinterpret_cast<const int32_t*>(saved + L.sv_perm);
+  a.s = FfnShape{L.H, L.I};
+  if (mx) {
+    a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
+  } else {
+    a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),
+                     static_cast<const uint8_t*>(w.wd), nullptr, nullptr, nullptr};
+  }
+  ActPlanes xp = act_planes(const_cast<uint8_t*>(xd), L.rows_max, L.H, L.I, L.dtype, true);
+  a.pl = act_planes(act, L.rows_max, L.H, L.I, L.dtype, false);
+  a.pl.x = xp.x;
+  a.pl.xs = xp.xs;
+  a.slots = slots;
+  const int G = device_cus() > 0 ? device_cus() : 256;
+  if (mx) hipLaunchKernelGGL(k_gateup_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else hipLaunchKernelGGL(k_gateup_staged<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (mx) hipLaunchKernelGGL(k_down_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else hipLaunchKernelGGL(k_down_staged<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mok

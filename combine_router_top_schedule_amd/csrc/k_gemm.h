@@ -1,0 +1,209 @@
+// Grouped-GEMM tile engine for gfx950: one 256 x 256 output tile per workgroup of 4 waves
+// (2 x 2, each wave 128 x 128 = 4 x 4 MFMA 32x32 blocks), K consumed in stages of 128 bytes
+// per row (64 BF16 or 128 E4M3 values), double-buffered in LDS.
+//
+// Both operands are staged "K-contiguous": LDS holds [256 rows][128 bytes] per stage, 16-byte
+// chunks XOR-swizzled by (row & 7) so the MFMA fragment reads (32 rows at one chunk per
+// half-wave) are free of bank conflicts. Stages are filled by buffer loads that write LDS
+// directly, issued one stage ahead of the MFMA work.
+//
+// MFMA result layout (v_mfma_f32_32x32x16_bf16 and v_mfma_scale_f32_32x32x64_f8f6f4, checked
+// on gfx950): accumulator register v of lane l holds row 8*(v/4) + 4*(l/32) + (v%4), column
+// l%32. Lanes 0-31 and 32-63 carry the two K-halves of each BF16 operand fragment; the fp8
+// layout is described at mma_stage_mx.
+#pragma once
+
+#include "mok_device.h"
+#include "mok_internal.h"
+
+namespace mok {
+
+constexpr int kStageRowBytes = 128;
+constexpr int kStageBytes = kTileM * kStageRowBytes;   // 32 KB per operand per stage
+
+struct GemmLds {
+  uint8_t a[2][kStageBytes];
+  uint8_t b[2][kStageBytes];
+  uint32_t as[2][kTileM];   // MXFP8: the 4 scale bytes of each row for the stage
+  uint32_t bs[2][kTileN];
+};
+constexpr size_t kGemmLdsBytes = sizeof(GemmLds);
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kStageRowBytes + ((chunk ^ (row & 7)) << 4);
+}
+
+// Hide a value from loop-invariant code motion: persistent kernels would otherwise hoist
+// hundreds of per-row epilogue addresses out of the tile loop and spill them.
+template <class T>
+__device__ __forceinline__ T opaque(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Accumulator row of register v for this lane, inside a 32 x 32 block.
+__device__ __forceinline__ int acc_row(int v, int lane) {
+  return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+// ---- operand source: rows with the reduction axis contiguous in memory -------------------
+// Staged straight from global memory into LDS with buffer loads (no registers in between).
+// A buffer resource covers exactly the valid rows of the tile, so rows past a ragged edge
+// read as zeros. With `interleave`, 64-row blocks of the tile alternate between two matrices
+// (r0/s0 for even blocks, r1/s1 for odd), block q reading rows (q/2)*64 .. of its matrix; a
+// 64-row block is exactly one wave's share of a stage, so every load has one resource.
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct Operand {
+  __amdgpu_buffer_rsrc_t r0, r1;    // codes / BF16 values
+  __amdgpu_buffer_rsrc_t s0, s1;    // MXFP8 scales
+  int stride;                       // bytes per row
+  int sstride;                      // scale bytes per row
+  int interleave;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  // Raw buffer: stride 0, num_records = bytes (clamped to the 32-bit field).
+  const int nrec = int(bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0ll : (bytes < 0 ? 0 : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+}
+
+// Issue the loads of stage kt (128 bytes of every row, and in MXFP8 mode the 4 scale bytes of
+// every row) into one LDS stage. Wave w covers rows 64w .. 64w+63: 8 loads of 8 rows x 128
+// bytes. Lane L of a load lands at LDS offset 16*L: row 8c + L/8, physical chunk L%8, which
+// holds the logical chunk (L%8) ^ (row & 7) of the swizzled layout.
+__device__ __forceinline__ void issue_stage(const Operand& op, uint8_t* lds, uint32_t* lds_s, int kt,
+                                            bool mx) {
+  const int w = wave_id(), L = threadIdx.x & 63;
+  const int lchunk = (L & 7) ^ (L >> 3);
+  const bool odd = op.interleave && (w & 1);
+  const __amdgpu_buffer_rsrc_t r = odd ? op.r1 : op.r0;
+  const int rbase = op.interleave ? (w >> 1) * 64 : w * 64;   // first row inside the matrix
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int lrow = rbase + 8 * c + (L >> 3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + (w * 64 + 8 * c) * kStageRowBytes),
+                                             16, lrow * op.stride + kt * kStageRowBytes + lchunk * 16,
+                                             0, 0, 0);
+  }
+  if (mx) {
+    const __amdgpu_buffer_rsrc_t rs = odd ? op.s1 : op.s0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_s + w * 64), 4,
+                                             (rbase + L) * op.sstride + kt * 4, 0, 0, 0);
+  }
+}
+
+// ---- one LDS stage of MFMA work -----------------------------------------------------------
+__device__ __forceinline__ void mma_stage_bf16(const uint8_t* A, const uint8_t* B, f32x16 (&acc)[4][4],
+                                               int wm, int wn, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    bf16x8 a[4], b[4];
+    const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + i * 32 + (lane & 31), ch));
+      b[i] = *reinterpret_cast<const bf16x8*>(B + swz(wn * 128 + i * 32 + (lane & 31), ch));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void mma_stage_mx(const uint8_t* A, const uint8_t* B, const uint32_t* As,
+                                             const uint32_t* Bs, f32x16 (&acc)[4][4], int wm,
+                                             int wn, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    i32x8 a[4], b[4];
+    int sa[4], sb[4];
+    // One instruction consumes 64 K = MX blocks 2kk and 2kk+1. Lane half h carries elements
+    // 16h..16h+15 of block 2kk in bytes 0-15 and of block 2kk+1 in bytes 16-31, and its scale
+    // byte is that of block 2kk+h (checked on gfx950).
+    const int h = lane >> 5;
+    const int blk = kk * 2 + h;
+    const int ch0 = kk * 4 + h, ch1 = kk * 4 + 2 + h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra = wm * 128 + i * 32 + (lane & 31);
+      const int rb = wn * 128 + i * 32 + (lane & 31);
+      u32x4 a0 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch0));
+      u32x4 a1 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch1));
+      u32x4 b0 = *reinterpret_cast<const u32x4*>(B + swz(rb, ch0));
+      u32x4 b1 = *reinterpret_cast<const u32x4*>(B + swz(rb, ch1));
+      a[i] = i32x8{int(a0[0]), int(a0[1]), int(a0[2]), int(a0[3]),
+                   int(a1[0]), int(a1[1]), int(a1[2]), int(a1[3])};
+      b[i] = i32x8{int(b0[0]), int(b0[1]), int(b0[2]), int(b0[3]),
+                   int(b1[0]), int(b1[1]), int(b1[2]), int(b1[3])};
+      sa[i] = int((As[ra] >> (8 * blk)) & 0xFFu);
+      sb[i] = int((Bs[rb] >> (8 * blk)) & 0xFFu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0,
+                                                                    0, sa[i], 0, sb[j]);
+  }
+}
+
+// ---- the tile loop -----------------------------------------------------------------------
+// Runs the K loop of one output tile; on return acc holds the fp32 tile (no split-K, stages
+// in ascending K order, so the result depends only on the operands).
+template <bool MX>
+__device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const Operand& B,
+                                          int ksteps, f32x16 (&acc)[4][4], int wm, int wn,
+                                          int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  issue_stage(A, sm.a[0], sm.as[0], 0, MX);
+  issue_stage(B, sm.b[0], sm.bs[0], 0, MX);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < ksteps) {
+      issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX);
+      issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX);
+    }
+    if (MX) mma_stage_mx(sm.a[cur], sm.b[cur], sm.as[cur], sm.bs[cur], acc, wm, wn, lane);
+    else mma_stage_bf16(sm.a[cur], sm.b[cur], acc, wm, wn, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
+// ---- tile scheduling ------------------------------------------------------------------------
+// Logical workgroup id that gives the workgroups resident on one XCD (blockIdx % 8 on MI355X)
+// consecutive ids, so consecutive tiles -- which share operands -- land in one L2.
+__device__ __forceinline__ int xcd_logical_id() {
+  const int G = gridDim.x, b = blockIdx.x;
+  if (G % 8) return b;
+  return (b % 8) * (G / 8) + b / 8;
+}
+
+// Grouped order: tile t -> (m-tile, n-tile), sweeping kGroupM m-tiles per group so that a
+// run of consecutive tiles reuses kGroupM row panels and a few column panels.
+constexpr int kGroupM = 4;
+__device__ __forceinline__ void tile_coords(int t, int mtiles, int ntiles, int& mt, int& nt) {
+  const int gsize = kGroupM * ntiles;
+  const int g = t / gsize;
+  const int first = g * kGroupM;
+  const int gm = min(kGroupM, mtiles - first);
+  const int local = t % gsize;
+  mt = first + local % gm;
+  nt = local / gm;
+}
+
+}  // namespace mok

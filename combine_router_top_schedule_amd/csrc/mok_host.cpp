@@ -1,0 +1,215 @@
+// Host side of libmok: the C ABI declared in include/mok.h. Validates arguments, derives
+// buffer layouts from host-known bounds, and enqueues kernels on the caller's stream. No call
+// except mok_device_status synchronises or reads device memory back.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "mok_internal.h"
+
+using namespace mok;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int default_minibatch(const mok_desc& d) {
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  int64_t m = mok_two_wave_floor(cus, kTileM, kTileN, d.intermediate);
+  m = align_up(m, 32);
+  return int(m);
+}
+
+mok_status check_desc(const mok_desc* d) {
+  if (!d) return MOK_ERR_NULL;
+  if (d->dtype != MOK_BF16 && d->dtype != MOK_MXFP8) return MOK_ERR_DTYPE;
+  if (d->hidden <= 0 || d->hidden % 128 || d->intermediate <= 0 || d->intermediate % 128)
+    return MOK_ERR_SHAPE;
+  if (d->num_experts < 1 || d->num_experts > kMaxExperts) return MOK_ERR_SHAPE;
+  if (d->top_k < 1 || d->top_k > kMaxTopK || d->top_k > d->num_experts) return MOK_ERR_SHAPE;
+  if (d->num_segments < 1 || d->tokens_per_segment < 1) return MOK_ERR_SHAPE;
+  if (d->expert_begin < 0 || d->num_local_experts < 1 || d->num_local_experts > kMaxLocalExperts ||
+      d->expert_begin + d->num_local_experts > d->num_experts)
+    return MOK_ERR_SHAPE;
+  // MXFP8 weight gradients quantise along tokens in 32-row blocks, which minibatch cuts must
+  // not split; BF16 takes any minibatch size.
+  if (d->minibatch_tokens < 0) return MOK_ERR_SHAPE;
+  if (d->dtype == MOK_MXFP8 && d->minibatch_tokens % 32) return MOK_ERR_SHAPE;
+  if (d->comm_cus < 0 || d->ring_bytes < 0) return MOK_ERR_SHAPE;
+  const int64_t N = int64_t(d->num_segments) * d->tokens_per_segment;
+  // Look-back words keep counts in 30 bits; pair ids and rows are int32.
+  if (N * d->top_k >= (int64_t(1) << 30)) return MOK_ERR_SHAPE;
+  return MOK_OK;
+}
+
+Layout layout_of(const mok_desc& d) {
+  mok_desc e = d;
+  if (e.minibatch_tokens == 0) e.minibatch_tokens = default_minibatch(d);
+  return make_layout(e);
+}
+
+mok_status hip_status(hipError_t e) { return e == hipSuccess ? MOK_OK : MOK_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int mok_abi_version(void) { return MOK_ABI_VERSION; }
+
+const char* mok_status_str(mok_status s) {
+  switch (s) {
+    case MOK_OK: return "ok";
+    case MOK_ERR_NULL: return "null pointer argument";
+    case MOK_ERR_SHAPE: return "invalid shape";
+    case MOK_ERR_DTYPE: return "invalid dtype or missing dtype-specific field";
+    case MOK_ERR_ALIGN: return "misaligned device pointer";
+    case MOK_ERR_WORKSPACE: return "workspace error";
+    case MOK_ERR_RING: return "ring buffer holds fewer than two minibatch slots";
+    case MOK_ERR_HIP: return "HIP runtime or launch failure";
+    case MOK_ERR_DEVICE_TIMEOUT: return "device-side bounded wait expired";
+    case MOK_ERR_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+int64_t mok_two_wave_floor(int32_t cus, int32_t tile_m, int32_t tile_n, int32_t intermediate) {
+  if (cus <= 0 || tile_m <= 0 || tile_n <= 0 || intermediate <= 0) return 0;
+  const int64_t num = int64_t(2) * cus * tile_m * tile_n;
+  const int64_t den = int64_t(2) * intermediate;
+  return (num + den - 1) / den;
+}
+
+int32_t mok_device_cus(void) { return device_cus(); }
+
+mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!sizes) return MOK_ERR_NULL;
+  const Layout L = layout_of(*desc);
+  sizes->saved_bytes = size_t(L.sv_bytes);
+  sizes->ws_bytes = size_t(L.ws_bytes);
+  sizes->slots_bytes = size_t(L.slots_bytes);
+  sizes->xd_bytes = size_t(L.xd_bytes);
+  sizes->act_bytes = size_t(L.act_bytes);
+  sizes->wq_bytes = size_t(L.wq_bytes);
+  sizes->rows_max = L.rows_max;
+  sizes->ring_slots = L.R;
+  sizes->minibatch = L.M;
+  sizes->slot_bytes = L.slot_bytes;
+  sizes->perm_offset = L.sv_perm;
+  sizes->tokpos_offset = L.sv_tokpos;
+  sizes->touched_offset = L.sv_touched;
+  return MOK_OK;
+}
+
+mok_status mok_schedule(const mok_desc* desc, const float* logits_dev, int32_t* topk_idx_dev,
+                        float* topk_p_dev, void* saved_dev, void* ws_dev, void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!logits_dev || !topk_idx_dev || !topk_p_dev || !saved_dev || !ws_dev) return MOK_ERR_NULL;
+  if (!aligned16(logits_dev) || !aligned16(saved_dev) || !aligned16(ws_dev)) return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(ws_dev), 0u, kWsWords, s);
+  if (e != hipSuccess) return MOK_ERR_HIP;
+  return hip_status(launch_router(L, logits_dev, topk_idx_dev, topk_p_dev,
+                                  static_cast<uint8_t*>(saved_dev), static_cast<uint8_t*>(ws_dev), s));
+}
+
+mok_status mok_dispatch(const mok_desc* desc, const void* saved_dev, const void* const* x_seg_dev,
+                        void* xd_dev, void* ws_dev, void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!saved_dev || !x_seg_dev || !xd_dev || !ws_dev) return MOK_ERR_NULL;
+  if (!aligned16(xd_dev) || !aligned16(saved_dev)) return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  return hip_status(launch_dispatch(L, static_cast<const uint8_t*>(saved_dev), x_seg_dev,
+                                    static_cast<uint8_t*>(xd_dev), as_stream(stream)));
+}
+
+mok_status mok_expert_ffn(const mok_desc* desc, const void* saved_dev, const void* xd_dev,
+                          const mok_weights* w, void* act_dev, void* slots_dev, void* ws_dev,
+                          void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!saved_dev || !xd_dev || !w || !act_dev || !slots_dev || !ws_dev) return MOK_ERR_NULL;
+  if (desc->dtype == MOK_BF16) {
+    if (!w->wg || !w->wu || !w->wd) return MOK_ERR_NULL;
+    if (!aligned16(w->wg) || !aligned16(w->wu) || !aligned16(w->wd)) return MOK_ERR_ALIGN;
+  } else {
+    if (!w->wg_q || !w->wg_s || !w->wu_q || !w->wu_s || !w->wd_q || !w->wd_s) return MOK_ERR_DTYPE;
+    if (!aligned16(w->wg_q) || !aligned16(w->wu_q) || !aligned16(w->wd_q)) return MOK_ERR_ALIGN;
+  }
+  if (!aligned16(xd_dev) || !aligned16(act_dev) || !aligned16(slots_dev)) return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  return hip_status(launch_ffn_staged(L, static_cast<const uint8_t*>(saved_dev),
+                                      static_cast<const uint8_t*>(xd_dev), *w,
+                                      static_cast<uint8_t*>(act_dev),
+                                      static_cast<uint16_t*>(slots_dev),
+                                      static_cast<uint8_t*>(ws_dev), as_stream(stream)));
+}
+
+mok_status mok_combine(const mok_desc* desc, const void* saved_dev, const int32_t* topk_idx_dev,
+                       const float* topk_p_dev, const void* slots_dev, void* const* out_seg_dev,
+                       void* ws_dev, void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!saved_dev || !topk_idx_dev || !slots_dev || !out_seg_dev || !ws_dev) return MOK_ERR_NULL;
+  if (!aligned16(slots_dev)) return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  return hip_status(launch_combine(L, static_cast<const uint8_t*>(saved_dev), topk_idx_dev,
+                                   topk_p_dev, static_cast<const uint16_t*>(slots_dev), out_seg_dev,
+                                   as_stream(stream)));
+}
+
+mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void* src_dev,
+                           int32_t transpose, uint8_t* codes_dev, uint8_t* scales_dev,
+                           void* stream) {
+  if (!src_dev || !codes_dev || !scales_dev) return MOK_ERR_NULL;
+  if (batch < 1 || rows < 1 || cols < 1) return MOK_ERR_SHAPE;
+  if ((transpose ? rows : cols) % 32) return MOK_ERR_SHAPE;
+  if (transpose != 0 && transpose != 1) return MOK_ERR_SHAPE;
+  if (!aligned16(codes_dev)) return MOK_ERR_ALIGN;
+  return hip_status(launch_quantize_mx(batch, rows, cols, static_cast<const uint16_t*>(src_dev),
+                                       transpose, codes_dev, scales_dev, as_stream(stream)));
+}
+
+mok_status mok_device_status(const void* ws_dev, void* stream, mok_status* out) {
+  if (!ws_dev || !out) return MOK_ERR_NULL;
+  if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return MOK_ERR_HIP;
+  int32_t word = 0;
+  if (hipMemcpy(&word, ws_dev, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return MOK_ERR_HIP;
+  *out = static_cast<mok_status>(word);
+  return MOK_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
+                         const float* logits_dev, const mok_weights* w,
+                         void* const* out_seg_dev, int32_t* topk_idx_dev, float* topk_p_dev,
+                         void* saved_dev, void* ring_dev, void* slots_dev, void* ws_dev,
+                         void* stream) {
+  (void)desc; (void)x_seg_dev; (void)logits_dev; (void)w; (void)out_seg_dev; (void)topk_idx_dev;
+  (void)topk_p_dev; (void)saved_dev; (void)ring_dev; (void)slots_dev; (void)ws_dev; (void)stream;
+  return MOK_ERR_UNSUPPORTED;
+}
+
+mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
+                         const void* const* x_seg_dev, const mok_weights* w,
+                         const int32_t* topk_idx_dev, const float* topk_p_dev,
+                         const void* saved_dev, void* ring_dev, void* slots_dev,
+                         void* const* dx_seg_dev, float* dp_dev, float* dlogits_dev,
+                         const mok_weight_grads* g, void* ws_dev, void* stream) {
+  (void)desc; (void)dout_seg_dev; (void)x_seg_dev; (void)w; (void)topk_idx_dev; (void)topk_p_dev;
+  (void)saved_dev; (void)ring_dev; (void)slots_dev; (void)dx_seg_dev; (void)dp_dev;
+  (void)dlogits_dev; (void)g; (void)ws_dev; (void)stream;
+  return MOK_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

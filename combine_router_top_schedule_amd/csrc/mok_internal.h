@@ -1,0 +1,154 @@
+// Internal definitions shared by the host code and the kernels of libmok (not part of the
+// ABI). Buffer layouts are computed here once, from host-known bounds only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mok.h"
+
+namespace mok {
+
+// ---- fixed kernel geometry -------------------------------------------------------------
+constexpr int kTileM = 256;         // GEMM tile rows (tokens)
+constexpr int kTileN = 256;         // GEMM tile columns
+constexpr int kThreads = 256;       // threads per GEMM workgroup (4 waves, 2 x 2)
+constexpr int kTopkTokensPerBlock = 256;
+constexpr int kMaxLocalExperts = 64;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 1024;
+
+__host__ __device__ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- saved (schedule table) header, int32 words ----------------------------------------
+enum SavedHeader : int {
+  kHdrP = 0,        // local pairs
+  kHdrRows = 1,     // expert-order rows (P + per-expert padding in MXFP8 mode)
+  kHdrU = 2,        // touched tokens
+  kHdrCounts = 16,  // [E_loc]
+  kHdrOffsets = 96, // [E_loc + 1]
+  kHdrWords = 192,
+};
+
+// ---- ws header, int32 words ------------------------------------------------------------
+enum WsHeader : int {
+  kWsError = 0,     // mok_status of the first device-side failure, 0 if none
+  kWsTicket = 1,    // dynamic block id for the router's single-pass scan
+  kWsNumTiles = 2,  // m-tiles in the tile table
+  kWsWords = 64,
+};
+
+struct Layout {
+  // shapes
+  int H, E, K, I, S, T, e0, El, M, dtype;
+  int64_t N, NK, rows_max;
+  int row_align;
+  // saved
+  int64_t sv_perm, sv_tokpos, sv_touched, sv_bytes;
+  // ws
+  int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_bytes;
+  int topk_blocks;
+  int64_t tiles_max, J_max;
+  // ring slot (fused forward): X | GU | Hact per row
+  int64_t x_row_bytes, gu_row_bytes, h_row_bytes, slot_bytes;
+  int R;
+  // staged buffers
+  int64_t xd_bytes, act_bytes, slots_bytes, wq_bytes;
+};
+
+// Bytes of an activation row of width `w` elements in the activation format: BF16, or
+// MXFP8 codes followed (in a separate plane) by one scale per 32 elements.
+__host__ __device__ inline int64_t act_row_bytes(int w, int dtype) {
+  return dtype == MOK_BF16 ? int64_t(w) * 2 : int64_t(w) + w / 32;
+}
+
+inline Layout make_layout(const mok_desc& d) {
+  Layout L{};
+  L.H = d.hidden; L.E = d.num_experts; L.K = d.top_k; L.I = d.intermediate;
+  L.S = d.num_segments; L.T = d.tokens_per_segment; L.e0 = d.expert_begin;
+  L.El = d.num_local_experts; L.dtype = d.dtype;
+  L.N = int64_t(L.S) * L.T;
+  L.NK = L.N * L.K;
+  L.row_align = d.dtype == MOK_MXFP8 ? 32 : 1;
+  int kk = L.K < L.El ? L.K : L.El;
+  L.rows_max = L.N * kk + int64_t(L.El) * (L.row_align - 1);
+  L.M = d.minibatch_tokens;
+  // saved
+  int64_t off = 1024;
+  L.sv_perm = off; off = align_up(off + 4 * L.rows_max, 256);
+  L.sv_tokpos = off; off = align_up(off + 4 * L.NK, 256);
+  L.sv_touched = off; off = align_up(off + 4 * L.N, 256);
+  L.sv_bytes = off;
+  // ws
+  L.topk_blocks = int(cdiv(L.N, kTopkTokensPerBlock));
+  L.J_max = L.M > 0 ? cdiv(L.rows_max, L.M) : 1;
+  L.tiles_max = cdiv(L.rows_max, kTileM) + L.J_max + L.El + 1;
+  off = 256;
+  L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 1), 256);
+  L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
+  L.ws_counters = off; off = align_up(off + 4 * (4 * L.J_max + 1024), 256);
+  L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
+  L.ws_bytes = off;
+  // ring
+  L.x_row_bytes = act_row_bytes(L.H, L.dtype);
+  L.gu_row_bytes = int64_t(2) * L.I * 2;
+  L.h_row_bytes = act_row_bytes(L.I, L.dtype);
+  L.slot_bytes = align_up(int64_t(L.M) * (L.x_row_bytes + L.gu_row_bytes + L.h_row_bytes), 256);
+  L.R = L.slot_bytes > 0 ? int(d.ring_bytes / L.slot_bytes) : 0;
+  // staged
+  L.xd_bytes = align_up(L.rows_max * L.x_row_bytes, 256);
+  L.act_bytes = align_up(L.rows_max * (L.gu_row_bytes + L.h_row_bytes), 256);
+  L.slots_bytes = align_up(L.NK * L.H * 2, 256);
+  L.wq_bytes = align_up(int64_t(L.El) * L.I * L.H * 33 / 32, 256);
+  return L;
+}
+
+// Activation plane pointers for `rows` rows starting at `base`: X (codes) then X scales, etc.
+struct ActPlanes {
+  uint8_t* x;      // BF16 [rows][H] or codes [rows][H]
+  uint8_t* xs;     // MXFP8 scales [rows][H/32] (null in BF16)
+  uint16_t* gu;    // BF16 [rows][2I]: g in [0, I), u in [I, 2I)
+  uint8_t* h;      // BF16 [rows][I] or codes [rows][I]
+  uint8_t* hs;     // MXFP8 scales [rows][I/32]
+};
+
+__host__ __device__ inline ActPlanes act_planes(uint8_t* base, int64_t rows, int H, int I, int dtype,
+                                                bool with_x) {
+  ActPlanes p{};
+  uint8_t* q = base;
+  if (with_x) {
+    p.x = q;
+    if (dtype == MOK_BF16) { q += rows * H * 2; }
+    else { q += rows * H; p.xs = q; q += rows * (H / 32); }
+  }
+  p.gu = reinterpret_cast<uint16_t*>(q); q += rows * 2 * I * 2;
+  p.h = q;
+  if (dtype == MOK_BF16) { q += rows * I * 2; }
+  else { q += rows * I; p.hs = q; }
+  return p;
+}
+
+// One m-tile of a grouped GEMM: rows [row0, row0 + nrows) of expert e, inside minibatch j.
+struct MTile {
+  int32_t j, e, row0, nrows;
+};
+
+// ---- launch wrappers (defined in the .hip files) ----------------------------------------
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, float* p,
+                         uint8_t* saved, uint8_t* ws, hipStream_t s);
+hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s);
+hipError_t launch_dispatch(const Layout& L, const uint8_t* saved, const void* const* x_seg,
+                           uint8_t* xd, hipStream_t s);
+hipError_t launch_combine(const Layout& L, const uint8_t* saved, const int32_t* idx, const float* p,
+                          const uint16_t* slots, void* const* out_seg, hipStream_t s);
+hipError_t launch_quantize_mx(int batch, int rows, int cols, const uint16_t* src, int transpose,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                             const mok_weights& w, uint8_t* act, uint16_t* slots, uint8_t* ws,
+                             hipStream_t s);
+
+int device_cus();
+
+}  // namespace mok

@@ -1,0 +1,103 @@
+// Per-row device routines shared by the staged kernels and the fused persistent kernels.
+// A whole wave (64 lanes) works on one row; lanes take consecutive 16-byte chunks.
+#pragma once
+
+#include "mok_device.h"
+#include "mok_internal.h"
+
+namespace mok {
+
+// Copy one BF16 row of H elements (src == nullptr writes zeros).
+__device__ __forceinline__ void copy_row_bf16(const uint16_t* src, uint16_t* dst, int H, int lane) {
+  const int nch = H / 8;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = c0 + q * 64 + lane;
+      v[q] = (src && c < nch) ? s[c] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = c0 + q * 64 + lane;
+      if (c < nch) d[c] = v[q];
+    }
+  }
+}
+
+// Quantise one BF16 row of H elements to MXFP8 along H: codes [H], scales [H/32].
+__device__ __forceinline__ void quant_row_mx(const uint16_t* src, uint8_t* codes, uint8_t* scales,
+                                             int H, int lane) {
+  const int nblk = H / 32;
+  for (int b = lane; b < nblk; b += 64) {
+    float v[32];
+    if (src) {
+      const u32x4* s = reinterpret_cast<const u32x4*>(src + b * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 w = s[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[q * 8 + 2 * i] = __uint_as_float(w[i] << 16);
+          v[q * 8 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = 0.f;
+    }
+    uint32_t c8[8];
+    const uint32_t sc = mx_quant32(v, c8);
+    u32x4* d = reinterpret_cast<u32x4*>(codes + b * 32);
+    d[0] = u32x4{c8[0], c8[1], c8[2], c8[3]};
+    d[1] = u32x4{c8[4], c8[5], c8[6], c8[7]};
+    scales[b] = uint8_t(sc);
+  }
+}
+
+// Fixed-order merge of token n's local pairs: dst = bf16( sum over k ascending, idx[n,k]
+// local, of w_k * slots[n*K+k] ), w_k = p[n,k] (or 1 when p == nullptr). fp32 accumulation,
+// one fused multiply-add per term in k order, so the result is bit-reproducible.
+__device__ __forceinline__ void merge_row(int64_t n, const int32_t* idx, const float* p,
+                                         const uint16_t* slots, uint16_t* dst, int H, int K, int e0,
+                                         int El, int lane) {
+  const int nch = H / 8;
+  for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
+    float acc[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int le = idx[n * K + k] - e0;
+      if (le < 0 || le >= El) continue;
+      const float w = p ? p[n * K + k] : 1.f;
+      const u32x4* z = reinterpret_cast<const u32x4*>(slots + (n * K + k) * int64_t(H));
+      u32x4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + q * 64 + lane;
+        v[q] = c < nch ? z[c] : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[q][2 * i] = fmaf(w, __uint_as_float(v[q][i] << 16), acc[q][2 * i]);
+          acc[q][2 * i + 1] = fmaf(w, __uint_as_float(v[q][i] & 0xFFFF0000u), acc[q][2 * i + 1]);
+        }
+    }
+    u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + q * 64 + lane;
+      if (c < nch)
+        d[c] = u32x4{pack_bf2(acc[q][0], acc[q][1]), pack_bf2(acc[q][2], acc[q][3]),
+                     pack_bf2(acc[q][4], acc[q][5]), pack_bf2(acc[q][6], acc[q][7])};
+    }
+  }
+}
+
+}  // namespace mok

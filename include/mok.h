@@ -1,0 +1,238 @@
+/*
+ * mok.h — C ABI of an MI355X (gfx950) implementation of one GPU's share of a deterministic
+ * fused Mixture-of-Experts layer: router top-k, schedule table, pull dispatch into a ring
+ * token buffer, grouped SwiGLU expert GEMM, push combine with a fixed-order weighted merge,
+ * and the backward pass with the router-weight gradient fused into SwiGLU backward.
+ *
+ * The layer is the one described on the "Mixture-of-Kittens (MoK)" pages ("Mixture-of-Kittens
+ * (MoK)"; "Cursor Open-Sources Mixture-of-Kittens (MoK): A Deterministic MoE Training
+ * Megakernel for GB300 NVL72 Racks"; "把 MoE 通信延迟从 103μs 压到 18μs：Cursor 开源 GPU
+ * 内核 MoK"). Each entry point below names the passage that defines its operation.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named *_dev, and every pointer inside mok_weights / mok_weight_grads, are device
+ *   pointers (HBM). mok_desc, mok_weights, mok_weight_grads and mok_sizes are host structs.
+ * - Ownership: the caller allocates and frees every buffer. The library never allocates
+ *   device memory and keeps no mutable global state; calls on different streams with
+ *   different buffers are independent.
+ * - Streams: every call is asynchronous and stream-ordered on `stream` (a hipStream_t passed
+ *   as void*; NULL is the default stream). No call synchronises the host or copies device
+ *   data to the host, except mok_device_status.
+ * - Errors: argument errors are detected on the host and returned before anything is
+ *   launched. A failed launch returns MOK_ERR_HIP. A device-side failure (a bounded wait that
+ *   ran out) is recorded in the workspace's error word and reported by mok_device_status.
+ * - Determinism: identical inputs give bit-identical outputs on every call. No reduction uses
+ *   floating-point atomics; every sum has a fixed order.
+ * - Segments: x_seg, out_seg, dout_seg and dx_seg are DEVICE arrays of S device pointers,
+ *   each to a BF16 [T][H] row-major block (token t of segment s is global token n = s*T + t).
+ *   They stand in for the peer ranks an expert-parallel layer pulls from.
+ * - Layouts: BF16 is stored as 16-bit patterns. Weights keep the reduction axis contiguous:
+ *   wg, wu [E_loc][I][H]; wd [E_loc][H][I]. Logits are fp32 [N][E]; topk_idx int32 [N][K];
+ *   topk_p fp32 [N][K]. A pair id is n*K + k.
+ */
+#ifndef MOK_H_
+#define MOK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOK_ABI_VERSION 1
+
+typedef enum {
+  MOK_OK = 0,
+  MOK_ERR_NULL = 1,            /* a required pointer is NULL                             */
+  MOK_ERR_SHAPE = 2,           /* a size is out of range or inconsistent                 */
+  MOK_ERR_DTYPE = 3,           /* unknown dtype, or a field the dtype needs is missing   */
+  MOK_ERR_ALIGN = 4,           /* a device pointer is not 16-byte aligned                */
+  MOK_ERR_WORKSPACE = 5,       /* reserved                                               */
+  MOK_ERR_RING = 6,            /* ring_bytes holds fewer than two minibatch slots        */
+  MOK_ERR_HIP = 7,             /* a HIP runtime call or kernel launch failed             */
+  MOK_ERR_DEVICE_TIMEOUT = 8,  /* a device-side bounded wait ran out (see ws error word) */
+  MOK_ERR_UNSUPPORTED = 9      /* not supported on this device                           */
+} mok_status;
+
+typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
+
+/* Debug flags (mok_desc.flags). */
+#define MOK_FLAG_SKIP_ONE_SIGNAL 0x1u  /* test only: withhold one ring signal so the bounded
+                                          wait must expire and report a device timeout     */
+
+/* Shapes and tunables of the layer, as the pages state it: hidden size, expert count, top-k,
+ * expert intermediate size, BF16 or MXFP8 ("Mixture-of-Kittens (MoK)", benchmark section;
+ * "把 MoE 通信延迟从 103μs 压到 18μs", section 03 part ②). */
+typedef struct {
+  int32_t hidden;              /* H; multiple of 128                                      */
+  int32_t num_experts;         /* E; 1..1024                                              */
+  int32_t top_k;               /* K; 1..min(E, 16)                                        */
+  int32_t intermediate;        /* I; multiple of 128                                      */
+  int32_t num_segments;        /* S >= 1 (stand-ins for peer ranks)                       */
+  int32_t tokens_per_segment;  /* T >= 1                                                  */
+  int32_t expert_begin;        /* e0: first local expert                                  */
+  int32_t num_local_experts;   /* E_loc: 1..64, e0 + E_loc <= E                           */
+  int32_t minibatch_tokens;    /* M: ring minibatch rows (MXFP8: multiple of 32); 0 = default */
+  int32_t comm_cus;            /* CUs given to dispatch/combine in the fused kernels;
+                                  0 = library default                                     */
+  int64_t ring_bytes;          /* size of the caller's ring token buffer                  */
+  int32_t dtype;               /* mok_dtype                                               */
+  uint32_t flags;              /* MOK_FLAG_*                                              */
+} mok_desc;
+
+/* Buffer sizes for a descriptor. Everything is sized from host-known bounds only
+ * (rows_max = N * min(K, E_loc), plus row padding in MXFP8 mode), so no call needs to read a
+ * device-side count back to the host. */
+typedef struct {
+  size_t saved_bytes;    /* schedule table; written by mok_schedule / mok_layer_fwd, read by
+                            every later stage and by mok_layer_bwd                          */
+  size_t ws_bytes;       /* scratch of one call (counters, error word, tile tables, ...)   */
+  size_t slots_bytes;    /* push/receive buffer Z: N*K rows of H BF16, indexed by pair id   */
+  size_t xd_bytes;       /* staged path: dispatched rows in expert order                    */
+  size_t act_bytes;      /* staged path: g|u and h per dispatched row                       */
+  size_t wq_bytes;       /* MXFP8: one quantised weight tensor (codes + scales)             */
+  int64_t rows_max;      /* bound on expert-order rows                                       */
+  int32_t ring_slots;    /* R = ring_bytes / slot bytes (fused path)                        */
+  int32_t minibatch;     /* M actually used (after the default is applied)                  */
+  int64_t slot_bytes;    /* bytes of one ring slot                                          */
+  /* Layout of the schedule table inside `saved` (byte offsets). Words 0..191 are a header:
+   * [0] P (local pairs), [1] rows (P plus MXFP8 padding), [2] U (touched tokens),
+   * [16 + e] count of local expert e, [96 + e] first row of expert e (e = 0..E_loc). */
+  int64_t perm_offset;    /* int32 [rows_max]: expert-order row -> pair id (-1: pad row)     */
+  int64_t tokpos_offset;  /* int32 [N*K]: pair id -> row (-1: not local)                     */
+  int64_t touched_offset; /* int32 [N]: tokens with a local pair, ascending (first U valid)  */
+} mok_sizes;
+
+/* Expert weights (device pointers). BF16 mode uses wg/wu/wd only. MXFP8 mode uses E4M3 codes
+ * with UE8M0 scales per 32 elements along each GEMM's reduction axis, produced by
+ * mok_quantize_mx:
+ *   forward : wg_q/wg_s, wu_q/wu_s = Wg, Wu [E_loc][I][H] blocked along H;
+ *             wd_q/wd_s = Wd [E_loc][H][I] blocked along I;
+ *   backward: wgt_q/wgt_s, wut_q/wut_s = Wg^T, Wu^T [E_loc][H][I] blocked along I;
+ *             wdt_q/wdt_s = Wd^T [E_loc][I][H] blocked along H.
+ * Codes have the shape of the matrix, scales the shape with the last axis divided by 32. */
+typedef struct {
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const uint8_t *wg_q, *wg_s, *wu_q, *wu_s, *wd_q, *wd_s;
+  const uint8_t *wgt_q, *wgt_s, *wut_q, *wut_s, *wdt_q, *wdt_s;
+} mok_weights;
+
+/* Weight gradients, fp32, same layouts as the BF16 weights. Fully overwritten. */
+typedef struct {
+  float* dwg;
+  float* dwu;
+  float* dwd;
+} mok_weight_grads;
+
+int mok_abi_version(void);
+const char* mok_status_str(mok_status s);
+
+/* Validate `desc` and report every buffer size. Host only; launches nothing. */
+mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes);
+
+/* Two-wave minibatch floor: the smallest minibatch for which the gate/up grouped GEMM
+ * (N = 2*I columns) gives every one of `cus` compute units at least two tiles of
+ * tile_m x tile_n. The pages size minibatches this way ("Mixture-of-Kittens (MoK)", section
+ * on overlap granularity; "把 MoE 通信延迟从 103μs 压到 18μs", section 03 part ②). Host only. */
+int64_t mok_two_wave_floor(int32_t cus, int32_t tile_m, int32_t tile_n, int32_t intermediate);
+
+/* Router top-k + gating + schedule table ("把 MoE 通信延迟从 103μs 压到 18μs", section 02:
+ * the router decides each token's experts, then the table counts tokens per expert, fixes
+ * their rows on the receiving side and keeps each expert's rows contiguous; "Mixture-of-Kittens
+ * (MoK)", section on pull dispatch: one table serves all four transfer operations).
+ *   logits_dev   fp32 [N][E]
+ *   topk_idx_dev int32 [N][K] out: experts by descending logit, ties to the lower id
+ *   topk_p_dev   fp32 [N][K] out: softmax over the K selected logits
+ *   saved_dev    out: counts, offsets, row -> pair map (perm), pair -> row map (tokpos),
+ *                touched-token list; P, U and J stay on the device
+ *   ws_dev       scratch (ws_bytes) */
+mok_status mok_schedule(const mok_desc* desc, const float* logits_dev, int32_t* topk_idx_dev,
+                        float* topk_p_dev, void* saved_dev, void* ws_dev, void* stream);
+
+/* Pull dispatch, staged form: the receiving side reads every routed token row from its
+ * source segment and writes it in expert order ("Mixture-of-Kittens (MoK)", section on pull
+ * dispatch; "把 MoE 通信延迟从 103μs 压到 18μs", section 03 part ①). In MXFP8 mode each row is
+ * quantised along H on the way (same page, section 03 part ③).
+ *   x_seg_dev  device array of S pointers to BF16 [T][H]
+ *   xd_dev     out, xd_bytes: BF16 [rows_max][H], or (MXFP8) codes [rows_max][H] followed by
+ *              scales [rows_max][H/32]; only rows < rows(P) are written */
+mok_status mok_dispatch(const mok_desc* desc, const void* saved_dev,
+                        const void* const* x_seg_dev, void* xd_dev, void* ws_dev, void* stream);
+
+/* Grouped SwiGLU expert FFN, staged form, with the push-combine epilogue: for each local
+ * expert over its rows, g = x Wg^T, u = x Wu^T, h = silu(g) u, y = h Wd^T; y is written in
+ * BF16 to slots[pair id] (the token's receive slot) ("把 MoE 通信延迟从 103μs 压到 18μs",
+ * section 03 parts ① and ②).
+ *   xd_dev     from mok_dispatch
+ *   act_dev    out, act_bytes: g|u BF16 [rows_max][2I] then h ([rows_max][I] BF16, or MXFP8
+ *              codes [rows_max][I] + scales [rows_max][I/32])
+ *   slots_dev  out: BF16 [N*K][H]; only local pairs' rows are written */
+mok_status mok_expert_ffn(const mok_desc* desc, const void* saved_dev, const void* xd_dev,
+                          const mok_weights* w, void* act_dev, void* slots_dev, void* ws_dev,
+                          void* stream);
+
+/* Final weighted merge ("把 MoE 通信延迟从 103μs 压到 18μs", section 04: the benchmarked layer
+ * ends with it): out[n] = bf16( sum over k ascending with idx[n,k] local of
+ * p[n,k] * float(slots[n*K+k]) ) for every token with at least one local pair. With
+ * topk_p_dev == NULL the sum is unweighted (the input-gradient merge of backward).
+ * Rows of tokens with no local pair are not written. */
+mok_status mok_combine(const mok_desc* desc, const void* saved_dev, const int32_t* topk_idx_dev,
+                       const float* topk_p_dev, const void* slots_dev, void* const* out_seg_dev,
+                       void* ws_dev, void* stream);
+
+/* Fused forward: schedule, then one persistent kernel whose compute units are split between
+ * dispatch/combine workers and GEMM workers, coordinated through counters in HBM with no
+ * host synchronisation; tokens flow through the fixed-size ring in minibatches of M rows
+ * ("把 MoE 通信延迟从 103μs 压到 18μs", section 03 parts ② and ③; "Mixture-of-Kittens (MoK)",
+ * section on the ring token buffer). Outputs as mok_schedule + mok_combine. The ring keeps
+ * the last R minibatches' X, g|u and h for mok_layer_bwd. */
+mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
+                         const float* logits_dev, const mok_weights* w,
+                         void* const* out_seg_dev, int32_t* topk_idx_dev, float* topk_p_dev,
+                         void* saved_dev, void* ring_dev, void* slots_dev, void* ws_dev,
+                         void* stream);
+
+/* Fused backward of L = sum_n <dOut[n], out[n]>, walking the ring in reverse so the
+ * minibatches still resident after the forward are not replayed ("Mixture-of-Kittens (MoK)",
+ * section on the ring token buffer; "Cursor Open-Sources Mixture-of-Kittens (MoK)",
+ * Technical Details). Per minibatch: pull dOut rows (reverse combine), a = dOut Wd_e with
+ * dp = <a, h>, dh = p a and SwiGLU backward fused in the epilogue (the router-weight
+ * gradient inside SwiGLU backward, "Mixture-of-Kittens (MoK)", benchmark section),
+ * dx = dg Wg_e + du Wu_e pushed to slots[pair id], and the weight gradients. Then the dX
+ * merge over k ascending and, when E_loc == E, dlogits.
+ *   dp_dev       fp32 [N][K], written at local pairs only
+ *   dlogits_dev  fp32 [N][E] or NULL; must be NULL unless E_loc == E
+ *   g            weight gradients, fully overwritten
+ * saved_dev and ring_dev must hold the state the matching mok_layer_fwd left. */
+mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
+                         const void* const* x_seg_dev, const mok_weights* w,
+                         const int32_t* topk_idx_dev, const float* topk_p_dev,
+                         const void* saved_dev, void* ring_dev, void* slots_dev,
+                         void* const* dx_seg_dev, float* dp_dev, float* dlogits_dev,
+                         const mok_weight_grads* g, void* ws_dev, void* stream);
+
+/* MXFP8 quantiser (OCP MX v1.0: E4M3 codes, one UE8M0 scale per 32 elements; shared scale
+ * 2^(floor(log2 amax) - 8), round to nearest even, saturate to +-448, amax 0 -> scale 0).
+ * Quantises `batch` BF16 matrices [rows][cols]. transpose == 0: blocks run along cols, codes
+ * [batch][rows][cols], scales [batch][rows][cols/32]. transpose == 1: the output is the
+ * transposed matrix blocked along the input's rows: codes [batch][cols][rows], scales
+ * [batch][cols][rows/32]. The blocked axis must be a multiple of 32. */
+mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void* src_dev,
+                           int32_t transpose, uint8_t* codes_dev, uint8_t* scales_dev,
+                           void* stream);
+
+/* Waits for `stream`, then reads the workspace error word. The only synchronising call. */
+mok_status mok_device_status(const void* ws_dev, void* stream, mok_status* out);
+
+/* Number of compute units of the current device (0 if unknown). */
+int32_t mok_device_cus(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOK_H_ */

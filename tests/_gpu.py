@@ -1,0 +1,85 @@
+"""Helpers for the GPU parity tests: move datagen's arrays to the device, run libmok through its
+binding, and bring results back as numpy arrays in the oracle's conventions."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import combine_router_top_schedule_amd as mok
+import datagen
+from combine_router_top_schedule_amd.layer import MokLayer
+from oracle import moe_oracle as mo
+
+
+def dev_u16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def bf16_to_f64(a: np.ndarray) -> np.ndarray:
+    return mo.decode_bf16(a)
+
+
+class Case:
+    """Device inputs and a MokLayer for one datagen config."""
+
+    def __init__(self, cfg: datagen.Config, M=None, ring_bytes=None, staged=True, fused=False,
+                 with_dout=False, logits=None, flags=0):
+        self.cfg = cfg
+        self.d = mok.desc_from_config(cfg, M=M, ring_bytes=ring_bytes, flags=flags)
+        self.layer = MokLayer(self.d, staged=staged, fused=fused)
+        self.logits_h = datagen.logits(cfg) if logits is None else logits
+        self.x_h = datagen.x_all(cfg)
+        self.w_h = datagen.weights(cfg)
+        self.logits = torch.from_numpy(self.logits_h).cuda()
+        self.x = dev_u16(self.x_h)
+        self.x_seg = self.layer.segs(self.x)
+        self.wg, self.wu, self.wd = (dev_u16(self.w_h[k]) for k in ("wg", "wu", "wd"))
+        self.layer.set_weights(self.wg, self.wu, self.wd)
+        self.out = torch.zeros((cfg.N, cfg.H), dtype=torch.int16, device="cuda")
+        self.out_seg = self.layer.segs(self.out)
+        if with_dout:
+            self.dout_h = datagen.dout_all(cfg)
+            self.dout = dev_u16(self.dout_h)
+            self.dout_seg = self.layer.segs(self.dout)
+
+    # ---- oracle --------------------------------------------------------------------------
+    def oracle_weights(self):
+        return mo.weights_from_bits(self.w_h, self.cfg.dtype)
+
+    def oracle_forward(self, tokens=None):
+        """Oracle forward on all tokens, or only on `tokens` (outputs are per token)."""
+        cfg = self.cfg
+        W = self.oracle_weights()
+        if tokens is None:
+            return mo.forward(mo.bf16_rows(self.x_h), self.logits_h, W, cfg.K, cfg.e0, cfg.E_loc,
+                              cfg.M, 32 if cfg.dtype == "mxfp8" else 1)
+        tokens = np.asarray(tokens)
+        return mo.forward(lambda r: mo.decode_bf16(self.x_h[tokens[r]]), self.logits_h[tokens], W,
+                          cfg.K, cfg.e0, cfg.E_loc, cfg.M, 32 if cfg.dtype == "mxfp8" else 1)
+
+    # ---- results ---------------------------------------------------------------------------
+    def idx_p(self):
+        K = self.cfg.K
+        return (self.layer.idx.cpu().numpy().reshape(-1, K),
+                self.layer.p.cpu().numpy().reshape(-1, K))
+
+    def out_rows(self, tokens):
+        return bf16_to_f64(host_u16(self.out)[np.asarray(tokens)])
+
+
+def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref| (the BF16 tolerance metric)."""
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def frob_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_F / ||ref||_F (the MXFP8 tolerance metric)."""
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+BF16_TOL = 1e-2      # max |err| <= 1e-2 * max |ref|
+MX_TOL = 3e-2        # relative Frobenius error
