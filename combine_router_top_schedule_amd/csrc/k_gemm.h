@@ -3,7 +3,7 @@
 // per row (64 BF16 or 128 E4M3 values), double-buffered in LDS.
 //
 // Both operands are staged "K-contiguous": LDS holds [256 rows][128 bytes] per stage, 16-byte
-// chunks XOR-swizzled by (row & 7) so the MFMA fragment reads (32 rows at one chunk per
+// chunks XOR-swizzled per row (swz) so the MFMA fragment reads (32 rows at one chunk per
 // half-wave) are free of bank conflicts. Stages are filled by buffer loads that write LDS
 // directly, issued one stage ahead of the MFMA work.
 //
@@ -12,6 +12,8 @@
 // l%32. Lanes 0-31 and 32-63 carry the two K-halves of each BF16 operand fragment; the fp8
 // layout is described at mma_stage_mx.
 #pragma once
+
+#include <type_traits>
 
 #include "mok_device.h"
 #include "mok_internal.h"
@@ -29,8 +31,14 @@ struct GemmLds {
 };
 constexpr size_t kGemmLdsBytes = sizeof(GemmLds);
 
+// Physical chunk of logical 16-byte chunk `chunk` in row `row`: chunk ^ f(row) with
+// f(row) = (row & 7) ^ ((row >> 3) & 1). Any 8 consecutive rows, and the 8 even (or odd) rows
+// of any aligned 16-row group, then occupy 8 different chunk positions, so a half-wave reading
+// one chunk of 32 consecutive rows is free of bank conflicts whether the LDS serves 8 or 16
+// lanes of a 16-byte read per cycle (measured: 2-way conflicts with f(row) = row & 7).
+__device__ __forceinline__ int swz_f(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kStageRowBytes + ((chunk ^ (row & 7)) << 4);
+  return row * kStageRowBytes + ((chunk ^ swz_f(row)) << 4);
 }
 
 // Hide a value from loop-invariant code motion: persistent kernels would otherwise hoist
@@ -74,18 +82,20 @@ __device__ __forceinline__ int wave_id() {
 
 // Issue the loads of stage kt (128 bytes of every row, and in MXFP8 mode the 4 scale bytes of
 // every row) into one LDS stage. Wave w covers rows 64w .. 64w+63: 8 loads of 8 rows x 128
-// bytes. Lane L of a load lands at LDS offset 16*L: row 8c + L/8, physical chunk L%8, which
-// holds the logical chunk (L%8) ^ (row & 7) of the swizzled layout.
+// bytes. Lane L of load c lands at LDS offset 16*L: row 64w + 8c + L/8, physical chunk L%8,
+// which holds the logical chunk (L%8) ^ f(row) of the swizzled layout, where
+// f(row) = (L/8) ^ (c & 1) because 64w + 8c is a multiple of 8.
 __device__ __forceinline__ void issue_stage(const Operand& op, uint8_t* lds, uint32_t* lds_s, int kt,
                                             bool mx) {
   const int w = wave_id(), L = threadIdx.x & 63;
-  const int lchunk = (L & 7) ^ (L >> 3);
+  const int lchunk0 = (L & 7) ^ (L >> 3);
   const bool odd = op.interleave && (w & 1);
   const __amdgpu_buffer_rsrc_t r = odd ? op.r1 : op.r0;
   const int rbase = op.interleave ? (w >> 1) * 64 : w * 64;   // first row inside the matrix
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const int lrow = rbase + 8 * c + (L >> 3);
+    const int lchunk = lchunk0 ^ (c & 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + (w * 64 + 8 * c) * kStageRowBytes),
                                              16, lrow * op.stride + kt * kStageRowBytes + lchunk * 16,
                                              0, 0, 0);
@@ -97,70 +107,90 @@ __device__ __forceinline__ void issue_stage(const Operand& op, uint8_t* lds, uin
   }
 }
 
-// ---- one LDS stage of MFMA work -----------------------------------------------------------
-__device__ __forceinline__ void mma_stage_bf16(const uint8_t* A, const uint8_t* B, f32x16 (&acc)[4][4],
-                                               int wm, int wn, int lane) {
+// ---- MFMA fragments ------------------------------------------------------------------------
+// One "kk" step is one MFMA K-slice: 16 BF16 (32x32x16) or 64 E4M3 (32x32x64). A stage of 128
+// bytes per row holds 4 BF16 slices or 2 E4M3 slices. Fragments of slice kk+1 are loaded from
+// LDS while the 16 MFMAs of slice kk run, so LDS latency hides under matrix work.
+struct FragBF16 {
+  bf16x8 a[4], b[4];
+};
+struct FragMX {
+  i32x8 a[4], b[4];
+  int sa[4], sb[4];
+};
+
+__device__ __forceinline__ void load_frag(FragBF16& f, const uint8_t* A, const uint8_t* B,
+                                          const uint32_t*, const uint32_t*, int kk, int wm, int wn,
+                                          int lane) {
+  const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8 a[4], b[4];
-    const int ch = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + i * 32 + (lane & 31), ch));
-      b[i] = *reinterpret_cast<const bf16x8*>(B + swz(wn * 128 + i * 32 + (lane & 31), ch));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int i = 0; i < 4; ++i) {
+    f.a[i] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + i * 32 + (lane & 31), ch));
+    f.b[i] = *reinterpret_cast<const bf16x8*>(B + swz(wn * 128 + i * 32 + (lane & 31), ch));
   }
 }
 
-__device__ __forceinline__ void mma_stage_mx(const uint8_t* A, const uint8_t* B, const uint32_t* As,
-                                             const uint32_t* Bs, f32x16 (&acc)[4][4], int wm,
-                                             int wn, int lane) {
+// E4M3 slice kk covers MX blocks 2kk and 2kk+1. Lane half h carries elements 16h..16h+15 of
+// block 2kk in bytes 0-15 and of block 2kk+1 in bytes 16-31, and its scale byte is that of
+// block 2kk+h (checked on gfx950).
+__device__ __forceinline__ void load_frag(FragMX& f, const uint8_t* A, const uint8_t* B,
+                                          const uint32_t* As, const uint32_t* Bs, int kk, int wm,
+                                          int wn, int lane) {
+  const int h = lane >> 5;
+  const int blk = kk * 2 + h;
+  const int ch0 = kk * 4 + h, ch1 = kk * 4 + 2 + h;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    i32x8 a[4], b[4];
-    int sa[4], sb[4];
-    // One instruction consumes 64 K = MX blocks 2kk and 2kk+1. Lane half h carries elements
-    // 16h..16h+15 of block 2kk in bytes 0-15 and of block 2kk+1 in bytes 16-31, and its scale
-    // byte is that of block 2kk+h (checked on gfx950).
-    const int h = lane >> 5;
-    const int blk = kk * 2 + h;
-    const int ch0 = kk * 4 + h, ch1 = kk * 4 + 2 + h;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + i * 32 + (lane & 31);
-      const int rb = wn * 128 + i * 32 + (lane & 31);
-      u32x4 a0 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch0));
-      u32x4 a1 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch1));
-      u32x4 b0 = *reinterpret_cast<const u32x4*>(B + swz(rb, ch0));
-      u32x4 b1 = *reinterpret_cast<const u32x4*>(B + swz(rb, ch1));
-      a[i] = i32x8{int(a0[0]), int(a0[1]), int(a0[2]), int(a0[3]),
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + (lane & 31);
+    const int rb = wn * 128 + i * 32 + (lane & 31);
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch0));
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch1));
+    const u32x4 b0 = *reinterpret_cast<const u32x4*>(B + swz(rb, ch0));
+    const u32x4 b1 = *reinterpret_cast<const u32x4*>(B + swz(rb, ch1));
+    f.a[i] = i32x8{int(a0[0]), int(a0[1]), int(a0[2]), int(a0[3]),
                    int(a1[0]), int(a1[1]), int(a1[2]), int(a1[3])};
-      b[i] = i32x8{int(b0[0]), int(b0[1]), int(b0[2]), int(b0[3]),
+    f.b[i] = i32x8{int(b0[0]), int(b0[1]), int(b0[2]), int(b0[3]),
                    int(b1[0]), int(b1[1]), int(b1[2]), int(b1[3])};
-      sa[i] = int((As[ra] >> (8 * blk)) & 0xFFu);
-      sb[i] = int((Bs[rb] >> (8 * blk)) & 0xFFu);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0,
-                                                                    0, sa[i], 0, sb[j]);
+    f.sa[i] = int((As[ra] >> (8 * blk)) & 0xFFu);
+    f.sb[i] = int((Bs[rb] >> (8 * blk)) & 0xFFu);
   }
 }
+
+__device__ __forceinline__ void mma(const FragBF16& f, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma(const FragMX& f, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0,
+                                                                  0, f.sa[i], 0, f.sb[j]);
+}
+
+// s_waitcnt with only the vector-memory counter at zero (gfx9 encoding: expcnt and lgkmcnt
+// fields left at their maxima), so fragment reads from LDS stay in flight.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---- the tile loop -----------------------------------------------------------------------
-// Runs the K loop of one output tile; on return acc holds the fp32 tile (no split-K, stages
-// in ascending K order, so the result depends only on the operands).
+// Runs the K loop of one output tile; on return acc holds the fp32 tile (no split-K, slices
+// in ascending K order, so the result depends only on the operands). Per stage: issue the
+// next stage's buffer loads, then for each slice load the next slice's fragments and run the
+// current slice's MFMAs; the stage barrier sits before the last slice, so the first fragments
+// of the next stage also load under MFMA work. After return every LDS read of the stage
+// buffers has completed (the last barrier precedes the last slice's MFMAs, whose fragments
+// are already in registers), so the caller may reuse the LDS.
 template <bool MX>
 __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const Operand& B,
                                           int ksteps, f32x16 (&acc)[4][4], int wm, int wn,
                                           int lane) {
+  using Frag = typename std::conditional<MX, FragMX, FragBF16>::type;
+  constexpr int KK = MX ? 2 : 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -171,16 +201,34 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
   issue_stage(B, sm.b[0], sm.bs[0], 0, MX);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  Frag f[2];
+  load_frag(f[0], sm.a[0], sm.b[0], sm.as[0], sm.bs[0], 0, wm, wn, lane);
   for (int kt = 0; kt < ksteps; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < ksteps) {
+    const bool more = kt + 1 < ksteps;
+    if (more) {
       issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX);
       issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX);
     }
-    if (MX) mma_stage_mx(sm.a[cur], sm.b[cur], sm.as[cur], sm.bs[cur], acc, wm, wn, lane);
-    else mma_stage_bf16(sm.a[cur], sm.b[cur], acc, wm, wn, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      // Scheduling fences keep each phase whole: the compiler would otherwise interleave the
+      // MFMAs of slice kk with the fragment reads of slice kk+1 and wait on those reads.
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < KK) {
+        load_frag(f[(kk + 1) & 1], sm.a[cur], sm.b[cur], sm.as[cur], sm.bs[cur], kk + 1, wm, wn,
+                  lane);
+      } else {
+        wait_vmem();
+        __syncthreads();
+        if (more)
+          load_frag(f[(kk + 1) & 1], sm.a[cur ^ 1], sm.b[cur ^ 1], sm.as[cur ^ 1], sm.bs[cur ^ 1],
+                    0, wm, wn, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f[kk & 1], acc);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

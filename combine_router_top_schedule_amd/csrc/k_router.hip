@@ -7,7 +7,7 @@
 // ("Mixture-of-Kittens (MoK)", section on pull dispatch).
 //
 // Two kernels, no host synchronisation:
-//  1. k_topk_scan: one wave per token computes top-k and the softmax gate; the block then
+//  1. k_topk_scan: one thread per token computes top-k and the softmax gate; the block then
 //     counts, per local expert, the pairs of its 256 tokens (ballot + popcount, an LDS
 //     histogram per wave) and joins a single-pass decoupled look-back scan over blocks
 //     (Merrill & Garland, 2016) that yields each pair's rank inside its expert, in ascending
@@ -27,25 +27,6 @@ constexpr uint32_t kFlagInc = 2u << 30;
 constexpr uint32_t kValMask = (1u << 30) - 1;
 constexpr int kSpinLimit = 1 << 22;
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);   // -0.0 ties with +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor(uint32_t(v), off, 64);
-    uint32_t hi = __shfl_xor(uint32_t(v >> 32), off, 64);
-    uint64_t o = (uint64_t(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 struct RouterArgs {
   const float* logits;
   int32_t* idx;
@@ -60,11 +41,32 @@ struct RouterArgs {
   int E, K, e0, El, row_align, nblocks;
 };
 
-template <int CPL>
+// Insert (x, e) into a top-KM list held in registers, ordered by (value descending, expert id
+// ascending): one bubble pass that keeps the element ranking first at each position and
+// carries the other one down. Comparing ids on equal values keeps ties in expert order also
+// for elements that are carried down.
+template <int KM>
+__device__ __forceinline__ void topk_insert(float (&v)[KM], int (&id)[KM], float x, int e) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    const bool c = x > v[j] || (x == v[j] && e < id[j]);
+    const float vj = v[j];
+    const int ij = id[j];
+    v[j] = c ? x : vj;
+    id[j] = c ? e : ij;
+    x = c ? vj : x;
+    e = c ? ij : e;
+  }
+}
+
+// One thread per token: the block's 256 tokens stream their logits through LDS in chunks of
+// 32 experts (coalesced 128-byte row pieces in, conflict-free column reads out), and each
+// thread keeps its token's top-KM in registers.
+template <int KM>
 __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   __shared__ int s_b;
+  __shared__ float s_l[kTopkTokensPerBlock][33];
   __shared__ uint64_t s_mask[kTopkTokensPerBlock];
-  __shared__ uint16_t s_idx[kTopkTokensPerBlock][kMaxTopK];
   __shared__ int s_wcnt[4][kMaxLocalExperts + 1];
   __shared__ int s_excl[kMaxLocalExperts + 1];
 
@@ -73,54 +75,77 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   __syncthreads();
   const int b = s_b;
   const int64_t n_base = int64_t(b) * kTopkTokensPerBlock;
+  const int64_t n_me = n_base + tid;
 
-  // ---- top-k + gating, one wave per token; lane l holds experts l, l+64, ... ----
-  for (int i = 0; i < 64; ++i) {
-    const int slot = wave * 64 + i;
-    const int64_t n = n_base + slot;
-    if (n >= a.N) {
-      if (lane == 0) s_mask[slot] = 0;
-      continue;
-    }
-    uint32_t keys[CPL];
-    const float* row = a.logits + n * a.E;
+  float v[KM];
+  int id[KM];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      int e = lane + 64 * c;
-      keys[c] = e < a.E ? order_key(row[e]) : 0u;
-    }
-    float l0 = 0.f, sum = 0.f, my_l = 0.f;
-    int my_e = 0;
-    uint64_t mask = 0;
-    for (int k = 0; k < a.K; ++k) {
-      // Composite key: ordered logit, then the complement of the expert id, so the maximum is
-      // the largest logit with ties to the lower id.
-      uint64_t best = 0;
+  for (int j = 0; j < KM; ++j) { v[j] = -INFINITY; id[j] = 0x7FFFFFFF; }
+  const bool vec4 = (a.E & 3) == 0;
+  for (int c0 = 0; c0 < a.E; c0 += 32) {
+    // Thread t covers rows t/8 + 32q, experts c0 + 4*(t%8) .. +3. Every load is issued
+    // unconditionally from a clamped (in-bounds) address and masked afterwards, so all eight
+    // rows' loads are in flight together.
+    float4 val[8];
+    const int col = c0 + 4 * (tid & 7);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        uint64_t cand = keys[c] ? ((uint64_t(keys[c]) << 32) | uint32_t(~(lane + 64 * c))) : 0;
-        best = cand > best ? cand : best;
+    for (int q = 0; q < 8; ++q) {
+      const int64_t n = min(n_base + (tid >> 3) + 32 * q, a.N - 1);
+      if (vec4) {
+        const int cc = min(col, a.E - 4);
+        val[q] = *reinterpret_cast<const float4*>(a.logits + n * a.E + cc);
+      } else {
+        val[q].x = a.logits[n * a.E + min(col, a.E - 1)];
+        val[q].y = a.logits[n * a.E + min(col + 1, a.E - 1)];
+        val[q].z = a.logits[n * a.E + min(col + 2, a.E - 1)];
+        val[q].w = a.logits[n * a.E + min(col + 3, a.E - 1)];
       }
-      best = wave_max_u64(best);
-      const int we = int(~uint32_t(best));
-      const float wl = key_value(uint32_t(best >> 32));
+    }
 #pragma unroll
-      for (int c = 0; c < CPL; ++c)
-        if (lane + 64 * c == we) keys[c] = 0u;
-      if (k == 0) l0 = wl;
-      sum += expf(wl - l0);                    // fixed order k = 0, 1, ... on every lane
-      if (lane == k) { my_l = wl; my_e = we; }
-      const int le = we - a.e0;
-      if (le >= 0 && le < a.El) mask |= 1ull << le;
+    for (int q = 0; q < 8; ++q) {
+      const int r = (tid >> 3) + 32 * q;
+      const bool rok = n_base + r < a.N;
+      s_l[r][4 * (tid & 7) + 0] = (rok && col + 0 < a.E) ? val[q].x : -INFINITY;
+      s_l[r][4 * (tid & 7) + 1] = (rok && col + 1 < a.E) ? val[q].y : -INFINITY;
+      s_l[r][4 * (tid & 7) + 2] = (rok && col + 2 < a.E) ? val[q].z : -INFINITY;
+      s_l[r][4 * (tid & 7) + 3] = (rok && col + 3 < a.E) ? val[q].w : -INFINITY;
     }
-    // p_k = exp(l_k - l_0) / sum_j exp(l_j - l_0)
-    if (lane < a.K) {
-      a.idx[n * a.K + lane] = my_e;
-      a.p[n * a.K + lane] = expf(my_l - l0) / sum;
-      s_idx[slot][lane] = uint16_t(my_e);
+    __syncthreads();
+    const int ce = min(32, a.E - c0);
+    if (ce == 32) {
+#pragma unroll 8
+      for (int u = 0; u < 32; ++u) {
+        float x = s_l[tid][u];
+        x = x == 0.f ? 0.f : x;               // -0.0 ties with +0.0
+        topk_insert<KM>(v, id, x, c0 + u);
+      }
+    } else {
+      for (int u = 0; u < ce; ++u) {
+        float x = s_l[tid][u];
+        x = x == 0.f ? 0.f : x;
+        topk_insert<KM>(v, id, x, c0 + u);
+      }
     }
-    if (lane == 0) s_mask[slot] = mask;
+    __syncthreads();
   }
+  uint64_t mask = 0;
+  if (n_me < a.N) {
+    // p_k = exp(l_k - l_0) / sum_j exp(l_j - l_0), fp32, k ascending
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < KM; ++k)
+      if (k < a.K) sum += expf(v[k] - v[0]);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+      if (k < a.K) {
+        a.idx[n_me * a.K + k] = id[k];
+        a.p[n_me * a.K + k] = expf(v[k] - v[0]) / sum;
+        const int le = id[k] - a.e0;
+        if (le >= 0 && le < a.El) mask |= 1ull << le;
+      }
+    }
+  }
+  s_mask[tid] = mask;
   __syncthreads();
 
   // ---- per-block counts per local expert (value El counts touched tokens) ----
@@ -133,37 +158,49 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   }
   __syncthreads();
 
-  // ---- single-pass decoupled look-back, one lane per counted value ----
-  if (wave == 0 && lane <= a.El) {
-    const int e = lane;
+  // ---- single-pass decoupled look-back ----
+  // Publish this block's aggregates, then each wave takes counted values e = wave, wave+4, ...
+  // and inspects predecessors 64 at a time (lane i looks at block base - i): the nearest
+  // inclusive prefix ends the walk; aggregates before it are summed; an unpublished
+  // predecessor makes the wave re-read the window (bounded).
+  if (tid <= a.El) {
+    const uint32_t agg = uint32_t(s_wcnt[0][tid] + s_wcnt[1][tid] + s_wcnt[2][tid] + s_wcnt[3][tid]);
+    st_relaxed_u(a.state + int64_t(b) * (a.El + 1) + tid, (b == 0 ? kFlagInc : kFlagAgg) | agg);
+  }
+  for (int e = wave; e <= a.El; e += 4) {
     const uint32_t agg = uint32_t(s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e]);
-    uint32_t* my = a.state + int64_t(b) * (a.El + 1) + e;
     uint32_t excl = 0;
-    if (b == 0) {
-      st_release_u(my, kFlagInc | agg);
-    } else {
-      st_release_u(my, kFlagAgg | agg);
-      int pred = b - 1;
-      int spins = 0;
-      while (pred >= 0) {
-        uint32_t w = ld_acquire_u(a.state + int64_t(pred) * (a.El + 1) + e);
-        if ((w & ~kValMask) == 0) {
-          if (++spins > kSpinLimit) { set_error(a.err, MOK_ERR_DEVICE_TIMEOUT); break; }
-          __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        excl += w & kValMask;
-        if ((w & ~kValMask) == kFlagInc) break;
-        --pred;
+    int base = b - 1;
+    int spins = 0;
+    while (base >= 0) {
+      const int j = base - lane;
+      const uint32_t w = j >= 0 ? ld_relaxed_u(a.state + int64_t(j) * (a.El + 1) + e) : kFlagInc;
+      const uint32_t flag = w & ~kValMask;
+      const uint64_t inc = __ballot(flag == kFlagInc);
+      const uint64_t inv = __ballot(flag == 0);
+      const int first = inc ? __builtin_ctzll(inc) : 64;          // nearest inclusive prefix
+      const uint64_t upto = first >= 63 ? ~0ull : ((2ull << first) - 1);   // lanes 0..first
+      if (inv & upto & (first == 64 ? ~0ull : upto)) {            // a nearer block unpublished
+        if (++spins > kSpinLimit) { set_error(a.err, MOK_ERR_DEVICE_TIMEOUT); break; }
+        __builtin_amdgcn_s_sleep(1);
+        continue;
       }
-      st_release_u(my, kFlagInc | (excl + agg));
+      uint32_t part = (uint64_t(1) << lane) & upto ? (w & kValMask) : 0u;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      excl += part;
+      if (first < 64) break;
+      base -= 64;
     }
-    s_excl[e] = int(excl);
-    if (b == a.nblocks - 1) {
-      // Last block: inclusive values are the totals.
-      const int total = int(excl + agg);
-      if (e < a.El) a.hdr[kHdrCounts + e] = total;
-      else a.hdr[kHdrU] = total;
+    if (lane == 0) {
+      if (b > 0) st_relaxed_u(a.state + int64_t(b) * (a.El + 1) + e, kFlagInc | (excl + agg));
+      s_excl[e] = int(excl);
+      if (b == a.nblocks - 1) {
+        // Last block: inclusive values are the totals.
+        const int total = int(excl + agg);
+        if (e < a.El) a.hdr[kHdrCounts + e] = total;
+        else a.hdr[kHdrU] = total;
+      }
     }
   }
   __syncthreads();
@@ -179,7 +216,7 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
       if (e < a.El) {
         int k = 0;
         for (int q = 0; q < a.K; ++q)
-          if (int(s_idx[tid][q]) == a.e0 + e) k = q;
+          if (a.idx[n * a.K + q] == a.e0 + e) k = q;
         a.rank[n * a.K + k] = r;
       } else if (r < a.N) {
         a.touched[r] = int32_t(n);
@@ -283,12 +320,11 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
                reinterpret_cast<int32_t*>(saved + L.sv_touched),
                state, wsh + kWsTicket, wsh + kWsError,
                L.N, L.E, L.K, L.e0, L.El, L.row_align, L.topk_blocks};
-  const int cpl = (L.E + 63) / 64;
-  if (cpl <= 1) hipLaunchKernelGGL(k_topk_scan<1>, dim3(L.topk_blocks), dim3(256), 0, s, a);
-  else if (cpl <= 2) hipLaunchKernelGGL(k_topk_scan<2>, dim3(L.topk_blocks), dim3(256), 0, s, a);
-  else if (cpl <= 4) hipLaunchKernelGGL(k_topk_scan<4>, dim3(L.topk_blocks), dim3(256), 0, s, a);
-  else if (cpl <= 6) hipLaunchKernelGGL(k_topk_scan<6>, dim3(L.topk_blocks), dim3(256), 0, s, a);
-  else if (cpl <= 8) hipLaunchKernelGGL(k_topk_scan<8>, dim3(L.topk_blocks), dim3(256), 0, s, a);
+  // top-KM list with KM >= K; its first K entries are the top-K
+  if (L.K <= 1) hipLaunchKernelGGL(k_topk_scan<1>, dim3(L.topk_blocks), dim3(256), 0, s, a);
+  else if (L.K <= 2) hipLaunchKernelGGL(k_topk_scan<2>, dim3(L.topk_blocks), dim3(256), 0, s, a);
+  else if (L.K <= 4) hipLaunchKernelGGL(k_topk_scan<4>, dim3(L.topk_blocks), dim3(256), 0, s, a);
+  else if (L.K <= 8) hipLaunchKernelGGL(k_topk_scan<8>, dim3(L.topk_blocks), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_topk_scan<16>, dim3(L.topk_blocks), dim3(256), 0, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -71,6 +71,19 @@ __device__ __forceinline__ uint32_t mx_quant32(const float* v, uint32_t* out8) {
 }
 
 // ---- agent-scope signalling ---------------------------------------------------------------
+// On MI355X every XCD has its own L2. An agent-scope release writes back the whole local L2
+// and an acquire invalidates it, so they are used once around a hand-off, never inside a
+// polling loop. Words that carry their own payload (scan states, counters) are accessed with
+// relaxed agent-scope atomics, which are coherent across XCDs without any cache maintenance.
+__device__ __forceinline__ uint32_t ld_relaxed_u(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed_u(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ int ld_acquire(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
