@@ -37,6 +37,7 @@ class MokDesc(ctypes.Structure):
 
 class MokSizes(ctypes.Structure):
     _fields_ = [("saved_bytes", ctypes.c_size_t), ("ws_bytes", ctypes.c_size_t),
+                ("bwd_ws_bytes", ctypes.c_size_t),
                 ("slots_bytes", ctypes.c_size_t), ("xd_bytes", ctypes.c_size_t),
                 ("act_bytes", ctypes.c_size_t), ("wq_bytes", ctypes.c_size_t),
                 ("rows_max", ctypes.c_int64), ("ring_slots", ctypes.c_int32),

@@ -1,0 +1,165 @@
+// Backward GEMM tiles: the "a" GEMM with the router-weight gradient and SwiGLU backward in its
+// epilogue, the dx GEMM with the push epilogue, and the weight-gradient GEMM with an fp32
+// epilogue. Same tile engine as the forward (k_gemm.h).
+#pragma once
+
+#include "k_ffn.h"
+
+namespace mok {
+
+// E4M3 code -> float (finite codes; the quantiser never produces NaN).
+__device__ __forceinline__ float e4m3_value(uint8_t c) {
+  const int ex = (c >> 3) & 0xF, m = c & 7;
+  const float mag = ex == 0 ? float(m) * 0.001953125f                       // m/8 * 2^-6
+                            : (1.f + float(m) * 0.125f) * exp2i(ex - 7);
+  return (c & 0x80) ? -mag : mag;
+}
+
+// a = D Wd_e for the 256 intermediate columns [c0, c0+256) of expert e, rows [row0, row0+nrows)
+// of the expert-ordered stream (plane rows of `act` and of D). Epilogue per element (row, i):
+//   dh = p a, dg = dh u s(g) (1 + g (1 - s(g))), du = dh g s(g)     -> dgu[row][i], [I + i]
+//   dp partial = sum over this tile's columns of a h (fixed tree)   -> dp_part[row][c0/256]
+template <bool MX>
+__device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t row0, int nrows,
+                                       int e, int c0, const uint8_t* d, const uint8_t* d_s,
+                                       const uint8_t* wdt, const uint8_t* wdt_s,
+                                       const ActPlanes& act, const int32_t* perm, const float* p,
+                                       uint16_t* dgu, float* dp_part) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int eb = MX ? 1 : 2;
+  const int xrow = s.H * eb;
+  const int ncols = min(kTileN, s.I - c0);
+  Operand A = operand(make_rsrc(d + row0 * xrow, int64_t(nrows) * xrow), xrow);
+  const int64_t wrow0 = int64_t(e) * s.I + c0;
+  Operand B = operand(make_rsrc(wdt + wrow0 * xrow, int64_t(ncols) * xrow), xrow);
+  if (MX) {
+    A.sstride = B.sstride = s.H / 32;
+    A.s0 = A.s1 = make_rsrc(d_s + row0 * (s.H / 32), int64_t(nrows) * (s.H / 32));
+    B.s0 = B.s1 = make_rsrc(wdt_s + wrow0 * (s.H / 32), int64_t(ncols) * (s.H / 32));
+  }
+  f32x16 acc[4][4];
+  gemm_tile<MX>(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
+
+  float* s_dp = reinterpret_cast<float*>(sm.a[0]);     // [2][256] row partials of the two wn
+  const int nparts = (s.I + kTileN - 1) / kTileN;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 128 + i * 32 + acc_row(v, lane);
+      const bool rok = r < nrows;
+      const int64_t pr = row0 + (rok ? r : 0);
+      const float pg = rok ? p[perm[pr]] : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + wn * 128 + j * 32 + (lane & 31);
+        const bool ok = rok && c < s.I;
+        const int cc = ok ? c : 0;
+        const float av = acc[i][j][v];
+        const float g = bf2f(act.gu[pr * 2 * s.I + cc]);
+        const float u = bf2f(act.gu[pr * 2 * s.I + s.I + cc]);
+        float h;
+        if (MX) h = e4m3_value(act.h[pr * s.I + cc]) * exp2i(int(act.hs[pr * (s.I / 32) + cc / 32]) - 127);
+        else h = bf2f(reinterpret_cast<const uint16_t*>(act.h)[pr * s.I + cc]);
+        const float dh = pg * av;
+        const float sg = 1.f / (1.f + expf(-g));
+        const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
+        const float duv = dh * g * sg;
+        if (ok) {
+          dgu[pr * 2 * s.I + c] = f2bf(dgv);
+          dgu[pr * 2 * s.I + s.I + c] = f2bf(duv);
+          part = fmaf(av, h, part);
+        }
+      }
+      // sum over the 32 columns of this half-wave, then over the two wn waves
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      if ((lane & 31) == 0) s_dp[wn * 256 + r] = part;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < nrows; r += blockDim.x)
+    dp_part[(row0 + r) * nparts + c0 / kTileN] = s_dp[r] + s_dp[256 + r];
+  __syncthreads();
+}
+
+// dx = [dg | du] [Wg_e ; Wu_e] for output columns [c0, c0+256) of H: A = dg|du rows (K = 2I),
+// B = rows h of Wg_e^T for the first I of K and of Wu_e^T for the second; pushed to the slots.
+template <bool MX>
+__device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t row0, int nrows,
+                                        int e, int c0, const uint8_t* dgu, const uint8_t* dgu_s,
+                                        const uint8_t* wgt, const uint8_t* wgt_s,
+                                        const uint8_t* wut, const uint8_t* wut_s,
+                                        const int32_t* perm, uint16_t* slots) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int eb = MX ? 1 : 2;
+  const int arow = 2 * s.I * eb, brow = s.I * eb;
+  const int ncols = min(kTileN, s.H - c0);
+  Operand A = operand(make_rsrc(dgu + row0 * arow, int64_t(nrows) * arow), arow);
+  const int64_t wrow0 = int64_t(e) * s.H + c0;
+  Operand B = operand(make_rsrc(wgt + wrow0 * brow, int64_t(ncols) * brow), brow);
+  B.r1 = make_rsrc(wut + wrow0 * brow, int64_t(ncols) * brow);
+  B.ksplit = brow / kStageRowBytes;
+  if (MX) {
+    A.sstride = 2 * s.I / 32;
+    A.s0 = A.s1 = make_rsrc(dgu_s + row0 * A.sstride, int64_t(nrows) * A.sstride);
+    B.sstride = s.I / 32;
+    B.s0 = make_rsrc(wgt_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
+    B.s1 = make_rsrc(wut_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
+  }
+  f32x16 acc[4][4];
+  gemm_tile<MX>(sm, A, B, arow / kStageRowBytes, acc, wm, wn, lane);
+  push_epilogue(sm, acc, nrows, row0, c0, s.H, perm, slots);
+}
+
+// Weight-gradient tile: out[m0 + m][n0 + n] = sum over the expert's padded columns c of
+// Ta[m0 + m][c] Tb[n0 + n][c]; fp32 output [Fa][Fb] (fully overwritten).
+template <bool MX>
+__device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const uint8_t* ta_s,
+                                           const uint8_t* tb, const uint8_t* tb_s, int64_t ld,
+                                           int c0, int ncols, int m0, int n0, int Fa, int Fb,
+                                           float* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int eb = MX ? 1 : 2;
+  const int64_t stride = ld * eb;
+  const int ma = min(kTileM, Fa - m0), nb = min(kTileN, Fb - n0);
+  f32x16 acc[4][4];
+  if (ncols > 0) {
+    Operand A = operand(make_rsrc(ta + int64_t(m0) * stride + int64_t(c0) * eb, int64_t(ma) * stride),
+                        int(stride));
+    Operand B = operand(make_rsrc(tb + int64_t(n0) * stride + int64_t(c0) * eb, int64_t(nb) * stride),
+                        int(stride));
+    if (MX) {
+      A.sstride = B.sstride = int(ld / 32);
+      A.s0 = A.s1 = make_rsrc(ta_s + int64_t(m0) * (ld / 32) + c0 / 32, int64_t(ma) * (ld / 32));
+      B.s0 = B.s1 = make_rsrc(tb_s + int64_t(n0) * (ld / 32) + c0 / 32, int64_t(nb) * (ld / 32));
+    }
+    gemm_tile<MX>(sm, A, B, ncols * eb / kStageRowBytes, acc, wm, wn, lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = wm * 128 + i * 32 + acc_row(v, lane);
+      if (m >= ma) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = wn * 128 + j * 32 + (lane & 31);
+        if (n < nb) out[int64_t(m0 + m) * Fb + n0 + n] = acc[i][j][v];
+      }
+    }
+  __syncthreads();
+}
+
+}  // namespace mok

@@ -1,0 +1,386 @@
+// Backward of the MoE layer for L = sum_n <dOut[n], out[n]>.
+//
+// Per expert-order row r (pair n*K+k of expert e, gate p = p[n,k]), with D[r] = dOut[n]:
+//   a   = D Wd_e                      (the "a" GEMM, reduction over H)
+//   dp  = <a, h>                      (router-weight gradient, inside SwiGLU backward)
+//   dh  = p a;  dg = dh u s(g) (1 + g (1 - s(g)));  du = dh silu(g)
+//   dx  = dg Wg_e + du Wu_e           (the dx GEMM, reduction over 2I), pushed to slots[pair]
+//   dWg_e = sum_r dg_r^T x_r, dWu_e = sum_r du_r^T x_r, dWd_e = sum_r (p_r D_r)^T h_r
+// The pages fuse the router-weight gradient into SwiGLU backward ("Mixture-of-Kittens (MoK)",
+// benchmark section; "Cursor Open-Sources Mixture-of-Kittens (MoK)", Technical Details) and
+// run backward as pull reverse-combine + push reverse-dispatch (same pages, pull dispatch).
+//
+// GEMM operands are staged K-contiguous. Weights are transposed once per call (BF16) or come
+// pre-quantised in the transposed blocking (MXFP8). Weight-gradient operands are transposed per
+// expert into [feature][row] planes whose expert column ranges start at multiples of 128 and
+// are zero-padded, so the weight-gradient GEMM reduces over tokens in K-stages of 64 (BF16) or
+// 128 (E4M3) rows with no ragged edge. Every reduction has a fixed order.
+#include "k_bwd.h"
+
+namespace mok {
+namespace {
+
+// ---- transposes -------------------------------------------------------------------------
+
+// W [batch][R][C] -> WT [batch][C][R], BF16; 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* src, uint16_t* dst, int batch,
+                                                     int R, int C) {
+  __shared__ uint16_t t[64][66];
+  const int tr = R / 64, tc = C / 64;
+  const int64_t total = int64_t(batch) * tr * tc;
+  for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+    const int b = int(q / (int64_t(tr) * tc));
+    const int rem = int(q % (int64_t(tr) * tc));
+    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 64;
+    const uint16_t* s = src + int64_t(b) * R * C;
+    uint16_t* d = dst + int64_t(b) * R * C;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int rr = i / 64, cc = i % 64;
+      t[rr][cc] = s[int64_t(r0 + rr) * C + c0 + cc];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int cc = i / 64, rr = i % 64;
+      d[int64_t(c0 + cc) * R + r0 + rr] = t[rr][cc];
+    }
+    __syncthreads();
+  }
+}
+
+// Padded column layout of the per-expert transposed planes: expert e's rows go to columns
+// [colpad[e], colpad[e] + count[e]), colpad[e] a multiple of kPadRows; the rest of its
+// rounded-up range is zero. hdr2[0] = total padded columns.
+__global__ void k_colpad(const int32_t* hdr, int32_t* hdr2, int El) {
+  if (threadIdx.x != 0) return;
+  int off = 0;
+  for (int e = 0; e < El; ++e) {
+    hdr2[kB2ColPad + e] = off;
+    off += (hdr[kHdrCounts + e] + kPadRows - 1) / kPadRows * kPadRows;
+  }
+  hdr2[kB2ColPad + El] = off;
+  hdr2[kB2RowsPad] = off;
+}
+
+// Gather-transpose for the weight-gradient operands: T[f][colpad_e + i] = value of feature f of
+// row off_e + i of expert e. Sources: a BF16 plane [rows][F] (with column offset), an MXFP8
+// plane (dequantised), or the token segments through perm (optionally scaled by p of the
+// pair: the p * D operand of dWd). Tiles of 64 padded columns x 64 features.
+struct TransposeArgs {
+  const int32_t* hdr;
+  const int32_t* hdr2;
+  const int32_t* perm;
+  const float* p;              // non-null: scale rows by p[pair]
+  const uint16_t* const* seg;  // non-null: rows come from segments
+  const uint8_t* plane;        // else rows come from this plane
+  const uint8_t* plane_s;      // MXFP8 scales of the plane (null: BF16 plane)
+  int64_t plane_stride;        // elements per plane row
+  int plane_col0;              // first feature column inside the plane
+  uint16_t* dst;               // [F][ld]
+  int64_t ld;
+  int F, K, T, El;
+};
+
+__global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
+  __shared__ float t[64][65];
+  __shared__ int s_off[kMaxLocalExperts + 1], s_pad[kMaxLocalExperts + 1], s_cnt[kMaxLocalExperts];
+  if (threadIdx.x <= a.El) {
+    s_pad[threadIdx.x] = a.hdr2[kB2ColPad + threadIdx.x];
+    s_off[threadIdx.x] = a.hdr[kHdrOffsets + threadIdx.x];
+    if (threadIdx.x < a.El) s_cnt[threadIdx.x] = a.hdr[kHdrCounts + threadIdx.x];
+  }
+  __syncthreads();
+  const int cols = s_pad[a.El];
+  const int tc = cols / 64, tf = a.F / 64;
+  const int64_t total = int64_t(tc) * tf;
+  for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
+    const int c0 = int(q / tf) * 64, f0 = int(q % tf) * 64;
+    // expert of this column tile (padding keeps tiles inside one expert)
+    int e = 0;
+    while (e + 1 < a.El && s_pad[e + 1] <= c0) ++e;
+    // load 64 rows (columns of T) x 64 features
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int rr = i / 64, ff = i % 64;
+      const int li = c0 + rr - s_pad[e];
+      float v = 0.f;
+      if (li < s_cnt[e]) {
+        const int64_t row = s_off[e] + li;
+        if (a.seg) {
+          const int32_t pair = a.perm[row];
+          const int64_t n = pair / a.K;
+          v = bf2f(a.seg[n / a.T][(n % a.T) * int64_t(a.F) + f0 + ff]);
+          if (a.p) v *= a.p[pair];
+        } else if (a.plane_s) {
+          const int64_t col = a.plane_col0 + f0 + ff;
+          const uint8_t code = a.plane[row * a.plane_stride + col];
+          const int sc = a.plane_s[row * (a.plane_stride / 32) + col / 32];
+          v = e4m3_value(code) * exp2i(sc - 127);
+        } else {
+          v = bf2f(reinterpret_cast<const uint16_t*>(a.plane)[row * a.plane_stride + a.plane_col0 + f0 + ff]);
+        }
+      }
+      t[rr][ff] = v;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int ff = i / 64, rr = i % 64;
+      a.dst[int64_t(f0 + ff) * a.ld + c0 + rr] = f2bf(t[rr][ff]);
+    }
+    __syncthreads();
+  }
+}
+
+// ---- backward GEMM kernels ------------------------------------------------------------------
+
+struct BwdArgs {
+  const MTile* tiles;
+  const int32_t* ntiles;
+  const int32_t* perm;
+  const float* p;
+  const int32_t* hdr2;
+  FfnShape s;
+  // a GEMM
+  const uint8_t* d;        // D rows: BF16 [rows][H] or codes
+  const uint8_t* d_s;      // MXFP8 scales [rows][H/32]
+  const uint8_t* wdt;      // Wd^T [El][I][H] (BF16 or codes)
+  const uint8_t* wdt_s;
+  ActPlanes act;           // g|u and h of the forward (replayed)
+  uint16_t* dgu;           // out: dg|du BF16 [rows][2I]
+  float* dp_part;          // out: [rows][I/256]
+  // dx GEMM
+  const uint8_t* dgu_a;    // dg|du as the dx GEMM reads it: BF16 or codes [rows][2I]
+  const uint8_t* dgu_s;    // MXFP8 scales [rows][2I/32]
+  const uint8_t* wgt;      // Wg^T [El][H][I]
+  const uint8_t* wgt_s;
+  const uint8_t* wut;      // Wu^T [El][H][I]
+  const uint8_t* wut_s;
+  uint16_t* slots;
+  // weight gradients
+  const uint8_t* t_a;      // [F_a][ld] BF16 or codes (first operand, rows = output rows)
+  const uint8_t* t_a_s;
+  const uint8_t* t_b;      // [F_b][ld]
+  const uint8_t* t_b_s;
+  int64_t ld;              // padded columns of the transposed planes
+  int Fa, Fb;              // output rows, output columns
+  float* dw;               // [El][Fa][Fb]
+};
+
+template <bool MX>
+__global__ __launch_bounds__(256, 1) void k_a_gemm(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  const int mtiles = *a.ntiles;
+  const int ntn = (a.s.I + kTileN - 1) / kTileN;
+  const int total = mtiles * ntn;
+  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
+    int mt, nt;
+    tile_coords(t, mtiles, ntn, mt, nt);
+    const MTile tl = a.tiles[mt];
+    a_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.d, a.d_s, a.wdt, a.wdt_s, a.act,
+               a.perm, a.p, a.dgu, a.dp_part);
+  }
+}
+
+template <bool MX>
+__global__ __launch_bounds__(256, 1) void k_dx_gemm(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  const int mtiles = *a.ntiles;
+  const int ntn = (a.s.H + kTileN - 1) / kTileN;
+  const int total = mtiles * ntn;
+  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
+    int mt, nt;
+    tile_coords(t, mtiles, ntn, mt, nt);
+    const MTile tl = a.tiles[mt];
+    dx_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.dgu_a, a.dgu_s, a.wgt, a.wgt_s,
+                a.wut, a.wut_s, a.perm, a.slots);
+  }
+}
+
+// dW_e [Fa][Fb] = T_a[:, cols of e] . T_b[:, cols of e]^T ; one expert per blockIdx.y.
+template <bool MX>
+__global__ __launch_bounds__(256, 1) void k_wgrad_gemm(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  const int e = blockIdx.y;
+  const int c0 = a.hdr2[kB2ColPad + e];
+  const int ncols = a.hdr2[kB2ColPad + e + 1] - c0;
+  const int mtn = (a.Fa + kTileM - 1) / kTileM, ntn = (a.Fb + kTileN - 1) / kTileN;
+  const int total = mtn * ntn;
+  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
+    int mt, nt;
+    tile_coords(t, mtn, ntn, mt, nt);
+    wgrad_tile<MX>(sm, a.t_a, a.t_a_s, a.t_b, a.t_b_s, a.ld, c0, ncols, mt * kTileM, nt * kTileN,
+                   a.Fa, a.Fb, a.dw + int64_t(e) * a.Fa * a.Fb);
+  }
+}
+
+// dp[pair] = sum of the I/256 partials of its row, in column-tile order; then, when every
+// expert is local, dlogits[n, idx_k] = p_k (dp_k - sum_j p_j dp_j).
+__global__ void k_dp_finalize(const int32_t* hdr, const int32_t* perm, const float* dp_part,
+                              int nparts, float* dp, int64_t rows_max) {
+  const int64_t rows = min(int64_t(hdr[kHdrRows]), rows_max);
+  for (int64_t r = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; r < rows;
+       r += int64_t(gridDim.x) * blockDim.x) {
+    const int32_t pair = perm[r];
+    if (pair < 0) continue;
+    float s = 0.f;
+    for (int q = 0; q < nparts; ++q) s += dp_part[r * nparts + q];
+    dp[pair] = s;
+  }
+}
+
+__global__ void k_dlogits(const int32_t* idx, const float* p, const float* dp, float* dl,
+                          int64_t N, int K, int E) {
+  for (int64_t n = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; n < N;
+       n += int64_t(gridDim.x) * blockDim.x) {
+    float s = 0.f;
+    for (int k = 0; k < K; ++k) s = fmaf(p[n * K + k], dp[n * K + k], s);
+    for (int e = 0; e < E; ++e) dl[n * E + e] = 0.f;
+    for (int k = 0; k < K; ++k) dl[n * E + idx[n * K + k]] = p[n * K + k] * (dp[n * K + k] - s);
+  }
+}
+
+template <class F>
+hipError_t allow_big_lds(F* f) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(f),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kGemmLdsBytes));
+}
+
+int grid_cap(int64_t items, int cap) {
+  return int(items < 1 ? 1 : (items > cap ? cap : items));
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) {
+  static bool attr_done = false;
+  hipError_t err;
+  if (!attr_done) {
+    if ((err = allow_big_lds(k_a_gemm<false>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_a_gemm<true>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_dx_gemm<false>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_dx_gemm<true>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_wgrad_gemm<false>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_wgrad_gemm<true>)) != hipSuccess) return err;
+    attr_done = true;
+  }
+  const bool mx = L.dtype == MOK_MXFP8;
+  const int G = device_cus() > 0 ? device_cus() : 256;
+  const int H = L.H, I = L.I, El = L.El;
+  const int32_t* hdr = reinterpret_cast<const int32_t*>(b.saved);
+  const int32_t* perm = reinterpret_cast<const int32_t*>(b.saved + L.sv_perm);
+
+  // 1. replay the forward activations (same kernels, so g|u and h are bit-identical)
+  if ((err = launch_dispatch(L, b.saved, b.x_seg, b.xd, s)) != hipSuccess) return err;
+  if ((err = launch_ffn_gateup(L, b.saved, b.xd, b.w, b.act, b.ws, s)) != hipSuccess) return err;
+  // 2. pull reverse-combine: D[r] = dOut[n(r)] (BF16; quantised along H for the a GEMM)
+  Layout Lb = L;
+  Lb.dtype = MOK_BF16;
+  if ((err = launch_dispatch(Lb, b.saved, b.dout_seg, b.d, s)) != hipSuccess) return err;
+  if (mx && (err = launch_quantize_mx(1, int(L.rows_max), H, reinterpret_cast<const uint16_t*>(b.d),
+                                      0, b.dq, b.dq + L.rows_max * H, s)) != hipSuccess)
+    return err;
+  // 3. transposed BF16 weights for the backward GEMMs
+  if (!mx) {
+    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 4096, 8192)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(b.w.wd), b.wdt, El, H, I);
+    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 4096, 8192)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(b.w.wg), b.wgt, El, I, H);
+    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 4096, 8192)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(b.w.wu), b.wut, El, I, H);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  // 4. a GEMM with fused dp / SwiGLU backward
+  BwdArgs a{};
+  a.tiles = reinterpret_cast<const MTile*>(b.ws + L.ws_tiles);
+  a.ntiles = reinterpret_cast<const int32_t*>(b.ws) + kWsNumTiles;
+  a.perm = perm;
+  a.p = b.topk_p;
+  a.hdr2 = b.hdr2;
+  a.s = FfnShape{H, I};
+  a.d = mx ? b.dq : b.d;
+  a.d_s = mx ? b.dq + L.rows_max * H : nullptr;
+  a.wdt = mx ? b.w.wdt_q : reinterpret_cast<const uint8_t*>(b.wdt);
+  a.wdt_s = mx ? b.w.wdt_s : nullptr;
+  a.act = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
+  a.dgu = b.dgu;
+  a.dp_part = b.dp_part;
+  a.dgu_a = mx ? b.dguq : reinterpret_cast<const uint8_t*>(b.dgu);
+  a.dgu_s = mx ? b.dguq + L.rows_max * 2 * I : nullptr;
+  a.wgt = mx ? b.w.wgt_q : reinterpret_cast<const uint8_t*>(b.wgt);
+  a.wgt_s = mx ? b.w.wgt_s : nullptr;
+  a.wut = mx ? b.w.wut_q : reinterpret_cast<const uint8_t*>(b.wut);
+  a.wut_s = mx ? b.w.wut_s : nullptr;
+  a.slots = b.slots;
+  if (mx) hipLaunchKernelGGL(k_a_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else hipLaunchKernelGGL(k_a_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // 5. dx GEMM, pushed to the slots; then the unweighted fixed-order merge
+  if (mx && (err = launch_quantize_mx(1, int(L.rows_max), 2 * I, b.dgu, 0, b.dguq,
+                                      b.dguq + L.rows_max * 2 * I, s)) != hipSuccess)
+    return err;
+  if (mx) hipLaunchKernelGGL(k_dx_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else hipLaunchKernelGGL(k_dx_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_combine(L, b.saved, b.topk_idx, nullptr, b.slots, b.dx_seg, s)) != hipSuccess)
+    return err;
+  // 6. router-weight gradient per pair, and dlogits when every expert is local
+  hipLaunchKernelGGL(k_dp_finalize, dim3(grid_cap(L.rows_max / 256 + 1, 4096)), dim3(256), 0, s,
+                     hdr, perm, b.dp_part, int(cdiv(I, kTileN)), b.dp, L.rows_max);
+  if (b.dlogits)
+    hipLaunchKernelGGL(k_dlogits, dim3(grid_cap(L.N / 256 + 1, 4096)), dim3(256), 0, s, b.topk_idx,
+                       b.topk_p, b.dp, b.dlogits, L.N, L.K, L.E);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // 7. weight gradients from per-expert transposed operands
+  hipLaunchKernelGGL(k_colpad, dim3(1), dim3(64), 0, s, hdr, b.hdr2, El);
+  const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
+  const uint16_t* const* ds = reinterpret_cast<const uint16_t* const*>(b.dout_seg);
+  const int64_t ld = L.rp_max;
+  auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
+                int64_t stride, int col0, int F, uint16_t* dst) {
+    TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, ld, F, L.K, L.T, El};
+    hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / 64 * (F / 64), 8192)), dim3(256), 0, s, t);
+  };
+  const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
+  tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt);                         // X^T
+  tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt);                        // (p D)^T
+  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, 0, I, b.dgt);   // dg^T
+  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, I, I, b.dut);   // du^T
+  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht);          // h^T
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  struct WG { const uint16_t *ta, *tb; uint8_t *qa, *qb; int Fa, Fb; float* dw; };
+  const WG jobs[3] = {{b.dgt, b.xt, b.q_dgt, b.q_xt, I, H, b.g.dwg},
+                      {b.dut, b.xt, b.q_dut, b.q_xt, I, H, b.g.dwu},
+                      {b.dt, b.ht, b.q_dt, b.q_ht, H, I, b.g.dwd}};
+  if (mx) {
+    // quantise the transposed planes along tokens (blocks of 32 columns)
+    const uint16_t* srcs[5] = {b.xt, b.dt, b.dgt, b.dut, b.ht};
+    uint8_t* dsts[5] = {b.q_xt, b.q_dt, b.q_dgt, b.q_dut, b.q_ht};
+    const int F[5] = {H, H, I, I, I};
+    for (int q = 0; q < 5; ++q)
+      if ((err = launch_quantize_mx(1, F[q], int(ld), srcs[q], 0, dsts[q], dsts[q] + int64_t(F[q]) * ld, s)) !=
+          hipSuccess)
+        return err;
+  }
+  for (const WG& j : jobs) {
+    BwdArgs w = a;
+    w.ld = ld;
+    w.Fa = j.Fa;
+    w.Fb = j.Fb;
+    w.dw = j.dw;
+    if (mx) {
+      w.t_a = j.qa; w.t_a_s = j.qa + int64_t(j.Fa) * ld;
+      w.t_b = j.qb; w.t_b_s = j.qb + int64_t(j.Fb) * ld;
+    } else {
+      w.t_a = reinterpret_cast<const uint8_t*>(j.ta); w.t_a_s = nullptr;
+      w.t_b = reinterpret_cast<const uint8_t*>(j.tb); w.t_b_s = nullptr;
+    }
+    const int gx = G;
+    if (mx) hipLaunchKernelGGL(k_wgrad_gemm<true>, dim3(gx, El), dim3(kThreads), kGemmLdsBytes, s, w);
+    else hipLaunchKernelGGL(k_wgrad_gemm<false>, dim3(gx, El), dim3(kThreads), kGemmLdsBytes, s, w);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace mok

@@ -34,6 +34,7 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
   const int xrow = s.H * eb;
   Operand A, B;
   A.interleave = 0;
+  A.ksplit = B.ksplit = 0x7FFFFFFF;
   A.stride = xrow;
   A.sstride = s.H / 32;
   A.r0 = A.r1 = make_rsrc(pl.x + prow0 * xrow, int64_t(nrows) * xrow);
@@ -130,34 +131,13 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
   __syncthreads();
 }
 
-// y = h Wd^T over the 256 output columns [c0, c0+256) of expert e; the epilogue pushes each
-// row to its token's receive slot: slots[perm[row]][c] = bf16(y).
-template <bool MX>
-__device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
-                                          const ActPlanes& pl, int64_t prow0, int64_t row0,
-                                          int nrows, int e, int c0, const int32_t* perm,
-                                          uint16_t* slots) {
+// Push epilogue shared by the down GEMM and the dx GEMM: stage the BF16 tile in LDS, then
+// write whole rows (512 B, 16 B per lane) to the receive slot of each row's pair.
+__device__ __forceinline__ void push_epilogue(GemmLds& sm, const f32x16 (&acc)[4][4], int nrows,
+                                              int64_t row0, int c0, int H, const int32_t* perm,
+                                              uint16_t* slots) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int eb = MX ? 1 : 2;
-  const int hrow = s.I * eb;
-  Operand A, B;
-  A.interleave = B.interleave = 0;
-  A.stride = B.stride = hrow;
-  A.sstride = B.sstride = s.I / 32;
-  A.r0 = A.r1 = make_rsrc(pl.h + prow0 * hrow, int64_t(nrows) * hrow);
-  const int ncols = min(kTileN, s.H - c0);
-  const int64_t wrow0 = int64_t(e) * s.H + c0;
-  B.r0 = B.r1 = make_rsrc(w.wd + wrow0 * hrow, int64_t(ncols) * hrow);
-  if (MX) {
-    A.s0 = A.s1 = make_rsrc(pl.hs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
-    B.s0 = B.s1 = make_rsrc(w.wd_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
-  }
-  f32x16 acc[4][4];
-  gemm_tile<MX>(sm, A, B, hrow / kStageRowBytes, acc, wm, wn, lane);
-
-  // Push epilogue: stage the BF16 tile in LDS, then write whole rows (512 B, 16 B per lane)
-  // to the receive slot of each row's pair.
   uint16_t* t = reinterpret_cast<uint16_t*>(sm.a[0]);
   {
     uint16_t* tl = t + opaque((wm * 128 + 4 * (lane >> 5)) * 256 + wn * 128 + (lane & 31));
@@ -172,14 +152,44 @@ __device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const 
   __syncthreads();
   {
     const int half = lane >> 5, c = lane & 31;
-    const bool colok = c0 + c * 8 < s.H;
+    const bool colok = c0 + c * 8 < H;
     for (int r = wave * 2 + half; r < nrows; r += 8) {
       const int32_t pair = perm[row0 + r];
       const u32x4 val = *reinterpret_cast<const u32x4*>(t + r * 256 + c * 8);
-      if (colok) *reinterpret_cast<u32x4*>(slots + int64_t(pair) * s.H + c0 + c * 8) = val;
+      if (colok) *reinterpret_cast<u32x4*>(slots + int64_t(pair) * H + c0 + c * 8) = val;
     }
   }
   __syncthreads();
+}
+
+// y = h Wd^T over the 256 output columns [c0, c0+256) of expert e; the epilogue pushes each
+// row to its token's receive slot: slots[perm[row]][c] = bf16(y).
+template <bool MX>
+__device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
+                                          const ActPlanes& pl, int64_t prow0, int64_t row0,
+                                          int nrows, int e, int c0, const int32_t* perm,
+                                          uint16_t* slots) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int eb = MX ? 1 : 2;
+  const int hrow = s.I * eb;
+  Operand A, B;
+  A.interleave = B.interleave = 0;
+  A.ksplit = B.ksplit = 0x7FFFFFFF;
+  A.stride = B.stride = hrow;
+  A.sstride = B.sstride = s.I / 32;
+  A.r0 = A.r1 = make_rsrc(pl.h + prow0 * hrow, int64_t(nrows) * hrow);
+  const int ncols = min(kTileN, s.H - c0);
+  const int64_t wrow0 = int64_t(e) * s.H + c0;
+  B.r0 = B.r1 = make_rsrc(w.wd + wrow0 * hrow, int64_t(ncols) * hrow);
+  if (MX) {
+    A.s0 = A.s1 = make_rsrc(pl.hs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
+    B.s0 = B.s1 = make_rsrc(w.wd_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
+  }
+  f32x16 acc[4][4];
+  gemm_tile<MX>(sm, A, B, hrow / kStageRowBytes, acc, wm, wn, lane);
+
+  push_epilogue(sm, acc, nrows, row0, c0, s.H, perm, slots);
 }
 
 }  // namespace mok

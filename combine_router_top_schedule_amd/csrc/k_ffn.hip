@@ -55,20 +55,22 @@ hipError_t allow_big_lds(F* f) {
 
 }  // namespace
 
-hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_t* xd,
-                             const mok_weights& w, uint8_t* act, uint16_t* slots, uint8_t* ws,
-                             hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e;
-    if ((e = allow_big_lds(k_gateup_staged<false>)) != hipSuccess) return e;
-    if ((e = allow_big_lds(k_gateup_staged<true>)) != hipSuccess) return e;
-    if ((e = allow_big_lds(k_down_staged<false>)) != hipSuccess) return e;
-    if ((e = allow_big_lds(k_down_staged<true>)) != hipSuccess) return e;
-    attr_done = true;
-  }
-  hipError_t err = launch_tiles(L, int(L.rows_max), saved, ws, s);
-  if (err != hipSuccess) return err;
+namespace {
+bool g_attr_done = false;
+
+hipError_t ffn_init() {
+  if (g_attr_done) return hipSuccess;
+  hipError_t e;
+  if ((e = allow_big_lds(k_gateup_staged<false>)) != hipSuccess) return e;
+  if ((e = allow_big_lds(k_gateup_staged<true>)) != hipSuccess) return e;
+  if ((e = allow_big_lds(k_down_staged<false>)) != hipSuccess) return e;
+  if ((e = allow_big_lds(k_down_staged<true>)) != hipSuccess) return e;
+  g_attr_done = true;
+  return hipSuccess;
+}
+
+FfnStagedArgs staged_args(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                          const mok_weights& w, uint8_t* act, uint16_t* slots, uint8_t* ws) {
   const bool mx = L.dtype == MOK_MXFP8;
   FfnStagedArgs a{};
   a.tiles = reinterpret_cast<const MTile*>(ws + L.ws_tiles);
@@ -86,12 +88,35 @@ hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_
   a.pl.x = xp.x;
   a.pl.xs = xp.xs;
   a.slots = slots;
+  return a;
+}
+}  // namespace
+
+hipError_t launch_ffn_gateup(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                             const mok_weights& w, uint8_t* act, uint8_t* ws, hipStream_t s) {
+  hipError_t err = ffn_init();
+  if (err != hipSuccess) return err;
+  if ((err = launch_tiles(L, int(L.rows_max), saved, ws, s)) != hipSuccess) return err;
+  const FfnStagedArgs a = staged_args(L, saved, xd, w, act, nullptr, ws);
   const int G = device_cus() > 0 ? device_cus() : 256;
-  if (mx) hipLaunchKernelGGL(k_gateup_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
-  else hipLaunchKernelGGL(k_gateup_staged<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (mx) hipLaunchKernelGGL(k_down_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
-  else hipLaunchKernelGGL(k_down_staged<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  if (L.dtype == MOK_MXFP8)
+    hipLaunchKernelGGL(k_gateup_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else
+    hipLaunchKernelGGL(k_gateup_staged<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                             const mok_weights& w, uint8_t* act, uint16_t* slots, uint8_t* ws,
+                             hipStream_t s) {
+  hipError_t err = launch_ffn_gateup(L, saved, xd, w, act, ws, s);
+  if (err != hipSuccess) return err;
+  const FfnStagedArgs a = staged_args(L, saved, xd, w, act, slots, ws);
+  const int G = device_cus() > 0 ? device_cus() : 256;
+  if (L.dtype == MOK_MXFP8)
+    hipLaunchKernelGGL(k_down_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else
+    hipLaunchKernelGGL(k_down_staged<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   return hipGetLastError();
 }
 

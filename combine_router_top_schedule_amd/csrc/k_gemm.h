@@ -67,8 +67,20 @@ struct Operand {
   __amdgpu_buffer_rsrc_t s0, s1;    // MXFP8 scales
   int stride;                       // bytes per row
   int sstride;                      // scale bytes per row
-  int interleave;
+  int interleave;                   // 64-row blocks alternate r0 / r1
+  int ksplit;                       // stages kt >= ksplit read r1/s1 at stage kt - ksplit
 };
+
+__device__ __forceinline__ Operand operand(__amdgpu_buffer_rsrc_t r, int stride) {
+  Operand o;
+  o.r0 = o.r1 = r;
+  o.s0 = o.s1 = r;
+  o.stride = stride;
+  o.sstride = 0;
+  o.interleave = 0;
+  o.ksplit = 0x7FFFFFFF;
+  return o;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   // Raw buffer: stride 0, num_records = bytes (clamped to the 32-bit field).
@@ -89,7 +101,9 @@ __device__ __forceinline__ void issue_stage(const Operand& op, uint8_t* lds, uin
                                             bool mx) {
   const int w = wave_id(), L = threadIdx.x & 63;
   const int lchunk0 = (L & 7) ^ (L >> 3);
-  const bool odd = op.interleave && (w & 1);
+  const bool second = kt >= op.ksplit;                 // K split across two sources
+  if (second) kt -= op.ksplit;
+  const bool odd = (op.interleave && (w & 1)) || second;
   const __amdgpu_buffer_rsrc_t r = odd ? op.r1 : op.r0;
   const int rbase = op.interleave ? (w >> 1) * 64 : w * 64;   // first row inside the matrix
 #pragma unroll
@@ -197,6 +211,7 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (ksteps <= 0) return;
   issue_stage(A, sm.a[0], sm.as[0], 0, MX);
   issue_stage(B, sm.b[0], sm.bs[0], 0, MX);
   __builtin_amdgcn_s_waitcnt(0);

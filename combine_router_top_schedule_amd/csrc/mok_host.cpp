@@ -43,6 +43,21 @@ mok_status check_desc(const mok_desc* d) {
   return MOK_OK;
 }
 
+mok_status check_weights(const mok_desc* d, const mok_weights* w, bool backward) {
+  if (d->dtype == MOK_BF16) {
+    if (!w->wg || !w->wu || !w->wd) return MOK_ERR_NULL;
+    if (!aligned16(w->wg) || !aligned16(w->wu) || !aligned16(w->wd)) return MOK_ERR_ALIGN;
+  } else {
+    if (!w->wg_q || !w->wg_s || !w->wu_q || !w->wu_s || !w->wd_q || !w->wd_s) return MOK_ERR_DTYPE;
+    if (!aligned16(w->wg_q) || !aligned16(w->wu_q) || !aligned16(w->wd_q)) return MOK_ERR_ALIGN;
+    if (backward) {
+      if (!w->wgt_q || !w->wgt_s || !w->wut_q || !w->wut_s || !w->wdt_q || !w->wdt_s) return MOK_ERR_DTYPE;
+      if (!aligned16(w->wgt_q) || !aligned16(w->wut_q) || !aligned16(w->wdt_q)) return MOK_ERR_ALIGN;
+    }
+  }
+  return MOK_OK;
+}
+
 Layout layout_of(const mok_desc& d) {
   mok_desc e = d;
   if (e.minibatch_tokens == 0) e.minibatch_tokens = default_minibatch(d);
@@ -91,6 +106,7 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   const Layout L = layout_of(*desc);
   sizes->saved_bytes = size_t(L.sv_bytes);
   sizes->ws_bytes = size_t(L.ws_bytes);
+  sizes->bwd_ws_bytes = size_t(L.b_bytes);
   sizes->slots_bytes = size_t(L.slots_bytes);
   sizes->xd_bytes = size_t(L.xd_bytes);
   sizes->act_bytes = size_t(L.act_bytes);
@@ -136,13 +152,8 @@ mok_status mok_expert_ffn(const mok_desc* desc, const void* saved_dev, const voi
   mok_status st = check_desc(desc);
   if (st != MOK_OK) return st;
   if (!saved_dev || !xd_dev || !w || !act_dev || !slots_dev || !ws_dev) return MOK_ERR_NULL;
-  if (desc->dtype == MOK_BF16) {
-    if (!w->wg || !w->wu || !w->wd) return MOK_ERR_NULL;
-    if (!aligned16(w->wg) || !aligned16(w->wu) || !aligned16(w->wd)) return MOK_ERR_ALIGN;
-  } else {
-    if (!w->wg_q || !w->wg_s || !w->wu_q || !w->wu_s || !w->wd_q || !w->wd_s) return MOK_ERR_DTYPE;
-    if (!aligned16(w->wg_q) || !aligned16(w->wu_q) || !aligned16(w->wd_q)) return MOK_ERR_ALIGN;
-  }
+  st = check_weights(desc, w, false);
+  if (st != MOK_OK) return st;
   if (!aligned16(xd_dev) || !aligned16(act_dev) || !aligned16(slots_dev)) return MOK_ERR_ALIGN;
   const Layout L = layout_of(*desc);
   return hip_status(launch_ffn_staged(L, static_cast<const uint8_t*>(saved_dev),
@@ -206,10 +217,55 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
                          const void* saved_dev, void* ring_dev, void* slots_dev,
                          void* const* dx_seg_dev, float* dp_dev, float* dlogits_dev,
                          const mok_weight_grads* g, void* ws_dev, void* stream) {
-  (void)desc; (void)dout_seg_dev; (void)x_seg_dev; (void)w; (void)topk_idx_dev; (void)topk_p_dev;
-  (void)saved_dev; (void)ring_dev; (void)slots_dev; (void)dx_seg_dev; (void)dp_dev;
-  (void)dlogits_dev; (void)g; (void)ws_dev; (void)stream;
-  return MOK_ERR_UNSUPPORTED;
+  (void)ring_dev;
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!dout_seg_dev || !x_seg_dev || !w || !topk_idx_dev || !topk_p_dev || !saved_dev ||
+      !slots_dev || !dx_seg_dev || !dp_dev || !g || !g->dwg || !g->dwu || !g->dwd || !ws_dev)
+    return MOK_ERR_NULL;
+  if (dlogits_dev && desc->num_local_experts != desc->num_experts) return MOK_ERR_SHAPE;
+  st = check_weights(desc, w, true);
+  if (st != MOK_OK) return st;
+  if (!aligned16(slots_dev) || !aligned16(ws_dev) || !aligned16(g->dwg) || !aligned16(g->dwu) ||
+      !aligned16(g->dwd))
+    return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  BwdBuffers b{};
+  b.saved = static_cast<const uint8_t*>(saved_dev);
+  b.ws = ws;
+  b.x_seg = x_seg_dev;
+  b.dout_seg = dout_seg_dev;
+  b.dx_seg = dx_seg_dev;
+  b.topk_idx = topk_idx_dev;
+  b.topk_p = topk_p_dev;
+  b.w = *w;
+  b.g = *g;
+  b.slots = static_cast<uint16_t*>(slots_dev);
+  b.dp = dp_dev;
+  b.dlogits = dlogits_dev;
+  b.hdr2 = reinterpret_cast<int32_t*>(ws + L.b_hdr2);
+  b.xd = ws + L.b_xd;
+  b.act = ws + L.b_act;
+  b.d = ws + L.b_d;
+  b.dq = ws + L.b_dq;
+  b.dgu = reinterpret_cast<uint16_t*>(ws + L.b_dgu);
+  b.dguq = ws + L.b_dguq;
+  b.dp_part = reinterpret_cast<float*>(ws + L.b_dp);
+  b.wdt = reinterpret_cast<uint16_t*>(ws + L.b_wdt);
+  b.wgt = reinterpret_cast<uint16_t*>(ws + L.b_wgt);
+  b.wut = reinterpret_cast<uint16_t*>(ws + L.b_wut);
+  b.xt = reinterpret_cast<uint16_t*>(ws + L.b_xt);
+  b.dt = reinterpret_cast<uint16_t*>(ws + L.b_dt);
+  b.dgt = reinterpret_cast<uint16_t*>(ws + L.b_dgt);
+  b.dut = reinterpret_cast<uint16_t*>(ws + L.b_dut);
+  b.ht = reinterpret_cast<uint16_t*>(ws + L.b_ht);
+  b.q_xt = ws + L.b_qxt;
+  b.q_dt = ws + L.b_qdt;
+  b.q_dgt = ws + L.b_qdgt;
+  b.q_dut = ws + L.b_qdut;
+  b.q_ht = ws + L.b_qht;
+  return hip_status(launch_backward(L, b, as_stream(stream)));
 }
 
 }  // extern "C"

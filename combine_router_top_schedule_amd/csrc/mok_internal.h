@@ -39,6 +39,16 @@ enum WsHeader : int {
   kWsWords = 64,
 };
 
+// Backward header (its own 256 words in the backward part of the workspace).
+enum Bwd2Header : int {
+  kB2RowsPad = 0,   // padded columns of the per-expert transposed planes
+  kB2ColPad = 16,   // [E_loc + 1] first padded column of each expert
+  kB2Words = 256,
+};
+// Expert column ranges of the transposed planes start at multiples of this, so the weight-
+// gradient GEMM reduces in whole K-stages (64 BF16 or 128 E4M3 rows) with zero padding.
+constexpr int kPadRows = 128;
+
 struct Layout {
   // shapes
   int H, E, K, I, S, T, e0, El, M, dtype;
@@ -55,6 +65,10 @@ struct Layout {
   int R;
   // staged buffers
   int64_t xd_bytes, act_bytes, slots_bytes, wq_bytes;
+  // backward workspace (after the forward ws): byte offsets from the ws start
+  int64_t rp_max;
+  int64_t b_hdr2, b_xd, b_act, b_d, b_dq, b_dgu, b_dguq, b_dp, b_wdt, b_wgt, b_wut;
+  int64_t b_xt, b_dt, b_dgt, b_dut, b_ht, b_qxt, b_qdt, b_qdgt, b_qdut, b_qht, b_bytes;
 };
 
 // Bytes of an activation row of width `w` elements in the activation format: BF16, or
@@ -101,6 +115,34 @@ inline Layout make_layout(const mok_desc& d) {
   L.act_bytes = align_up(L.rows_max * (L.gu_row_bytes + L.h_row_bytes), 256);
   L.slots_bytes = align_up(L.NK * L.H * 2, 256);
   L.wq_bytes = align_up(int64_t(L.El) * L.I * L.H * 33 / 32, 256);
+  // backward
+  const bool mx = L.dtype == MOK_MXFP8;
+  L.rp_max = align_up(L.rows_max + int64_t(kPadRows) * L.El, kPadRows);
+  const int64_t rm = L.rows_max, rp = L.rp_max, H = L.H, I = L.I;
+  off = align_up(L.ws_bytes, 256);
+  auto take = [&](int64_t bytes) { int64_t o = off; off = align_up(off + bytes, 256); return o; };
+  L.b_hdr2 = take(4 * kB2Words);
+  L.b_xd = take(L.xd_bytes);
+  L.b_act = take(L.act_bytes);
+  L.b_d = take(rm * H * 2);
+  L.b_dq = take(mx ? rm * (H + H / 32) : 0);
+  L.b_dgu = take(rm * 2 * I * 2);
+  L.b_dguq = take(mx ? rm * (2 * I + 2 * I / 32) : 0);
+  L.b_dp = take(rm * (I / kTileN + 1) * 4);
+  L.b_wdt = take(mx ? 0 : int64_t(L.El) * H * I * 2);
+  L.b_wgt = take(mx ? 0 : int64_t(L.El) * H * I * 2);
+  L.b_wut = take(mx ? 0 : int64_t(L.El) * H * I * 2);
+  L.b_xt = take(H * rp * 2);
+  L.b_dt = take(H * rp * 2);
+  L.b_dgt = take(I * rp * 2);
+  L.b_dut = take(I * rp * 2);
+  L.b_ht = take(I * rp * 2);
+  L.b_qxt = take(mx ? H * rp * 33 / 32 : 0);
+  L.b_qdt = take(mx ? H * rp * 33 / 32 : 0);
+  L.b_qdgt = take(mx ? I * rp * 33 / 32 : 0);
+  L.b_qdut = take(mx ? I * rp * 33 / 32 : 0);
+  L.b_qht = take(mx ? I * rp * 33 / 32 : 0);
+  L.b_bytes = off;
   return L;
 }
 
@@ -148,6 +190,32 @@ hipError_t launch_quantize_mx(int batch, int rows, int cols, const uint16_t* src
 hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_t* xd,
                              const mok_weights& w, uint8_t* act, uint16_t* slots, uint8_t* ws,
                              hipStream_t s);
+hipError_t launch_ffn_gateup(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                             const mok_weights& w, uint8_t* act, uint8_t* ws, hipStream_t s);
+
+// Device buffers of one backward call (carved out of the workspace by the host code).
+struct BwdBuffers {
+  const uint8_t* saved;
+  uint8_t* ws;
+  const void* const* x_seg;
+  const void* const* dout_seg;
+  void* const* dx_seg;
+  const int32_t* topk_idx;
+  const float* topk_p;
+  mok_weights w;
+  mok_weight_grads g;
+  uint16_t* slots;
+  float* dp;
+  float* dlogits;
+  int32_t* hdr2;
+  uint8_t *xd, *act, *d, *dq, *dguq;
+  uint16_t* dgu;
+  float* dp_part;
+  uint16_t *wdt, *wgt, *wut;
+  uint16_t *xt, *dt, *dgt, *dut, *ht;
+  uint8_t *q_xt, *q_dt, *q_dgt, *q_dut, *q_ht;
+};
+hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
 
 int device_cus();
 

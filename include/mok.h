@@ -89,6 +89,8 @@ typedef struct {
   size_t saved_bytes;    /* schedule table; written by mok_schedule / mok_layer_fwd, read by
                             every later stage and by mok_layer_bwd                          */
   size_t ws_bytes;       /* scratch of one call (counters, error word, tile tables, ...)   */
+  size_t bwd_ws_bytes;   /* scratch of mok_layer_bwd (>= ws_bytes): replayed activations,
+                            gathered dOut, dg|du, transposed weight-gradient operands        */
   size_t slots_bytes;    /* push/receive buffer Z: N*K rows of H BF16, indexed by pair id   */
   size_t xd_bytes;       /* staged path: dispatched rows in expert order                    */
   size_t act_bytes;      /* staged path: g|u and h per dispatched row                       */
@@ -214,6 +216,7 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
                          const void* saved_dev, void* ring_dev, void* slots_dev,
                          void* const* dx_seg_dev, float* dp_dev, float* dlogits_dev,
                          const mok_weight_grads* g, void* ws_dev, void* stream);
+/* (mok_layer_bwd: ws_dev must hold bwd_ws_bytes.) */
 
 /* MXFP8 quantiser (OCP MX v1.0: E4M3 codes, one UE8M0 scale per 32 elements; shared scale
  * 2^(floor(log2 amax) - 8), round to nearest even, saturate to +-448, amax 0 -> scale 0).

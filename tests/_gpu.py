@@ -83,3 +83,36 @@ def frob_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 BF16_TOL = 1e-2      # max |err| <= 1e-2 * max |ref|
 MX_TOL = 3e-2        # relative Frobenius error
+
+
+class BwdCase(Case):
+    """Case with dOut and backward outputs; forward through the staged path (it fills the
+    schedule table that mok_layer_bwd reads)."""
+
+    def __init__(self, cfg, **kw):
+        super().__init__(cfg, with_dout=True, **kw)
+        d = self.d
+        sz = self.layer.sizes
+        self.bws = torch.empty(int(sz.bwd_ws_bytes), dtype=torch.uint8, device="cuda")
+        self.dx = torch.zeros((cfg.N, cfg.H), dtype=torch.int16, device="cuda")
+        self.dx_seg = self.layer.segs(self.dx)
+        self.dp = torch.zeros(cfg.N * cfg.K, dtype=torch.float32, device="cuda")
+        self.dlogits = (torch.zeros((cfg.N, cfg.E), dtype=torch.float32, device="cuda")
+                        if cfg.E_loc == cfg.E else None)
+        self.dwg = torch.empty((cfg.E_loc, cfg.I, cfg.H), dtype=torch.float32, device="cuda")
+        self.dwu = torch.empty_like(self.dwg)
+        self.dwd = torch.empty((cfg.E_loc, cfg.H, cfg.I), dtype=torch.float32, device="cuda")
+
+    def run(self):
+        L = self.layer
+        L.forward_staged(self.x_seg, self.logits, self.out_seg)
+        mok.mok_layer_bwd(self.d, self.dout_seg, self.x_seg, L.w, L.idx, L.p, L.saved, L.ring,
+                          L.slots, self.dx_seg, self.dp, self.dlogits, self.dwg, self.dwu,
+                          self.dwd, self.bws)
+        torch.cuda.synchronize()
+
+    def oracle_backward(self, fw=None):
+        cfg = self.cfg
+        fw = fw or self.oracle_forward()
+        W = self.oracle_weights()
+        return fw, mo.backward(fw, mo.bf16_rows(self.dout_h), W, cfg.K, cfg.e0, cfg.E_loc, cfg.E)

@@ -1,0 +1,116 @@
+"""GPU parity of mok_layer_bwd (input gradient, router-weight gradient, weight gradients and,
+with every expert local, dlogits) against the CPU oracle's backward."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import datagen
+from oracle import moe_oracle as mo
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from tests._gpu import BF16_TOL, MX_TOL, BwdCase, frob_rel_err, host_u16, max_rel_err
+
+
+def _compare(case, fw, bw, tol_fn, tol):
+    cfg = case.cfg
+    errs = {}
+    tok = fw.sched.touched
+    errs["dx"] = tol_fn(mo.decode_bf16(host_u16(case.dx)[tok]), bw.dx)
+    dp = case.dp.cpu().numpy().reshape(cfg.N, cfg.K)
+    local = (fw.idx >= cfg.e0) & (fw.idx < cfg.e0 + cfg.E_loc)
+    errs["dp"] = tol_fn(dp[local], bw.dp[local])
+    for name in ("dwg", "dwu", "dwd"):
+        errs[name] = tol_fn(getattr(case, name).cpu().numpy().astype(np.float64), getattr(bw, name))
+    if case.dlogits is not None:
+        errs["dlogits"] = tol_fn(case.dlogits.cpu().numpy().astype(np.float64), bw.dlogits)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (errs, tol)
+    return errs
+
+
+def _run(cfg, tol_fn, tol):
+    case = BwdCase(cfg)
+    case.run()
+    fw, bw = case.oracle_backward()
+    errs = _compare(case, fw, bw, tol_fn, tol)
+    # run-to-run bit-identical
+    first = [t.clone() for t in (case.dx, case.dp, case.dwg, case.dwu, case.dwd)]
+    case.run()
+    for a, b in zip(first, (case.dx, case.dp, case.dwg, case.dwu, case.dwd)):
+        assert torch.equal(a, b)
+    return errs
+
+
+@pytest.mark.parametrize("e0,E_loc", [(0, 8), (2, 3)])
+def test_backward_tiny_bf16(e0, E_loc):
+    _run(datagen.CONFIGS["tiny"].replace(e0=e0, E_loc=E_loc), max_rel_err, BF16_TOL)
+
+
+@pytest.mark.parametrize("e0,E_loc", [(0, 8), (1, 5)])
+def test_backward_tiny_mxfp8(e0, E_loc):
+    cfg = datagen.CONFIGS["tiny"].replace(e0=e0, E_loc=E_loc, dtype="mxfp8", x_std=1.0, M=32)
+    _run(cfg, frob_rel_err, MX_TOL)
+
+
+def test_backward_multitile_bf16():
+    # 1536 tokens, H 1024, I 384 (a partial 256-column tile), 16 experts, top-4, experts 4..7:
+    # several row tiles per expert with ragged edges, several weight-gradient K stages.
+    cfg = datagen.CONFIGS["tiny"].replace(S=3, T=512, H=1024, E=16, K=4, I=384, e0=4, E_loc=4,
+                                          x_std=1.0)
+    _run(cfg, max_rel_err, BF16_TOL)
+
+
+def test_backward_multitile_mxfp8():
+    cfg = datagen.CONFIGS["tiny"].replace(S=3, T=512, H=1024, E=16, K=4, I=384, e0=4, E_loc=4,
+                                          x_std=1.0, dtype="mxfp8", M=256)
+    _run(cfg, frob_rel_err, MX_TOL)
+
+
+def test_backward_dsv3_sampled():
+    """DeepSeek-V3-shaped local share at full size; dX and dp of 64 sampled touched tokens and
+    8 sampled rows of dWg / dWu are recomputed by the oracle."""
+    cfg = datagen.CONFIGS["dsv3"]
+    case = BwdCase(cfg)
+    case.run()
+    hdr, perm, tokpos, touched = case.layer.table()
+    U = int(hdr[2])
+    rng = np.random.default_rng(1)
+    sample = np.sort(rng.choice(touched.numpy()[:U], 64, replace=False))
+    fw = case.oracle_forward(tokens=sample)
+    W = case.oracle_weights()
+    bw = mo.backward(fw, lambda r: mo.decode_bf16(case.dout_h[sample[r]]), W, cfg.K, cfg.e0,
+                     cfg.E_loc, cfg.E)
+    got = mo.decode_bf16(host_u16(case.dx)[sample])
+    assert max_rel_err(got, bw.dx) <= BF16_TOL
+    dp = case.dp.cpu().numpy().reshape(cfg.N, cfg.K)[sample]
+    local = (fw.idx >= cfg.e0) & (fw.idx < cfg.e0 + cfg.E_loc)
+    assert max_rel_err(dp[local], bw.dp[local]) <= BF16_TOL
+    # Sampled rows i of dWg_e / dWu_e need only column i of the gate/up and down products
+    # over the expert's rows: dWg_e[i] = sum_r dg[r, i] x_r.
+    counts = hdr[16:16 + cfg.E_loc].numpy()
+    offs = hdr[96:96 + cfg.E_loc + 1].numpy()
+    perm = perm.numpy()
+    p_all = case.layer.p.cpu().numpy()
+    e = 1
+    rows = perm[offs[e]:offs[e] + counts[e]]
+    n_of = rows // cfg.K
+    X = mo.decode_bf16(case.x_h[n_of])
+    D = mo.decode_bf16(case.dout_h[n_of])
+    p_row = p_all[rows].astype(np.float64)
+    dwg = case.dwg[e].cpu().numpy()
+    dwu = case.dwu[e].cpu().numpy()
+    for i in rng.choice(cfg.I, 8, replace=False):
+        g = X @ W.wg[e, i]
+        u = X @ W.wu[e, i]
+        a = D @ W.wd[e, :, i]
+        sg = 1 / (1 + np.exp(-g))
+        dh = p_row * a
+        dg = dh * u * sg * (1 + g * (1 - sg))
+        du = dh * g * sg
+        assert max_rel_err(dwg[i], dg @ X) <= BF16_TOL
+        assert max_rel_err(dwu[i], du @ X) <= BF16_TOL
