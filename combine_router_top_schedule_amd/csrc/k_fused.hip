@@ -1,0 +1,245 @@
+// Fused forward: one persistent kernel whose compute units are split into dispatch workers and
+// GEMM workers that hand tiles to each other through counters in HBM, with no host
+// synchronisation ("把 MoE 通信延迟从 103μs 压到 18μs", section 03 part ②: SMs split into a
+// communication group and an expert-FFN group that notify each other with local counters;
+// part ③ and "Mixture-of-Kittens (MoK)", ring section: a fixed-size ring reused as soon as a
+// batch of tokens has been consumed, no CPU involvement).
+//
+// MI355X layout of that idea: every XCD (8 per device, each with its own L2) runs its own
+// pipeline. Workgroups learn their XCD from the hardware id; per XCD the first `comm` of them
+// gather token rows (pull dispatch, MXFP8 quantisation fused) and the others run the gate/up
+// and down GEMM tiles of the same row tiles. A row tile (<= 256 expert-ordered rows of one
+// expert inside one minibatch) is produced and consumed inside one XCD, so its ring bytes stay
+// coherent in that XCD's L2: producers complete their stores before bumping a counter, and a
+// consumer invalidates only its CU's L1 after seeing the counter. Each XCD owns a fixed share
+// of the ring, cut into tile slots that are reused round-robin once the tile's down GEMM is
+// done. Down-GEMM results are pushed to the pair slots; the weighted merge runs as the next
+// kernel on the stream.
+//
+// Deadlock freedom: all workgroups are co-resident (cooperative launch, one per CU). Within an
+// XCD, GEMM work items are numbered tile by tile (gate/up tiles, then down tiles) and each
+// GEMM worker takes items i = worker, worker + G, ... in order; every wait is on an earlier
+// item or on the gather of a tile whose slot was released by earlier items. Every wait is
+// bounded; an expired wait sets the error word and all workers drain.
+#include "k_ffn.h"
+#include "mok_rows.h"
+
+namespace mok {
+namespace {
+
+constexpr int kMaxXcd = 8;
+
+struct FusedArgs {
+  const int32_t* hdr;
+  const int32_t* perm;
+  const MTile* tiles;
+  const int32_t* ntiles;
+  const uint16_t* const* x_seg;
+  uint8_t* ring;
+  int64_t ring_share;        // bytes of the ring owned by one XCD
+  int64_t tsb;               // bytes of one tile slot
+  int capt;                  // tile slots per XCD
+  FfnShape s;
+  FfnWeights w;
+  uint16_t* slots;
+  int32_t* cnt;              // [kCntWords + 3 * tiles_max]
+  int32_t* err;
+  int64_t tiles_max;
+  int comm_per_xcd;
+  int K, T, dtype;
+  int spin_limit;
+  uint32_t flags;
+};
+
+enum CntWords : int { kCntArrived = 0, kCntReg = 8, kCntWords = 64 };
+
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kMaxXcd - 1);  // HW_REG_XCC_ID
+}
+
+// Invalidate this CU's vector L1 so later loads see data other CUs of the XCD stored to L2.
+__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
+// Thread 0 waits until *p >= target (bounded); returns false (for the whole workgroup) if the
+// wait failed or another worker already reported an error.
+__device__ bool wait_geq(const int32_t* p, int target, int32_t* err, int limit) {
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    int spins = 0, ok = 1;
+    while (ld_relaxed(p) < target) {
+      if (ld_relaxed(err) != 0) { ok = 0; break; }
+      if (++spins > limit) { set_error(err, MOK_ERR_DEVICE_TIMEOUT); ok = 0; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (ok && ld_relaxed(err) != 0) ok = 0;
+    s_ok = ok;
+  }
+  __syncthreads();
+  const bool ok = s_ok != 0;
+  __syncthreads();
+  return ok;
+}
+
+// All stores of this workgroup are complete (in L2), then thread 0 bumps the counter.
+__device__ __forceinline__ void signal(int32_t* p) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) add_relaxed(p, 1);
+}
+
+template <bool MX>
+__global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  __shared__ int s_x, s_local, s_n[kMaxXcd];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // ---- registration: which XCD am I on, and how many workgroups share it ----
+  if (tid == 0) {
+    const int x = xcc_id();
+    s_x = x;
+    s_local = add_relaxed(a.cnt + kCntReg + x, 1);
+    add_relaxed(a.cnt + kCntArrived, 1);
+    int spins = 0;
+    while (ld_relaxed(a.cnt + kCntArrived) < int(gridDim.x)) {
+      if (++spins > a.spin_limit) { set_error(a.err, MOK_ERR_DEVICE_TIMEOUT); break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    for (int i = 0; i < kMaxXcd; ++i) s_n[i] = ld_relaxed(a.cnt + kCntReg + i);
+  }
+  __syncthreads();
+  if (ld_relaxed(a.err) != 0) return;
+  const int x = s_x, local = s_local;
+  // active XCDs: those with at least one comm and one GEMM worker
+  int nact = 0, ax = -1;
+  for (int i = 0; i < kMaxXcd; ++i) {
+    if (s_n[i] >= 2) {
+      if (i == x) ax = nact;
+      ++nact;
+    }
+  }
+  if (ax < 0) return;
+  const int nx = s_n[x];
+  const int C = min(a.comm_per_xcd, nx - 1);
+  const int G = nx - C;
+  const int nt = *a.ntiles;
+  const int ngu = a.s.I / 128;
+  const int ndn = (a.s.H + kTileN - 1) / kTileN;
+  int32_t* landed = a.cnt + kCntWords;
+  int32_t* gu_done = landed + a.tiles_max;
+  int32_t* dn_done = gu_done + a.tiles_max;
+  uint8_t* share = a.ring + int64_t(x) * a.ring_share;
+
+  if (local < C) {
+    // ---- dispatch worker: pull the rows of this XCD's tiles into their ring slots ----
+    for (int q = 0;; ++q) {
+      const int mt = ax + q * nact;
+      if (mt >= nt) break;
+      if (q >= a.capt && !wait_geq(dn_done + (mt - a.capt * nact), ndn, a.err, a.spin_limit)) return;
+      const MTile tl = a.tiles[mt];
+      const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
+                                      a.dtype, true);
+      for (int r = local * 4 + wave; r < tl.nrows; r += 4 * C) {
+        const int32_t pair = a.perm[tl.row0 + r];
+        const int64_t n = pair / a.K;
+        const uint16_t* src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.s.H);
+        if (MX) quant_row_mx(src, pl.x + int64_t(r) * a.s.H, pl.xs + int64_t(r) * (a.s.H / 32), a.s.H, lane);
+        else copy_row_bf16(src, reinterpret_cast<uint16_t*>(pl.x) + int64_t(r) * a.s.H, a.s.H, lane);
+      }
+      const bool skip = (a.flags & MOK_FLAG_SKIP_ONE_SIGNAL) && q == 0 && ax == 0 && local == 0;
+      if (!skip) signal(landed + mt);
+    }
+    return;
+  }
+
+  // ---- GEMM worker ----
+  const int gi = local - C;
+  const int per_tile = ngu + ndn;
+  for (int it = gi;; it += G) {
+    const int q = it / per_tile, k = it % per_tile;
+    const int mt = ax + q * nact;
+    if (mt >= nt) break;
+    const MTile tl = a.tiles[mt];
+    const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
+                                    a.dtype, true);
+    if (k < ngu) {
+      if (!wait_geq(landed + mt, C, a.err, a.spin_limit)) return;
+      l1_invalidate();
+      gateup_tile<MX>(sm, a.s, a.w, pl, 0, tl.nrows, tl.e, k * 128);
+      signal(gu_done + mt);
+    } else {
+      if (!wait_geq(gu_done + mt, ngu, a.err, a.spin_limit)) return;
+      l1_invalidate();
+      down_tile<MX>(sm, a.s, a.w, pl, 0, tl.row0, tl.nrows, tl.e, (k - ngu) * kTileN, a.perm,
+                    a.slots);
+      signal(dn_done + mt);
+    }
+  }
+}
+
+template <class F>
+hipError_t allow_big_lds(F* f) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(f),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, int(kGemmLdsBytes));
+}
+
+}  // namespace
+
+int64_t fused_tile_slot_bytes(const Layout& L) {
+  return align_up(int64_t(kTileM) * (L.x_row_bytes + L.gu_row_bytes + L.h_row_bytes), 256);
+}
+
+int fused_slots_per_xcd(const Layout& L, int64_t ring_bytes) {
+  const int64_t share = ring_bytes / kMaxXcd / 256 * 256;
+  return int(share / fused_tile_slot_bytes(L));
+}
+
+hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
+                            const void* const* x_seg, const mok_weights& w, uint8_t* ring,
+                            uint16_t* slots, uint8_t* ws, hipStream_t s) {
+  static bool attr_done = false;
+  hipError_t err;
+  if (!attr_done) {
+    if ((err = allow_big_lds(k_layer_fwd<false>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_layer_fwd<true>)) != hipSuccess) return err;
+    attr_done = true;
+  }
+  if ((err = launch_tiles(L, L.M, saved, ws, s)) != hipSuccess) return err;
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.ws_counters);
+  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(cnt), 0u, kCntWords + 3 * L.tiles_max, s)) !=
+      hipSuccess)
+    return err;
+  const bool mx = L.dtype == MOK_MXFP8;
+  FusedArgs a{};
+  a.hdr = reinterpret_cast<const int32_t*>(saved);
+  a.perm = reinterpret_cast<const int32_t*>(saved + L.sv_perm);
+  a.tiles = reinterpret_cast<const MTile*>(ws + L.ws_tiles);
+  a.ntiles = reinterpret_cast<const int32_t*>(ws) + kWsNumTiles;
+  a.x_seg = reinterpret_cast<const uint16_t* const*>(x_seg);
+  a.ring = ring;
+  a.ring_share = d.ring_bytes / kMaxXcd / 256 * 256;
+  a.tsb = fused_tile_slot_bytes(L);
+  a.capt = fused_slots_per_xcd(L, d.ring_bytes);
+  a.s = FfnShape{L.H, L.I};
+  if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
+  else a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),
+                        static_cast<const uint8_t*>(w.wd), nullptr, nullptr, nullptr};
+  a.slots = slots;
+  a.cnt = cnt;
+  a.err = reinterpret_cast<int32_t*>(ws) + kWsError;
+  a.tiles_max = L.tiles_max;
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int comm_total = d.comm_cus > 0 ? d.comm_cus : 16;
+  a.comm_per_xcd = comm_total / kMaxXcd > 0 ? comm_total / kMaxXcd : 1;
+  a.K = L.K;
+  a.T = L.T;
+  a.dtype = L.dtype;
+  a.flags = d.flags;
+  a.spin_limit = (d.flags & MOK_FLAG_SKIP_ONE_SIGNAL) ? (1 << 12) : (1 << 24);
+  void* args[] = {&a};
+  const void* fn = mx ? reinterpret_cast<const void*>(k_layer_fwd<true>)
+                      : reinterpret_cast<const void*>(k_layer_fwd<false>);
+  return hipLaunchCooperativeKernel(fn, dim3(cus), dim3(kThreads), args, kGemmLdsBytes, s);
+}
+
+}  // namespace mok

@@ -112,9 +112,9 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   sizes->act_bytes = size_t(L.act_bytes);
   sizes->wq_bytes = size_t(L.wq_bytes);
   sizes->rows_max = L.rows_max;
-  sizes->ring_slots = L.R;
+  sizes->ring_slots = 8 * fused_slots_per_xcd(L, desc->ring_bytes);
   sizes->minibatch = L.M;
-  sizes->slot_bytes = L.slot_bytes;
+  sizes->slot_bytes = fused_tile_slot_bytes(L);
   sizes->perm_offset = L.sv_perm;
   sizes->tokpos_offset = L.sv_tokpos;
   sizes->touched_offset = L.sv_touched;
@@ -206,9 +206,30 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
                          void* const* out_seg_dev, int32_t* topk_idx_dev, float* topk_p_dev,
                          void* saved_dev, void* ring_dev, void* slots_dev, void* ws_dev,
                          void* stream) {
-  (void)desc; (void)x_seg_dev; (void)logits_dev; (void)w; (void)out_seg_dev; (void)topk_idx_dev;
-  (void)topk_p_dev; (void)saved_dev; (void)ring_dev; (void)slots_dev; (void)ws_dev; (void)stream;
-  return MOK_ERR_UNSUPPORTED;
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!x_seg_dev || !logits_dev || !w || !out_seg_dev || !topk_idx_dev || !topk_p_dev ||
+      !saved_dev || !ring_dev || !slots_dev || !ws_dev)
+    return MOK_ERR_NULL;
+  st = check_weights(desc, w, false);
+  if (st != MOK_OK) return st;
+  if (!aligned16(logits_dev) || !aligned16(saved_dev) || !aligned16(ring_dev) ||
+      !aligned16(slots_dev) || !aligned16(ws_dev))
+    return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  if (fused_slots_per_xcd(L, desc->ring_bytes) < 2) return MOK_ERR_RING;
+  hipStream_t s = as_stream(stream);
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  uint8_t* saved = static_cast<uint8_t*>(saved_dev);
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(ws), 0u, kWsWords, s);
+  if (e == hipSuccess) e = launch_router(L, logits_dev, topk_idx_dev, topk_p_dev, saved, ws, s);
+  if (e == hipSuccess)
+    e = launch_layer_fwd(L, *desc, saved, x_seg_dev, *w, static_cast<uint8_t*>(ring_dev),
+                         static_cast<uint16_t*>(slots_dev), ws, s);
+  if (e == hipSuccess)
+    e = launch_combine(L, saved, topk_idx_dev, topk_p_dev, static_cast<const uint16_t*>(slots_dev),
+                       out_seg_dev, s);
+  return hip_status(e);
 }
 
 mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,

@@ -60,9 +60,8 @@ struct Layout {
   int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_bytes;
   int topk_blocks;
   int64_t tiles_max, J_max;
-  // ring slot (fused forward): X | GU | Hact per row
-  int64_t x_row_bytes, gu_row_bytes, h_row_bytes, slot_bytes;
-  int R;
+  // activation row bytes: X | GU | Hact
+  int64_t x_row_bytes, gu_row_bytes, h_row_bytes;
   // staged buffers
   int64_t xd_bytes, act_bytes, slots_bytes, wq_bytes;
   // backward workspace (after the forward ws): byte offsets from the ws start
@@ -101,15 +100,13 @@ inline Layout make_layout(const mok_desc& d) {
   off = 256;
   L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 1), 256);
   L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
-  L.ws_counters = off; off = align_up(off + 4 * (4 * L.J_max + 1024), 256);
+  L.ws_counters = off; off = align_up(off + 4 * (64 + 3 * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
   L.ws_bytes = off;
-  // ring
+  // activation rows
   L.x_row_bytes = act_row_bytes(L.H, L.dtype);
   L.gu_row_bytes = int64_t(2) * L.I * 2;
   L.h_row_bytes = act_row_bytes(L.I, L.dtype);
-  L.slot_bytes = align_up(int64_t(L.M) * (L.x_row_bytes + L.gu_row_bytes + L.h_row_bytes), 256);
-  L.R = L.slot_bytes > 0 ? int(d.ring_bytes / L.slot_bytes) : 0;
   // staged
   L.xd_bytes = align_up(L.rows_max * L.x_row_bytes, 256);
   L.act_bytes = align_up(L.rows_max * (L.gu_row_bytes + L.h_row_bytes), 256);
@@ -216,6 +213,14 @@ struct BwdBuffers {
   uint8_t *q_xt, *q_dt, *q_dgt, *q_dut, *q_ht;
 };
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
+
+// Fused forward (k_fused.hip): the ring is split into one share per XCD, each cut into tile
+// slots of 256 expert-ordered rows (X | g,u | h).
+int64_t fused_tile_slot_bytes(const Layout& L);
+int fused_slots_per_xcd(const Layout& L, int64_t ring_bytes);
+hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
+                            const void* const* x_seg, const mok_weights& w, uint8_t* ring,
+                            uint16_t* slots, uint8_t* ws, hipStream_t s);
 
 int device_cus();
 

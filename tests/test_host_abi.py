@@ -66,11 +66,13 @@ def test_sizes_follow_host_bounds():
     assert s.rows_max == N * 4                                # N * min(K, E_loc)
     assert s.slots_bytes >= N * 8 * 7168 * 2                  # Z: [N*K][H] BF16
     assert s.xd_bytes >= s.rows_max * 7168 * 2
-    assert s.slot_bytes >= 2368 * (7168 + 2 * 2048 + 2048) * 2
-    assert s.ring_slots == (256 << 20) // s.slot_bytes == 4   # 26,624 B rows, M = 2368
+    # the ring is split into 8 per-XCD shares of 256-row tile slots (26,624 B BF16 rows)
+    assert s.slot_bytes == 256 * (7168 + 2 * 2048 + 2048) * 2
+    assert s.ring_slots == 8 * ((256 << 20) // 8 // s.slot_bytes) == 32
     sm = mok.query_sizes(_d(dtype="mxfp8"))
     assert sm.rows_max == N * 4 + 4 * 31                      # per-expert padding to 32 rows
-    assert sm.ring_slots == 6                                 # MXFP8 rows take 17,696 B
+    assert sm.slot_bytes == 256 * 17696                       # MXFP8 rows take 17,696 B
+    assert sm.ring_slots == 8 * 7
     # null arguments are rejected before anything runs
     assert mok.lib().mok_schedule(ctypes.byref(_d()), None, None, None, None, None, None) == 1
 
