@@ -15,6 +15,83 @@ __device__ __forceinline__ float e4m3_value(uint8_t c) {
   return (c & 0x80) ? -mag : mag;
 }
 
+// One 32-row block (i) of the a-GEMM epilogue; i is a template argument so the accumulator
+// stays in registers.
+template <bool MX, int i>
+__device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], const FfnShape& s,
+                                                 int64_t row0, int nrows, int colw,
+                                                 const ActPlanes& act, const int32_t* perm,
+                                                 const float* p, uint16_t* dgu, float* s_dp,
+                                                 uint16_t* lg, uint16_t* lu, uint16_t* lh, int wm,
+                                                 int wn, int lane) {
+
+    const int rbase = wm * 128 + i * 32;                                // tile row of lg row 0
+    // 32 rows x 128 columns: 16 lanes x 16 B cover a row of g (or u); 4 rows per instruction.
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
+      const bool ok = rbase + rr < nrows && colw + cc < s.I;
+      const int64_t pr = row0 + (ok ? rbase + rr : 0);
+      const int col = ok ? colw + cc : 0;
+      u32x4 gv = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + col);
+      u32x4 uv = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + s.I + col);
+      *reinterpret_cast<u32x4*>(lg + rr * 128 + cc) = gv;
+      *reinterpret_cast<u32x4*>(lu + rr * 128 + cc) = uv;
+      if (MX) {
+        // 8 codes at col (8-byte aligned), decoded with the block's scale
+        const uint2 hv = *reinterpret_cast<const uint2*>(act.h + pr * s.I + col);
+        const float scale = exp2i(int(act.hs[pr * (s.I / 32) + col / 32]) - 127);
+        u32x4 packed;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w = k < 2 ? hv.x : hv.y;
+          const int sh = (k & 1) * 16;
+          packed[k] = pack_bf2(e4m3_value(uint8_t(w >> sh)) * scale,
+                               e4m3_value(uint8_t(w >> (sh + 8))) * scale);
+        }
+        *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) = packed;
+      } else {
+        *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) =
+            *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(act.h) + pr * s.I + col);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int lr = acc_row(v, lane);                                  // row inside the block
+      const int r = rbase + lr;
+      const bool rok = r < nrows;
+      const int64_t pr = row0 + (rok ? r : 0);
+      const float pg = rok ? p[perm[pr]] : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int lc = j * 32 + (lane & 31);
+        const int c = colw + lc;
+        const bool ok = rok && c < s.I;
+        const float av = acc[i][j][v];
+        const float g = bf2f(lg[lr * 128 + lc]);
+        const float u = bf2f(lu[lr * 128 + lc]);
+        const float h = bf2f(lh[lr * 128 + lc]);
+        const float dh = pg * av;
+        const float sg = 1.f / (1.f + expf(-g));
+        const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
+        const float duv = dh * g * sg;
+        if (ok) {
+          dgu[pr * 2 * s.I + c] = f2bf(dgv);
+          dgu[pr * 2 * s.I + s.I + c] = f2bf(duv);
+          part = fmaf(av, h, part);
+        }
+      }
+      // sum over the 32 columns of this half-wave, then over the two wn waves
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      if ((lane & 31) == 0) s_dp[wn * 256 + r] = part;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
 // a = D Wd_e for the 256 intermediate columns [c0, c0+256) of expert e, rows [row0, row0+nrows)
 // of the expert-ordered stream (plane rows of `act` and of D). Epilogue per element (row, i):
 //   dh = p a, dg = dh u s(g) (1 + g (1 - s(g))), du = dh g s(g)     -> dgu[row][i], [I + i]
@@ -41,44 +118,21 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   f32x16 acc[4][4];
   gemm_tile<MX>(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
 
-  float* s_dp = reinterpret_cast<float*>(sm.a[0]);     // [2][256] row partials of the two wn
+  // Epilogue. For each 32-row block i, every wave first copies the g, u and h values of its
+  // 32 rows x 128 columns into its own LDS region with coalesced 16-byte loads (all issued
+  // together), then forms dg, du and the dp partials from LDS. h is staged as fp32 (MXFP8 h is
+  // decoded on the way).
   const int nparts = (s.I + kTileN - 1) / kTileN;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * 128 + i * 32 + acc_row(v, lane);
-      const bool rok = r < nrows;
-      const int64_t pr = row0 + (rok ? r : 0);
-      const float pg = rok ? p[perm[pr]] : 0.f;
-      float part = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = c0 + wn * 128 + j * 32 + (lane & 31);
-        const bool ok = rok && c < s.I;
-        const int cc = ok ? c : 0;
-        const float av = acc[i][j][v];
-        const float g = bf2f(act.gu[pr * 2 * s.I + cc]);
-        const float u = bf2f(act.gu[pr * 2 * s.I + s.I + cc]);
-        float h;
-        if (MX) h = e4m3_value(act.h[pr * s.I + cc]) * exp2i(int(act.hs[pr * (s.I / 32) + cc / 32]) - 127);
-        else h = bf2f(reinterpret_cast<const uint16_t*>(act.h)[pr * s.I + cc]);
-        const float dh = pg * av;
-        const float sg = 1.f / (1.f + expf(-g));
-        const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
-        const float duv = dh * g * sg;
-        if (ok) {
-          dgu[pr * 2 * s.I + c] = f2bf(dgv);
-          dgu[pr * 2 * s.I + s.I + c] = f2bf(duv);
-          part = fmaf(av, h, part);
-        }
-      }
-      // sum over the 32 columns of this half-wave, then over the two wn waves
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-      if ((lane & 31) == 0) s_dp[wn * 256 + r] = part;
-    }
-  }
+  float* s_dp = reinterpret_cast<float*>(sm.b[1]);                      // [2][256]
+  uint8_t* wreg = sm.a[0] + wave * 24576;                               // 24 KB per wave
+  uint16_t* lg = reinterpret_cast<uint16_t*>(wreg);                     // [32][128] BF16
+  uint16_t* lu = lg + 32 * 128;
+  uint16_t* lh = lu + 32 * 128;   // BF16 (exact for decoded E4M3 values too)
+  const int colw = c0 + wn * 128;                                       // wave's first column
+  a_epilogue_block<MX, 0>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
+  a_epilogue_block<MX, 1>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
+  a_epilogue_block<MX, 2>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
+  a_epilogue_block<MX, 3>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
   __syncthreads();
   for (int r = tid; r < nrows; r += blockDim.x)
     dp_part[(row0 + r) * nparts + c0 / kTileN] = s_dp[r] + s_dp[256 + r];
