@@ -78,7 +78,10 @@ _SIGS = {
                                        ctypes.c_int32, _P, _P, _P]),
     "mok_device_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
     "mok_device_cus": (ctypes.c_int32, []),
+    "mok_trace_kernel": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
 }
+
+MOK_TRACE_NONE, MOK_TRACE_FUSED_FWD, MOK_TRACE_A_GEMM, MOK_TRACE_DX_GEMM, MOK_TRACE_WGRAD = range(5)
 
 _lib = None
 
@@ -236,3 +239,11 @@ def mok_device_status(ws, stream=None) -> int:
     out = ctypes.c_int(0)
     _check("mok_device_status", lib().mok_device_status(_ptr(ws), _stream(stream), ctypes.byref(out)))
     return int(out.value)
+
+
+def mok_trace_kernel(kernel: int, before=None, after=None):
+    """Record torch.cuda.Event `before` / `after` around one kernel group of the next calls
+    (benchmark measurement; MOK_TRACE_NONE switches it off)."""
+    b = None if before is None else int(before.cuda_event)
+    a = None if after is None else int(after.cuda_event)
+    _check("mok_trace_kernel", lib().mok_trace_kernel(int(kernel), b, a))

@@ -312,15 +312,19 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.wut = mx ? b.w.wut_q : reinterpret_cast<const uint8_t*>(b.wut);
   a.wut_s = mx ? b.w.wut_s : nullptr;
   a.slots = b.slots;
+  trace_before(MOK_TRACE_A_GEMM, s);
   if (mx) hipLaunchKernelGGL(k_a_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   else hipLaunchKernelGGL(k_a_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  trace_after(MOK_TRACE_A_GEMM, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // 5. dx GEMM, pushed to the slots; then the unweighted fixed-order merge
   if (mx && (err = launch_quantize_mx(1, int(L.rows_max), 2 * I, b.dgu, 0, b.dguq,
                                       b.dguq + L.rows_max * 2 * I, s)) != hipSuccess)
     return err;
+  trace_before(MOK_TRACE_DX_GEMM, s);
   if (mx) hipLaunchKernelGGL(k_dx_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   else hipLaunchKernelGGL(k_dx_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  trace_after(MOK_TRACE_DX_GEMM, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if ((err = launch_combine(L, b.saved, b.topk_idx, nullptr, b.slots, b.dx_seg, s)) != hipSuccess)
     return err;
@@ -362,6 +366,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
           hipSuccess)
         return err;
   }
+  trace_before(MOK_TRACE_WGRAD, s);
   for (const WG& j : jobs) {
     BwdArgs w = a;
     w.ld = ld;
@@ -380,6 +385,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
     else hipLaunchKernelGGL(k_wgrad_gemm<false>, dim3(gx, El), dim3(kThreads), kGemmLdsBytes, s, w);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  trace_after(MOK_TRACE_WGRAD, s);
   return hipSuccess;
 }
 

@@ -239,7 +239,10 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   void* args[] = {&a};
   const void* fn = mx ? reinterpret_cast<const void*>(k_layer_fwd<true>)
                       : reinterpret_cast<const void*>(k_layer_fwd<false>);
-  return hipLaunchCooperativeKernel(fn, dim3(cus), dim3(kThreads), args, kGemmLdsBytes, s);
+  trace_before(MOK_TRACE_FUSED_FWD, s);
+  err = hipLaunchCooperativeKernel(fn, dim3(cus), dim3(kThreads), args, kGemmLdsBytes, s);
+  trace_after(MOK_TRACE_FUSED_FWD, s);
+  return err;
 }
 
 }  // namespace mok

@@ -10,6 +10,10 @@
 
 using namespace mok;
 
+namespace mok {
+TraceHook g_trace = {MOK_TRACE_NONE, nullptr, nullptr};
+}
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -98,6 +102,14 @@ int64_t mok_two_wave_floor(int32_t cus, int32_t tile_m, int32_t tile_n, int32_t 
 }
 
 int32_t mok_device_cus(void) { return device_cus(); }
+
+mok_status mok_trace_kernel(int32_t kernel, void* before, void* after) {
+  if (kernel < MOK_TRACE_NONE || kernel > MOK_TRACE_WGRAD) return MOK_ERR_SHAPE;
+  g_trace.kernel = (before && after) ? kernel : MOK_TRACE_NONE;
+  g_trace.before = reinterpret_cast<hipEvent_t>(before);
+  g_trace.after = reinterpret_cast<hipEvent_t>(after);
+  return MOK_OK;
+}
 
 mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   mok_status st = check_desc(desc);

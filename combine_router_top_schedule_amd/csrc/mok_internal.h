@@ -224,4 +224,17 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
 
 int device_cus();
 
+// Measurement hook (mok_trace_kernel): events recorded around one kernel group.
+struct TraceHook {
+  int kernel;
+  hipEvent_t before, after;
+};
+extern TraceHook g_trace;
+inline void trace_before(int kernel, hipStream_t s) {
+  if (g_trace.kernel == kernel && g_trace.before) (void)hipEventRecord(g_trace.before, s);
+}
+inline void trace_after(int kernel, hipStream_t s) {
+  if (g_trace.kernel == kernel && g_trace.after) (void)hipEventRecord(g_trace.after, s);
+}
+
 }  // namespace mok

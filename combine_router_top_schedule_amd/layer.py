@@ -37,6 +37,7 @@ class MokLayer:
         self.xd = _bytes(s.xd_bytes, device) if staged else None
         self.act = _bytes(s.act_bytes, device) if staged else None
         self.ring = _bytes(d.ring_bytes, device) if fused else None
+        self.bws = None
         self.w = None
         self._keep = []
 
@@ -102,8 +103,11 @@ class MokLayer:
                       self.ring, self.slots, self.ws)
 
     def backward(self, dout_seg, x_seg, dx_seg, dp, dlogits, dwg, dwu, dwd):
+        """Backward of the last forward (reads the schedule table, ring and slots it left)."""
+        if self.bws is None:
+            self.bws = _bytes(self.sizes.bwd_ws_bytes, self.device)
         mok_layer_bwd(self.d, dout_seg, x_seg, self.w, self.idx, self.p, self.saved, self.ring,
-                      self.slots, dx_seg, dp, dlogits, dwg, dwu, dwd, self.ws)
+                      self.slots, dx_seg, dp, dlogits, dwg, dwu, dwd, self.bws)
 
     # ---- views of the schedule table (tests) ------------------------------------------------
     def header(self):
