@@ -14,8 +14,8 @@
  * - Pointers named *_dev, and every pointer inside mok_weights / mok_weight_grads, are device
  *   pointers (HBM). mok_desc, mok_weights, mok_weight_grads and mok_sizes are host structs.
  * - Ownership: the caller allocates and frees every buffer. The library never allocates
- *   device memory and keeps no mutable global state; calls on different streams with
- *   different buffers are independent.
+ *   device memory and keeps no mutable global state apart from the benchmark hook set by
+ *   mok_trace_kernel; calls on different streams with different buffers are independent.
  * - Streams: every call is asynchronous and stream-ordered on `stream` (a hipStream_t passed
  *   as void*; NULL is the default stream). No call synchronises the host or copies device
  *   data to the host, except mok_device_status.
