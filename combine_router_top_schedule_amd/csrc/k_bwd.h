@@ -22,10 +22,14 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
                                                  int64_t row0, int nrows, int colw,
                                                  const ActPlanes& act, const int32_t* perm,
                                                  const float* p, uint16_t* dgu, float* s_dp,
-                                                 uint16_t* lg, uint16_t* lu, uint16_t* lh, int wm,
-                                                 int wn, int lane) {
+                                                 uint16_t* lg, uint16_t* lu, uint16_t* lh,
+                                                 float* lpg, int wm, int wn, int lane) {
 
     const int rbase = wm * 128 + i * 32;                                // tile row of lg row 0
+    if (lane < 32) {
+      const bool ok = rbase + lane < nrows;
+      lpg[lane] = ok ? p[perm[row0 + rbase + lane]] : 0.f;
+    }
     // 32 rows x 128 columns: 16 lanes x 16 B cover a row of g (or u); 4 rows per instruction.
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -62,8 +66,7 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
       const int lr = acc_row(v, lane);                                  // row inside the block
       const int r = rbase + lr;
       const bool rok = r < nrows;
-      const int64_t pr = row0 + (rok ? r : 0);
-      const float pg = rok ? p[perm[pr]] : 0.f;
+      const float pg = lpg[lr];
       float part = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -78,17 +81,29 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         const float sg = 1.f / (1.f + expf(-g));
         const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
         const float duv = dh * g * sg;
-        if (ok) {
-          dgu[pr * 2 * s.I + c] = f2bf(dgv);
-          dgu[pr * 2 * s.I + s.I + c] = f2bf(duv);
-          part = fmaf(av, h, part);
-        }
+        // dg and du replace g and u in place (each element is read and written by this lane)
+        lg[lr * 128 + lc] = f2bf(dgv);
+        lu[lr * 128 + lc] = f2bf(duv);
+        if (ok) part = fmaf(av, h, part);
       }
       // sum over the 32 columns of this half-wave, then over the two wn waves
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
       if ((lane & 31) == 0) s_dp[wn * 256 + r] = part;
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    // dg | du rows out with 16-byte stores, 16 lanes per row
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
+      if (rbase + rr < nrows && colw + cc < s.I) {
+        uint16_t* dst = dgu + (row0 + rbase + rr) * 2 * s.I + colw + cc;
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(lg + rr * 128 + cc);
+        *reinterpret_cast<u32x4*>(dst + s.I) = *reinterpret_cast<const u32x4*>(lu + rr * 128 + cc);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
   }
 
@@ -102,7 +117,7 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
                                        const uint8_t* wdt, const uint8_t* wdt_s,
                                        const ActPlanes& act, const int32_t* perm, const float* p,
                                        uint16_t* dgu, float* dp_part) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
   const int xrow = s.H * eb;
@@ -129,10 +144,11 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   uint16_t* lu = lg + 32 * 128;
   uint16_t* lh = lu + 32 * 128;   // BF16 (exact for decoded E4M3 values too)
   const int colw = c0 + wn * 128;                                       // wave's first column
-  a_epilogue_block<MX, 0>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
-  a_epilogue_block<MX, 1>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
-  a_epilogue_block<MX, 2>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
-  a_epilogue_block<MX, 3>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, wm, wn, lane);
+  float* lpg = reinterpret_cast<float*>(sm.b[1] + 4096) + wave * 32;     // gates of the 32 rows
+  a_epilogue_block<MX, 0>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
+  a_epilogue_block<MX, 1>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
+  a_epilogue_block<MX, 2>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
+  a_epilogue_block<MX, 3>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
   __syncthreads();
   for (int r = tid; r < nrows; r += blockDim.x)
     dp_part[(row0 + r) * nparts + c0 / kTileN] = s_dp[r] + s_dp[256 + r];
@@ -147,7 +163,7 @@ __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t 
                                         const uint8_t* wgt, const uint8_t* wgt_s,
                                         const uint8_t* wut, const uint8_t* wut_s,
                                         const int32_t* perm, uint16_t* slots) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
   const int arow = 2 * s.I * eb, brow = s.I * eb;
@@ -164,9 +180,10 @@ __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t 
     B.s0 = make_rsrc(wgt_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
     B.s1 = make_rsrc(wut_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
   }
+  const int32_t my_pair = tid < nrows ? perm[row0 + tid] : 0;
   f32x16 acc[4][4];
   gemm_tile<MX>(sm, A, B, arow / kStageRowBytes, acc, wm, wn, lane);
-  push_epilogue(sm, acc, nrows, row0, c0, s.H, perm, slots);
+  push_epilogue(sm, acc, nrows, c0, s.H, my_pair, slots);
 }
 
 // Weight-gradient tile: out[m0 + m][n0 + n] = sum over the expert's padded columns c of
@@ -176,7 +193,7 @@ __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const
                                            const uint8_t* tb, const uint8_t* tb_s, int64_t ld,
                                            int c0, int ncols, int m0, int n0, int Fa, int Fb,
                                            float* out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
   const int64_t stride = ld * eb;

@@ -28,7 +28,7 @@ template <bool MX>
 __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
                                             const ActPlanes& pl, int64_t prow0, int nrows, int e,
                                             int i0) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;                              // bytes per element
   const int xrow = s.H * eb;
@@ -133,12 +133,15 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
 
 // Push epilogue shared by the down GEMM and the dx GEMM: stage the BF16 tile in LDS, then
 // write whole rows (512 B, 16 B per lane) to the receive slot of each row's pair.
+// `my_pair` is the pair id of tile row threadIdx.x (loaded by the caller before the K loop, so
+// its latency is hidden and no wait on outstanding stores is needed here).
 __device__ __forceinline__ void push_epilogue(GemmLds& sm, const f32x16 (&acc)[4][4], int nrows,
-                                              int64_t row0, int c0, int H, const int32_t* perm,
-                                              uint16_t* slots) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                              int c0, int H, int32_t my_pair, uint16_t* slots) {
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   uint16_t* t = reinterpret_cast<uint16_t*>(sm.a[0]);
+  int32_t* s_perm = reinterpret_cast<int32_t*>(sm.as[0]);
+  s_perm[tid] = my_pair;
   {
     uint16_t* tl = t + opaque((wm * 128 + 4 * (lane >> 5)) * 256 + wn * 128 + (lane & 31));
 #pragma unroll
@@ -154,7 +157,7 @@ __device__ __forceinline__ void push_epilogue(GemmLds& sm, const f32x16 (&acc)[4
     const int half = lane >> 5, c = lane & 31;
     const bool colok = c0 + c * 8 < H;
     for (int r = wave * 2 + half; r < nrows; r += 8) {
-      const int32_t pair = perm[row0 + r];
+      const int32_t pair = s_perm[r];
       const u32x4 val = *reinterpret_cast<const u32x4*>(t + r * 256 + c * 8);
       if (colok) *reinterpret_cast<u32x4*>(slots + int64_t(pair) * H + c0 + c * 8) = val;
     }
@@ -169,7 +172,7 @@ __device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const 
                                           const ActPlanes& pl, int64_t prow0, int64_t row0,
                                           int nrows, int e, int c0, const int32_t* perm,
                                           uint16_t* slots) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
   const int hrow = s.I * eb;
@@ -186,10 +189,11 @@ __device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const 
     A.s0 = A.s1 = make_rsrc(pl.hs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
     B.s0 = B.s1 = make_rsrc(w.wd_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
   }
+  const int32_t my_pair = tid < nrows ? perm[row0 + tid] : 0;
   f32x16 acc[4][4];
   gemm_tile<MX>(sm, A, B, hrow / kStageRowBytes, acc, wm, wn, lane);
 
-  push_epilogue(sm, acc, nrows, row0, c0, s.H, perm, slots);
+  push_epilogue(sm, acc, nrows, c0, s.H, my_pair, slots);
 }
 
 }  // namespace mok

@@ -49,6 +49,11 @@ __device__ __forceinline__ T opaque(T v) {
   return v;
 }
 
+// Thread index for per-tile code. Laundered through opaque() so that lane-dependent epilogue
+// addresses are recomputed per tile instead of being hoisted out of the persistent tile loop
+// and kept live (in VGPRs, or spilled) across the K loop.
+__device__ __forceinline__ int tile_tid() { return opaque(int(threadIdx.x)); }
+
 // Accumulator row of register v for this lane, inside a 32 x 32 block.
 __device__ __forceinline__ int acc_row(int v, int lane) {
   return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
