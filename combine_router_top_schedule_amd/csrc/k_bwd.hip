@@ -80,50 +80,103 @@ struct TransposeArgs {
   int F, K, T, El;
 };
 
+// One tile = 64 padded columns (source rows) x 128 features. Source rows are read with 16-byte
+// loads (8 features per lane; 8 E4M3 codes for an MXFP8 plane) into an LDS tile
+// [row][feature] whose 260-byte pitch spreads the column gathers of the store phase over
+// distinct banks; the store phase writes 16 bytes (8 consecutive columns of one feature) per
+// lane. Per-row source addresses, gates and MX scales are looked up once per tile.
+constexpr int kTrCols = 64, kTrFeat = 128, kTrPitch = kTrFeat + 2;   // pitch in BF16 elements
+
 __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
-  __shared__ float t[64][65];
+  __shared__ __attribute__((aligned(16))) uint16_t t[kTrCols * kTrPitch];
   __shared__ int s_off[kMaxLocalExperts + 1], s_pad[kMaxLocalExperts + 1], s_cnt[kMaxLocalExperts];
-  if (threadIdx.x <= a.El) {
-    s_pad[threadIdx.x] = a.hdr2[kB2ColPad + threadIdx.x];
-    s_off[threadIdx.x] = a.hdr[kHdrOffsets + threadIdx.x];
-    if (threadIdx.x < a.El) s_cnt[threadIdx.x] = a.hdr[kHdrCounts + threadIdx.x];
+  __shared__ const uint8_t* s_src[kTrCols];   // first byte of the row's tile features (null: zero)
+  __shared__ float s_gate[kTrCols];           // p of the row's pair (scaled sources)
+  __shared__ uint32_t s_sc4[kTrCols];         // MXFP8 plane: the 4 scale codes of the tile's blocks
+  const int tid = threadIdx.x;
+  if (tid <= a.El) {
+    s_pad[tid] = a.hdr2[kB2ColPad + tid];
+    s_off[tid] = a.hdr[kHdrOffsets + tid];
+    if (tid < a.El) s_cnt[tid] = a.hdr[kHdrCounts + tid];
   }
   __syncthreads();
   const int cols = s_pad[a.El];
-  const int tc = cols / 64, tf = a.F / 64;
+  const int tc = cols / kTrCols, tf = a.F / kTrFeat;
   const int64_t total = int64_t(tc) * tf;
+  const bool mxp = a.plane_s != nullptr;
   for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
-    const int c0 = int(q / tf) * 64, f0 = int(q % tf) * 64;
-    // expert of this column tile (padding keeps tiles inside one expert)
-    int e = 0;
-    while (e + 1 < a.El && s_pad[e + 1] <= c0) ++e;
-    // load 64 rows (columns of T) x 64 features
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-      const int rr = i / 64, ff = i % 64;
-      const int li = c0 + rr - s_pad[e];
-      float v = 0.f;
+    const int c0 = int(q / tf) * kTrCols, f0 = int(q % tf) * kTrFeat;
+    if (tid < kTrCols) {
+      // expert of this column tile (padding keeps tiles inside one expert)
+      int e = 0;
+      while (e + 1 < a.El && s_pad[e + 1] <= c0) ++e;
+      const int li = c0 + tid - s_pad[e];
+      const uint8_t* src = nullptr;
+      float gate = 1.f;
+      uint32_t sc4 = 0;
       if (li < s_cnt[e]) {
         const int64_t row = s_off[e] + li;
         if (a.seg) {
           const int32_t pair = a.perm[row];
           const int64_t n = pair / a.K;
-          v = bf2f(a.seg[n / a.T][(n % a.T) * int64_t(a.F) + f0 + ff]);
-          if (a.p) v *= a.p[pair];
-        } else if (a.plane_s) {
-          const int64_t col = a.plane_col0 + f0 + ff;
-          const uint8_t code = a.plane[row * a.plane_stride + col];
-          const int sc = a.plane_s[row * (a.plane_stride / 32) + col / 32];
-          v = e4m3_value(code) * exp2i(sc - 127);
+          src = reinterpret_cast<const uint8_t*>(a.seg[n / a.T] + (n % a.T) * int64_t(a.F) + f0);
+          if (a.p) gate = a.p[pair];
+        } else if (mxp) {
+          src = a.plane + row * a.plane_stride + a.plane_col0 + f0;
+          sc4 = *reinterpret_cast<const uint32_t*>(a.plane_s + row * (a.plane_stride / 32) +
+                                                   (a.plane_col0 + f0) / 32);
         } else {
-          v = bf2f(reinterpret_cast<const uint16_t*>(a.plane)[row * a.plane_stride + a.plane_col0 + f0 + ff]);
+          src = a.plane + (row * a.plane_stride + a.plane_col0 + f0) * 2;
         }
       }
-      t[rr][ff] = v;
+      s_src[tid] = src;
+      s_gate[tid] = gate;
+      s_sc4[tid] = sc4;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-      const int ff = i / 64, rr = i % 64;
-      a.dst[int64_t(f0 + ff) * a.ld + c0 + rr] = f2bf(t[rr][ff]);
+    // load: 64 rows x 16 chunks of 8 features
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, r = idx >> 4, ch = idx & 15;
+      const uint8_t* src = s_src[r];
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (src) {
+        if (mxp) {
+          const uint2 c8 = *reinterpret_cast<const uint2*>(src + ch * 8);
+          const float sc = exp2i(int((s_sc4[r] >> (8 * (ch >> 2))) & 0xFFu) - 127);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t cw = k < 2 ? c8.x : c8.y;
+            const int sh = (k & 1) * 16;
+            w[k] = pack_bf2(e4m3_value(uint8_t(cw >> sh)) * sc, e4m3_value(uint8_t(cw >> (sh + 8))) * sc);
+          }
+        } else {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(src + ch * 16);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = v[k];
+          if (a.p) {
+            const float g = s_gate[r];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              w[k] = pack_bf2(bf2f(uint16_t(w[k])) * g, bf2f(uint16_t(w[k] >> 16)) * g);
+          }
+        }
+      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(t + r * kTrPitch + ch * 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[k] = w[k];
+    }
+    __syncthreads();
+    // store: 128 features x 8 chunks of 8 columns
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, f = idx >> 3, cc = idx & 7;
+      u32x4 out;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        out[k] = uint32_t(t[(cc * 8 + 2 * k) * kTrPitch + f]) |
+                 (uint32_t(t[(cc * 8 + 2 * k + 1) * kTrPitch + f]) << 16);
+      *reinterpret_cast<u32x4*>(a.dst + int64_t(f0 + f) * a.ld + c0 + cc * 8) = out;
     }
     __syncthreads();
   }
@@ -343,7 +396,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
                 int64_t stride, int col0, int F, uint16_t* dst) {
     TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, ld, F, L.K, L.T, El};
-    hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / 64 * (F / 64), 8192)), dim3(256), 0, s, t);
+    hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
   };
   const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
   tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt);                         // X^T
