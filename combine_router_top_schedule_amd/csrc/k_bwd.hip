@@ -16,6 +16,7 @@
 // are zero-padded, so the weight-gradient GEMM reduces over tokens in K-stages of 64 (BF16) or
 // 128 (E4M3) rows with no ragged edge. Every reduction has a fixed order.
 #include "k_bwd.h"
+#include "mok_rows.h"
 
 namespace mok {
 namespace {
@@ -182,6 +183,101 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
   }
 }
 
+// ---- reverse ring walk: reuse what the forward left resident, replay the rest -------------
+
+// Split the forward's tiles into those whose ring slot still holds them (their g|u and h are
+// copied back) and those to replay (X gathered again, gate/up recomputed). Without ring state
+// (staged forward, or no ring passed) every row is replayed, in per-expert tiles. One thread,
+// tile order, so the lists are deterministic.
+__global__ void k_bwd_plan(const int32_t* hdr, const int32_t* rhdr, const MTile* rtiles,
+                           const int32_t* rslot, const int32_t* rowner, int have_ring,
+                           MTile* restore, int32_t* restore_slot, MTile* replay, int32_t* counts,
+                           int El, int64_t tiles_max) {
+  if (threadIdx.x != 0) return;
+  int64_t nr = 0, np = 0;
+  const int nt = have_ring ? rhdr[kRhTiles] : 0;
+  if (nt > 0) {
+    for (int mt = 0; mt < nt && mt < tiles_max; ++mt) {
+      const MTile t = rtiles[mt];
+      const int sl = rslot[mt];
+      if (rowner[sl] == mt) {
+        restore[nr] = t;
+        restore_slot[nr] = sl;
+        ++nr;
+      } else {
+        replay[np++] = t;
+      }
+    }
+  } else {
+    for (int e = 0; e < El; ++e) {
+      const int r0 = hdr[kHdrOffsets + e], r1 = r0 + hdr[kHdrCounts + e];
+      for (int r = r0; r < r1 && np < tiles_max; r += kTileM) replay[np++] = MTile{0, e, r, min(kTileM, r1 - r)};
+    }
+  }
+  counts[0] = int32_t(nr);
+  counts[1] = int32_t(np);
+}
+
+// Work item = 16 rows of one listed tile. Restored tiles: copy each row's g|u and h (with MX
+// scales) from its ring slot to the expert-ordered activation planes. Replayed tiles: gather the
+// row's X from its segment into the dispatch plane (MXFP8: quantised along H). One wave per row.
+struct StageArgs {
+  const MTile* restore;
+  const int32_t* restore_slot;
+  const MTile* replay;
+  const int32_t* counts;
+  const int32_t* perm;
+  const uint16_t* const* x_seg;
+  const uint8_t* ring;
+  int64_t ring_share, tsb;
+  int capt;
+  uint8_t* xd;          // dispatch plane [rows_max] (codes then scales in MXFP8)
+  ActPlanes act;        // g|u and h planes [rows_max]
+  int64_t rows_max;
+  int H, I, K, T, dtype;
+  int64_t NK;
+};
+
+__global__ __launch_bounds__(256) void k_bwd_stage(StageArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nr = a.counts[0], np = a.counts[1];
+  const int64_t items = int64_t(nr + np) * (kTileM / 16);
+  const bool mx = a.dtype == MOK_MXFP8;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = int(it / (kTileM / 16)), chunk = int(it % (kTileM / 16));
+    const bool rest = t < nr;
+    const MTile tl = rest ? a.restore[t] : a.replay[t - nr];
+    for (int i = chunk * 16 + wave; i < min(tl.nrows, chunk * 16 + 16); i += 4) {
+      const int64_t row = tl.row0 + i;
+      if (rest) {
+        const int sl = a.restore_slot[t];
+        uint8_t* slot = const_cast<uint8_t*>(a.ring) + int64_t(sl / a.capt) * a.ring_share +
+                        int64_t(sl % a.capt) * a.tsb;
+        const ActPlanes sp = act_planes(slot, kTileM, a.H, a.I, a.dtype, true);
+        copy_row_bf16(sp.gu + int64_t(i) * 2 * a.I, a.act.gu + row * 2 * a.I, 2 * a.I, lane);
+        if (mx) {
+          // I codes (as I/2 16-bit units) and I/32 scale bytes
+          copy_row_bf16(reinterpret_cast<const uint16_t*>(sp.h + int64_t(i) * a.I),
+                        reinterpret_cast<uint16_t*>(a.act.h + row * a.I), a.I / 2, lane);
+          for (int b = lane; b < a.I / 32; b += 64) a.act.hs[row * (a.I / 32) + b] = sp.hs[int64_t(i) * (a.I / 32) + b];
+        } else {
+          copy_row_bf16(reinterpret_cast<const uint16_t*>(sp.h) + int64_t(i) * a.I,
+                        reinterpret_cast<uint16_t*>(a.act.h) + row * a.I, a.I, lane);
+        }
+      } else {
+        const int32_t pair = a.perm[row];
+        const uint16_t* src = nullptr;
+        if (pair >= 0 && pair < a.NK) {
+          const int64_t n = pair / a.K;
+          src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.H);
+        }
+        if (mx) quant_row_mx(src, a.xd + row * a.H, a.xd + a.rows_max * a.H + row * (a.H / 32), a.H, lane);
+        else copy_row_bf16(src, reinterpret_cast<uint16_t*>(a.xd) + row * a.H, a.H, lane);
+      }
+    }
+  }
+}
+
 // ---- backward GEMM kernels ------------------------------------------------------------------
 
 struct BwdArgs {
@@ -323,9 +419,45 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   const int32_t* hdr = reinterpret_cast<const int32_t*>(b.saved);
   const int32_t* perm = reinterpret_cast<const int32_t*>(b.saved + L.sv_perm);
 
-  // 1. replay the forward activations (same kernels, so g|u and h are bit-identical)
-  if ((err = launch_dispatch(L, b.saved, b.x_seg, b.xd, s)) != hipSuccess) return err;
-  if ((err = launch_ffn_gateup(L, b.saved, b.xd, b.w, b.act, b.ws, s)) != hipSuccess) return err;
+  // 1. reverse ring walk: tiles still resident in the ring give back their g|u and h; the
+  //    others are replayed (X gathered again, gate/up recomputed by the same tile code, so the
+  //    values are bit-identical either way)
+  MTile* restore = reinterpret_cast<MTile*>(b.ws + L.b_restore);
+  MTile* replay = reinterpret_cast<MTile*>(b.ws + L.b_replay);
+  int32_t* rsl = reinterpret_cast<int32_t*>(b.ws + L.b_rsl);
+  int32_t* counts = reinterpret_cast<int32_t*>(b.ws + L.b_counts);
+  hipLaunchKernelGGL(k_bwd_plan, dim3(1), dim3(64), 0, s, hdr,
+                     reinterpret_cast<const int32_t*>(b.saved + L.sv_rhdr),
+                     reinterpret_cast<const MTile*>(b.saved + L.sv_rtiles),
+                     reinterpret_cast<const int32_t*>(b.saved + L.sv_rslot),
+                     reinterpret_cast<const int32_t*>(b.saved + L.sv_rowner),
+                     int(b.ring != nullptr && L.ring_capt > 0), restore, rsl, replay, counts, El,
+                     L.tiles_max);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  {
+    StageArgs st{};
+    st.restore = restore;
+    st.restore_slot = rsl;
+    st.replay = replay;
+    st.counts = counts;
+    st.perm = perm;
+    st.x_seg = reinterpret_cast<const uint16_t* const*>(b.x_seg);
+    st.ring = b.ring;
+    st.ring_share = L.ring_share;
+    st.tsb = L.tsb;
+    st.capt = L.ring_capt > 0 ? L.ring_capt : 1;
+    st.xd = b.xd;
+    st.act = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
+    st.rows_max = L.rows_max;
+    st.H = H; st.I = I; st.K = L.K; st.T = L.T; st.dtype = L.dtype;
+    st.NK = L.NK;
+    hipLaunchKernelGGL(k_bwd_stage, dim3(grid_cap(L.tiles_max * (kTileM / 16), 4 * G)), dim3(256), 0, s, st);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if ((err = launch_ffn_gateup_list(L, b.saved, b.xd, b.w, b.act, replay, counts + 1, s)) != hipSuccess)
+    return err;
+  // per-expert tiles (no minibatch cuts) for the backward GEMMs
+  if ((err = launch_tiles(L, int(L.rows_max), b.saved, b.ws, s)) != hipSuccess) return err;
   // 2. pull reverse-combine: D[r] = dOut[n(r)] (BF16; quantised along H for the a GEMM)
   Layout Lb = L;
   Lb.dtype = MOK_BF16;

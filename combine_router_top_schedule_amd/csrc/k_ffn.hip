@@ -73,8 +73,10 @@ FfnStagedArgs staged_args(const Layout& L, const uint8_t* saved, const uint8_t* 
                           const mok_weights& w, uint8_t* act, uint16_t* slots, uint8_t* ws) {
   const bool mx = L.dtype == MOK_MXFP8;
   FfnStagedArgs a{};
-  a.tiles = reinterpret_cast<const MTile*>(ws + L.ws_tiles);
-  a.ntiles = reinterpret_cast<const int32_t*>(ws) + kWsNumTiles;
+  if (ws) {
+    a.tiles = reinterpret_cast<const MTile*>(ws + L.ws_tiles);
+    a.ntiles = reinterpret_cast<const int32_t*>(ws) + kWsNumTiles;
+  }
   a.perm = reinterpret_cast<const int32_t*>(saved + L.sv_perm);
   a.s = FfnShape{L.H, L.I};
   if (mx) {
@@ -98,6 +100,22 @@ hipError_t launch_ffn_gateup(const Layout& L, const uint8_t* saved, const uint8_
   if (err != hipSuccess) return err;
   if ((err = launch_tiles(L, int(L.rows_max), saved, ws, s)) != hipSuccess) return err;
   const FfnStagedArgs a = staged_args(L, saved, xd, w, act, nullptr, ws);
+  const int G = device_cus() > 0 ? device_cus() : 256;
+  if (L.dtype == MOK_MXFP8)
+    hipLaunchKernelGGL(k_gateup_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else
+    hipLaunchKernelGGL(k_gateup_staged<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_gateup_list(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                                  const mok_weights& w, uint8_t* act, const MTile* tiles,
+                                  const int32_t* ntiles, hipStream_t s) {
+  hipError_t err = ffn_init();
+  if (err != hipSuccess) return err;
+  FfnStagedArgs a = staged_args(L, saved, xd, w, act, nullptr, nullptr);
+  a.tiles = tiles;
+  a.ntiles = ntiles;
   const int G = device_cus() > 0 ? device_cus() : 256;
   if (L.dtype == MOK_MXFP8)
     hipLaunchKernelGGL(k_gateup_staged<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);

@@ -27,7 +27,7 @@
 namespace mok {
 namespace {
 
-constexpr int kMaxXcd = 8;
+constexpr int kMaxXcd = kXcds;
 
 struct FusedArgs {
   const int32_t* hdr;
@@ -44,6 +44,10 @@ struct FusedArgs {
   uint16_t* slots;
   int32_t* cnt;              // [kCntWords + 3 * tiles_max]
   int32_t* err;
+  int32_t* rhdr;             // ring state for the backward (in saved): header,
+  MTile* rtiles;             //   copy of the tile table,
+  int32_t* rslot;            //   slot id (x * capt + slot) of every tile,
+  int32_t* rowner;           //   last tile written to every slot
   int64_t tiles_max;
   int comm_per_xcd;
   int K, T, dtype;
@@ -132,11 +136,23 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
 
   if (local < C) {
     // ---- dispatch worker: pull the rows of this XCD's tiles into their ring slots ----
+    if (ax == 0 && local == 0 && tid == 0) {
+      a.rhdr[kRhTiles] = nt;
+      a.rhdr[kRhCapt] = a.capt;
+    }
     for (int q = 0;; ++q) {
       const int mt = ax + q * nact;
       if (mt >= nt) break;
       if (q >= a.capt && !wait_geq(dn_done + (mt - a.capt * nact), ndn, a.err, a.spin_limit)) return;
       const MTile tl = a.tiles[mt];
+      if (local == 0 && tid == 0) {
+        // One thread per XCD records the tiles in order, so each slot's owner ends as the
+        // last tile that used it.
+        const int slot = x * a.capt + q % a.capt;
+        a.rtiles[mt] = tl;
+        a.rslot[mt] = slot;
+        a.rowner[slot] = mt;
+      }
       const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
                                       a.dtype, true);
       for (int r = local * 4 + wave; r < tl.nrows; r += 4 * C) {
@@ -185,14 +201,9 @@ hipError_t allow_big_lds(F* f) {
 
 }  // namespace
 
-int64_t fused_tile_slot_bytes(const Layout& L) {
-  return align_up(int64_t(kTileM) * (L.x_row_bytes + L.gu_row_bytes + L.h_row_bytes), 256);
-}
+int64_t fused_tile_slot_bytes(const Layout& L) { return L.tsb; }
 
-int fused_slots_per_xcd(const Layout& L, int64_t ring_bytes) {
-  const int64_t share = ring_bytes / kMaxXcd / 256 * 256;
-  return int(share / fused_tile_slot_bytes(L));
-}
+int fused_slots_per_xcd(const Layout& L) { return L.ring_capt; }
 
 hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
                             const void* const* x_seg, const mok_weights& w, uint8_t* ring,
@@ -217,9 +228,18 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   a.ntiles = reinterpret_cast<const int32_t*>(ws) + kWsNumTiles;
   a.x_seg = reinterpret_cast<const uint16_t* const*>(x_seg);
   a.ring = ring;
-  a.ring_share = d.ring_bytes / kMaxXcd / 256 * 256;
-  a.tsb = fused_tile_slot_bytes(L);
-  a.capt = fused_slots_per_xcd(L, d.ring_bytes);
+  a.ring_share = L.ring_share;
+  a.tsb = L.tsb;
+  a.capt = L.ring_capt;
+  uint8_t* sv = const_cast<uint8_t*>(saved);
+  a.rhdr = reinterpret_cast<int32_t*>(sv + L.sv_rhdr);
+  a.rtiles = reinterpret_cast<MTile*>(sv + L.sv_rtiles);
+  a.rslot = reinterpret_cast<int32_t*>(sv + L.sv_rslot);
+  a.rowner = reinterpret_cast<int32_t*>(sv + L.sv_rowner);
+  // no tile is resident until the kernel records it
+  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(a.rowner), 0xFFFFFFFFu,
+                             int64_t(kXcds) * L.ring_capt, s)) != hipSuccess)
+    return err;
   a.s = FfnShape{L.H, L.I};
   if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
   else a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),

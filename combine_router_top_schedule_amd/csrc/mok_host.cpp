@@ -124,7 +124,7 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   sizes->act_bytes = size_t(L.act_bytes);
   sizes->wq_bytes = size_t(L.wq_bytes);
   sizes->rows_max = L.rows_max;
-  sizes->ring_slots = 8 * fused_slots_per_xcd(L, desc->ring_bytes);
+  sizes->ring_slots = kXcds * fused_slots_per_xcd(L);
   sizes->minibatch = L.M;
   sizes->slot_bytes = fused_tile_slot_bytes(L);
   sizes->perm_offset = L.sv_perm;
@@ -142,6 +142,10 @@ mok_status mok_schedule(const mok_desc* desc, const float* logits_dev, int32_t* 
   const Layout L = layout_of(*desc);
   hipStream_t s = as_stream(stream);
   hipError_t e = launch_fill_u32(static_cast<uint32_t*>(ws_dev), 0u, kWsWords, s);
+  // the staged path leaves nothing in the ring for the backward
+  if (e == hipSuccess)
+    e = launch_fill_u32(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(saved_dev) + L.sv_rhdr), 0u,
+                        kRhWords, s);
   if (e != hipSuccess) return MOK_ERR_HIP;
   return hip_status(launch_router(L, logits_dev, topk_idx_dev, topk_p_dev,
                                   static_cast<uint8_t*>(saved_dev), static_cast<uint8_t*>(ws_dev), s));
@@ -229,11 +233,12 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
       !aligned16(slots_dev) || !aligned16(ws_dev))
     return MOK_ERR_ALIGN;
   const Layout L = layout_of(*desc);
-  if (fused_slots_per_xcd(L, desc->ring_bytes) < 2) return MOK_ERR_RING;
+  if (fused_slots_per_xcd(L) < 2) return MOK_ERR_RING;
   hipStream_t s = as_stream(stream);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   uint8_t* saved = static_cast<uint8_t*>(saved_dev);
   hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(ws), 0u, kWsWords, s);
+  if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(saved + L.sv_rhdr), 0u, kRhWords, s);
   if (e == hipSuccess) e = launch_router(L, logits_dev, topk_idx_dev, topk_p_dev, saved, ws, s);
   if (e == hipSuccess)
     e = launch_layer_fwd(L, *desc, saved, x_seg_dev, *w, static_cast<uint8_t*>(ring_dev),
@@ -250,7 +255,6 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
                          const void* saved_dev, void* ring_dev, void* slots_dev,
                          void* const* dx_seg_dev, float* dp_dev, float* dlogits_dev,
                          const mok_weight_grads* g, void* ws_dev, void* stream) {
-  (void)ring_dev;
   mok_status st = check_desc(desc);
   if (st != MOK_OK) return st;
   if (!dout_seg_dev || !x_seg_dev || !w || !topk_idx_dev || !topk_p_dev || !saved_dev ||
@@ -298,6 +302,7 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
   b.q_dgt = ws + L.b_qdgt;
   b.q_dut = ws + L.b_qdut;
   b.q_ht = ws + L.b_qht;
+  b.ring = static_cast<uint8_t*>(ring_dev);
   return hip_status(launch_backward(L, b, as_stream(stream)));
 }
 

@@ -17,6 +17,7 @@ constexpr int kTopkTokensPerBlock = 256;
 constexpr int kMaxLocalExperts = 64;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
+constexpr int kXcds = 8;            // XCDs per MI355X device (each with its own L2)
 
 __host__ __device__ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -39,6 +40,14 @@ enum WsHeader : int {
   kWsWords = 64,
 };
 
+// Ring state left in `saved` by the fused forward for the backward: the forward's tile table,
+// the ring slot of every tile (x * capt + slot), and the last tile written to every slot.
+enum RingHeader : int {
+  kRhTiles = 0,     // forward tiles (0: the ring holds nothing, e.g. after the staged path)
+  kRhCapt = 1,      // tile slots per XCD
+  kRhWords = 16,
+};
+
 // Backward header (its own 256 words in the backward part of the workspace).
 enum Bwd2Header : int {
   kB2RowsPad = 0,   // padded columns of the per-expert transposed planes
@@ -56,6 +65,10 @@ struct Layout {
   int row_align;
   // saved
   int64_t sv_perm, sv_tokpos, sv_touched, sv_bytes;
+  int64_t sv_rhdr, sv_rtiles, sv_rslot, sv_rowner;
+  // fused-forward ring: bytes per XCD share, per tile slot, slots per XCD
+  int64_t ring_share, tsb;
+  int ring_capt;
   // ws
   int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_bytes;
   int topk_blocks;
@@ -67,7 +80,8 @@ struct Layout {
   // backward workspace (after the forward ws): byte offsets from the ws start
   int64_t rp_max;
   int64_t b_hdr2, b_xd, b_act, b_d, b_dq, b_dgu, b_dguq, b_dp, b_wdt, b_wgt, b_wut;
-  int64_t b_xt, b_dt, b_dgt, b_dut, b_ht, b_qxt, b_qdt, b_qdgt, b_qdut, b_qht, b_bytes;
+  int64_t b_xt, b_dt, b_dgt, b_dut, b_ht, b_qxt, b_qdt, b_qdgt, b_qdut, b_qht;
+  int64_t b_restore, b_replay, b_rsl, b_counts, b_bytes;
 };
 
 // Bytes of an activation row of width `w` elements in the activation format: BF16, or
@@ -87,26 +101,34 @@ inline Layout make_layout(const mok_desc& d) {
   int kk = L.K < L.El ? L.K : L.El;
   L.rows_max = L.N * kk + int64_t(L.El) * (L.row_align - 1);
   L.M = d.minibatch_tokens;
+  L.J_max = L.M > 0 ? cdiv(L.rows_max, L.M) : 1;
+  L.tiles_max = cdiv(L.rows_max, kTileM) + L.J_max + L.El + 1;
+  // activation rows
+  L.x_row_bytes = act_row_bytes(L.H, L.dtype);
+  L.gu_row_bytes = int64_t(2) * L.I * 2;
+  L.h_row_bytes = act_row_bytes(L.I, L.dtype);
+  // fused-forward ring: one share per XCD, cut into tile slots of kTileM rows (X | g,u | h)
+  L.tsb = align_up(int64_t(kTileM) * (L.x_row_bytes + L.gu_row_bytes + L.h_row_bytes), 256);
+  L.ring_share = d.ring_bytes / kXcds / 256 * 256;
+  L.ring_capt = int(L.ring_share / L.tsb);
   // saved
   int64_t off = 1024;
   L.sv_perm = off; off = align_up(off + 4 * L.rows_max, 256);
   L.sv_tokpos = off; off = align_up(off + 4 * L.NK, 256);
   L.sv_touched = off; off = align_up(off + 4 * L.N, 256);
+  L.sv_rhdr = off; off = align_up(off + 4 * kRhWords, 256);
+  L.sv_rtiles = off; off = align_up(off + 16 * L.tiles_max, 256);
+  L.sv_rslot = off; off = align_up(off + 4 * L.tiles_max, 256);
+  L.sv_rowner = off; off = align_up(off + 4 * int64_t(kXcds) * (L.ring_capt > 0 ? L.ring_capt : 1), 256);
   L.sv_bytes = off;
   // ws
   L.topk_blocks = int(cdiv(L.N, kTopkTokensPerBlock));
-  L.J_max = L.M > 0 ? cdiv(L.rows_max, L.M) : 1;
-  L.tiles_max = cdiv(L.rows_max, kTileM) + L.J_max + L.El + 1;
   off = 256;
   L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 1), 256);
   L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
   L.ws_counters = off; off = align_up(off + 4 * (64 + 3 * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
   L.ws_bytes = off;
-  // activation rows
-  L.x_row_bytes = act_row_bytes(L.H, L.dtype);
-  L.gu_row_bytes = int64_t(2) * L.I * 2;
-  L.h_row_bytes = act_row_bytes(L.I, L.dtype);
   // staged
   L.xd_bytes = align_up(L.rows_max * L.x_row_bytes, 256);
   L.act_bytes = align_up(L.rows_max * (L.gu_row_bytes + L.h_row_bytes), 256);
@@ -139,6 +161,10 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_qdgt = take(mx ? I * rp * 33 / 32 : 0);
   L.b_qdut = take(mx ? I * rp * 33 / 32 : 0);
   L.b_qht = take(mx ? I * rp * 33 / 32 : 0);
+  L.b_restore = take(16 * L.tiles_max);
+  L.b_replay = take(16 * L.tiles_max);
+  L.b_rsl = take(4 * L.tiles_max);
+  L.b_counts = take(64);
   L.b_bytes = off;
   return L;
 }
@@ -189,6 +215,10 @@ hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_
                              hipStream_t s);
 hipError_t launch_ffn_gateup(const Layout& L, const uint8_t* saved, const uint8_t* xd,
                              const mok_weights& w, uint8_t* act, uint8_t* ws, hipStream_t s);
+// Gate/up GEMM over an explicit tile list (device array and device count).
+hipError_t launch_ffn_gateup_list(const Layout& L, const uint8_t* saved, const uint8_t* xd,
+                                  const mok_weights& w, uint8_t* act, const MTile* tiles,
+                                  const int32_t* ntiles, hipStream_t s);
 
 // Device buffers of one backward call (carved out of the workspace by the host code).
 struct BwdBuffers {
@@ -211,13 +241,14 @@ struct BwdBuffers {
   uint16_t *wdt, *wgt, *wut;
   uint16_t *xt, *dt, *dgt, *dut, *ht;
   uint8_t *q_xt, *q_dt, *q_dgt, *q_dut, *q_ht;
+  uint8_t* ring;      // the forward's ring (null: replay every row)
 };
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
 
 // Fused forward (k_fused.hip): the ring is split into one share per XCD, each cut into tile
 // slots of 256 expert-ordered rows (X | g,u | h).
 int64_t fused_tile_slot_bytes(const Layout& L);
-int fused_slots_per_xcd(const Layout& L, int64_t ring_bytes);
+int fused_slots_per_xcd(const Layout& L);
 hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
                             const void* const* x_seg, const mok_weights& w, uint8_t* ring,
                             uint16_t* slots, uint8_t* ws, hipStream_t s);

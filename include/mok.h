@@ -209,7 +209,12 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
  *   dp_dev       fp32 [N][K], written at local pairs only
  *   dlogits_dev  fp32 [N][E] or NULL; must be NULL unless E_loc == E
  *   g            weight gradients, fully overwritten
- * saved_dev and ring_dev must hold the state the matching mok_layer_fwd left. */
+ *   ring_dev     the ring the matching mok_layer_fwd used, untouched since (or NULL). Row tiles
+ *                whose ring slot still holds them give back their g|u and h; all other rows
+ *                are replayed (X gathered again, gate/up recomputed). After the staged path
+ *                (mok_schedule ...) or with NULL every row is replayed. The results are the
+ *                same bit for bit either way.
+ * saved_dev must hold the state the matching forward left (schedule table and ring record). */
 mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
                          const void* const* x_seg_dev, const mok_weights* w,
                          const int32_t* topk_idx_dev, const float* topk_p_dev,

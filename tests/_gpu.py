@@ -103,13 +103,25 @@ class BwdCase(Case):
         self.dwu = torch.empty_like(self.dwg)
         self.dwd = torch.empty((cfg.E_loc, cfg.H, cfg.I), dtype=torch.float32, device="cuda")
 
-    def run(self):
+    def run(self, fused: bool = False):
+        """Forward (staged, or fused through the ring) then mok_layer_bwd."""
         L = self.layer
-        L.forward_staged(self.x_seg, self.logits, self.out_seg)
+        if fused:
+            L.forward(self.x_seg, self.logits, self.out_seg)
+        else:
+            L.forward_staged(self.x_seg, self.logits, self.out_seg)
         mok.mok_layer_bwd(self.d, self.dout_seg, self.x_seg, L.w, L.idx, L.p, L.saved, L.ring,
                           L.slots, self.dx_seg, self.dp, self.dlogits, self.dwg, self.dwu,
                           self.dwd, self.bws)
         torch.cuda.synchronize()
+        assert mok.mok_device_status(L.ws) == 0
+
+    def grads(self):
+        """Copies of every backward output."""
+        out = [self.dx, self.dp, self.dwg, self.dwu, self.dwd]
+        if self.dlogits is not None:
+            out.append(self.dlogits)
+        return [t.clone() for t in out]
 
     def oracle_backward(self, fw=None):
         cfg = self.cfg

@@ -13,6 +13,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
+import combine_router_top_schedule_amd as mok
 from tests._gpu import BF16_TOL, MX_TOL, BwdCase, frob_rel_err, host_u16, max_rel_err
 
 
@@ -114,3 +115,36 @@ def test_backward_dsv3_sampled():
         du = dh * g * sg
         assert max_rel_err(dwg[i], dg @ X) <= BF16_TOL
         assert max_rel_err(dwu[i], du @ X) <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_backward_reuses_ring_after_fused_forward(dtype):
+    """Reverse ring walk: after a fused forward through a ring of 2 tile slots per XCD (~16 of
+    ~64 row tiles stay resident) the backward restores the resident tiles' activations and
+    replays the rest. Matches the oracle, and equals bit for bit the backward after a staged
+    forward (which leaves nothing resident, so every row is replayed)."""
+    cfg = datagen.CONFIGS["tiny"].replace(S=4, T=256, dtype=dtype, M=64, x_std=1.0)
+    tsb = mok.query_sizes(mok.desc_from_config(cfg)).slot_bytes
+    case = BwdCase(cfg, fused=True, ring_bytes=8 * 2 * tsb)
+    case.run(fused=True)
+    after_fused = case.grads()
+    fw, bw = case.oracle_backward()
+    tol_fn, tol = (max_rel_err, BF16_TOL) if dtype == "bf16" else (frob_rel_err, MX_TOL)
+    _compare(case, fw, bw, tol_fn, tol)
+    case.run(fused=False)
+    for a, b in zip(after_fused, case.grads()):
+        assert torch.equal(a, b)
+    case.run(fused=True)
+    for a, b in zip(after_fused, case.grads()):
+        assert torch.equal(a, b)
+
+
+def test_backward_dsv3_after_fused_forward_equals_staged():
+    """DeepSeek-V3-shaped local share through the 256 MiB ring: the backward that reuses the
+    resident tiles equals the full-replay backward bit for bit."""
+    case = BwdCase(datagen.CONFIGS["dsv3"], fused=True)
+    case.run(fused=True)
+    after_fused = case.grads()
+    case.run(fused=False)
+    for a, b in zip(after_fused, case.grads()):
+        assert torch.equal(a, b)
