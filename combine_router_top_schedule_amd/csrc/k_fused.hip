@@ -16,11 +16,14 @@
 // done. Down-GEMM results are pushed to the pair slots; the weighted merge runs as the next
 // kernel on the stream.
 //
-// Deadlock freedom: all workgroups are co-resident (cooperative launch, one per CU). Within an
-// XCD, GEMM work items are numbered tile by tile (gate/up tiles, then down tiles) and each
-// GEMM worker takes items i = worker, worker + G, ... in order; every wait is on an earlier
-// item or on the gather of a tile whose slot was released by earlier items. Every wait is
-// bounded; an expired wait sets the error word and all workers drain.
+// Work order and deadlock freedom: all workgroups are co-resident (cooperative launch, one per
+// CU). Within an XCD the GEMM items are numbered gu(0), then blocks [gu(q+1), dn(q)] for
+// q = 0, 1, ... (gu = the gate/up column tiles of a row tile, dn = its down column tiles), so
+// the down tiles of a row tile come one block after its gate/up tiles and workers rarely wait
+// for them. Each GEMM worker takes items i = worker, worker + G, ... in order. Every wait is on
+// a lower-numbered item: dn(q) on gu(q), and gu(q) on the gather of tile q, whose slot was freed
+// by dn(q - capt), numbered below gu(q) whenever capt >= 2. Every wait is bounded; an expired
+// wait sets the error word and all workers drain.
 #include "k_ffn.h"
 #include "mok_rows.h"
 
@@ -172,7 +175,23 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   const int gi = local - C;
   const int per_tile = ngu + ndn;
   for (int it = gi;; it += G) {
-    const int q = it / per_tile, k = it % per_tile;
+    // item -> (row tile q, column item k): k < ngu is gate/up column tile k, else down tile
+    int q, k;
+    if (it < ngu) {
+      q = 0;
+      k = it;
+    } else {
+      const int blk = (it - ngu) / per_tile, off = (it - ngu) % per_tile;
+      if (ax + blk * nact >= nt) break;               // no down work left: done
+      if (off < ngu) {
+        q = blk + 1;
+        k = off;
+        if (ax + q * nact >= nt) continue;            // no such row tile: nothing to do
+      } else {
+        q = blk;
+        k = off;
+      }
+    }
     const int mt = ax + q * nact;
     if (mt >= nt) break;
     const MTile tl = a.tiles[mt];
