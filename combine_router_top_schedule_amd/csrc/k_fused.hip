@@ -158,10 +158,22 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
       }
       const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
                                       a.dtype, true);
-      for (int r = local * 4 + wave; r < tl.nrows; r += 4 * C) {
-        const int32_t pair = a.perm[tl.row0 + r];
-        const int64_t n = pair / a.K;
-        const uint16_t* src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.s.H);
+      // This wave's rows are r = local*4 + wave + j*4C; lane j looks up row j's source first
+      // (one round of dependent loads per tile instead of one per row).
+      const int r0 = local * 4 + wave, rstep = 4 * C;
+      const uint16_t* my_src = nullptr;
+      {
+        const int r = r0 + lane * rstep;
+        if (lane * rstep < kTileM && r < tl.nrows) {
+          const int64_t n = a.perm[tl.row0 + r] / a.K;
+          my_src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.s.H);
+        }
+      }
+      for (int j = 0; r0 + j * rstep < tl.nrows; ++j) {
+        const int r = r0 + j * rstep;
+        const uint64_t sp = reinterpret_cast<uint64_t>(my_src);
+        const uint32_t lo = __shfl(uint32_t(sp), j, 64), hi = __shfl(uint32_t(sp >> 32), j, 64);
+        const uint16_t* src = reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
         if (MX) quant_row_mx(src, pl.x + int64_t(r) * a.s.H, pl.xs + int64_t(r) * (a.s.H / 32), a.s.H, lane);
         else copy_row_bf16(src, reinterpret_cast<uint16_t*>(pl.x) + int64_t(r) * a.s.H, a.s.H, lane);
       }

@@ -7,53 +7,60 @@
 
 namespace mok {
 
-// Copy one BF16 row of H elements (src == nullptr writes zeros).
+// Copy one BF16 row of H elements (src == nullptr writes zeros). Up to 16 chunks of 16 bytes
+// per lane are loaded before any is stored, so a wave keeps a whole 16 KB row in flight.
 __device__ __forceinline__ void copy_row_bf16(const uint16_t* src, uint16_t* dst, int H, int lane) {
   const int nch = H / 8;
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
   u32x4* d = reinterpret_cast<u32x4*>(dst);
-  for (int c0 = 0; c0 < nch; c0 += 64 * 8) {
-    u32x4 v[8];
+  for (int c0 = 0; c0 < nch; c0 += 64 * 16) {
+    u32x4 v[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int c = c0 + q * 64 + lane;
       v[q] = (src && c < nch) ? s[c] : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int c = c0 + q * 64 + lane;
       if (c < nch) d[c] = v[q];
     }
   }
 }
 
-// Quantise one BF16 row of H elements to MXFP8 along H: codes [H], scales [H/32].
+// Quantise one BF16 row of H elements to MXFP8 along H: codes [H], scales [H/32]. Each lane
+// loads the 64 bytes of up to 4 blocks before quantising any, to keep loads in flight.
 __device__ __forceinline__ void quant_row_mx(const uint16_t* src, uint8_t* codes, uint8_t* scales,
                                              int H, int lane) {
   const int nblk = H / 32;
-  for (int b = lane; b < nblk; b += 64) {
-    float v[32];
-    if (src) {
-      const u32x4* s = reinterpret_cast<const u32x4*>(src + b * 32);
+  for (int b0 = 0; b0 < nblk; b0 += 64 * 4) {
+    u32x4 raw[4][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 w = s[q];
+    for (int j = 0; j < 4; ++j) {
+      const int b = b0 + j * 64 + lane;
+      const u32x4* s = reinterpret_cast<const u32x4*>(src + int64_t(b) * 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) raw[j][q] = (src && b < nblk) ? s[q] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = b0 + j * 64 + lane;
+      if (b >= nblk) continue;
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[q * 8 + 2 * i] = __uint_as_float(w[i] << 16);
-          v[q * 8 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+          v[q * 8 + 2 * i] = __uint_as_float(raw[j][q][i] << 16);
+          v[q * 8 + 2 * i + 1] = __uint_as_float(raw[j][q][i] & 0xFFFF0000u);
         }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = 0.f;
+      uint32_t c8[8];
+      const uint32_t sc = mx_quant32(v, c8);
+      u32x4* d = reinterpret_cast<u32x4*>(codes + b * 32);
+      d[0] = u32x4{c8[0], c8[1], c8[2], c8[3]};
+      d[1] = u32x4{c8[4], c8[5], c8[6], c8[7]};
+      scales[b] = uint8_t(sc);
     }
-    uint32_t c8[8];
-    const uint32_t sc = mx_quant32(v, c8);
-    u32x4* d = reinterpret_cast<u32x4*>(codes + b * 32);
-    d[0] = u32x4{c8[0], c8[1], c8[2], c8[3]};
-    d[1] = u32x4{c8[4], c8[5], c8[6], c8[7]};
-    scales[b] = uint8_t(sc);
   }
 }
 
