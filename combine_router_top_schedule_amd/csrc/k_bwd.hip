@@ -280,6 +280,15 @@ __global__ __launch_bounds__(256) void k_bwd_stage(StageArgs a) {
 
 // ---- backward GEMM kernels ------------------------------------------------------------------
 
+struct WJob {
+  const uint8_t* t_a;      // [Fa][ld] BF16 or codes (rows = output rows)
+  const uint8_t* t_a_s;    // MXFP8 scales [Fa][ld/32]
+  const uint8_t* t_b;      // [Fb][ld]
+  const uint8_t* t_b_s;
+  int Fa, Fb;              // output rows, output columns
+  float* dw;               // [El][Fa][Fb]
+};
+
 struct BwdArgs {
   const MTile* tiles;
   const int32_t* ntiles;
@@ -303,14 +312,11 @@ struct BwdArgs {
   const uint8_t* wut;      // Wu^T [El][H][I]
   const uint8_t* wut_s;
   uint16_t* slots;
-  // weight gradients
-  const uint8_t* t_a;      // [F_a][ld] BF16 or codes (first operand, rows = output rows)
-  const uint8_t* t_a_s;
-  const uint8_t* t_b;      // [F_b][ld]
-  const uint8_t* t_b_s;
+  // weight gradients: up to three jobs dW[e] = Ta[:, cols of e] . Tb[:, cols of e]^T
+  WJob jobs[3];
+  int njobs;
+  int El;
   int64_t ld;              // padded columns of the transposed planes
-  int Fa, Fb;              // output rows, output columns
-  float* dw;               // [El][Fa][Fb]
 };
 
 template <bool MX>
@@ -345,21 +351,32 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(BwdArgs a) {
   }
 }
 
-// dW_e [Fa][Fb] = T_a[:, cols of e] . T_b[:, cols of e]^T ; one expert per blockIdx.y.
+// All weight gradients in one persistent launch (so the last wave is shared by every job):
+// tile t runs over jobs, then experts, then 256 x 256 output tiles of dW_e [Fa][Fb] =
+// Ta[:, cols of e] . Tb[:, cols of e]^T.
 template <bool MX>
 __global__ __launch_bounds__(256, 1) void k_wgrad_gemm(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
-  const int e = blockIdx.y;
-  const int c0 = a.hdr2[kB2ColPad + e];
-  const int ncols = a.hdr2[kB2ColPad + e + 1] - c0;
-  const int mtn = (a.Fa + kTileM - 1) / kTileM, ntn = (a.Fb + kTileN - 1) / kTileN;
-  const int total = mtn * ntn;
+  int total = 0;
+  for (int j = 0; j < a.njobs; ++j)
+    total += a.El * ((a.jobs[j].Fa + kTileM - 1) / kTileM) * ((a.jobs[j].Fb + kTileN - 1) / kTileN);
   for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
+    int j = 0, rem = t;
+    for (; j < a.njobs; ++j) {
+      const int per = a.El * ((a.jobs[j].Fa + kTileM - 1) / kTileM) * ((a.jobs[j].Fb + kTileN - 1) / kTileN);
+      if (rem < per) break;
+      rem -= per;
+    }
+    const WJob& jb = a.jobs[j];
+    const int mtn = (jb.Fa + kTileM - 1) / kTileM, ntn = (jb.Fb + kTileN - 1) / kTileN;
+    const int e = rem / (mtn * ntn);
     int mt, nt;
-    tile_coords(t, mtn, ntn, mt, nt);
-    wgrad_tile<MX>(sm, a.t_a, a.t_a_s, a.t_b, a.t_b_s, a.ld, c0, ncols, mt * kTileM, nt * kTileN,
-                   a.Fa, a.Fb, a.dw + int64_t(e) * a.Fa * a.Fb);
+    tile_coords(rem % (mtn * ntn), mtn, ntn, mt, nt);
+    const int c0 = a.hdr2[kB2ColPad + e];
+    const int ncols = a.hdr2[kB2ColPad + e + 1] - c0;
+    wgrad_tile<MX>(sm, jb.t_a, jb.t_a_s, jb.t_b, jb.t_b_s, a.ld, c0, ncols, mt * kTileM, nt * kTileN,
+                   jb.Fa, jb.Fb, jb.dw + int64_t(e) * jb.Fa * jb.Fb);
   }
 }
 
@@ -551,26 +568,29 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
           hipSuccess)
         return err;
   }
-  trace_before(MOK_TRACE_WGRAD, s);
-  for (const WG& j : jobs) {
-    BwdArgs w = a;
-    w.ld = ld;
-    w.Fa = j.Fa;
-    w.Fb = j.Fb;
-    w.dw = j.dw;
+  BwdArgs w = a;
+  w.ld = ld;
+  w.El = El;
+  w.njobs = 3;
+  for (int q = 0; q < 3; ++q) {
+    const WG& j = jobs[q];
+    WJob& o = w.jobs[q];
+    o.Fa = j.Fa;
+    o.Fb = j.Fb;
+    o.dw = j.dw;
     if (mx) {
-      w.t_a = j.qa; w.t_a_s = j.qa + int64_t(j.Fa) * ld;
-      w.t_b = j.qb; w.t_b_s = j.qb + int64_t(j.Fb) * ld;
+      o.t_a = j.qa; o.t_a_s = j.qa + int64_t(j.Fa) * ld;
+      o.t_b = j.qb; o.t_b_s = j.qb + int64_t(j.Fb) * ld;
     } else {
-      w.t_a = reinterpret_cast<const uint8_t*>(j.ta); w.t_a_s = nullptr;
-      w.t_b = reinterpret_cast<const uint8_t*>(j.tb); w.t_b_s = nullptr;
+      o.t_a = reinterpret_cast<const uint8_t*>(j.ta); o.t_a_s = nullptr;
+      o.t_b = reinterpret_cast<const uint8_t*>(j.tb); o.t_b_s = nullptr;
     }
-    const int gx = G;
-    if (mx) hipLaunchKernelGGL(k_wgrad_gemm<true>, dim3(gx, El), dim3(kThreads), kGemmLdsBytes, s, w);
-    else hipLaunchKernelGGL(k_wgrad_gemm<false>, dim3(gx, El), dim3(kThreads), kGemmLdsBytes, s, w);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  trace_before(MOK_TRACE_WGRAD, s);
+  if (mx) hipLaunchKernelGGL(k_wgrad_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, w);
+  else hipLaunchKernelGGL(k_wgrad_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, w);
   trace_after(MOK_TRACE_WGRAD, s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   return hipSuccess;
 }
 
