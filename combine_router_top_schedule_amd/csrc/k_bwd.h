@@ -15,52 +15,70 @@ __device__ __forceinline__ float e4m3_value(uint8_t c) {
   return (c & 0x80) ? -mag : mag;
 }
 
-// One 32-row block (i) of the a-GEMM epilogue; i is a template argument so the accumulator
-// stays in registers.
+// g, u and h of one 32-row x 128-column block of the a-GEMM epilogue, as loaded from the
+// planes: 16 lanes x 16 bytes cover a row, 4 rows per load. Held in registers so the next
+// block's loads are in flight while the current block is computed.
+struct AStage {
+  u32x4 g[8], u[8];
+  u32x4 h[8];          // BF16 values; MXFP8: 8 codes in .x/.y and the block scale code in .z
+};
+
+template <bool MX>
+__device__ __forceinline__ void a_stage_load(AStage& st, const FfnShape& s, int64_t row0,
+                                             int nrows, int colw, int rbase,
+                                             const ActPlanes& act, int lane) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
+    const bool ok = rbase + rr < nrows && colw + cc < s.I;
+    const int64_t pr = row0 + (ok ? rbase + rr : 0);
+    const int col = ok ? colw + cc : 0;
+    st.g[q] = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + col);
+    st.u[q] = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + s.I + col);
+    if (MX) {
+      const uint2 hv = *reinterpret_cast<const uint2*>(act.h + pr * s.I + col);
+      st.h[q] = u32x4{hv.x, hv.y, uint32_t(act.hs[pr * (s.I / 32) + col / 32]), 0u};
+    } else {
+      st.h[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(act.h) + pr * s.I + col);
+    }
+  }
+}
+
+// Write a loaded block into the wave's LDS region (MXFP8 h decoded to BF16, exact).
+template <bool MX>
+__device__ __forceinline__ void a_stage_store(const AStage& st, uint16_t* lg, uint16_t* lu,
+                                              uint16_t* lh, int lane) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
+    *reinterpret_cast<u32x4*>(lg + rr * 128 + cc) = st.g[q];
+    *reinterpret_cast<u32x4*>(lu + rr * 128 + cc) = st.u[q];
+    if (MX) {
+      const float scale = exp2i(int(st.h[q][2]) - 127);
+      u32x4 packed;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = k < 2 ? st.h[q][0] : st.h[q][1];
+        const int sh = (k & 1) * 16;
+        packed[k] = pack_bf2(e4m3_value(uint8_t(w >> sh)) * scale,
+                             e4m3_value(uint8_t(w >> (sh + 8))) * scale);
+      }
+      *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) = packed;
+    } else {
+      *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) = st.h[q];
+    }
+  }
+}
+
+// Compute one staged 32-row block (i, a template argument so the accumulator stays in
+// registers): dg, du in place of g, u in LDS, dp partials, then dg | du rows out.
 template <bool MX, int i>
 __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], const FfnShape& s,
                                                  int64_t row0, int nrows, int colw,
-                                                 const ActPlanes& act, const int32_t* perm,
-                                                 const float* p, uint16_t* dgu, float* s_dp,
-                                                 uint16_t* lg, uint16_t* lu, uint16_t* lh,
-                                                 float* lpg, int wm, int wn, int lane) {
-
+                                                 uint16_t* dgu, float* s_dp,
+                                                 uint16_t* lg, uint16_t* lu, const uint16_t* lh,
+                                                 const float* lpg, int wm, int wn, int lane) {
     const int rbase = wm * 128 + i * 32;                                // tile row of lg row 0
-    if (lane < 32) {
-      const bool ok = rbase + lane < nrows;
-      lpg[lane] = ok ? p[perm[row0 + rbase + lane]] : 0.f;
-    }
-    // 32 rows x 128 columns: 16 lanes x 16 B cover a row of g (or u); 4 rows per instruction.
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
-      const bool ok = rbase + rr < nrows && colw + cc < s.I;
-      const int64_t pr = row0 + (ok ? rbase + rr : 0);
-      const int col = ok ? colw + cc : 0;
-      u32x4 gv = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + col);
-      u32x4 uv = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + s.I + col);
-      *reinterpret_cast<u32x4*>(lg + rr * 128 + cc) = gv;
-      *reinterpret_cast<u32x4*>(lu + rr * 128 + cc) = uv;
-      if (MX) {
-        // 8 codes at col (8-byte aligned), decoded with the block's scale
-        const uint2 hv = *reinterpret_cast<const uint2*>(act.h + pr * s.I + col);
-        const float scale = exp2i(int(act.hs[pr * (s.I / 32) + col / 32]) - 127);
-        u32x4 packed;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t w = k < 2 ? hv.x : hv.y;
-          const int sh = (k & 1) * 16;
-          packed[k] = pack_bf2(e4m3_value(uint8_t(w >> sh)) * scale,
-                               e4m3_value(uint8_t(w >> (sh + 8))) * scale);
-        }
-        *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) = packed;
-      } else {
-        *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) =
-            *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(act.h) + pr * s.I + col);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int lr = acc_row(v, lane);                                  // row inside the block
@@ -78,7 +96,7 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         const float u = bf2f(lu[lr * 128 + lc]);
         const float h = bf2f(lh[lr * 128 + lc]);
         const float dh = pg * av;
-        const float sg = 1.f / (1.f + expf(-g));
+        const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
         const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
         const float duv = dh * g * sg;
         // dg and du replace g and u in place (each element is read and written by this lane)
@@ -91,7 +109,7 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
       for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
       if ((lane & 31) == 0) s_dp[wn * 256 + r] = part;
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    // (a wave's LDS accesses complete in order: no wait before reading dg | du back)
     __builtin_amdgcn_wave_barrier();
     // dg | du rows out with 16-byte stores, 16 lanes per row
 #pragma unroll
@@ -103,7 +121,6 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         *reinterpret_cast<u32x4*>(dst + s.I) = *reinterpret_cast<const u32x4*>(lu + rr * 128 + cc);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
   }
 
@@ -144,11 +161,28 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   uint16_t* lu = lg + 32 * 128;
   uint16_t* lh = lu + 32 * 128;   // BF16 (exact for decoded E4M3 values too)
   const int colw = c0 + wn * 128;                                       // wave's first column
-  float* lpg = reinterpret_cast<float*>(sm.b[1] + 4096) + wave * 32;     // gates of the 32 rows
-  a_epilogue_block<MX, 0>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
-  a_epilogue_block<MX, 1>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
-  a_epilogue_block<MX, 2>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
-  a_epilogue_block<MX, 3>(acc, s, row0, nrows, colw, act, perm, p, dgu, s_dp, lg, lu, lh, lpg, wm, wn, lane);
+  float* lpg = reinterpret_cast<float*>(sm.b[1] + 4096) + wave * 128;    // gates of the wave's rows
+  // gates of the wave's 128 rows (lane l: row wm*128 + l, l < 128 over two halves)
+  for (int l = lane; l < 128; l += 64) {
+    const int r = wm * 128 + l;
+    lpg[l] = r < nrows ? p[perm[row0 + r]] : 0.f;
+  }
+  AStage st;
+  a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128, act, lane);
+#define MOK_A_BLOCK(I_)                                                                          \
+  {                                                                                              \
+    __builtin_amdgcn_s_waitcnt(0);                                                               \
+    a_stage_store<MX>(st, lg, lu, lh, lane);                                                     \
+    if (I_ < 3) a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act, lane);  \
+    __builtin_amdgcn_wave_barrier();                                                             \
+    a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, s_dp, lg, lu, lh, lpg + I_ * 32, wm, \
+                             wn, lane);                                                          \
+  }
+  MOK_A_BLOCK(0)
+  MOK_A_BLOCK(1)
+  MOK_A_BLOCK(2)
+  MOK_A_BLOCK(3)
+#undef MOK_A_BLOCK
   __syncthreads();
   for (int r = tid; r < nrows; r += blockDim.x)
     dp_part[(row0 + r) * nparts + c0 / kTileN] = s_dp[r] + s_dp[256 + r];
