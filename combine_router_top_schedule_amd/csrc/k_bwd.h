@@ -75,7 +75,8 @@ __device__ __forceinline__ void a_stage_store(const AStage& st, uint16_t* lg, ui
 template <bool MX, int i>
 __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], const FfnShape& s,
                                                  int64_t row0, int nrows, int colw,
-                                                 uint16_t* dgu, float* s_dp,
+                                                 uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s,
+                                                 float* s_dp,
                                                  uint16_t* lg, uint16_t* lu, const uint16_t* lh,
                                                  const float* lpg, int wm, int wn, int lane) {
     const int rbase = wm * 128 + i * 32;                                // tile row of lg row 0
@@ -115,10 +116,28 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
-      if (rbase + rr < nrows && colw + cc < s.I) {
-        uint16_t* dst = dgu + (row0 + rbase + rr) * 2 * s.I + colw + cc;
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(lg + rr * 128 + cc);
-        *reinterpret_cast<u32x4*>(dst + s.I) = *reinterpret_cast<const u32x4*>(lu + rr * 128 + cc);
+      const bool wr = rbase + rr < nrows && colw + cc < s.I;
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(lg + rr * 128 + cc);
+      const u32x4 uv = *reinterpret_cast<const u32x4*>(lu + rr * 128 + cc);
+      const int64_t row = row0 + rbase + rr;
+      if (wr) {
+        uint16_t* dst = dgu + row * 2 * s.I + colw + cc;
+        *reinterpret_cast<u32x4*>(dst) = gv;
+        *reinterpret_cast<u32x4*>(dst + s.I) = uv;
+      }
+      if (MX) {
+        // dg | du quantised along I for the dx GEMM: 4 lanes = one 32-column block
+        uint32_t sg, su;
+        const uint2 cg = mx_quant8_group4(gv, &sg);
+        const uint2 cu = mx_quant8_group4(uv, &su);
+        if (wr) {
+          *reinterpret_cast<uint2*>(dgq + row * 2 * s.I + colw + cc) = cg;
+          *reinterpret_cast<uint2*>(dgq + row * 2 * s.I + s.I + colw + cc) = cu;
+          if ((lane & 3) == 0) {
+            dgq_s[row * (2 * s.I / 32) + (colw + cc) / 32] = uint8_t(sg);
+            dgq_s[row * (2 * s.I / 32) + (s.I + colw + cc) / 32] = uint8_t(su);
+          }
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -133,7 +152,7 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
                                        int e, int c0, const uint8_t* d, const uint8_t* d_s,
                                        const uint8_t* wdt, const uint8_t* wdt_s,
                                        const ActPlanes& act, const int32_t* perm, const float* p,
-                                       uint16_t* dgu, float* dp_part) {
+                                       uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s, float* dp_part) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
@@ -175,7 +194,8 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
     a_stage_store<MX>(st, lg, lu, lh, lane);                                                     \
     if (I_ < 3) a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act, lane);  \
     __builtin_amdgcn_wave_barrier();                                                             \
-    a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, s_dp, lg, lu, lh, lpg + I_ * 32, wm, \
+    a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, dgq, dgq_s, s_dp, lg, lu, lh,        \
+                             lpg + I_ * 32, wm,                                                  \
                              wn, lane);                                                          \
   }
   MOK_A_BLOCK(0)

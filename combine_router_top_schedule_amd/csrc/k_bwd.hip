@@ -76,7 +76,8 @@ struct TransposeArgs {
   const uint8_t* plane_s;      // MXFP8 scales of the plane (null: BF16 plane)
   int64_t plane_stride;        // elements per plane row
   int plane_col0;              // first feature column inside the plane
-  uint16_t* dst;               // [F][ld]
+  uint16_t* dst;               // [F][ld] BF16 (when qdst is null)
+  uint8_t* qdst;               // else MXFP8 along tokens: codes [F][ld], then scales [F][ld/32]
   int64_t ld;
   int F, K, T, El;
 };
@@ -177,7 +178,16 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
       for (int k = 0; k < 4; ++k)
         out[k] = uint32_t(t[(cc * 8 + 2 * k) * kTrPitch + f]) |
                  (uint32_t(t[(cc * 8 + 2 * k + 1) * kTrPitch + f]) << 16);
-      *reinterpret_cast<u32x4*>(a.dst + int64_t(f0 + f) * a.ld + c0 + cc * 8) = out;
+      if (a.qdst) {
+        // blocks of 32 padded columns (4 lanes); expert ranges start at multiples of 128
+        uint32_t sc;
+        const uint2 codes = mx_quant8_group4(out, &sc);
+        *reinterpret_cast<uint2*>(a.qdst + int64_t(f0 + f) * a.ld + c0 + cc * 8) = codes;
+        if ((cc & 3) == 0)
+          a.qdst[int64_t(a.F) * a.ld + int64_t(f0 + f) * (a.ld / 32) + (c0 + cc * 8) / 32] = uint8_t(sc);
+      } else {
+        *reinterpret_cast<u32x4*>(a.dst + int64_t(f0 + f) * a.ld + c0 + cc * 8) = out;
+      }
     }
     __syncthreads();
   }
@@ -331,7 +341,8 @@ __global__ __launch_bounds__(256, 1) void k_a_gemm(BwdArgs a) {
     tile_coords(t, mtiles, ntn, mt, nt);
     const MTile tl = a.tiles[mt];
     a_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.d, a.d_s, a.wdt, a.wdt_s, a.act,
-               a.perm, a.p, a.dgu, a.dp_part);
+               a.perm, a.p, a.dgu, const_cast<uint8_t*>(a.dgu_a), const_cast<uint8_t*>(a.dgu_s),
+               a.dp_part);
   }
 }
 
@@ -476,12 +487,8 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   // per-expert tiles (no minibatch cuts) for the backward GEMMs
   if ((err = launch_tiles(L, int(L.rows_max), b.saved, b.ws, s)) != hipSuccess) return err;
   // 2. pull reverse-combine: D[r] = dOut[n(r)] (BF16; quantised along H for the a GEMM)
-  Layout Lb = L;
-  Lb.dtype = MOK_BF16;
-  if ((err = launch_dispatch(Lb, b.saved, b.dout_seg, b.d, s)) != hipSuccess) return err;
-  if (mx && (err = launch_quantize_mx(1, int(L.rows_max), H, reinterpret_cast<const uint16_t*>(b.d),
-                                      0, b.dq, b.dq + L.rows_max * H, s)) != hipSuccess)
-    return err;
+  //    (MXFP8: the gather quantises along H on the way, like the forward dispatch)
+  if ((err = launch_dispatch(L, b.saved, b.dout_seg, mx ? b.dq : b.d, s)) != hipSuccess) return err;
   // 3. transposed BF16 weights for the backward GEMMs
   if (!mx) {
     hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 4096, 8192)), dim3(256), 0, s,
@@ -520,9 +527,6 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   trace_after(MOK_TRACE_A_GEMM, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // 5. dx GEMM, pushed to the slots; then the unweighted fixed-order merge
-  if (mx && (err = launch_quantize_mx(1, int(L.rows_max), 2 * I, b.dgu, 0, b.dguq,
-                                      b.dguq + L.rows_max * 2 * I, s)) != hipSuccess)
-    return err;
   trace_before(MOK_TRACE_DX_GEMM, s);
   if (mx) hipLaunchKernelGGL(k_dx_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   else hipLaunchKernelGGL(k_dx_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
@@ -542,32 +546,24 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
   const uint16_t* const* ds = reinterpret_cast<const uint16_t* const*>(b.dout_seg);
   const int64_t ld = L.rp_max;
+  // (MXFP8: the planes are quantised along tokens as they are written)
   auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
-                int64_t stride, int col0, int F, uint16_t* dst) {
-    TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, ld, F, L.K, L.T, El};
+                int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst) {
+    TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
+                    ld, F, L.K, L.T, El};
     hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
   };
   const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
-  tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt);                         // X^T
-  tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt);                        // (p D)^T
-  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, 0, I, b.dgt);   // dg^T
-  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, I, I, b.dut);   // du^T
-  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht);          // h^T
+  tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt);                         // X^T
+  tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt);                        // (p D)^T
+  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, 0, I, b.dgt, b.q_dgt);  // dg^T
+  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, I, I, b.dut, b.q_dut);  // du^T
+  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht);          // h^T
   if ((err = hipGetLastError()) != hipSuccess) return err;
   struct WG { const uint16_t *ta, *tb; uint8_t *qa, *qb; int Fa, Fb; float* dw; };
   const WG jobs[3] = {{b.dgt, b.xt, b.q_dgt, b.q_xt, I, H, b.g.dwg},
                       {b.dut, b.xt, b.q_dut, b.q_xt, I, H, b.g.dwu},
                       {b.dt, b.ht, b.q_dt, b.q_ht, H, I, b.g.dwd}};
-  if (mx) {
-    // quantise the transposed planes along tokens (blocks of 32 columns)
-    const uint16_t* srcs[5] = {b.xt, b.dt, b.dgt, b.dut, b.ht};
-    uint8_t* dsts[5] = {b.q_xt, b.q_dt, b.q_dgt, b.q_dut, b.q_ht};
-    const int F[5] = {H, H, I, I, I};
-    for (int q = 0; q < 5; ++q)
-      if ((err = launch_quantize_mx(1, F[q], int(ld), srcs[q], 0, dsts[q], dsts[q] + int64_t(F[q]) * ld, s)) !=
-          hipSuccess)
-        return err;
-  }
   BwdArgs w = a;
   w.ld = ld;
   w.El = El;
