@@ -143,7 +143,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_hdr2 = take(4 * kB2Words);
   L.b_xd = take(L.xd_bytes);
   L.b_act = take(L.act_bytes);
-  L.b_d = take(rm * H * 2);
+  L.b_d = take(mx ? 0 : rm * H * 2);      // BF16 D (MXFP8 gathers straight into b_dq)
   L.b_dq = take(mx ? rm * (H + H / 32) : 0);
   L.b_dgu = take(rm * 2 * I * 2);
   L.b_dguq = take(mx ? rm * (2 * I + 2 * I / 32) : 0);
@@ -151,11 +151,12 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_wdt = take(mx ? 0 : int64_t(L.El) * H * I * 2);
   L.b_wgt = take(mx ? 0 : int64_t(L.El) * H * I * 2);
   L.b_wut = take(mx ? 0 : int64_t(L.El) * H * I * 2);
-  L.b_xt = take(H * rp * 2);
-  L.b_dt = take(H * rp * 2);
-  L.b_dgt = take(I * rp * 2);
-  L.b_dut = take(I * rp * 2);
-  L.b_ht = take(I * rp * 2);
+  // BF16 transposed planes (MXFP8 writes only the quantised planes below)
+  L.b_xt = take(mx ? 0 : H * rp * 2);
+  L.b_dt = take(mx ? 0 : H * rp * 2);
+  L.b_dgt = take(mx ? 0 : I * rp * 2);
+  L.b_dut = take(mx ? 0 : I * rp * 2);
+  L.b_ht = take(mx ? 0 : I * rp * 2);
   L.b_qxt = take(mx ? H * rp * 33 / 32 : 0);
   L.b_qdt = take(mx ? H * rp * 33 / 32 : 0);
   L.b_qdgt = take(mx ? I * rp * 33 / 32 : 0);

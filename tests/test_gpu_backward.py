@@ -148,3 +148,30 @@ def test_backward_dsv3_after_fused_forward_equals_staged():
     case.run(fused=False)
     for a, b in zip(after_fused, case.grads()):
         assert torch.equal(a, b)
+
+
+def test_kimi_mxfp8_skew_sampled():
+    """Kimi-K2-shaped local share in MXFP8 under Zipf-skewed routing, full size, fused forward
+    through the ring and the backward that reuses it: counts bit-exact against the oracle's
+    top-k over all tokens; forward outputs, dX and dp of 48 sampled touched tokens recomputed
+    by the oracle one token at a time (every quantisation block of these outputs lies inside
+    one token's row)."""
+    cfg = datagen.CONFIGS["kimi_mx_skew"]
+    case = BwdCase(cfg, fused=True)
+    case.run(fused=True)
+    hdr, perm, tokpos, touched = case.layer.table()
+    idx_all, _ = mo.topk_gating(case.logits_h, cfg.K)
+    sched = mo.schedule(idx_all, cfg.e0, cfg.E_loc, cfg.M, 32)
+    assert np.array_equal(hdr[16:16 + cfg.E_loc].numpy(), sched.counts)
+    U = int(hdr[2])
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(touched.numpy()[:U], 48, replace=False))
+    fw = case.oracle_forward(tokens=sample)
+    assert frob_rel_err(case.out_rows(sample), fw.out) <= MX_TOL
+    W = case.oracle_weights()
+    bw = mo.backward(fw, lambda r: mo.decode_bf16(case.dout_h[sample[r]]), W, cfg.K, cfg.e0,
+                     cfg.E_loc, cfg.E)
+    assert frob_rel_err(mo.decode_bf16(host_u16(case.dx)[sample]), bw.dx) <= MX_TOL
+    dp = case.dp.cpu().numpy().reshape(cfg.N, cfg.K)[sample]
+    local = (fw.idx >= cfg.e0) & (fw.idx < cfg.e0 + cfg.E_loc)
+    assert frob_rel_err(dp[local], bw.dp[local]) <= MX_TOL
