@@ -23,26 +23,40 @@ namespace {
 
 // ---- transposes -------------------------------------------------------------------------
 
-// W [batch][R][C] -> WT [batch][C][R], BF16; 64 x 64 tiles through LDS.
+// W [batch][R][C] -> WT [batch][C][R], BF16 (R, C multiples of 128): tiles of 64 rows x 128
+// columns, 16-byte loads along C into an LDS tile with a 260-byte pitch, 16-byte stores of 8
+// consecutive rows of one column.
 __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* src, uint16_t* dst, int batch,
                                                      int R, int C) {
-  __shared__ uint16_t t[64][66];
-  const int tr = R / 64, tc = C / 64;
+  constexpr int kPitch = 130;
+  __shared__ __attribute__((aligned(16))) uint16_t t[64 * kPitch];
+  const int tid = threadIdx.x;
+  const int tr = R / 64, tc = C / 128;
   const int64_t total = int64_t(batch) * tr * tc;
   for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
-    const int b = int(q / (int64_t(tr) * tc));
+    const int bt = int(q / (int64_t(tr) * tc));
     const int rem = int(q % (int64_t(tr) * tc));
-    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 64;
-    const uint16_t* s = src + int64_t(b) * R * C;
-    uint16_t* d = dst + int64_t(b) * R * C;
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-      const int rr = i / 64, cc = i % 64;
-      t[rr][cc] = s[int64_t(r0 + rr) * C + c0 + cc];
+    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 128;
+    const uint16_t* sp = src + int64_t(bt) * R * C;
+    uint16_t* dp = dst + int64_t(bt) * R * C;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, r = idx >> 4, ch = idx & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sp + int64_t(r0 + r) * C + c0 + ch * 8);
+      uint32_t* w = reinterpret_cast<uint32_t*>(t + r * kPitch + ch * 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = v[k];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-      const int cc = i / 64, rr = i % 64;
-      d[int64_t(c0 + cc) * R + r0 + rr] = t[rr][cc];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, c = idx >> 3, rr = idx & 7;
+      u32x4 out;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        out[k] = uint32_t(t[(rr * 8 + 2 * k) * kPitch + c]) |
+                 (uint32_t(t[(rr * 8 + 2 * k + 1) * kPitch + c]) << 16);
+      *reinterpret_cast<u32x4*>(dp + int64_t(c0 + c) * R + r0 + rr * 8) = out;
     }
     __syncthreads();
   }
@@ -491,11 +505,11 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   if ((err = launch_dispatch(L, b.saved, b.dout_seg, mx ? b.dq : b.d, s)) != hipSuccess) return err;
   // 3. transposed BF16 weights for the backward GEMMs
   if (!mx) {
-    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 4096, 8192)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 8192, 8192)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(b.w.wd), b.wdt, El, H, I);
-    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 4096, 8192)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 8192, 8192)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(b.w.wg), b.wgt, El, I, H);
-    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 4096, 8192)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 8192, 8192)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(b.w.wu), b.wut, El, I, H);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

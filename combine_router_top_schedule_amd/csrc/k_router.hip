@@ -61,11 +61,12 @@ __device__ __forceinline__ void topk_insert(float (&v)[KM], int (&id)[KM], float
 
 // One thread per token: the block's 256 tokens stream their logits through LDS in chunks of
 // 32 experts (coalesced 128-byte row pieces in, conflict-free column reads out), and each
-// thread keeps its token's top-KM in registers.
+// thread keeps its token's top-KM in registers. Two LDS chunk buffers: the loads of chunk
+// c+1 are in flight while chunk c is ranked.
 template <int KM>
 __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   __shared__ int s_b;
-  __shared__ float s_l[kTopkTokensPerBlock][33];
+  __shared__ float s_l[2][kTopkTokensPerBlock][33];
   __shared__ uint64_t s_mask[kTopkTokensPerBlock];
   __shared__ int s_wcnt[4][kMaxLocalExperts + 1];
   __shared__ int s_excl[kMaxLocalExperts + 1];
@@ -82,11 +83,11 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
 #pragma unroll
   for (int j = 0; j < KM; ++j) { v[j] = -INFINITY; id[j] = 0x7FFFFFFF; }
   const bool vec4 = (a.E & 3) == 0;
-  for (int c0 = 0; c0 < a.E; c0 += 32) {
-    // Thread t covers rows t/8 + 32q, experts c0 + 4*(t%8) .. +3. Every load is issued
-    // unconditionally from a clamped (in-bounds) address and masked afterwards, so all eight
-    // rows' loads are in flight together.
-    float4 val[8];
+  // Thread t covers rows t/8 + 32q, experts c0 + 4*(t%8) .. +3. Every load is issued
+  // unconditionally from a clamped (in-bounds) address and masked when stored, so all eight
+  // rows' loads are in flight together.
+  float4 val[8];
+  auto load_chunk = [&](int c0) {
     const int col = c0 + 4 * (tid & 7);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -101,32 +102,38 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
         val[q].w = a.logits[n * a.E + min(col + 3, a.E - 1)];
       }
     }
+  };
+  load_chunk(0);
+  for (int c0 = 0, buf = 0; c0 < a.E; c0 += 32, buf ^= 1) {
+    const int col = c0 + 4 * (tid & 7);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int r = (tid >> 3) + 32 * q;
       const bool rok = n_base + r < a.N;
-      s_l[r][4 * (tid & 7) + 0] = (rok && col + 0 < a.E) ? val[q].x : -INFINITY;
-      s_l[r][4 * (tid & 7) + 1] = (rok && col + 1 < a.E) ? val[q].y : -INFINITY;
-      s_l[r][4 * (tid & 7) + 2] = (rok && col + 2 < a.E) ? val[q].z : -INFINITY;
-      s_l[r][4 * (tid & 7) + 3] = (rok && col + 3 < a.E) ? val[q].w : -INFINITY;
+      s_l[buf][r][4 * (tid & 7) + 0] = (rok && col + 0 < a.E) ? val[q].x : -INFINITY;
+      s_l[buf][r][4 * (tid & 7) + 1] = (rok && col + 1 < a.E) ? val[q].y : -INFINITY;
+      s_l[buf][r][4 * (tid & 7) + 2] = (rok && col + 2 < a.E) ? val[q].z : -INFINITY;
+      s_l[buf][r][4 * (tid & 7) + 3] = (rok && col + 3 < a.E) ? val[q].w : -INFINITY;
     }
+    // One barrier per chunk suffices with two buffers: a thread writing buffer `buf` again
+    // (two chunks later) has passed the barrier after which every thread finished ranking it.
     __syncthreads();
+    if (c0 + 32 < a.E) load_chunk(c0 + 32);
     const int ce = min(32, a.E - c0);
     if (ce == 32) {
 #pragma unroll 8
       for (int u = 0; u < 32; ++u) {
-        float x = s_l[tid][u];
+        float x = s_l[buf][tid][u];
         x = x == 0.f ? 0.f : x;               // -0.0 ties with +0.0
         topk_insert<KM>(v, id, x, c0 + u);
       }
     } else {
       for (int u = 0; u < ce; ++u) {
-        float x = s_l[tid][u];
+        float x = s_l[buf][tid][u];
         x = x == 0.f ? 0.f : x;
         topk_insert<KM>(v, id, x, c0 + u);
       }
     }
-    __syncthreads();
   }
   uint64_t mask = 0;
   if (n_me < a.N) {

@@ -66,30 +66,38 @@ __device__ __forceinline__ void quant_row_mx(const uint16_t* src, uint8_t* codes
 
 // Fixed-order merge of token n's local pairs: dst = bf16( sum over k ascending, idx[n,k]
 // local, of w_k * slots[n*K+k] ), w_k = p[n,k] (or 1 when p == nullptr). fp32 accumulation,
-// one fused multiply-add per term in k order, so the result is bit-reproducible.
+// one fused multiply-add per term in k order, so the result is bit-reproducible. The token's
+// K indices and weights are read once (lane k), and a pass keeps 16 chunks of 16 bytes per
+// lane of every term in flight.
 __device__ __forceinline__ void merge_row(int64_t n, const int32_t* idx, const float* p,
                                          const uint16_t* slots, uint16_t* dst, int H, int K, int e0,
                                          int El, int lane) {
+  int my_le = -1;
+  float my_w = 0.f;
+  if (lane < K) {
+    my_le = idx[n * K + lane] - e0;
+    my_w = p ? p[n * K + lane] : 1.f;
+  }
+  const uint64_t local = __ballot(my_le >= 0 && my_le < El);
   const int nch = H / 8;
-  for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
-    float acc[4][8];
+  for (int c0 = 0; c0 < nch; c0 += 64 * 16) {
+    float acc[16][8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 16; ++q)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int le = idx[n * K + k] - e0;
-      if (le < 0 || le >= El) continue;
-      const float w = p ? p[n * K + k] : 1.f;
+    for (uint64_t m = local; m; m &= m - 1) {
+      const int k = __builtin_ctzll(m);
+      const float w = __shfl(my_w, k, 64);
       const u32x4* z = reinterpret_cast<const u32x4*>(slots + (n * K + k) * int64_t(H));
-      u32x4 v[4];
+      u32x4 v[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 16; ++q) {
         const int c = c0 + q * 64 + lane;
         v[q] = c < nch ? z[c] : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 16; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[q][2 * i] = fmaf(w, __uint_as_float(v[q][i] << 16), acc[q][2 * i]);
@@ -98,7 +106,7 @@ __device__ __forceinline__ void merge_row(int64_t n, const int32_t* idx, const f
     }
     u32x4* d = reinterpret_cast<u32x4*>(dst);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int c = c0 + q * 64 + lane;
       if (c < nch)
         d[c] = u32x4{pack_bf2(acc[q][0], acc[q][1]), pack_bf2(acc[q][2], acc[q][3]),
