@@ -226,12 +226,18 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
   for (int kt = 0; kt < ksteps; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < ksteps;
-    if (more) {
+    // BF16 (4 slices per stage): the next stage's A loads go out before slice 0 and its B loads
+    // before slice 1, so the DMA writes into LDS are spread over the stage instead of
+    // competing with one slice's fragment reads (measured +9 %). E4M3 (2 slices): both before
+    // slice 0, which leaves the whole stage to cover their latency.
+    if (more && MX) {
       issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX);
       issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX);
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
+      if (!MX && more && kk == 0) issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX);
+      if (!MX && more && kk == 1) issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX);
       // Scheduling fences keep each phase whole: the compiler would otherwise interleave the
       // MFMAs of slice kk with the fragment reads of slice kk+1 and wait on those reads.
       __builtin_amdgcn_sched_barrier(0);
@@ -245,8 +251,17 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
           load_frag(f[(kk + 1) & 1], sm.a[cur ^ 1], sm.b[cur ^ 1], sm.as[cur ^ 1], sm.bs[cur ^ 1],
                     0, wm, wn, lane);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (MX) __builtin_amdgcn_sched_barrier(0);
       mma(f[kk & 1], acc);
+      if (!MX) {
+        // BF16: one fragment read between consecutive MFMAs of the slice
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
