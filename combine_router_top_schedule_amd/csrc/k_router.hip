@@ -41,21 +41,34 @@ struct RouterArgs {
   int E, K, e0, El, row_align, nblocks;
 };
 
-// Insert (x, e) into a top-KM list held in registers, ordered by (value descending, expert id
-// ascending): one bubble pass that keeps the element ranking first at each position and
-// carries the other one down. Comparing ids on equal values keeps ties in expert order also
-// for elements that are carried down.
+// Ranking key of (logit x, expert e): the fp32 bits mapped to an order-preserving unsigned
+// integer in the high word (negative values flipped entirely, non-negative ones with the sign
+// bit set), and 0xFFFFFFFF - e in the low word. Larger key = larger logit, and on equal logits
+// the lower expert id. -0.0 is mapped to +0.0 first so the two tie.
+__device__ __forceinline__ uint64_t rank_key(float x, int e) {
+  x = x == 0.f ? 0.f : x;
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t m = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (uint64_t(m) << 32) | uint32_t(0xFFFFFFFFu - uint32_t(e));
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t m = uint32_t(k >> 32);
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) {
+  return int(0xFFFFFFFFu - uint32_t(k));
+}
+
+// Insert a key into a descending top-KM list held in registers: one branch-free bubble pass
+// that keeps the larger key at each position and carries the smaller one down.
 template <int KM>
-__device__ __forceinline__ void topk_insert(float (&v)[KM], int (&id)[KM], float x, int e) {
+__device__ __forceinline__ void topk_insert(uint64_t (&key)[KM], uint64_t k) {
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
-    const bool c = x > v[j] || (x == v[j] && e < id[j]);
-    const float vj = v[j];
-    const int ij = id[j];
-    v[j] = c ? x : vj;
-    id[j] = c ? e : ij;
-    x = c ? vj : x;
-    e = c ? ij : e;
+    const uint64_t kj = key[j];
+    const bool c = k > kj;
+    key[j] = c ? k : kj;
+    k = c ? kj : k;
   }
 }
 
@@ -78,10 +91,9 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   const int64_t n_base = int64_t(b) * kTopkTokensPerBlock;
   const int64_t n_me = n_base + tid;
 
-  float v[KM];
-  int id[KM];
+  uint64_t key[KM];
 #pragma unroll
-  for (int j = 0; j < KM; ++j) { v[j] = -INFINITY; id[j] = 0x7FFFFFFF; }
+  for (int j = 0; j < KM; ++j) key[j] = 0;   // below every real key
   const bool vec4 = (a.E & 3) == 0;
   // Thread t covers rows t/8 + 32q, experts c0 + 4*(t%8) .. +3. Every load is issued
   // unconditionally from a clamped (in-bounds) address and masked when stored, so all eight
@@ -122,18 +134,17 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
     const int ce = min(32, a.E - c0);
     if (ce == 32) {
 #pragma unroll 8
-      for (int u = 0; u < 32; ++u) {
-        float x = s_l[buf][tid][u];
-        x = x == 0.f ? 0.f : x;               // -0.0 ties with +0.0
-        topk_insert<KM>(v, id, x, c0 + u);
-      }
+      for (int u = 0; u < 32; ++u) topk_insert<KM>(key, rank_key(s_l[buf][tid][u], c0 + u));
     } else {
-      for (int u = 0; u < ce; ++u) {
-        float x = s_l[buf][tid][u];
-        x = x == 0.f ? 0.f : x;
-        topk_insert<KM>(v, id, x, c0 + u);
-      }
+      for (int u = 0; u < ce; ++u) topk_insert<KM>(key, rank_key(s_l[buf][tid][u], c0 + u));
     }
+  }
+  float v[KM];
+  int id[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    v[j] = key_value(key[j]);
+    id[j] = key_expert(key[j]);
   }
   uint64_t mask = 0;
   if (n_me < a.N) {
