@@ -101,6 +101,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3", choices=["dsv3", "kimi", "kimi_mx_skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--minibatch", type=int, default=0,
+                    help="override the workload's minibatch rows M (ring granularity)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time mok_layer_fwd alone (minibatch sweeps); not the headline metric")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is one "
@@ -118,6 +122,8 @@ def main() -> int:
     from combine_router_top_schedule_amd.layer import MokLayer
 
     cfg = datagen.CONFIGS[args.workload]
+    if args.minibatch:
+        cfg = cfg.replace(M=args.minibatch)
     mx = cfg.dtype == "mxfp8"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
@@ -154,7 +160,8 @@ def main() -> int:
 
     def step():
         L.forward(x_seg, logits, out_seg)
-        L.backward(dout_seg, x_seg, dx_seg, dp, dlogits, dwg, dwu, dwd)
+        if not args.forward_only:
+            L.backward(dout_seg, x_seg, dx_seg, dp, dlogits, dwg, dwu, dwd)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -195,8 +202,9 @@ def main() -> int:
 
     # ---- after the timed region: the other kernel groups, one untimed step each ----
     groups = {}
-    for name, kid in (("a_gemm", mok.MOK_TRACE_A_GEMM), ("dx_gemm", mok.MOK_TRACE_DX_GEMM),
-                      ("wgrad", mok.MOK_TRACE_WGRAD)):
+    for name, kid in (() if args.forward_only else
+                      (("a_gemm_and_dwd", mok.MOK_TRACE_BWD_GEMM1),
+                       ("dx_gemm_and_dwg_dwu", mok.MOK_TRACE_BWD_GEMM2))):
         (a, b), = events(1)
         mok.mok_trace_kernel(kid, a, b)
         step()
@@ -207,13 +215,14 @@ def main() -> int:
     P = int(L.header()[0])
     HI = cfg.H * cfg.I
     fwd_flop = 6.0 * P * HI
-    step_flop = 18.0 * P * HI
+    step_flop = (6.0 if args.forward_only else 18.0) * P * HI
     peak = PEAK_MXFP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     achieved = fwd_flop / (fused_ms * 1e-3) / 1e12
     traffic = stored_traffic()
     tokens_s = cfg.T / (ms * 1e-3)
     line = {
-        "metric": "MoE layer tokens/sec fwd+bwd on 1 MI355X; % MFMA peak and % HBM BW",
+        "metric": ("MoE layer tokens/sec fwd only on 1 MI355X (minibatch sweep)" if args.forward_only
+                   else "MoE layer tokens/sec fwd+bwd on 1 MI355X; % MFMA peak and % HBM BW"),
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -225,7 +234,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded PCG64: X, dOut ~ N(0,1), logits ~ N(0,1), W ~ N(0,0.02^2))",
-        "config": {"workload": f"{cfg.name} local share, fwd+bwd", "hidden": cfg.H,
+        "config": {"workload": f"{cfg.name} local share, {'fwd' if args.forward_only else 'fwd+bwd'}",
+                   "hidden": cfg.H,
                    "experts": cfg.E, "top_k": cfg.K, "intermediate": cfg.I,
                    "local_experts": cfg.E_loc, "segments": cfg.S,
                    "tokens_per_segment": cfg.T, "minibatch": cfg.M,
@@ -239,7 +249,7 @@ def main() -> int:
                    "fused_fwd_ms": round(fused_ms, 4), "bwd_group_ms": groups,
                    "wall_s": round(wall, 3)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.forward_only:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

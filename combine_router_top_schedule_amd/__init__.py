@@ -81,7 +81,7 @@ _SIGS = {
     "mok_trace_kernel": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
 }
 
-MOK_TRACE_NONE, MOK_TRACE_FUSED_FWD, MOK_TRACE_A_GEMM, MOK_TRACE_DX_GEMM, MOK_TRACE_WGRAD = range(5)
+MOK_TRACE_NONE, MOK_TRACE_FUSED_FWD, MOK_TRACE_BWD_GEMM1, MOK_TRACE_BWD_GEMM2 = range(4)
 
 _lib = None
 

@@ -341,67 +341,76 @@ struct BwdArgs {
   int njobs;
   int El;
   int64_t ld;              // padded columns of the transposed planes
+  int32_t* queue;          // [kXcds] work counters of one launch (zeroed before it)
 };
 
-template <bool MX>
-__global__ __launch_bounds__(256, 1) void k_a_gemm(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
-  const int mtiles = *a.ntiles;
-  const int ntn = (a.s.I + kTileN - 1) / kTileN;
-  const int total = mtiles * ntn;
-  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
-    int mt, nt;
-    tile_coords(t, mtiles, ntn, mt, nt);
-    const MTile tl = a.tiles[mt];
-    a_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.d, a.d_s, a.wdt, a.wdt_s, a.act,
-               a.perm, a.p, a.dgu, const_cast<uint8_t*>(a.dgu_a), const_cast<uint8_t*>(a.dgu_s),
-               a.dp_part);
-  }
+// The backward's GEMM work in two persistent launches with no dependencies inside either:
+//   phase 0: the a GEMM (with dp / SwiGLU backward) and dWd = (p D)^T h;
+//   phase 1: the dx GEMM (pushed to the slots) and dWg = dg^T X, dWu = du^T X.
+// Mixing two kinds of tiles fills the last wave of the first kind. Items are numbered primary
+// tiles first (the heavier ones), then weight-gradient tiles; blocks of kQBlock consecutive items
+// belong to the XCDs in turn (consecutive tiles share operands in that XCD's L2). A workgroup
+// takes items from its own XCD's counter, then from the others' until all are done. Which
+// workgroup computes an item does not change the item's result.
+constexpr int kQBlock = 32;
+
+__device__ __forceinline__ int bwd_xcc_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kXcds - 1);   // HW_REG_XCC_ID
 }
 
-template <bool MX>
-__global__ __launch_bounds__(256, 1) void k_dx_gemm(BwdArgs a) {
+template <bool MX, int PHASE>
+__global__ __launch_bounds__(256, 1) void k_bwd_gemms(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  __shared__ int s_item;
   const int mtiles = *a.ntiles;
-  const int ntn = (a.s.H + kTileN - 1) / kTileN;
-  const int total = mtiles * ntn;
-  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
-    int mt, nt;
-    tile_coords(t, mtiles, ntn, mt, nt);
-    const MTile tl = a.tiles[mt];
-    dx_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.dgu_a, a.dgu_s, a.wgt, a.wgt_s,
-                a.wut, a.wut_s, a.perm, a.slots);
-  }
-}
-
-// All weight gradients in one persistent launch (so the last wave is shared by every job):
-// tile t runs over jobs, then experts, then 256 x 256 output tiles of dW_e [Fa][Fb] =
-// Ta[:, cols of e] . Tb[:, cols of e]^T.
-template <bool MX>
-__global__ __launch_bounds__(256, 1) void k_wgrad_gemm(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
-  int total = 0;
+  const int ntn = int(PHASE == 0 ? cdiv(a.s.I, kTileN) : cdiv(a.s.H, kTileN));
+  const int n_p = mtiles * ntn;
+  int total = n_p;
   for (int j = 0; j < a.njobs; ++j)
     total += a.El * ((a.jobs[j].Fa + kTileM - 1) / kTileM) * ((a.jobs[j].Fb + kTileN - 1) / kTileN);
-  for (int t = xcd_logical_id(); t < total; t += gridDim.x) {
-    int j = 0, rem = t;
-    for (; j < a.njobs; ++j) {
-      const int per = a.El * ((a.jobs[j].Fa + kTileM - 1) / kTileM) * ((a.jobs[j].Fb + kTileN - 1) / kTileN);
-      if (rem < per) break;
-      rem -= per;
+  const int x0 = bwd_xcc_id();
+  for (int probe = 0; probe < kXcds; ++probe) {
+    const int x = (x0 + probe) & (kXcds - 1);
+    for (;;) {
+      if (threadIdx.x == 0) {
+        const int k = add_relaxed(a.queue + x, 1);
+        const int i = ((k / kQBlock) * kXcds + x) * kQBlock + k % kQBlock;
+        s_item = i < total ? i : -1;
+      }
+      __syncthreads();
+      const int t = s_item;
+      __syncthreads();
+      if (t < 0) break;
+      if (t < n_p) {
+        int mt, nt;
+        tile_coords(t, mtiles, ntn, mt, nt);
+        const MTile tl = a.tiles[mt];
+        if (PHASE == 0)
+          a_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.d, a.d_s, a.wdt, a.wdt_s,
+                     a.act, a.perm, a.p, a.dgu, const_cast<uint8_t*>(a.dgu_a),
+                     const_cast<uint8_t*>(a.dgu_s), a.dp_part);
+        else
+          dx_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.dgu_a, a.dgu_s, a.wgt,
+                      a.wgt_s, a.wut, a.wut_s, a.perm, a.slots);
+      } else {
+        int j = 0, rem = t - n_p;
+        for (; j < a.njobs; ++j) {
+          const int per = a.El * ((a.jobs[j].Fa + kTileM - 1) / kTileM) * ((a.jobs[j].Fb + kTileN - 1) / kTileN);
+          if (rem < per) break;
+          rem -= per;
+        }
+        const WJob& jb = a.jobs[j];
+        const int mtn = (jb.Fa + kTileM - 1) / kTileM, ntw = (jb.Fb + kTileN - 1) / kTileN;
+        const int e = rem / (mtn * ntw);
+        int mt, nt;
+        tile_coords(rem % (mtn * ntw), mtn, ntw, mt, nt);
+        const int c0 = a.hdr2[kB2ColPad + e];
+        const int ncols = a.hdr2[kB2ColPad + e + 1] - c0;
+        wgrad_tile<MX>(sm, jb.t_a, jb.t_a_s, jb.t_b, jb.t_b_s, a.ld, c0, ncols, mt * kTileM,
+                       nt * kTileN, jb.Fa, jb.Fb, jb.dw + int64_t(e) * jb.Fa * jb.Fb);
+      }
     }
-    const WJob& jb = a.jobs[j];
-    const int mtn = (jb.Fa + kTileM - 1) / kTileM, ntn = (jb.Fb + kTileN - 1) / kTileN;
-    const int e = rem / (mtn * ntn);
-    int mt, nt;
-    tile_coords(rem % (mtn * ntn), mtn, ntn, mt, nt);
-    const int c0 = a.hdr2[kB2ColPad + e];
-    const int ncols = a.hdr2[kB2ColPad + e + 1] - c0;
-    wgrad_tile<MX>(sm, jb.t_a, jb.t_a_s, jb.t_b, jb.t_b_s, a.ld, c0, ncols, mt * kTileM, nt * kTileN,
-                   jb.Fa, jb.Fb, jb.dw + int64_t(e) * jb.Fa * jb.Fb);
   }
 }
 
@@ -447,12 +456,10 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   static bool attr_done = false;
   hipError_t err;
   if (!attr_done) {
-    if ((err = allow_big_lds(k_a_gemm<false>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_a_gemm<true>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_dx_gemm<false>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_dx_gemm<true>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_wgrad_gemm<false>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_wgrad_gemm<true>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_bwd_gemms<false, 0>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_bwd_gemms<true, 0>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_bwd_gemms<false, 1>)) != hipSuccess) return err;
+    if ((err = allow_big_lds(k_bwd_gemms<true, 1>)) != hipSuccess) return err;
     attr_done = true;
   }
   const bool mx = L.dtype == MOK_MXFP8;
@@ -513,7 +520,24 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
                        static_cast<const uint16_t*>(b.w.wu), b.wut, El, I, H);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  // 4. a GEMM with fused dp / SwiGLU backward
+  // 4. weight-gradient operand planes that do not need dg|du: per-expert column ranges, X^T,
+  //    (p D)^T and h^T (MXFP8: quantised along tokens as they are written)
+  hipLaunchKernelGGL(k_colpad, dim3(1), dim3(64), 0, s, hdr, b.hdr2, El);
+  const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
+  const uint16_t* const* ds = reinterpret_cast<const uint16_t* const*>(b.dout_seg);
+  const int64_t ld = L.rp_max;
+  auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
+                int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst) {
+    TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
+                    ld, F, L.K, L.T, El};
+    hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
+  };
+  const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
+  tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt);                         // X^T
+  tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt);                        // (p D)^T
+  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht);          // h^T
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
   BwdArgs a{};
   a.tiles = reinterpret_cast<const MTile*>(b.ws + L.ws_tiles);
   a.ntiles = reinterpret_cast<const int32_t*>(b.ws) + kWsNumTiles;
@@ -525,7 +549,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.d_s = mx ? b.dq + L.rows_max * H : nullptr;
   a.wdt = mx ? b.w.wdt_q : reinterpret_cast<const uint8_t*>(b.wdt);
   a.wdt_s = mx ? b.w.wdt_s : nullptr;
-  a.act = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
+  a.act = ap;
   a.dgu = b.dgu;
   a.dp_part = b.dp_part;
   a.dgu_a = mx ? b.dguq : reinterpret_cast<const uint8_t*>(b.dgu);
@@ -535,71 +559,55 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.wut = mx ? b.w.wut_q : reinterpret_cast<const uint8_t*>(b.wut);
   a.wut_s = mx ? b.w.wut_s : nullptr;
   a.slots = b.slots;
-  trace_before(MOK_TRACE_A_GEMM, s);
-  if (mx) hipLaunchKernelGGL(k_a_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
-  else hipLaunchKernelGGL(k_a_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
-  trace_after(MOK_TRACE_A_GEMM, s);
+  a.ld = ld;
+  a.El = El;
+  a.queue = counts + 4;
+  auto job = [&](WJob& o, const uint16_t* ta, const uint16_t* tb, uint8_t* qa, uint8_t* qb, int Fa,
+                 int Fb, float* dw) {
+    o.Fa = Fa;
+    o.Fb = Fb;
+    o.dw = dw;
+    if (mx) {
+      o.t_a = qa; o.t_a_s = qa + int64_t(Fa) * ld;
+      o.t_b = qb; o.t_b_s = qb + int64_t(Fb) * ld;
+    } else {
+      o.t_a = reinterpret_cast<const uint8_t*>(ta); o.t_a_s = nullptr;
+      o.t_b = reinterpret_cast<const uint8_t*>(tb); o.t_b_s = nullptr;
+    }
+  };
+  // 5. phase 0: a GEMM with fused dp / SwiGLU backward, and dWd
+  a.njobs = 1;
+  job(a.jobs[0], b.dt, b.ht, b.q_dt, b.q_ht, H, I, b.g.dwd);
+  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(a.queue), 0u, kXcds, s)) != hipSuccess) return err;
+  trace_before(MOK_TRACE_BWD_GEMM1, s);
+  if (mx) hipLaunchKernelGGL((k_bwd_gemms<true, 0>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else hipLaunchKernelGGL((k_bwd_gemms<false, 0>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  trace_after(MOK_TRACE_BWD_GEMM1, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 5. dx GEMM, pushed to the slots; then the unweighted fixed-order merge
-  trace_before(MOK_TRACE_DX_GEMM, s);
-  if (mx) hipLaunchKernelGGL(k_dx_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
-  else hipLaunchKernelGGL(k_dx_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
-  trace_after(MOK_TRACE_DX_GEMM, s);
+  // 6. dg^T, du^T; phase 1: dx GEMM pushed to the slots, dWg and dWu
+  const uint8_t* dgu8 = reinterpret_cast<const uint8_t*>(b.dgu);
+  tr(nullptr, nullptr, dgu8, nullptr, 2 * I, 0, I, b.dgt, b.q_dgt);                   // dg^T
+  tr(nullptr, nullptr, dgu8, nullptr, 2 * I, I, I, b.dut, b.q_dut);                   // du^T
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  a.njobs = 2;
+  job(a.jobs[0], b.dgt, b.xt, b.q_dgt, b.q_xt, I, H, b.g.dwg);
+  job(a.jobs[1], b.dut, b.xt, b.q_dut, b.q_xt, I, H, b.g.dwu);
+  a.queue = counts + 4 + kXcds;
+  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(a.queue), 0u, kXcds, s)) != hipSuccess) return err;
+  trace_before(MOK_TRACE_BWD_GEMM2, s);
+  if (mx) hipLaunchKernelGGL((k_bwd_gemms<true, 1>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  else hipLaunchKernelGGL((k_bwd_gemms<false, 1>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
+  trace_after(MOK_TRACE_BWD_GEMM2, s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // 7. the unweighted fixed-order dX merge, the router-weight gradient per pair, and dlogits
+  //    when every expert is local
   if ((err = launch_combine(L, b.saved, b.topk_idx, nullptr, b.slots, b.dx_seg, s)) != hipSuccess)
     return err;
-  // 6. router-weight gradient per pair, and dlogits when every expert is local
   hipLaunchKernelGGL(k_dp_finalize, dim3(grid_cap(L.rows_max / 256 + 1, 4096)), dim3(256), 0, s,
                      hdr, perm, b.dp_part, int(cdiv(I, kTileN)), b.dp, L.rows_max);
   if (b.dlogits)
     hipLaunchKernelGGL(k_dlogits, dim3(grid_cap(L.N / 256 + 1, 4096)), dim3(256), 0, s, b.topk_idx,
                        b.topk_p, b.dp, b.dlogits, L.N, L.K, L.E);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 7. weight gradients from per-expert transposed operands
-  hipLaunchKernelGGL(k_colpad, dim3(1), dim3(64), 0, s, hdr, b.hdr2, El);
-  const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
-  const uint16_t* const* ds = reinterpret_cast<const uint16_t* const*>(b.dout_seg);
-  const int64_t ld = L.rp_max;
-  // (MXFP8: the planes are quantised along tokens as they are written)
-  auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
-                int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst) {
-    TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
-                    ld, F, L.K, L.T, El};
-    hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
-  };
-  const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
-  tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt);                         // X^T
-  tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt);                        // (p D)^T
-  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, 0, I, b.dgt, b.q_dgt);  // dg^T
-  tr(nullptr, nullptr, reinterpret_cast<const uint8_t*>(b.dgu), nullptr, 2 * I, I, I, b.dut, b.q_dut);  // du^T
-  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht);          // h^T
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  struct WG { const uint16_t *ta, *tb; uint8_t *qa, *qb; int Fa, Fb; float* dw; };
-  const WG jobs[3] = {{b.dgt, b.xt, b.q_dgt, b.q_xt, I, H, b.g.dwg},
-                      {b.dut, b.xt, b.q_dut, b.q_xt, I, H, b.g.dwu},
-                      {b.dt, b.ht, b.q_dt, b.q_ht, H, I, b.g.dwd}};
-  BwdArgs w = a;
-  w.ld = ld;
-  w.El = El;
-  w.njobs = 3;
-  for (int q = 0; q < 3; ++q) {
-    const WG& j = jobs[q];
-    WJob& o = w.jobs[q];
-    o.Fa = j.Fa;
-    o.Fb = j.Fb;
-    o.dw = j.dw;
-    if (mx) {
-      o.t_a = j.qa; o.t_a_s = j.qa + int64_t(j.Fa) * ld;
-      o.t_b = j.qb; o.t_b_s = j.qb + int64_t(j.Fb) * ld;
-    } else {
-      o.t_a = reinterpret_cast<const uint8_t*>(j.ta); o.t_a_s = nullptr;
-      o.t_b = reinterpret_cast<const uint8_t*>(j.tb); o.t_b_s = nullptr;
-    }
-  }
-  trace_before(MOK_TRACE_WGRAD, s);
-  if (mx) hipLaunchKernelGGL(k_wgrad_gemm<true>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, w);
-  else hipLaunchKernelGGL(k_wgrad_gemm<false>, dim3(G), dim3(kThreads), kGemmLdsBytes, s, w);
-  trace_after(MOK_TRACE_WGRAD, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return hipSuccess;
 }

@@ -165,7 +165,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_restore = take(16 * L.tiles_max);
   L.b_replay = take(16 * L.tiles_max);
   L.b_rsl = take(4 * L.tiles_max);
-  L.b_counts = take(64);
+  L.b_counts = take(4 * (4 + 2 * kXcds));   // plan counts, then two work-queue counter sets
   L.b_bytes = off;
   return L;
 }

@@ -240,18 +240,17 @@ mok_status mok_device_status(const void* ws_dev, void* stream, mok_status* out);
 int32_t mok_device_cus(void);
 
 /* Measurement hook (benchmarks only): from the next call on, the library records `before`
- * (a hipEvent_t) on the call's stream right before it launches the kernel group `kernel` and
- * `after` right after it; MOK_TRACE_NONE (or NULL events) switches it off. Groups:
- * MOK_TRACE_FUSED_FWD  the persistent forward kernel of mok_layer_fwd;
- * MOK_TRACE_A_GEMM     the a = dOut Wd GEMM (with dp / SwiGLU backward) of mok_layer_bwd;
- * MOK_TRACE_DX_GEMM    the dx GEMM of mok_layer_bwd;
- * MOK_TRACE_WGRAD      the three weight-gradient GEMMs of mok_layer_bwd (one bracket).
+ * (a hipEvent_t) on the call's stream right before it launches the kernel `kernel` and `after`
+ * right after it; MOK_TRACE_NONE (or NULL events) switches it off. Kernels:
+ * MOK_TRACE_FUSED_FWD   the persistent forward kernel of mok_layer_fwd;
+ * MOK_TRACE_BWD_GEMM1   mok_layer_bwd's first GEMM launch: a = dOut Wd (with dp and SwiGLU
+ *                       backward) and dW_down;
+ * MOK_TRACE_BWD_GEMM2   its second: dx (pushed to the slots), dW_gate and dW_up.
  * Process-wide setting, not thread-safe; it changes no result. */
 #define MOK_TRACE_NONE 0
 #define MOK_TRACE_FUSED_FWD 1
-#define MOK_TRACE_A_GEMM 2
-#define MOK_TRACE_DX_GEMM 3
-#define MOK_TRACE_WGRAD 4
+#define MOK_TRACE_BWD_GEMM1 2
+#define MOK_TRACE_BWD_GEMM2 3
 mok_status mok_trace_kernel(int32_t kernel, void* before, void* after);
 
 #ifdef __cplusplus
