@@ -8,7 +8,8 @@
 // MI355X layout of that idea: every XCD (8 per device, each with its own L2) runs its own
 // pipeline. Workgroups learn their XCD from the hardware id; per XCD the first `comm` of them
 // gather token rows (pull dispatch, MXFP8 quantisation fused) and the others run the gate/up
-// and down GEMM tiles of the same row tiles. A row tile (<= 256 expert-ordered rows of one
+// and down GEMM tiles of the same row tiles. An XCD takes its next row tile from one global
+// counter whenever it has a free ring slot, so the row tiles spread over the XCDs by speed. A row tile (<= 256 expert-ordered rows of one
 // expert inside one minibatch) is produced and consumed inside one XCD, so its ring bytes stay
 // coherent in that XCD's L2: producers complete their stores before bumping a counter, and a
 // consumer invalidates only its CU's L1 after seeing the counter. Each XCD owns a fixed share
@@ -58,7 +59,10 @@ struct FusedArgs {
   uint32_t flags;
 };
 
-enum CntWords : int { kCntArrived = 0, kCntReg = 8, kCntWords = 64 };
+// Counter words: registration, the global row-tile counter, and per XCD the number of row
+// tiles it ended up with (-1 until known). After them: landed / gu_done / dn_done per tile,
+// then per XCD the tile id of its q-th row tile (-1 until known).
+enum CntWords : int { kCntArrived = 0, kCntReg = 8, kCntEnd = 16, kCntNext = 24, kCntWords = 64 };
 
 __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kMaxXcd - 1);  // HW_REG_XCC_ID
@@ -85,6 +89,32 @@ __device__ bool wait_geq(const int32_t* p, int target, int32_t* err, int limit) 
   const bool ok = s_ok != 0;
   __syncthreads();
   return ok;
+}
+
+// The tile id of this XCD's q-th row tile, once its dispatch worker has taken it: >= 0, or
+// INT32_MAX when the XCD gets no q-th tile, or -1 if the wait failed (for the whole workgroup).
+// xq has tiles_max entries; no XCD can get more tiles than that.
+__device__ int tile_of(const int32_t* xq, const int32_t* xend, int q, int64_t tiles_max,
+                       int32_t* err, int limit) {
+  __shared__ int s_t;
+  if (threadIdx.x == 0) {
+    int spins = 0, t = -1;
+    if (q >= tiles_max) t = 0x7FFFFFFF;
+    while (t < 0) {
+      const int v = ld_relaxed(xq + q);
+      if (v >= 0) { t = v; break; }
+      const int e = ld_relaxed(xend);
+      if (e >= 0 && q >= e) { t = 0x7FFFFFFF; break; }
+      if (ld_relaxed(err) != 0) break;
+      if (++spins > limit) { set_error(err, MOK_ERR_DEVICE_TIMEOUT); break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    s_t = t;
+  }
+  __syncthreads();
+  const int t = s_t;
+  __syncthreads();
+  return t;
 }
 
 // All stores of this workgroup are complete (in L2), then thread 0 bumps the counter.
@@ -135,6 +165,8 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   int32_t* landed = a.cnt + kCntWords;
   int32_t* gu_done = landed + a.tiles_max;
   int32_t* dn_done = gu_done + a.tiles_max;
+  int32_t* xq = dn_done + a.tiles_max + int64_t(x) * a.tiles_max;   // this XCD's tile ids
+  int32_t* xend = a.cnt + kCntEnd + x;
   uint8_t* share = a.ring + int64_t(x) * a.ring_share;
 
   if (local < C) {
@@ -143,19 +175,39 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
       a.rhdr[kRhTiles] = nt;
       a.rhdr[kRhCapt] = a.capt;
     }
+    // Row tiles are taken from one global counter when this XCD has a free slot, so faster
+    // XCDs take more of them. Dispatch worker 0 takes the tile and publishes its id.
+    __shared__ int s_mt;
     for (int q = 0;; ++q) {
-      const int mt = ax + q * nact;
-      if (mt >= nt) break;
-      if (q >= a.capt && !wait_geq(dn_done + (mt - a.capt * nact), ndn, a.err, a.spin_limit)) return;
-      const MTile tl = a.tiles[mt];
-      if (local == 0 && tid == 0) {
-        // One thread per XCD records the tiles in order, so each slot's owner ends as the
-        // last tile that used it.
-        const int slot = x * a.capt + q % a.capt;
-        a.rtiles[mt] = tl;
-        a.rslot[mt] = slot;
-        a.rowner[slot] = mt;
+      if (q >= a.capt && !wait_geq(dn_done + ld_relaxed(xq + q - a.capt), ndn, a.err, a.spin_limit))
+        return;
+      int mt;
+      if (local == 0) {
+        if (tid == 0) {
+          int t = add_relaxed(a.cnt + kCntNext, 1);
+          if (t >= nt) {
+            t = 0x7FFFFFFF;
+            __hip_atomic_store(xend, q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            // One thread per XCD records its tiles in order, so each slot's owner ends as the
+            // last tile that used it.
+            const int slot = x * a.capt + q % a.capt;
+            a.rtiles[t] = a.tiles[t];
+            a.rslot[t] = slot;
+            a.rowner[slot] = t;
+            __hip_atomic_store(xq + q, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          s_mt = t;
+        }
+        __syncthreads();
+        mt = s_mt;
+        __syncthreads();
+      } else {
+        mt = tile_of(xq, xend, q, a.tiles_max, a.err, a.spin_limit);
+        if (mt < 0) return;
       }
+      if (mt >= nt) break;
+      const MTile tl = a.tiles[mt];
       const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
                                       a.dtype, true);
       // This wave's rows are r = local*4 + wave + j*4C; lane j looks up row j's source first
@@ -194,18 +246,23 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
       k = it;
     } else {
       const int blk = (it - ngu) / per_tile, off = (it - ngu) % per_tile;
-      if (ax + blk * nact >= nt) break;               // no down work left: done
+      const int tb = tile_of(xq, xend, blk, a.tiles_max, a.err, a.spin_limit);
+      if (tb < 0) return;
+      if (tb >= nt) break;                            // no down work left: done
       if (off < ngu) {
         q = blk + 1;
         k = off;
-        if (ax + q * nact >= nt) continue;            // no such row tile: nothing to do
       } else {
         q = blk;
         k = off;
       }
     }
-    const int mt = ax + q * nact;
-    if (mt >= nt) break;
+    const int mt = tile_of(xq, xend, q, a.tiles_max, a.err, a.spin_limit);
+    if (mt < 0) return;
+    if (mt >= nt) {
+      if (q == 0) break;                              // this XCD got no row tile at all
+      continue;                                       // no such row tile: nothing to do
+    }
     const MTile tl = a.tiles[mt];
     const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
                                     a.dtype, true);
@@ -249,6 +306,12 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   if ((err = launch_tiles(L, L.M, saved, ws, s)) != hipSuccess) return err;
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.ws_counters);
   if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(cnt), 0u, kCntWords + 3 * L.tiles_max, s)) !=
+      hipSuccess)
+    return err;
+  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(cnt + kCntWords + 3 * L.tiles_max), 0xFFFFFFFFu,
+                             int64_t(kMaxXcd) * L.tiles_max, s)) != hipSuccess)
+    return err;
+  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(cnt + kCntEnd), 0xFFFFFFFFu, kMaxXcd, s)) !=
       hipSuccess)
     return err;
   const bool mx = L.dtype == MOK_MXFP8;

@@ -126,7 +126,7 @@ inline Layout make_layout(const mok_desc& d) {
   off = 256;
   L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 1), 256);
   L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
-  L.ws_counters = off; off = align_up(off + 4 * (64 + 3 * L.tiles_max), 256);
+  L.ws_counters = off; off = align_up(off + 4 * (64 + (3 + kXcds) * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
   L.ws_bytes = off;
   // staged
