@@ -18,13 +18,17 @@
 // kernel on the stream.
 //
 // Work order and deadlock freedom: all workgroups are co-resident (cooperative launch, one per
-// CU). Within an XCD the GEMM items are numbered gu(0), then blocks [gu(q+1), dn(q)] for
-// q = 0, 1, ... (gu = the gate/up column tiles of a row tile, dn = its down column tiles), so
-// the down tiles of a row tile come one block after its gate/up tiles and workers rarely wait
-// for them. Each GEMM worker takes items i = worker, worker + G, ... in order. Every wait is on
-// a lower-numbered item: dn(q) on gu(q), and gu(q) on the gather of tile q, whose slot was freed
-// by dn(q - capt), numbered below gu(q) whenever capt >= 2. Every wait is bounded; an expired
-// wait sets the error word and all workers drain.
+// CU). The first `lag` row tiles of an XCD (lag = 2 with at least 3 slots per XCD, else 1) are
+// gathered by all of its workgroups together, since no GEMM work exists before them; the later
+// ones by the dispatch workers alone. Within an XCD the GEMM items are numbered gu(0) ..
+// gu(lag-1), then blocks [gu(q+lag), dn(q)] for q = 0, 1, ... (gu = the gate/up column tiles of
+// a row tile, dn = its down column tiles), so the down tiles of a row tile come `lag` blocks
+// after its gate/up tiles and rarely wait for them. A GEMM worker that finishes an item takes
+// the next number from the XCD's item counter, so items are handed out in increasing order to
+// whichever worker is free. Every wait is on a lower-numbered item, already held by a running
+// worker: dn(q) on gu(q), and gu(q) on the gather of tile q, whose slot was freed by
+// dn(q - capt), numbered below gu(q) because capt > lag. Every wait is bounded; an expired wait
+// sets the error word and all workers drain.
 #include "k_ffn.h"
 #include "mok_rows.h"
 
@@ -59,10 +63,12 @@ struct FusedArgs {
   uint32_t flags;
 };
 
-// Counter words: registration, the global row-tile counter, and per XCD the number of row
-// tiles it ended up with (-1 until known). After them: landed / gu_done / dn_done per tile,
-// then per XCD the tile id of its q-th row tile (-1 until known).
-enum CntWords : int { kCntArrived = 0, kCntReg = 8, kCntEnd = 16, kCntNext = 24, kCntWords = 64 };
+// Counter words: registration, the global row-tile counter, per XCD the number of row tiles it
+// ended up with (-1 until known) and per XCD the next GEMM item. After them: landed / gu_done /
+// dn_done per tile, then per XCD the tile id of its q-th row tile (-1 until known).
+enum CntWords : int {
+  kCntArrived = 0, kCntReg = 8, kCntEnd = 16, kCntNext = 24, kCntItem = 32, kCntWords = 64
+};
 
 __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kMaxXcd - 1);  // HW_REG_XCC_ID
@@ -158,7 +164,6 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   if (ax < 0) return;
   const int nx = s_n[x];
   const int C = min(a.comm_per_xcd, nx - 1);
-  const int G = nx - C;
   const int nt = *a.ntiles;
   const int ngu = a.s.I / 128;
   const int ndn = (a.s.H + kTileN - 1) / kTileN;
@@ -169,88 +174,122 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   int32_t* xend = a.cnt + kCntEnd + x;
   uint8_t* share = a.ring + int64_t(x) * a.ring_share;
 
-  if (local < C) {
-    // ---- dispatch worker: pull the rows of this XCD's tiles into their ring slots ----
-    if (ax == 0 && local == 0 && tid == 0) {
-      a.rhdr[kRhTiles] = nt;
-      a.rhdr[kRhCapt] = a.capt;
-    }
-    // Row tiles are taken from one global counter when this XCD has a free slot, so faster
-    // XCDs take more of them. Dispatch worker 0 takes the tile and publishes its id.
-    __shared__ int s_mt;
-    for (int q = 0;; ++q) {
-      if (q >= a.capt && !wait_geq(dn_done + ld_relaxed(xq + q - a.capt), ndn, a.err, a.spin_limit))
-        return;
-      int mt;
-      if (local == 0) {
-        if (tid == 0) {
-          int t = add_relaxed(a.cnt + kCntNext, 1);
-          if (t >= nt) {
-            t = 0x7FFFFFFF;
-            __hip_atomic_store(xend, q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            // One thread per XCD records its tiles in order, so each slot's owner ends as the
-            // last tile that used it.
-            const int slot = x * a.capt + q % a.capt;
-            a.rtiles[t] = a.tiles[t];
-            a.rslot[t] = slot;
-            a.rowner[slot] = t;
-            __hip_atomic_store(xq + q, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          s_mt = t;
-        }
-        __syncthreads();
-        mt = s_mt;
-        __syncthreads();
+  if (ax == 0 && local == 0 && tid == 0) {
+    a.rhdr[kRhTiles] = nt;
+    a.rhdr[kRhCapt] = a.capt;
+  }
+  // The tile id of this XCD's q-th row tile: workgroup 0 takes it from the global counter and
+  // publishes it (row tiles are taken when this XCD has a free slot, so faster XCDs take more
+  // of them); the others wait for the publication. Returns >= nt when there is none, -1 after
+  // an error.
+  __shared__ int s_mt;
+  auto take_tile = [&](int q) -> int {
+    if (local != 0) return tile_of(xq, xend, q, a.tiles_max, a.err, a.spin_limit);
+    if (tid == 0) {
+      int t = add_relaxed(a.cnt + kCntNext, 1);
+      if (t >= nt) {
+        t = 0x7FFFFFFF;
+        __hip_atomic_store(xend, q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
-        mt = tile_of(xq, xend, q, a.tiles_max, a.err, a.spin_limit);
-        if (mt < 0) return;
+        // One thread per XCD records its tiles in order, so each slot's owner ends as the
+        // last tile that used it.
+        const int slot = x * a.capt + q % a.capt;
+        a.rtiles[t] = a.tiles[t];
+        a.rslot[t] = slot;
+        a.rowner[slot] = t;
+        __hip_atomic_store(xq + q, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (mt >= nt) break;
-      const MTile tl = a.tiles[mt];
-      const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
-                                      a.dtype, true);
-      // This wave's rows are r = local*4 + wave + j*4C; lane j looks up row j's source first
-      // (one round of dependent loads per tile instead of one per row).
-      const int r0 = local * 4 + wave, rstep = 4 * C;
-      const uint16_t* my_src = nullptr;
-      {
-        const int r = r0 + lane * rstep;
-        if (lane * rstep < kTileM && r < tl.nrows) {
-          const int64_t n = a.perm[tl.row0 + r] / a.K;
-          my_src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.s.H);
-        }
+      s_mt = t;
+    }
+    __syncthreads();
+    const int mt = s_mt;
+    __syncthreads();
+    return mt;
+  };
+  // Pull the rows r = r0, r0 + rstep, ... of row tile mt into ring slot q % capt, then count
+  // this workgroup in landed[mt]. Lane j looks up row j's source first (one round of
+  // dependent loads per tile instead of one per row).
+  auto gather = [&](int q, int mt, int r0, int rstep) {
+    const MTile tl = a.tiles[mt];
+    const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
+                                    a.dtype, true);
+    const uint16_t* my_src = nullptr;
+    {
+      const int r = r0 + lane * rstep;
+      if (lane * rstep < kTileM && r < tl.nrows) {
+        const int64_t n = a.perm[tl.row0 + r] / a.K;
+        my_src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.s.H);
       }
+    }
+    const uint64_t sp = reinterpret_cast<uint64_t>(my_src);
+    auto src_of = [&](int j) {
+      const uint32_t lo = __shfl(uint32_t(sp), j, 64), hi = __shfl(uint32_t(sp >> 32), j, 64);
+      return reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
+    };
+    if (!MX && a.s.H <= 8 * kRowBatchChunks) {
+      const int nr = r0 < tl.nrows ? (tl.nrows - r0 + rstep - 1) / rstep : 0;
+      copy_rows_bf16_2(nr, a.s.H, lane, src_of, [&](int j) {
+        return reinterpret_cast<uint16_t*>(pl.x) + int64_t(r0 + j * rstep) * a.s.H;
+      });
+    } else {
       for (int j = 0; r0 + j * rstep < tl.nrows; ++j) {
         const int r = r0 + j * rstep;
-        const uint64_t sp = reinterpret_cast<uint64_t>(my_src);
-        const uint32_t lo = __shfl(uint32_t(sp), j, 64), hi = __shfl(uint32_t(sp >> 32), j, 64);
-        const uint16_t* src = reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
+        const uint16_t* src = src_of(j);
         if (MX) quant_row_mx(src, pl.x + int64_t(r) * a.s.H, pl.xs + int64_t(r) * (a.s.H / 32), a.s.H, lane);
         else copy_row_bf16(src, reinterpret_cast<uint16_t*>(pl.x) + int64_t(r) * a.s.H, a.s.H, lane);
       }
-      const bool skip = (a.flags & MOK_FLAG_SKIP_ONE_SIGNAL) && q == 0 && ax == 0 && local == 0;
-      if (!skip) signal(landed + mt);
+    }
+    const bool skip = (a.flags & MOK_FLAG_SKIP_ONE_SIGNAL) && q == 0 && ax == 0 && local == 0;
+    if (!skip) signal(landed + mt);
+  };
+
+  // ---- prologue: the first `lag` row tiles are gathered by every workgroup of the XCD ----
+  const int lag = a.capt > 2 ? 2 : 1;
+  bool ended = false;
+  for (int q = 0; q < lag; ++q) {
+    const int mt = take_tile(q);
+    if (mt < 0) return;
+    if (mt >= nt) {
+      ended = true;
+      break;
+    }
+    gather(q, mt, local * 4 + wave, 4 * nx);
+  }
+
+  if (local < C) {
+    // ---- dispatch worker: the later row tiles, each into the slot its tile q - capt freed ----
+    for (int q = lag; !ended; ++q) {
+      if (q >= a.capt && !wait_geq(dn_done + ld_relaxed(xq + q - a.capt), ndn, a.err, a.spin_limit))
+        return;
+      const int mt = take_tile(q);
+      if (mt < 0) return;
+      if (mt >= nt) break;
+      gather(q, mt, local * 4 + wave, 4 * C);
     }
     return;
   }
 
-  // ---- GEMM worker ----
-  const int gi = local - C;
+  // ---- GEMM worker: takes the XCD's items in order from its item counter ----
   const int per_tile = ngu + ndn;
-  for (int it = gi;; it += G) {
+  int32_t* item_ctr = a.cnt + kCntItem + x;
+  __shared__ int s_it;
+  for (;;) {
+    if (tid == 0) s_it = add_relaxed(item_ctr, 1);
+    __syncthreads();
+    const int it = s_it;
+    __syncthreads();
     // item -> (row tile q, column item k): k < ngu is gate/up column tile k, else down tile
     int q, k;
-    if (it < ngu) {
-      q = 0;
-      k = it;
+    if (it < lag * ngu) {
+      q = it / ngu;
+      k = it % ngu;
     } else {
-      const int blk = (it - ngu) / per_tile, off = (it - ngu) % per_tile;
+      const int blk = (it - lag * ngu) / per_tile, off = (it - lag * ngu) % per_tile;
       const int tb = tile_of(xq, xend, blk, a.tiles_max, a.err, a.spin_limit);
       if (tb < 0) return;
       if (tb >= nt) break;                            // no down work left: done
       if (off < ngu) {
-        q = blk + 1;
+        q = blk + lag;
         k = off;
       } else {
         q = blk;
@@ -267,7 +306,7 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
     const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
                                     a.dtype, true);
     if (k < ngu) {
-      if (!wait_geq(landed + mt, C, a.err, a.spin_limit)) return;
+      if (!wait_geq(landed + mt, q < lag ? nx : C, a.err, a.spin_limit)) return;
       l1_invalidate();
       gateup_tile<MX>(sm, a.s, a.w, pl, 0, tl.nrows, tl.e, k * 128);
       signal(gu_done + mt);

@@ -28,6 +28,47 @@ __device__ __forceinline__ void copy_row_bf16(const uint16_t* src, uint16_t* dst
   }
 }
 
+// Rows of at most 64 x 16 chunks of 16 bytes (H <= 8192 BF16) fit one register batch per lane.
+constexpr int kRowBatchChunks = 64 * 16;
+
+__device__ __forceinline__ void load_row16(const uint16_t* src, u32x4 (&v)[16], int nch, int lane) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int c = q * 64 + lane;
+    v[q] = c < nch ? s[c] : u32x4{0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ void store_row16(uint16_t* dst, const u32x4 (&v)[16], int nch, int lane) {
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int c = q * 64 + lane;
+    if (c < nch) d[c] = v[q];
+  }
+}
+
+// Copy rows j = 0 .. nrows-1 of BF16 (H <= 8192 elements) from src_of(j) to dst_of(j), keeping
+// two rows in flight per wave: row j+1 is loaded before row j is stored.
+template <class Src, class Dst>
+__device__ __forceinline__ void copy_rows_bf16_2(int nrows, int H, int lane, Src src_of, Dst dst_of) {
+  const int nch = H / 8;
+  u32x4 va[16], vb[16];
+  if (nrows <= 0) return;
+  load_row16(src_of(0), va, nch, lane);
+  for (int j = 0;; j += 2) {
+    const bool has1 = j + 1 < nrows;
+    if (has1) load_row16(src_of(j + 1), vb, nch, lane);
+    store_row16(dst_of(j), va, nch, lane);
+    if (!has1) break;
+    const bool has2 = j + 2 < nrows;
+    if (has2) load_row16(src_of(j + 2), va, nch, lane);
+    store_row16(dst_of(j + 1), vb, nch, lane);
+    if (!has2) break;
+  }
+}
+
 // Quantise one BF16 row of H elements to MXFP8 along H: codes [H], scales [H/32]. Each lane
 // loads the 64 bytes of up to 4 blocks before quantising any, to keep loads in flight.
 __device__ __forceinline__ void quant_row_mx(const uint16_t* src, uint8_t* codes, uint8_t* scales,
