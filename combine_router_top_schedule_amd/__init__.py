@@ -43,7 +43,8 @@ class MokSizes(ctypes.Structure):
                 ("rows_max", ctypes.c_int64), ("ring_slots", ctypes.c_int32),
                 ("minibatch", ctypes.c_int32), ("slot_bytes", ctypes.c_int64),
                 ("perm_offset", ctypes.c_int64), ("tokpos_offset", ctypes.c_int64),
-                ("touched_offset", ctypes.c_int64)]
+                ("touched_offset", ctypes.c_int64), ("x_slot_bytes", ctypes.c_int64),
+                ("ring_min_bytes", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p

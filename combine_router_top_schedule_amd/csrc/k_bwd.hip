@@ -253,8 +253,9 @@ struct StageArgs {
   const int32_t* perm;
   const uint16_t* const* x_seg;
   const uint8_t* ring;
-  int64_t ring_share, tsb;
-  int capt;
+  int64_t ring_share;   // bytes per XCD share
+  int64_t aofs, asb;    // offset of the activation slots inside a share, bytes per slot
+  int capa;             // activation slots per share
   uint8_t* xd;          // dispatch plane [rows_max] (codes then scales in MXFP8)
   ActPlanes act;        // g|u and h planes [rows_max]
   int64_t rows_max;
@@ -275,9 +276,9 @@ __global__ __launch_bounds__(256) void k_bwd_stage(StageArgs a) {
       const int64_t row = tl.row0 + i;
       if (rest) {
         const int sl = a.restore_slot[t];
-        uint8_t* slot = const_cast<uint8_t*>(a.ring) + int64_t(sl / a.capt) * a.ring_share +
-                        int64_t(sl % a.capt) * a.tsb;
-        const ActPlanes sp = act_planes(slot, kTileM, a.H, a.I, a.dtype, true);
+        uint8_t* slot = const_cast<uint8_t*>(a.ring) + int64_t(sl / a.capa) * a.ring_share +
+                        a.aofs + int64_t(sl % a.capa) * a.asb;
+        const ActPlanes sp = act_planes(slot, kTileM, a.H, a.I, a.dtype, false);
         copy_row_bf16(sp.gu + int64_t(i) * 2 * a.I, a.act.gu + row * 2 * a.I, 2 * a.I, lane);
         if (mx) {
           // I codes (as I/2 16-bit units) and I/32 scale bytes
@@ -480,7 +481,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
                      reinterpret_cast<const MTile*>(b.saved + L.sv_rtiles),
                      reinterpret_cast<const int32_t*>(b.saved + L.sv_rslot),
                      reinterpret_cast<const int32_t*>(b.saved + L.sv_rowner),
-                     int(b.ring != nullptr && L.ring_capt > 0), restore, rsl, replay, counts, El,
+                     int(b.ring != nullptr && L.ring_capa > 0), restore, rsl, replay, counts, El,
                      L.tiles_max);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
@@ -493,8 +494,9 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
     st.x_seg = reinterpret_cast<const uint16_t* const*>(b.x_seg);
     st.ring = b.ring;
     st.ring_share = L.ring_share;
-    st.tsb = L.tsb;
-    st.capt = L.ring_capt > 0 ? L.ring_capt : 1;
+    st.aofs = int64_t(L.ring_capx) * L.xsb;
+    st.asb = L.asb;
+    st.capa = L.ring_capa > 0 ? L.ring_capa : 1;
     st.xd = b.xd;
     st.act = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
     st.rows_max = L.rows_max;

@@ -9,26 +9,29 @@
 // pipeline. Workgroups learn their XCD from the hardware id; per XCD the first `comm` of them
 // gather token rows (pull dispatch, MXFP8 quantisation fused) and the others run the gate/up
 // and down GEMM tiles of the same row tiles. An XCD takes its next row tile from one global
-// counter whenever it has a free ring slot, so the row tiles spread over the XCDs by speed. A row tile (<= 256 expert-ordered rows of one
-// expert inside one minibatch) is produced and consumed inside one XCD, so its ring bytes stay
-// coherent in that XCD's L2: producers complete their stores before bumping a counter, and a
-// consumer invalidates only its CU's L1 after seeing the counter. Each XCD owns a fixed share
-// of the ring, cut into tile slots that are reused round-robin once the tile's down GEMM is
-// done. Down-GEMM results are pushed to the pair slots; the weighted merge runs as the next
-// kernel on the stream.
+// counter whenever it has free ring slots, so the row tiles spread over the XCDs by speed. A
+// row tile (<= 256 expert-ordered rows of one expert inside one minibatch) is produced and
+// consumed inside one XCD, so its ring bytes stay coherent in that XCD's L2: producers complete
+// their stores before bumping a counter, and a consumer invalidates only its CU's L1 after
+// seeing the counter. Each XCD owns a fixed share of the ring, cut into two kinds of slots used
+// round-robin: gather slots hold a row tile's X rows until its gate/up tiles are done;
+// activation slots hold its g|u and h until its down tiles are done, and after the kernel the
+// last capa of them stay for the backward's reverse walk. Splitting the two lets one ring keep
+// g|u and h of many more row tiles than whole-tile slots would. Down-GEMM results are pushed to
+// the pair slots; the weighted merge runs as the next kernel on the stream.
 //
 // Work order and deadlock freedom: all workgroups are co-resident (cooperative launch, one per
-// CU). The first `lag` row tiles of an XCD (lag = 2 with at least 3 slots per XCD, else 1) are
-// gathered by all of its workgroups together, since no GEMM work exists before them; the later
-// ones by the dispatch workers alone. Within an XCD the GEMM items are numbered gu(0) ..
+// CU). The first `lag` row tiles of an XCD (lag = 2 with at least 3 activation slots per XCD,
+// else 1; never more than the 2 gather slots) are gathered by all of its workgroups together,
+// since no GEMM work exists before them; the later ones by the dispatch workers alone. Within an XCD the GEMM items are numbered gu(0) ..
 // gu(lag-1), then blocks [gu(q+lag), dn(q)] for q = 0, 1, ... (gu = the gate/up column tiles of
 // a row tile, dn = its down column tiles), so the down tiles of a row tile come `lag` blocks
 // after its gate/up tiles and rarely wait for them. A GEMM worker that finishes an item takes
 // the next number from the XCD's item counter, so items are handed out in increasing order to
 // whichever worker is free. Every wait is on a lower-numbered item, already held by a running
 // worker: dn(q) on gu(q), and gu(q) on the gather of tile q, whose slot was freed by
-// dn(q - capt), numbered below gu(q) because capt > lag. Every wait is bounded; an expired wait
-// sets the error word and all workers drain.
+// dn(q - capa) and gu(q - capx), both numbered below gu(q) because capa > lag. Every wait is
+// bounded; an expired wait sets the error word and all workers drain.
 #include "k_ffn.h"
 #include "mok_rows.h"
 
@@ -45,8 +48,8 @@ struct FusedArgs {
   const uint16_t* const* x_seg;
   uint8_t* ring;
   int64_t ring_share;        // bytes of the ring owned by one XCD
-  int64_t tsb;               // bytes of one tile slot
-  int capt;                  // tile slots per XCD
+  int64_t xsb, asb;          // bytes of one gather slot / one activation slot
+  int capx, capa;            // gather slots / activation slots per XCD
   FfnShape s;
   FfnWeights w;
   uint16_t* slots;
@@ -54,7 +57,7 @@ struct FusedArgs {
   int32_t* err;
   int32_t* rhdr;             // ring state for the backward (in saved): header,
   MTile* rtiles;             //   copy of the tile table,
-  int32_t* rslot;            //   slot id (x * capt + slot) of every tile,
+  int32_t* rslot;            //   activation slot id (x * capa + slot) of every tile,
   int32_t* rowner;           //   last tile written to every slot
   int64_t tiles_max;
   int comm_per_xcd;
@@ -173,10 +176,21 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   int32_t* xq = dn_done + a.tiles_max + int64_t(x) * a.tiles_max;   // this XCD's tile ids
   int32_t* xend = a.cnt + kCntEnd + x;
   uint8_t* share = a.ring + int64_t(x) * a.ring_share;
+  // Planes of this XCD's q-th row tile: X in gather slot q % capx, g|u and h in activation
+  // slot q % capa.
+  auto planes = [&](int q) {
+    ActPlanes pl = act_planes(share + a.capx * a.xsb + int64_t(q % a.capa) * a.asb, kTileM, a.s.H,
+                              a.s.I, a.dtype, false);
+    const ActPlanes px = act_planes(share + int64_t(q % a.capx) * a.xsb, kTileM, a.s.H, a.s.I,
+                                    a.dtype, true);
+    pl.x = px.x;
+    pl.xs = px.xs;
+    return pl;
+  };
 
   if (ax == 0 && local == 0 && tid == 0) {
     a.rhdr[kRhTiles] = nt;
-    a.rhdr[kRhCapt] = a.capt;
+    a.rhdr[kRhCapt] = a.capa;
   }
   // The tile id of this XCD's q-th row tile: workgroup 0 takes it from the global counter and
   // publishes it (row tiles are taken when this XCD has a free slot, so faster XCDs take more
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
       } else {
         // One thread per XCD records its tiles in order, so each slot's owner ends as the
         // last tile that used it.
-        const int slot = x * a.capt + q % a.capt;
+        const int slot = x * a.capa + q % a.capa;
         a.rtiles[t] = a.tiles[t];
         a.rslot[t] = slot;
         a.rowner[slot] = t;
@@ -206,13 +220,12 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
     __syncthreads();
     return mt;
   };
-  // Pull the rows r = r0, r0 + rstep, ... of row tile mt into ring slot q % capt, then count
-  // this workgroup in landed[mt]. Lane j looks up row j's source first (one round of
-  // dependent loads per tile instead of one per row).
+  // Pull the rows r = r0, r0 + rstep, ... of row tile mt into its gather slot, then count this
+  // workgroup in landed[mt]. Lane j looks up row j's source first (one round of dependent
+  // loads per tile instead of one per row).
   auto gather = [&](int q, int mt, int r0, int rstep) {
     const MTile tl = a.tiles[mt];
-    const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
-                                    a.dtype, true);
+    const ActPlanes pl = planes(q);
     const uint16_t* my_src = nullptr;
     {
       const int r = r0 + lane * rstep;
@@ -244,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   };
 
   // ---- prologue: the first `lag` row tiles are gathered by every workgroup of the XCD ----
-  const int lag = a.capt > 2 ? 2 : 1;
+  const int lag = a.capa > 2 ? 2 : 1;                 // lag <= capx: the prologue never waits
   bool ended = false;
   for (int q = 0; q < lag; ++q) {
     const int mt = take_tile(q);
@@ -257,9 +270,13 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   }
 
   if (local < C) {
-    // ---- dispatch worker: the later row tiles, each into the slot its tile q - capt freed ----
+    // ---- dispatch worker: the later row tiles. Tile q reuses the gather slot of tile q - capx
+    // once its gate/up tiles are done, and the activation slot of tile q - capa once its down
+    // tiles are done.
     for (int q = lag; !ended; ++q) {
-      if (q >= a.capt && !wait_geq(dn_done + ld_relaxed(xq + q - a.capt), ndn, a.err, a.spin_limit))
+      if (q >= a.capx && !wait_geq(gu_done + ld_relaxed(xq + q - a.capx), ngu, a.err, a.spin_limit))
+        return;
+      if (q >= a.capa && !wait_geq(dn_done + ld_relaxed(xq + q - a.capa), ndn, a.err, a.spin_limit))
         return;
       const int mt = take_tile(q);
       if (mt < 0) return;
@@ -303,8 +320,7 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
       continue;                                       // no such row tile: nothing to do
     }
     const MTile tl = a.tiles[mt];
-    const ActPlanes pl = act_planes(share + int64_t(q % a.capt) * a.tsb, kTileM, a.s.H, a.s.I,
-                                    a.dtype, true);
+    const ActPlanes pl = planes(q);
     if (k < ngu) {
       if (!wait_geq(landed + mt, q < lag ? nx : C, a.err, a.spin_limit)) return;
       l1_invalidate();
@@ -328,9 +344,7 @@ hipError_t allow_big_lds(F* f) {
 
 }  // namespace
 
-int64_t fused_tile_slot_bytes(const Layout& L) { return L.tsb; }
-
-int fused_slots_per_xcd(const Layout& L) { return L.ring_capt; }
+int fused_slots_per_xcd(const Layout& L) { return L.ring_capa; }
 
 hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
                             const void* const* x_seg, const mok_weights& w, uint8_t* ring,
@@ -362,8 +376,10 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   a.x_seg = reinterpret_cast<const uint16_t* const*>(x_seg);
   a.ring = ring;
   a.ring_share = L.ring_share;
-  a.tsb = L.tsb;
-  a.capt = L.ring_capt;
+  a.xsb = L.xsb;
+  a.asb = L.asb;
+  a.capx = L.ring_capx;
+  a.capa = L.ring_capa;
   uint8_t* sv = const_cast<uint8_t*>(saved);
   a.rhdr = reinterpret_cast<int32_t*>(sv + L.sv_rhdr);
   a.rtiles = reinterpret_cast<MTile*>(sv + L.sv_rtiles);
@@ -371,7 +387,7 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   a.rowner = reinterpret_cast<int32_t*>(sv + L.sv_rowner);
   // no tile is resident until the kernel records it
   if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(a.rowner), 0xFFFFFFFFu,
-                             int64_t(kXcds) * L.ring_capt, s)) != hipSuccess)
+                             int64_t(kXcds) * L.ring_capa, s)) != hipSuccess)
     return err;
   a.s = FfnShape{L.H, L.I};
   if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};

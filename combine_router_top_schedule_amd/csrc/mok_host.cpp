@@ -86,7 +86,7 @@ const char* mok_status_str(mok_status s) {
     case MOK_ERR_DTYPE: return "invalid dtype or missing dtype-specific field";
     case MOK_ERR_ALIGN: return "misaligned device pointer";
     case MOK_ERR_WORKSPACE: return "workspace error";
-    case MOK_ERR_RING: return "ring buffer holds fewer than two minibatch slots";
+    case MOK_ERR_RING: return "ring buffer smaller than mok_sizes.ring_min_bytes";
     case MOK_ERR_HIP: return "HIP runtime or launch failure";
     case MOK_ERR_DEVICE_TIMEOUT: return "device-side bounded wait expired";
     case MOK_ERR_UNSUPPORTED: return "unsupported";
@@ -126,10 +126,12 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   sizes->rows_max = L.rows_max;
   sizes->ring_slots = kXcds * fused_slots_per_xcd(L);
   sizes->minibatch = L.M;
-  sizes->slot_bytes = fused_tile_slot_bytes(L);
+  sizes->slot_bytes = L.asb;
   sizes->perm_offset = L.sv_perm;
   sizes->tokpos_offset = L.sv_tokpos;
   sizes->touched_offset = L.sv_touched;
+  sizes->x_slot_bytes = L.xsb;
+  sizes->ring_min_bytes = int64_t(kXcds) * (kRingXSlots * L.xsb + 2 * L.asb);
   return MOK_OK;
 }
 

@@ -18,6 +18,7 @@ constexpr int kMaxLocalExperts = 64;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;            // XCDs per MI355X device (each with its own L2)
+constexpr int kRingXSlots = 2;      // gather slots per XCD share of the fused-forward ring
 
 __host__ __device__ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -66,9 +67,10 @@ struct Layout {
   // saved
   int64_t sv_perm, sv_tokpos, sv_touched, sv_bytes;
   int64_t sv_rhdr, sv_rtiles, sv_rslot, sv_rowner;
-  // fused-forward ring: bytes per XCD share, per tile slot, slots per XCD
-  int64_t ring_share, tsb;
-  int ring_capt;
+  // fused-forward ring, one share per XCD: gather slots (X of one row tile) and activation
+  // slots (g|u and h of one row tile)
+  int64_t ring_share, xsb, asb;
+  int ring_capx, ring_capa;
   // ws
   int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_bytes;
   int topk_blocks;
@@ -107,10 +109,17 @@ inline Layout make_layout(const mok_desc& d) {
   L.x_row_bytes = act_row_bytes(L.H, L.dtype);
   L.gu_row_bytes = int64_t(2) * L.I * 2;
   L.h_row_bytes = act_row_bytes(L.I, L.dtype);
-  // fused-forward ring: one share per XCD, cut into tile slots of kTileM rows (X | g,u | h)
-  L.tsb = align_up(int64_t(kTileM) * (L.x_row_bytes + L.gu_row_bytes + L.h_row_bytes), 256);
+  // fused-forward ring: one share per XCD = kRingXSlots gather slots (the X rows of a row tile,
+  // needed until its gate/up tiles are done) followed by activation slots (its g|u and h,
+  // needed until its down tiles are done, and kept for the backward afterwards)
+  L.xsb = align_up(int64_t(kTileM) * L.x_row_bytes, 256);
+  L.asb = align_up(int64_t(kTileM) * (L.gu_row_bytes + L.h_row_bytes), 256);
   L.ring_share = d.ring_bytes / kXcds / 256 * 256;
-  L.ring_capt = int(L.ring_share / L.tsb);
+  L.ring_capx = kRingXSlots;
+  {
+    const int64_t rest = L.ring_share - kRingXSlots * L.xsb;
+    L.ring_capa = rest > 0 ? int(rest / L.asb) : 0;
+  }
   // saved
   int64_t off = 1024;
   L.sv_perm = off; off = align_up(off + 4 * L.rows_max, 256);
@@ -119,7 +128,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.sv_rhdr = off; off = align_up(off + 4 * kRhWords, 256);
   L.sv_rtiles = off; off = align_up(off + 16 * L.tiles_max, 256);
   L.sv_rslot = off; off = align_up(off + 4 * L.tiles_max, 256);
-  L.sv_rowner = off; off = align_up(off + 4 * int64_t(kXcds) * (L.ring_capt > 0 ? L.ring_capt : 1), 256);
+  L.sv_rowner = off; off = align_up(off + 4 * int64_t(kXcds) * (L.ring_capa > 0 ? L.ring_capa : 1), 256);
   L.sv_bytes = off;
   // ws
   L.topk_blocks = int(cdiv(L.N, kTopkTokensPerBlock));
@@ -248,7 +257,6 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
 
 // Fused forward (k_fused.hip): the ring is split into one share per XCD, each cut into tile
 // slots of 256 expert-ordered rows (X | g,u | h).
-int64_t fused_tile_slot_bytes(const Layout& L);
 int fused_slots_per_xcd(const Layout& L);
 hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
                             const void* const* x_seg, const mok_weights& w, uint8_t* ring,

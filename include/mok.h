@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOK_ABI_VERSION 1
+#define MOK_ABI_VERSION 2
 
 typedef enum {
   MOK_OK = 0,
@@ -50,7 +50,7 @@ typedef enum {
   MOK_ERR_DTYPE = 3,           /* unknown dtype, or a field the dtype needs is missing   */
   MOK_ERR_ALIGN = 4,           /* a device pointer is not 16-byte aligned                */
   MOK_ERR_WORKSPACE = 5,       /* reserved                                               */
-  MOK_ERR_RING = 6,            /* ring_bytes holds fewer than two minibatch slots        */
+  MOK_ERR_RING = 6,            /* ring_bytes below mok_sizes.ring_min_bytes              */
   MOK_ERR_HIP = 7,             /* a HIP runtime call or kernel launch failed             */
   MOK_ERR_DEVICE_TIMEOUT = 8,  /* a device-side bounded wait ran out (see ws error word) */
   MOK_ERR_UNSUPPORTED = 9      /* not supported on this device                           */
@@ -96,15 +96,20 @@ typedef struct {
   size_t act_bytes;      /* staged path: g|u and h per dispatched row                       */
   size_t wq_bytes;       /* MXFP8: one quantised weight tensor (codes + scales)             */
   int64_t rows_max;      /* bound on expert-order rows                                       */
-  int32_t ring_slots;    /* R = ring_bytes / slot bytes (fused path)                        */
+  int32_t ring_slots;    /* R: activation slots of the fused-path ring, i.e. row tiles whose
+                            g|u and h the backward finds resident (8 XCD shares, each
+                            2 gather slots then R/8 activation slots)                        */
   int32_t minibatch;     /* M actually used (after the default is applied)                  */
-  int64_t slot_bytes;    /* bytes of one ring slot                                          */
+  int64_t slot_bytes;    /* bytes of one activation slot (g|u and h of 256 rows)            */
   /* Layout of the schedule table inside `saved` (byte offsets). Words 0..191 are a header:
    * [0] P (local pairs), [1] rows (P plus MXFP8 padding), [2] U (touched tokens),
    * [16 + e] count of local expert e, [96 + e] first row of expert e (e = 0..E_loc). */
   int64_t perm_offset;    /* int32 [rows_max]: expert-order row -> pair id (-1: pad row)     */
   int64_t tokpos_offset;  /* int32 [N*K]: pair id -> row (-1: not local)                     */
   int64_t touched_offset; /* int32 [N]: tokens with a local pair, ascending (first U valid)  */
+  int64_t x_slot_bytes;   /* bytes of one gather slot of the ring (X rows of 256 tokens)      */
+  int64_t ring_min_bytes; /* smallest ring_bytes the fused path accepts (two activation slots
+                             per XCD share)                                                  */
 } mok_sizes;
 
 /* Expert weights (device pointers). BF16 mode uses wg/wu/wd only. MXFP8 mode uses E4M3 codes
@@ -190,8 +195,9 @@ mok_status mok_combine(const mok_desc* desc, const void* saved_dev, const int32_
  * dispatch/combine workers and GEMM workers, coordinated through counters in HBM with no
  * host synchronisation; tokens flow through the fixed-size ring in minibatches of M rows
  * ("把 MoE 通信延迟从 103μs 压到 18μs", section 03 parts ② and ③; "Mixture-of-Kittens (MoK)",
- * section on the ring token buffer). Outputs as mok_schedule + mok_combine. The ring keeps
- * the last R minibatches' X, g|u and h for mok_layer_bwd. */
+ * section on the ring token buffer). Outputs as mok_schedule + mok_combine. ring_bytes must
+ * be at least mok_sizes.ring_min_bytes (else MOK_ERR_RING); the ring keeps g|u and h of the
+ * last R = mok_sizes.ring_slots row tiles (256 expert-ordered rows each) for mok_layer_bwd. */
 mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
                          const float* logits_dev, const mok_weights* w,
                          void* const* out_seg_dev, int32_t* topk_idx_dev, float* topk_p_dev,

@@ -119,13 +119,13 @@ def test_backward_dsv3_sampled():
 
 @pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
 def test_backward_reuses_ring_after_fused_forward(dtype):
-    """Reverse ring walk: after a fused forward through a ring of 2 tile slots per XCD (~16 of
-    ~64 row tiles stay resident) the backward restores the resident tiles' activations and
-    replays the rest. Matches the oracle, and equals bit for bit the backward after a staged
-    forward (which leaves nothing resident, so every row is replayed)."""
+    """Reverse ring walk: after a fused forward through the smallest ring (2 activation slots
+    per XCD: ~16 of ~64 row tiles stay resident) the backward restores the resident tiles'
+    activations and replays the rest. Matches the oracle, and equals bit for bit the backward
+    after a staged forward (which leaves nothing resident, so every row is replayed)."""
     cfg = datagen.CONFIGS["tiny"].replace(S=4, T=256, dtype=dtype, M=64, x_std=1.0)
-    tsb = mok.query_sizes(mok.desc_from_config(cfg)).slot_bytes
-    case = BwdCase(cfg, fused=True, ring_bytes=8 * 2 * tsb)
+    ring = mok.query_sizes(mok.desc_from_config(cfg)).ring_min_bytes
+    case = BwdCase(cfg, fused=True, ring_bytes=ring)
     case.run(fused=True)
     after_fused = case.grads()
     fw, bw = case.oracle_backward()

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert mok.abi_version() == 1
+    assert mok.abi_version() == 2
     for code in range(10):
         assert mok.lib().mok_status_str(code)
 
@@ -66,13 +66,18 @@ def test_sizes_follow_host_bounds():
     assert s.rows_max == N * 4                                # N * min(K, E_loc)
     assert s.slots_bytes >= N * 8 * 7168 * 2                  # Z: [N*K][H] BF16
     assert s.xd_bytes >= s.rows_max * 7168 * 2
-    # the ring is split into 8 per-XCD shares of 256-row tile slots (26,624 B BF16 rows)
-    assert s.slot_bytes == 256 * (7168 + 2 * 2048 + 2048) * 2
-    assert s.ring_slots == 8 * ((256 << 20) // 8 // s.slot_bytes) == 32
+    # the ring is split into 8 per-XCD shares; each holds 2 gather slots (X of 256 rows) and
+    # then as many activation slots (g|u and h of 256 rows) as fit
+    share = (256 << 20) // 8
+    assert s.x_slot_bytes == 256 * 7168 * 2
+    assert s.slot_bytes == 256 * (2 * 2048 + 2048) * 2
+    assert s.ring_slots == 8 * ((share - 2 * s.x_slot_bytes) // s.slot_bytes) == 64
+    assert s.ring_min_bytes == 8 * (2 * s.x_slot_bytes + 2 * s.slot_bytes)
     sm = mok.query_sizes(_d(dtype="mxfp8"))
     assert sm.rows_max == N * 4 + 4 * 31                      # per-expert padding to 32 rows
-    assert sm.slot_bytes == 256 * 17696                       # MXFP8 rows take 17,696 B
-    assert sm.ring_slots == 8 * 7
+    assert sm.x_slot_bytes == 256 * (7168 + 7168 // 32)       # E4M3 codes + UE8M0 scales
+    assert sm.slot_bytes == 256 * (2 * 2048 * 2 + 2048 + 2048 // 32)
+    assert sm.ring_slots == 8 * ((share - 2 * sm.x_slot_bytes) // sm.slot_bytes) == 88
     # null arguments are rejected before anything runs
     assert mok.lib().mok_schedule(ctypes.byref(_d()), None, None, None, None, None, None) == 1
 
