@@ -22,7 +22,7 @@
 //
 // Work order and deadlock freedom: all workgroups are co-resident (cooperative launch, one per
 // CU). The first `lag` row tiles of an XCD (lag = 2 with at least 3 activation slots per XCD,
-// else 1; never more than the 2 gather slots) are gathered by all of its workgroups together,
+// else 1; below the 3 gather slots) are gathered by all of its workgroups together,
 // since no GEMM work exists before them; the later ones by the dispatch workers alone. Within an XCD the GEMM items are numbered gu(0) ..
 // gu(lag-1), then blocks [gu(q+lag), dn(q)] for q = 0, 1, ... (gu = the gate/up column tiles of
 // a row tile, dn = its down column tiles), so the down tiles of a row tile come `lag` blocks
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   };
 
   // ---- prologue: the first `lag` row tiles are gathered by every workgroup of the XCD ----
-  const int lag = a.capa > 2 ? 2 : 1;                 // lag <= capx: the prologue never waits
+  const int lag = a.capa > 2 ? 2 : 1;                 // lag < capx: the prologue never waits
   bool ended = false;
   for (int q = 0; q < lag; ++q) {
     const int mt = take_tile(q);

@@ -18,7 +18,7 @@ constexpr int kMaxLocalExperts = 64;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;            // XCDs per MI355X device (each with its own L2)
-constexpr int kRingXSlots = 2;      // gather slots per XCD share of the fused-forward ring
+constexpr int kRingXSlots = 3;      // gather slots per XCD share of the fused-forward ring
 
 __host__ __device__ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

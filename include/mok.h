@@ -98,7 +98,7 @@ typedef struct {
   int64_t rows_max;      /* bound on expert-order rows                                       */
   int32_t ring_slots;    /* R: activation slots of the fused-path ring, i.e. row tiles whose
                             g|u and h the backward finds resident (8 XCD shares, each
-                            2 gather slots then R/8 activation slots)                        */
+                            3 gather slots then R/8 activation slots)                        */
   int32_t minibatch;     /* M actually used (after the default is applied)                  */
   int64_t slot_bytes;    /* bytes of one activation slot (g|u and h of 256 rows)            */
   /* Layout of the schedule table inside `saved` (byte offsets). Words 0..191 are a header:

@@ -50,7 +50,7 @@ def test_fused_forward_tiny_matches_oracle_and_staged(dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
 def test_fused_forward_ring_wraps(dtype):
     # 2048 pairs cut by 64-row minibatches into ~64 row tiles: ~8 tiles per XCD through the
-    # smallest ring (2 gather and 2 activation slots per XCD), so every slot is reused several
+    # smallest ring (3 gather and 2 activation slots per XCD), so every slot is reused several
     # times.
     cfg = datagen.CONFIGS["tiny"].replace(S=4, T=256, dtype=dtype, M=64, x_std=1.0)
     d = mok.desc_from_config(cfg)
