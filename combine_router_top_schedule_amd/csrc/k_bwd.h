@@ -241,7 +241,8 @@ __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t 
 }
 
 // Weight-gradient tile: out[m0 + m][n0 + n] = sum over the expert's padded columns c of
-// Ta[m0 + m][c] Tb[n0 + n][c]; fp32 output [Fa][Fb] (fully overwritten).
+// Ta[m0 + m][c] Tb[n0 + n][c]; fp32 output [Fa][Fb] (fully overwritten). ld = row pitch of Ta
+// and Tb (elements; their MXFP8 scale rows have ld / 32 bytes).
 template <bool MX>
 __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const uint8_t* ta_s,
                                            const uint8_t* tb, const uint8_t* tb_s, int64_t ld,

@@ -90,9 +90,11 @@ struct TransposeArgs {
   const uint8_t* plane_s;      // MXFP8 scales of the plane (null: BF16 plane)
   int64_t plane_stride;        // elements per plane row
   int plane_col0;              // first feature column inside the plane
-  uint16_t* dst;               // [F][ld] BF16 (when qdst is null)
-  uint8_t* qdst;               // else MXFP8 along tokens: codes [F][ld], then scales [F][ld/32]
-  int64_t ld;
+  // Rows of the transposed planes are packed at the padded column total `cols` (hdr2, known on
+  // the device only), so the bytes in use stay contiguous whatever the host-side bound.
+  uint16_t* dst;               // [F][cols] BF16 (when qdst is null)
+  uint8_t* qdst;               // else MXFP8 along tokens: codes [F][cols], scales at F * ld
+  int64_t ld;                  // host bound on cols (places the MXFP8 scale plane)
   int F, K, T, El;
 };
 
@@ -196,11 +198,11 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
         // blocks of 32 padded columns (4 lanes); expert ranges start at multiples of 128
         uint32_t sc;
         const uint2 codes = mx_quant8_group4(out, &sc);
-        *reinterpret_cast<uint2*>(a.qdst + int64_t(f0 + f) * a.ld + c0 + cc * 8) = codes;
+        *reinterpret_cast<uint2*>(a.qdst + int64_t(f0 + f) * cols + c0 + cc * 8) = codes;
         if ((cc & 3) == 0)
-          a.qdst[int64_t(a.F) * a.ld + int64_t(f0 + f) * (a.ld / 32) + (c0 + cc * 8) / 32] = uint8_t(sc);
+          a.qdst[int64_t(a.F) * a.ld + int64_t(f0 + f) * (cols / 32) + (c0 + cc * 8) / 32] = uint8_t(sc);
       } else {
-        *reinterpret_cast<u32x4*>(a.dst + int64_t(f0 + f) * a.ld + c0 + cc * 8) = out;
+        *reinterpret_cast<u32x4*>(a.dst + int64_t(f0 + f) * cols + c0 + cc * 8) = out;
       }
     }
     __syncthreads();
@@ -341,7 +343,8 @@ struct BwdArgs {
   WJob jobs[3];
   int njobs;
   int El;
-  int64_t ld;              // padded columns of the transposed planes
+  int64_t ld;              // host bound on the padded columns (places the MXFP8 scale planes;
+                           // rows are packed at the device-side total hdr2[kB2RowsPad])
   int32_t* queue;          // [kXcds] work counters of one launch (zeroed before it)
 };
 
@@ -408,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gemms(BwdArgs a) {
         tile_coords(rem % (mtn * ntw), mtn, ntw, mt, nt);
         const int c0 = a.hdr2[kB2ColPad + e];
         const int ncols = a.hdr2[kB2ColPad + e + 1] - c0;
-        wgrad_tile<MX>(sm, jb.t_a, jb.t_a_s, jb.t_b, jb.t_b_s, a.ld, c0, ncols, mt * kTileM,
+        wgrad_tile<MX>(sm, jb.t_a, jb.t_a_s, jb.t_b, jb.t_b_s, a.hdr2[kB2RowsPad], c0, ncols, mt * kTileM,
                        nt * kTileN, jb.Fa, jb.Fb, jb.dw + int64_t(e) * jb.Fa * jb.Fb);
       }
     }
