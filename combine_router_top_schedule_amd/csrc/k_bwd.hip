@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* src, uint16
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + 256 * i, r = idx >> 4, ch = idx & 15;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(sp + int64_t(r0 + r) * C + c0 + ch * 8);
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(sp + int64_t(r0 + r) * C + c0 + ch * 8));
       uint32_t* w = reinterpret_cast<uint32_t*>(t + r * kPitch + ch * 8);
 #pragma unroll
       for (int k = 0; k < 4; ++k) w[k] = v[k];
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
       uint32_t w[4] = {0u, 0u, 0u, 0u};
       if (src) {
         if (mxp) {
-          const uint2 c8 = *reinterpret_cast<const uint2*>(src + ch * 8);
+          const uint64_t c64 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(src + ch * 8));
+          const uint2 c8 = make_uint2(uint32_t(c64), uint32_t(c64 >> 32));
           const float sc = exp2i(int((s_sc4[r] >> (8 * (ch >> 2))) & 0xFFu) - 127);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
             w[k] = pack_bf2(e4m3_value(uint8_t(cw >> sh)) * sc, e4m3_value(uint8_t(cw >> (sh + 8))) * sc);
           }
         } else {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(src + ch * 16);
+          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ch * 16));
 #pragma unroll
           for (int k = 0; k < 4; ++k) w[k] = v[k];
           if (a.p) {
