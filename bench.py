@@ -218,7 +218,9 @@ def main() -> int:
     step_flop = (6.0 if args.forward_only else 18.0) * P * HI
     peak = PEAK_MXFP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     achieved = fwd_flop / (fused_ms * 1e-3) / 1e12
-    traffic = stored_traffic()
+    # the committed counter summary covers the default DeepSeek-V3 BF16 run only
+    traffic = stored_traffic() if (args.workload == "dsv3" and not args.minibatch
+                                   and not args.forward_only) else None
     tokens_s = cfg.T / (ms * 1e-3)
     line = {
         "metric": ("MoE layer tokens/sec fwd only on 1 MI355X (minibatch sweep)" if args.forward_only
