@@ -273,19 +273,32 @@ __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   }
+  // The fp32 tile leaves through LDS in two passes of 128 rows: the two waves holding those
+  // rows (wm == pass) stage their 128 x 128 blocks in the stage buffers ([128][256] fp32,
+  // 128 KB), then every wave writes whole 1 KB rows with 16-byte stores. Storing 4 bytes per
+  // lane straight from the accumulators is many times slower when many tiles end together.
+  // nb is a multiple of 32 (H and I are), so a lane's 4 columns are all in range or all out.
+  float* t = reinterpret_cast<float*>(sm.a[0]);
+  for (int pass = 0; pass < 2; ++pass) {
+    if (wm == pass) {
+      float* tl = t + opaque(4 * (lane >> 5) * 256 + wn * 128 + (lane & 31));
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = wm * 128 + i * 32 + acc_row(v, lane);
-      if (m >= ma) continue;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = wn * 128 + j * 32 + (lane & 31);
-        if (n < nb) out[int64_t(m0 + m) * Fb + n0 + n] = acc[i][j][v];
-      }
+          for (int v = 0; v < 16; ++v)
+            tl[(i * 32 + 8 * (v >> 2) + (v & 3)) * 256 + j * 32] = acc[i][j][v];
     }
-  __syncthreads();
+    __syncthreads();
+    for (int r = wave; r < 128; r += 4) {
+      const int m = pass * 128 + r;
+      if (m < ma && lane * 4 < nb)
+        *reinterpret_cast<f32x4*>(out + int64_t(m0 + m) * Fb + n0 + lane * 4) =
+            *reinterpret_cast<const f32x4*>(t + r * 256 + lane * 4);
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace mok
