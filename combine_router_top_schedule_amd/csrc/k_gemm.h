@@ -251,7 +251,6 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
           load_frag(f[(kk + 1) & 1], sm.a[cur ^ 1], sm.b[cur ^ 1], sm.as[cur ^ 1], sm.bs[cur ^ 1],
                     0, wm, wn, lane);
       }
-      if (MX) __builtin_amdgcn_sched_barrier(0);
       mma(f[kk & 1], acc);
       if (!MX) {
         // BF16: one fragment read between consecutive MFMAs of the slice
@@ -261,6 +260,15 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      } else {
+        // E4M3: the 24 LDS reads of the next slice (16 code fragments, 8 scale words), two
+        // between consecutive MFMAs (measured 3-8 % faster than issuing them all first)
+#pragma unroll
+        for (int q = 0; q < 12; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
