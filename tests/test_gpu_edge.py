@@ -48,8 +48,9 @@ def _run_both(case):
     case.out.zero_()
     case.run(fused=False)
     staged = case.grads() + [case.out.clone()]
-    for a, b in zip(fused, staged):
-        assert torch.equal(a, b)
+    names = ["dx", "dp", "dwg", "dwu", "dwd"] + (["dlogits"] if case.dlogits is not None else []) + ["out"]
+    for name, a, b in zip(names, fused, staged):
+        assert torch.equal(a, b), f"{name}: {int((a != b).sum())} elements differ"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
