@@ -34,12 +34,18 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_layer_fwd_dsv3_bf16.md")
 CSRC = os.path.join(HERE, "combine_router_top_schedule_amd", "csrc")
 
 
+# The sources the fused forward kernel (k_layer_fwd) is compiled from: its file and every header
+# it includes. A stored HBM-traffic figure for that kernel is valid only for these.
+FUSED_FWD_SOURCES = ("k_fused.hip", "k_ffn.h", "k_gemm.h", "mok_rows.h", "mok_device.h",
+                     "mok_internal.h", os.path.join("..", "..", "include", "mok.h"))
+
+
 def csrc_digest() -> str:
-    """Digest of the kernel sources: a stored HBM-traffic figure is valid only for these."""
+    """Digest of the fused forward kernel's sources."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in FUSED_FWD_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+            h.update(os.path.basename(name).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
