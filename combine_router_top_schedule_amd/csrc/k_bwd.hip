@@ -63,20 +63,6 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* src, uint16
   }
 }
 
-// Padded column layout of the per-expert transposed planes: expert e's rows go to columns
-// [colpad[e], colpad[e] + count[e]), colpad[e] a multiple of kPadRows; the rest of its
-// rounded-up range is zero. hdr2[0] = total padded columns.
-__global__ void k_colpad(const int32_t* hdr, int32_t* hdr2, int El) {
-  if (threadIdx.x != 0) return;
-  int off = 0;
-  for (int e = 0; e < El; ++e) {
-    hdr2[kB2ColPad + e] = off;
-    off += (hdr[kHdrCounts + e] + kPadRows - 1) / kPadRows * kPadRows;
-  }
-  hdr2[kB2ColPad + El] = off;
-  hdr2[kB2RowsPad] = off;
-}
-
 // Gather-transpose for the weight-gradient operands: T[f][colpad_e + i] = value of feature f of
 // row off_e + i of expert e. Sources: a BF16 plane [rows][F] (with column offset), an MXFP8
 // plane (dequantised), or the token segments through perm (optionally scaled by p of the
@@ -213,37 +199,88 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
 
 // ---- reverse ring walk: reuse what the forward left resident, replay the rest -------------
 
-// Split the forward's tiles into those whose ring slot still holds them (their g|u and h are
-// copied back) and those to replay (X gathered again, gate/up recomputed). Without ring state
-// (staged forward, or no ring passed) every row is replayed, in per-expert tiles. One thread,
-// tile order, so the lists are deterministic.
-__global__ void k_bwd_plan(const int32_t* hdr, const int32_t* rhdr, const MTile* rtiles,
-                           const int32_t* rslot, const int32_t* rowner, int have_ring,
-                           MTile* restore, int32_t* restore_slot, MTile* replay, int32_t* counts,
-                           int El, int64_t tiles_max) {
-  if (threadIdx.x != 0) return;
-  int64_t nr = 0, np = 0;
-  const int nt = have_ring ? rhdr[kRhTiles] : 0;
-  if (nt > 0) {
-    for (int mt = 0; mt < nt && mt < tiles_max; ++mt) {
-      const MTile t = rtiles[mt];
-      const int sl = rslot[mt];
-      if (rowner[sl] == mt) {
-        restore[nr] = t;
-        restore_slot[nr] = sl;
-        ++nr;
-      } else {
-        replay[np++] = t;
-      }
-    }
-  } else {
-    for (int e = 0; e < El; ++e) {
-      const int r0 = hdr[kHdrOffsets + e], r1 = r0 + hdr[kHdrCounts + e];
-      for (int r = r0; r < r1 && np < tiles_max; r += kTileM) replay[np++] = MTile{0, e, r, min(kTileM, r1 - r)};
+// Backward set-up, one wave, no host synchronisation:
+//  - split the forward's tiles into those whose ring slot still holds them (their g|u and h are
+//    copied back) and those to replay (X gathered again, gate/up recomputed), both in forward
+//    tile order (ballot compaction, so the lists are deterministic); without ring state (staged
+//    forward, or no ring passed) every row is replayed, in per-expert tiles;
+//  - the backward GEMMs' tile table: per-expert tiles of at most kTileM rows (no minibatch cuts);
+//  - the padded column layout of the per-expert transposed planes: expert e's rows go to
+//    columns [colpad[e], colpad[e] + count[e]), colpad[e] a multiple of kPadRows, the rest of its
+//    rounded-up range zero; hdr2[kB2RowsPad] = total padded columns;
+//  - zeroed work-queue counters of the two GEMM launches.
+// El <= 64, so lane e owns expert e.
+__global__ __launch_bounds__(64) void k_bwd_plan(const int32_t* hdr, const int32_t* rhdr,
+                                                 const MTile* rtiles, const int32_t* rslot,
+                                                 const int32_t* rowner, int have_ring,
+                                                 MTile* restore, int32_t* restore_slot,
+                                                 MTile* replay, int32_t* counts, MTile* tiles,
+                                                 int32_t* ntiles, int32_t* hdr2, int El,
+                                                 int64_t tiles_max) {
+  const int lane = threadIdx.x;
+  const uint64_t lt = (1ull << lane) - 1;
+  // per-expert rows and tile counts, exclusive prefix over experts (lanes)
+  const int off = lane < El ? hdr[kHdrOffsets + lane] : 0;
+  const int cnt = lane < El ? hdr[kHdrCounts + lane] : 0;
+  const int nt_e = (cnt + kTileM - 1) / kTileM;
+  const int pad_e = (cnt + kPadRows - 1) / kPadRows * kPadRows;
+  int t_ex = nt_e, p_ex = pad_e;                       // inclusive scans, then made exclusive
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int a = __shfl_up(t_ex, d, 64), b = __shfl_up(p_ex, d, 64);
+    if (lane >= d) {
+      t_ex += a;
+      p_ex += b;
     }
   }
-  counts[0] = int32_t(nr);
-  counts[1] = int32_t(np);
+  const int t_tot = __shfl(t_ex, 63, 64), p_tot = __shfl(p_ex, 63, 64);
+  t_ex -= nt_e;
+  p_ex -= pad_e;
+  // per-expert tiles: the GEMM tile table, and the replay list when there is no ring state
+  const int nt = have_ring ? rhdr[kRhTiles] : 0;
+  if (lane < El) {
+    for (int q = 0; q < nt_e && t_ex + q < tiles_max; ++q) {
+      const MTile t{0, lane, off + q * kTileM, min(kTileM, cnt - q * kTileM)};
+      tiles[t_ex + q] = t;
+      if (nt <= 0) replay[t_ex + q] = t;
+    }
+    hdr2[kB2ColPad + lane] = p_ex;
+  }
+  // forward tiles -> restore / replay lists in tile order
+  int64_t nr = 0, np = 0;
+  if (nt > 0) {
+    for (int base = 0; base < nt && base < tiles_max; base += 64) {
+      const int mt = base + lane;
+      const bool valid = mt < nt && mt < tiles_max;
+      MTile t{0, 0, 0, 0};
+      int sl = 0;
+      bool res = false;
+      if (valid) {
+        t = rtiles[mt];
+        sl = rslot[mt];
+        res = rowner[sl] == mt;
+      }
+      const uint64_t bres = __ballot(valid && res), brep = __ballot(valid && !res);
+      if (valid && res) {
+        const int64_t i = nr + __popcll(bres & lt);
+        restore[i] = t;
+        restore_slot[i] = sl;
+      }
+      if (valid && !res) replay[np + __popcll(brep & lt)] = t;
+      nr += __popcll(bres);
+      np += __popcll(brep);
+    }
+  } else {
+    np = min(int64_t(t_tot), tiles_max);
+  }
+  if (lane == 0) {
+    counts[0] = int32_t(nr);
+    counts[1] = int32_t(np);
+    *ntiles = int32_t(min(int64_t(t_tot), tiles_max));
+    hdr2[kB2ColPad + El] = p_tot;
+    hdr2[kB2RowsPad] = p_tot;
+  }
+  if (lane < 2 * kXcds) counts[4 + lane] = 0;          // the two GEMM launches' queue counters
 }
 
 // Work item = 16 rows of one listed tile. Restored tiles: copy each row's g|u and h (with MX
@@ -486,8 +523,9 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
                      reinterpret_cast<const MTile*>(b.saved + L.sv_rtiles),
                      reinterpret_cast<const int32_t*>(b.saved + L.sv_rslot),
                      reinterpret_cast<const int32_t*>(b.saved + L.sv_rowner),
-                     int(b.ring != nullptr && L.ring_capa > 0), restore, rsl, replay, counts, El,
-                     L.tiles_max);
+                     int(b.ring != nullptr && L.ring_capa > 0), restore, rsl, replay, counts,
+                     reinterpret_cast<MTile*>(b.ws + L.ws_tiles),
+                     reinterpret_cast<int32_t*>(b.ws) + kWsNumTiles, b.hdr2, El, L.tiles_max);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     StageArgs st{};
@@ -512,8 +550,6 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   }
   if ((err = launch_ffn_gateup_list(L, b.saved, b.xd, b.w, b.act, replay, counts + 1, s)) != hipSuccess)
     return err;
-  // per-expert tiles (no minibatch cuts) for the backward GEMMs
-  if ((err = launch_tiles(L, int(L.rows_max), b.saved, b.ws, s)) != hipSuccess) return err;
   // 2. pull reverse-combine: D[r] = dOut[n(r)] (BF16; quantised along H for the a GEMM)
   //    (MXFP8: the gather quantises along H on the way, like the forward dispatch)
   if ((err = launch_dispatch(L, b.saved, b.dout_seg, mx ? b.dq : b.d, s)) != hipSuccess) return err;
@@ -529,7 +565,6 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   }
   // 4. weight-gradient operand planes that do not need dg|du: per-expert column ranges, X^T,
   //    (p D)^T and h^T (MXFP8: quantised along tokens as they are written)
-  hipLaunchKernelGGL(k_colpad, dim3(1), dim3(64), 0, s, hdr, b.hdr2, El);
   const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
   const uint16_t* const* ds = reinterpret_cast<const uint16_t* const*>(b.dout_seg);
   const int64_t ld = L.rp_max;
@@ -585,7 +620,6 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   // 5. phase 0: a GEMM with fused dp / SwiGLU backward, and dWd
   a.njobs = 1;
   job(a.jobs[0], b.dt, b.ht, b.q_dt, b.q_ht, H, I, b.g.dwd);
-  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(a.queue), 0u, kXcds, s)) != hipSuccess) return err;
   trace_before(MOK_TRACE_BWD_GEMM1, s);
   if (mx) hipLaunchKernelGGL((k_bwd_gemms<true, 0>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   else hipLaunchKernelGGL((k_bwd_gemms<false, 0>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
@@ -600,7 +634,6 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   job(a.jobs[0], b.dgt, b.xt, b.q_dgt, b.q_xt, I, H, b.g.dwg);
   job(a.jobs[1], b.dut, b.xt, b.q_dut, b.q_xt, I, H, b.g.dwu);
   a.queue = counts + 4 + kXcds;
-  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(a.queue), 0u, kXcds, s)) != hipSuccess) return err;
   trace_before(MOK_TRACE_BWD_GEMM2, s);
   if (mx) hipLaunchKernelGGL((k_bwd_gemms<true, 1>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   else hipLaunchKernelGGL((k_bwd_gemms<false, 1>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);

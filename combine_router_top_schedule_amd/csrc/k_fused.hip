@@ -358,15 +358,6 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   }
   if ((err = launch_tiles(L, L.M, saved, ws, s)) != hipSuccess) return err;
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.ws_counters);
-  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(cnt), 0u, kCntWords + 3 * L.tiles_max, s)) !=
-      hipSuccess)
-    return err;
-  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(cnt + kCntWords + 3 * L.tiles_max), 0xFFFFFFFFu,
-                             int64_t(kMaxXcd) * L.tiles_max, s)) != hipSuccess)
-    return err;
-  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(cnt + kCntEnd), 0xFFFFFFFFu, kMaxXcd, s)) !=
-      hipSuccess)
-    return err;
   const bool mx = L.dtype == MOK_MXFP8;
   FusedArgs a{};
   a.hdr = reinterpret_cast<const int32_t*>(saved);
@@ -385,10 +376,20 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   a.rtiles = reinterpret_cast<MTile*>(sv + L.sv_rtiles);
   a.rslot = reinterpret_cast<int32_t*>(sv + L.sv_rslot);
   a.rowner = reinterpret_cast<int32_t*>(sv + L.sv_rowner);
-  // no tile is resident until the kernel records it
-  if ((err = launch_fill_u32(reinterpret_cast<uint32_t*>(a.rowner), 0xFFFFFFFFu,
-                             int64_t(kXcds) * L.ring_capa, s)) != hipSuccess)
-    return err;
+  // One launch sets the counters: zero, except the per-XCD tile counts (kCntEnd, -1 until
+  // known) and the per-XCD tile ids that follow the per-tile counters (-1 until taken); and no
+  // tile is resident in any activation slot until the kernel records it.
+  {
+    uint32_t* c = reinterpret_cast<uint32_t*>(cnt);
+    const FillRange fills[] = {
+        {c, kCntEnd, 0u},
+        {c + kCntEnd, kMaxXcd, 0xFFFFFFFFu},
+        {c + kCntEnd + kMaxXcd, kCntWords - kCntEnd - kMaxXcd + 3 * L.tiles_max, 0u},
+        {c + kCntWords + 3 * L.tiles_max, int64_t(kMaxXcd) * L.tiles_max, 0xFFFFFFFFu},
+        {reinterpret_cast<uint32_t*>(a.rowner), int64_t(kXcds) * L.ring_capa, 0xFFFFFFFFu},
+    };
+    if ((err = launch_fill_ranges(fills, 5, s)) != hipSuccess) return err;
+  }
   a.s = FfnShape{L.H, L.I};
   if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
   else a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),

@@ -14,6 +14,18 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int64_t n) {
     p[i] = v;
 }
 
+struct FillRanges {
+  FillRange r[kMaxFillRanges];
+  int count;
+};
+
+__global__ void k_fill_ranges(FillRanges a) {
+  for (int k = 0; k < a.count; ++k)
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < a.r[k].n;
+         i += int64_t(gridDim.x) * blockDim.x)
+      a.r[k].p[i] = a.r[k].v;
+}
+
 // Pull dispatch ("Mixture-of-Kittens (MoK)", section on pull dispatch; "把 MoE 通信延迟从 103μs
 // 压到 18μs", section 03 part ①): the receiving side reads each routed row from its source
 // segment and lays it out in expert order; MXFP8 rows are quantised along H on the way
@@ -116,6 +128,20 @@ int device_cus() {
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n, 256, 2048)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_ranges(const FillRange* r, int count, hipStream_t s) {
+  if (count > kMaxFillRanges) return hipErrorInvalidValue;
+  FillRanges a{};
+  int64_t nmax = 0;
+  for (int k = 0; k < count; ++k) {
+    if (r[k].n <= 0) continue;
+    a.r[a.count++] = r[k];
+    nmax = r[k].n > nmax ? r[k].n : nmax;
+  }
+  if (a.count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_ranges, dim3(grid_for(nmax, 256, 2048)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

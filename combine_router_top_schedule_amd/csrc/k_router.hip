@@ -327,11 +327,16 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
   int32_t* hdr = reinterpret_cast<int32_t*>(saved);
   int32_t* wsh = reinterpret_cast<int32_t*>(ws);
   uint32_t* state = reinterpret_cast<uint32_t*>(ws + L.ws_state);
-  hipError_t err = launch_fill_u32(state, 0u, int64_t(L.topk_blocks) * (L.El + 1), s);
-  if (err != hipSuccess) return err;
-  err = launch_fill_u32(reinterpret_cast<uint32_t*>(wsh + kWsTicket), 0u, 1, s);
-  if (err != hipSuccess) return err;
-  err = launch_fill_u32(reinterpret_cast<uint32_t*>(hdr), 0u, kHdrWords, s);
+  // One launch clears the workspace header (error word, scan ticket), the ring record header
+  // (nothing resident until a fused forward writes it), the look-back scan state and the
+  // schedule header.
+  const FillRange fills[] = {
+      {reinterpret_cast<uint32_t*>(wsh), kWsWords, 0u},
+      {reinterpret_cast<uint32_t*>(saved + L.sv_rhdr), kRhWords, 0u},
+      {state, int64_t(L.topk_blocks) * (L.El + 1), 0u},
+      {reinterpret_cast<uint32_t*>(hdr), kHdrWords, 0u},
+  };
+  hipError_t err = launch_fill_ranges(fills, 4, s);
   if (err != hipSuccess) return err;
   RouterArgs a{logits, idx, p, hdr,
                reinterpret_cast<int32_t*>(saved + L.sv_tokpos),

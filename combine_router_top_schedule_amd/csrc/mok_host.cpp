@@ -143,12 +143,8 @@ mok_status mok_schedule(const mok_desc* desc, const float* logits_dev, int32_t* 
   if (!aligned16(logits_dev) || !aligned16(saved_dev) || !aligned16(ws_dev)) return MOK_ERR_ALIGN;
   const Layout L = layout_of(*desc);
   hipStream_t s = as_stream(stream);
-  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(ws_dev), 0u, kWsWords, s);
-  // the staged path leaves nothing in the ring for the backward
-  if (e == hipSuccess)
-    e = launch_fill_u32(reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(saved_dev) + L.sv_rhdr), 0u,
-                        kRhWords, s);
-  if (e != hipSuccess) return MOK_ERR_HIP;
+  // (the router clears the workspace header and the ring record: the staged path leaves
+  // nothing in the ring for the backward)
   return hip_status(launch_router(L, logits_dev, topk_idx_dev, topk_p_dev,
                                   static_cast<uint8_t*>(saved_dev), static_cast<uint8_t*>(ws_dev), s));
 }
@@ -239,9 +235,7 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
   hipStream_t s = as_stream(stream);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   uint8_t* saved = static_cast<uint8_t*>(saved_dev);
-  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(ws), 0u, kWsWords, s);
-  if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(saved + L.sv_rhdr), 0u, kRhWords, s);
-  if (e == hipSuccess) e = launch_router(L, logits_dev, topk_idx_dev, topk_p_dev, saved, ws, s);
+  hipError_t e = launch_router(L, logits_dev, topk_idx_dev, topk_p_dev, saved, ws, s);
   if (e == hipSuccess)
     e = launch_layer_fwd(L, *desc, saved, x_seg_dev, *w, static_cast<uint8_t*>(ring_dev),
                          static_cast<uint16_t*>(slots_dev), ws, s);

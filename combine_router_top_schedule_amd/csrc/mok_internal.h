@@ -211,6 +211,14 @@ struct MTile {
 
 // ---- launch wrappers (defined in the .hip files) ----------------------------------------
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s);
+// Several disjoint word ranges set in one launch (ranges with n <= 0 are skipped).
+struct FillRange {
+  uint32_t* p;
+  int64_t n;
+  uint32_t v;
+};
+constexpr int kMaxFillRanges = 8;
+hipError_t launch_fill_ranges(const FillRange* r, int count, hipStream_t s);
 hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, float* p,
                          uint8_t* saved, uint8_t* ws, hipStream_t s);
 hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s);
