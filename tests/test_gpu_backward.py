@@ -115,6 +115,13 @@ def test_backward_dsv3_sampled():
         du = dh * g * sg
         assert max_rel_err(dwg[i], dg @ X) <= BF16_TOL
         assert max_rel_err(dwu[i], du @ X) <= BF16_TOL
+    # Sampled rows j of dWd_e = sum_r p_r D_r[j] h_r need the expert's whole h = silu(g) u.
+    G = X @ W.wg[e].T
+    U_ = X @ W.wu[e].T
+    Hh = G / (1 + np.exp(-G)) * U_
+    dwd = case.dwd[e].cpu().numpy()
+    for j in rng.choice(cfg.H, 8, replace=False):
+        assert max_rel_err(dwd[j], (p_row * D[:, j]) @ Hh) <= BF16_TOL
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])

@@ -76,6 +76,32 @@ def test_fused_forward_dsv3_equals_staged_and_is_minibatch_independent():
     assert torch.equal(_fused(case2), staged)
 
 
+def test_fused_forward_kimi_minibatch_sweep():
+    """Kimi-K2-shaped local share (experts 0..5 of 384, top-8, H 7168, I 2048) through the fixed
+    256 MiB ring at minibatch sizes 512, 1024, 2368 and 2560: every fused run equals the staged
+    path bit for bit, and 64 sampled touched tokens are recomputed by the oracle."""
+    from combine_router_top_schedule_amd.layer import MokLayer
+    cfg = datagen.CONFIGS["kimi"]
+    case = Case(cfg, fused=True)
+    staged = _staged(case)
+    for M in (512, 1024, 2368, 2560):
+        layer = MokLayer(mok.desc_from_config(cfg, M=M), staged=False, fused=True)
+        layer.set_weights(case.wg, case.wu, case.wd)
+        case.out.zero_()
+        layer.forward(case.x_seg, case.logits, case.out_seg)
+        torch.cuda.synchronize()
+        assert mok.mok_device_status(layer.ws) == 0
+        assert torch.equal(case.out, staged), f"minibatch {M}"
+        del layer
+    hdr, perm, tokpos, touched = case.layer.table()
+    U = int(hdr[2])
+    sample = np.sort(np.random.default_rng(2).choice(touched.numpy()[:U], 64, replace=False))
+    fw = case.oracle_forward(tokens=sample)
+    assert len(fw.sched.touched) == len(sample)
+    err = max_rel_err(case.out_rows(sample), fw.out)
+    assert err <= BF16_TOL, err
+
+
 def test_fused_forward_ring_too_small_is_rejected():
     cfg = datagen.CONFIGS["tiny"]
     case = Case(cfg, fused=True, ring_bytes=1 << 20)
