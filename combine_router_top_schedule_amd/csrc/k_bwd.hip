@@ -83,6 +83,9 @@ struct TransposeArgs {
   uint8_t* qdst;               // else MXFP8 along tokens: codes [F][cols], scales at F * ld
   int64_t ld;                  // host bound on cols (places the MXFP8 scale plane)
   int F, K, T, El;
+  // Non-null (BF16 rows from segments): every source row is also copied, unscaled, to
+  // rows_out[its expert-ordered row][F] (the dOut gather D of the backward, read once for both).
+  uint16_t* rows_out;
 };
 
 // One tile = 64 padded columns (source rows) x 128 features. Source rows are read with 16-byte
@@ -98,6 +101,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
   __shared__ const uint8_t* s_src[kTrCols];   // first byte of the row's tile features (null: zero)
   __shared__ float s_gate[kTrCols];           // p of the row's pair (scaled sources)
   __shared__ uint32_t s_sc4[kTrCols];         // MXFP8 plane: the 4 scale codes of the tile's blocks
+  __shared__ int s_row[kTrCols];              // expert-ordered row of the tile's column
   const int tid = threadIdx.x;
   if (tid <= a.El) {
     s_pad[tid] = a.hdr2[kB2ColPad + tid];
@@ -137,6 +141,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
       s_src[tid] = src;
       s_gate[tid] = gate;
       s_sc4[tid] = sc4;
+      s_row[tid] = li < s_cnt[e] ? s_off[e] + li : -1;
     }
     __syncthreads();
     // load: 64 rows x 16 chunks of 8 features
@@ -160,6 +165,8 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
           const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ch * 16));
 #pragma unroll
           for (int k = 0; k < 4; ++k) w[k] = v[k];
+          if (a.rows_out)
+            *reinterpret_cast<u32x4*>(a.rows_out + int64_t(s_row[r]) * a.F + f0 + ch * 8) = v;
           if (a.p) {
             const float g = s_gate[r];
 #pragma unroll
@@ -552,7 +559,8 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
     return err;
   // 2. pull reverse-combine: D[r] = dOut[n(r)] (BF16; quantised along H for the a GEMM)
   //    (MXFP8: the gather quantises along H on the way, like the forward dispatch)
-  if ((err = launch_dispatch(L, b.saved, b.dout_seg, mx ? b.dq : b.d, s)) != hipSuccess) return err;
+  //    (BF16: D is written by the (p D)^T gather-transpose below, which reads the same rows)
+  if (mx && (err = launch_dispatch(L, b.saved, b.dout_seg, b.dq, s)) != hipSuccess) return err;
   // 3. transposed BF16 weights for the backward GEMMs
   if (!mx) {
     hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 8192, 8192)), dim3(256), 0, s,
@@ -569,14 +577,16 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   const uint16_t* const* ds = reinterpret_cast<const uint16_t* const*>(b.dout_seg);
   const int64_t ld = L.rp_max;
   auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
-                int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst) {
+                int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst,
+                uint16_t* rows_out = nullptr) {
     TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
-                    ld, F, L.K, L.T, El};
+                    ld, F, L.K, L.T, El, rows_out};
     hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
   };
   const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
   tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt);                         // X^T
-  tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt);                        // (p D)^T
+  tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt,
+     mx ? nullptr : reinterpret_cast<uint16_t*>(b.d));                              // (p D)^T (+ D)
   tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht);          // h^T
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
