@@ -244,6 +244,12 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
       copy_rows_bf16_2(nr, a.s.H, lane, src_of, [&](int j) {
         return reinterpret_cast<uint16_t*>(pl.x) + int64_t(r0 + j * rstep) * a.s.H;
       });
+    } else if (MX && a.s.H <= 8 * kRowBatchChunks) {
+      const int nr = r0 < tl.nrows ? (tl.nrows - r0 + rstep - 1) / rstep : 0;
+      quant_rows_mx_2(
+          nr, a.s.H, lane, src_of,
+          [&](int j) { return pl.x + int64_t(r0 + j * rstep) * a.s.H; },
+          [&](int j) { return pl.xs + int64_t(r0 + j * rstep) * (a.s.H / 32); });
     } else {
       for (int j = 0; r0 + j * rstep < tl.nrows; ++j) {
         const int r = r0 + j * rstep;
