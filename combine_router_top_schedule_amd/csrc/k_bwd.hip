@@ -320,6 +320,30 @@ __global__ __launch_bounds__(256) void k_bwd_stage(StageArgs a) {
     const int t = int(it / (kTileM / 16)), chunk = int(it % (kTileM / 16));
     const bool rest = t < nr;
     const MTile tl = rest ? a.restore[t] : a.replay[t - nr];
+    if (!rest && mx && a.H <= 8 * kRowBatchChunks) {
+      // MXFP8 replay gather: the wave's rows i0, i0 + 4, ... quantised with the next row's
+      // loads in flight; lane j looks up the source of the wave's j-th row.
+      const int i0 = chunk * 16 + wave, iend = min(tl.nrows, chunk * 16 + 16);
+      const int nrw = i0 < iend ? (iend - i0 + 3) / 4 : 0;
+      const uint16_t* my_src = nullptr;
+      if (lane < nrw) {
+        const int32_t pair = a.perm[tl.row0 + i0 + 4 * lane];
+        if (pair >= 0 && pair < a.NK) {
+          const int64_t n = pair / a.K;
+          my_src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.H);
+        }
+      }
+      const uint64_t sp = reinterpret_cast<uint64_t>(my_src);
+      quant_rows_mx_2(
+          nrw, a.H, lane,
+          [&](int j) {
+            const uint32_t lo = __shfl(uint32_t(sp), j, 64), hi = __shfl(uint32_t(sp >> 32), j, 64);
+            return reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
+          },
+          [&](int j) { return a.xd + (tl.row0 + i0 + 4 * j) * int64_t(a.H); },
+          [&](int j) { return a.xd + a.rows_max * a.H + (tl.row0 + i0 + 4 * j) * int64_t(a.H / 32); });
+      continue;
+    }
     for (int i = chunk * 16 + wave; i < min(tl.nrows, chunk * 16 + 16); i += 4) {
       const int64_t row = tl.row0 + i;
       if (rest) {

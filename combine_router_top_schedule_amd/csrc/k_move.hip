@@ -39,6 +39,23 @@ __global__ __launch_bounds__(256) void k_dispatch(const int32_t* hdr, const int3
   const int64_t nwaves = (int64_t(gridDim.x) * blockDim.x) >> 6;
   const int64_t rows = min(int64_t(hdr[kHdrRows]), rows_max);
   const int64_t NK = int64_t(S) * T * K;
+  if (dtype != MOK_BF16 && H <= 8 * kRowBatchChunks) {
+    // MXFP8: the wave's rows wave, wave + nwaves, ... quantised with the next row's loads (and
+    // its source lookup) in flight.
+    const int nrw = wave < rows ? int((rows - 1 - wave) / nwaves + 1) : 0;
+    auto row_of = [&](int j) { return wave + int64_t(j) * nwaves; };
+    quant_rows_mx_2(
+        nrw, H, lane,
+        [&](int j) -> const uint16_t* {
+          const int32_t pair = perm[row_of(j)];
+          if (pair < 0 || pair >= NK) return nullptr;
+          const int64_t n = pair / K;
+          return x_seg[n / T] + (n % T) * int64_t(H);
+        },
+        [&](int j) { return xd + row_of(j) * H; },
+        [&](int j) { return xd + rows_max * H + row_of(j) * (H / 32); });
+    return;
+  }
   for (int64_t r = wave; r < rows; r += nwaves) {
     const int32_t pair = perm[r];
     const uint16_t* src = nullptr;
