@@ -300,24 +300,33 @@ __global__ __launch_bounds__(256) void k_place(PlaceArgs a) {
 }
 
 // Cut rows into m-tiles: for each minibatch j (rows [jM, (j+1)M)) and each local expert e,
-// the intersection with e's real rows, in chunks of kTileM. Ordered by j, then e, then row.
-__global__ void k_tiles(const int32_t* hdr, MTile* tiles, int32_t* ntiles, int El, int M,
-                        int64_t tiles_max) {
-  if (threadIdx.x != 0) return;
+// the intersection with e's real rows, in chunks of kTileM. Ordered by j, then e, then row. One
+// wave: lane e owns expert e (El <= 64); per minibatch an exclusive scan over the lanes places
+// each expert's tiles.
+__global__ __launch_bounds__(64) void k_tiles(const int32_t* hdr, MTile* tiles, int32_t* ntiles,
+                                              int El, int M, int64_t tiles_max) {
+  const int lane = threadIdx.x;
   const int rows = hdr[kHdrRows];
   const int J = M > 0 ? (rows + M - 1) / M : 0;
-  int64_t t = 0;
+  const int off = lane < El ? hdr[kHdrOffsets + lane] : 0;
+  const int cnt = lane < El ? hdr[kHdrCounts + lane] : 0;
+  int64_t base = 0;
   for (int j = 0; j < J; ++j) {
     const int lo = j * M, hi = min(rows, (j + 1) * M);
-    for (int e = 0; e < El; ++e) {
-      const int r0 = max(lo, hdr[kHdrOffsets + e]);
-      const int r1 = min(hi, hdr[kHdrOffsets + e] + hdr[kHdrCounts + e]);
-      for (int r = r0; r < r1 && t < tiles_max; r += kTileM) {
-        tiles[t++] = MTile{j, e, r, min(kTileM, r1 - r)};
-      }
+    const int r0 = max(lo, off), r1 = min(hi, off + cnt);
+    const int n = (lane < El && r1 > r0) ? (r1 - r0 + kTileM - 1) / kTileM : 0;
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
     }
+    const int64_t first = base + incl - n;
+    for (int q = 0; q < n && first + q < tiles_max; ++q)
+      tiles[first + q] = MTile{j, lane, r0 + q * kTileM, min(kTileM, r1 - r0 - q * kTileM)};
+    base += __shfl(incl, 63, 64);
   }
-  *ntiles = int32_t(t);
+  if (lane == 0) *ntiles = int32_t(min(base, tiles_max));
 }
 
 }  // namespace
