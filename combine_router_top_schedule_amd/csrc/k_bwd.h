@@ -15,31 +15,36 @@ __device__ __forceinline__ float e4m3_value(uint8_t c) {
   return (c & 0x80) ? -mag : mag;
 }
 
-// g, u and h of one 32-row x 128-column block of the a-GEMM epilogue, as loaded from the
-// planes: 16 lanes x 16 bytes cover a row, 4 rows per load. Held in registers so the next
-// block's loads are in flight while the current block is computed.
+// g, u and h of one 32-row x 128-column block of the a-GEMM epilogue, as loaded from where the
+// rows live (ring slot or activation plane): 16 lanes x 16 bytes cover a row, 4 rows per load.
+// Held in registers so the next block's loads are in flight while the current block is computed.
 struct AStage {
   u32x4 g[8], u[8];
   u32x4 h[8];          // BF16 values; MXFP8: 8 codes in .x/.y and the block scale code in .z
 };
 
+// lcode: the row-source codes of the block's 32 rows (LDS). Rows past the tile or columns past
+// I load zeros (their values are never stored).
 template <bool MX>
 __device__ __forceinline__ void a_stage_load(AStage& st, const FfnShape& s, int64_t row0,
                                              int nrows, int colw, int rbase,
-                                             const ActPlanes& act, int lane) {
+                                             const ActSource& src, const int32_t* lcode, int lane) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
     const bool ok = rbase + rr < nrows && colw + cc < s.I;
-    const int64_t pr = row0 + (ok ? rbase + rr : 0);
-    const int col = ok ? colw + cc : 0;
-    st.g[q] = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + col);
-    st.u[q] = *reinterpret_cast<const u32x4*>(act.gu + pr * 2 * s.I + s.I + col);
-    if (MX) {
-      const uint2 hv = *reinterpret_cast<const uint2*>(act.h + pr * s.I + col);
-      st.h[q] = u32x4{hv.x, hv.y, uint32_t(act.hs[pr * (s.I / 32) + col / 32]), 0u};
-    } else {
-      st.h[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(act.h) + pr * s.I + col);
+    st.g[q] = st.u[q] = st.h[q] = u32x4{0u, 0u, 0u, 0u};
+    if (ok) {
+      const ActRow ar = act_row(src, row0 + rbase + rr, lcode[rr], s.H, s.I, MX ? MOK_MXFP8 : MOK_BF16);
+      const int col = colw + cc;
+      st.g[q] = *reinterpret_cast<const u32x4*>(ar.gu + col);
+      st.u[q] = *reinterpret_cast<const u32x4*>(ar.gu + s.I + col);
+      if (MX) {
+        const uint2 hv = *reinterpret_cast<const uint2*>(ar.h + col);
+        st.h[q] = u32x4{hv.x, hv.y, uint32_t(ar.hs[col / 32]), 0u};
+      } else {
+        st.h[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(ar.h) + col);
+      }
     }
   }
 }
@@ -151,7 +156,7 @@ template <bool MX>
 __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t row0, int nrows,
                                        int e, int c0, const uint8_t* d, const uint8_t* d_s,
                                        const uint8_t* wdt, const uint8_t* wdt_s,
-                                       const ActPlanes& act, const int32_t* perm, const float* p,
+                                       const ActSource& act, const int32_t* perm, const float* p,
                                        uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s, float* dp_part) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -181,18 +186,23 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   uint16_t* lh = lu + 32 * 128;   // BF16 (exact for decoded E4M3 values too)
   const int colw = c0 + wn * 128;                                       // wave's first column
   float* lpg = reinterpret_cast<float*>(sm.b[1] + 4096) + wave * 128;    // gates of the wave's rows
-  // gates of the wave's 128 rows (lane l: row wm*128 + l, l < 128 over two halves)
+  int32_t* lcode = reinterpret_cast<int32_t*>(sm.b[1] + 6144) + wave * 128;  // their sources
+  // gates and row-source codes of the wave's 128 rows (lane l: row wm*128 + l, l < 128 over
+  // two halves)
   for (int l = lane; l < 128; l += 64) {
     const int r = wm * 128 + l;
     lpg[l] = r < nrows ? p[perm[row0 + r]] : 0.f;
+    lcode[l] = r < nrows ? act.code[row0 + r] : -1;
   }
+  __builtin_amdgcn_wave_barrier();
   AStage st;
-  a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128, act, lane);
+  a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128, act, lcode, lane);
 #define MOK_A_BLOCK(I_)                                                                          \
   {                                                                                              \
     __builtin_amdgcn_s_waitcnt(0);                                                               \
     a_stage_store<MX>(st, lg, lu, lh, lane);                                                     \
-    if (I_ < 3) a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act, lane);  \
+    if (I_ < 3) a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act,         \
+                                 lcode + (I_ + 1) * 32, lane);                                   \
     __builtin_amdgcn_wave_barrier();                                                             \
     a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, dgq, dgq_s, s_dp, lg, lu, lh,        \
                              lpg + I_ * 32, wm,                                                  \

@@ -86,6 +86,10 @@ struct TransposeArgs {
   // Non-null (BF16 rows from segments): every source row is also copied, unscaled, to
   // rows_out[its expert-ordered row][F] (the dOut gather D of the backward, read once for both).
   uint16_t* rows_out;
+  // from_act: rows are the h of the activations, read where each row lives (ActSource; the
+  // plane fields are unused)
+  int from_act;
+  ActSource act;
 };
 
 // One tile = 64 padded columns (source rows) x 128 features. Source rows are read with 16-byte
@@ -130,6 +134,14 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
           const int64_t n = pair / a.K;
           src = reinterpret_cast<const uint8_t*>(a.seg[n / a.T] + (n % a.T) * int64_t(a.F) + f0);
           if (a.p) gate = a.p[pair];
+        } else if (a.from_act) {
+          const ActRow ar = act_row(a.act, row, a.act.code[row], 0, a.F, mxp ? MOK_MXFP8 : MOK_BF16);
+          if (mxp) {
+            src = ar.h + f0;
+            sc4 = *reinterpret_cast<const uint32_t*>(ar.hs + f0 / 32);
+          } else {
+            src = ar.h + int64_t(f0) * 2;
+          }
         } else if (mxp) {
           src = a.plane + row * a.plane_stride + a.plane_col0 + f0;
           sc4 = *reinterpret_cast<const uint32_t*>(a.plane_s + row * (a.plane_stride / 32) +
@@ -290,9 +302,10 @@ __global__ __launch_bounds__(64) void k_bwd_plan(const int32_t* hdr, const int32
   if (lane < 2 * kXcds) counts[4 + lane] = 0;          // the two GEMM launches' queue counters
 }
 
-// Work item = 16 rows of one listed tile. Restored tiles: copy each row's g|u and h (with MX
-// scales) from its ring slot to the expert-ordered activation planes. Replayed tiles: gather the
-// row's X from its segment into the dispatch plane (MXFP8: quantised along H). One wave per row.
+// Work item = 16 rows of one listed tile. Every row gets its row-source code: restored tiles
+// point at their ring slot (their g|u and h are read there, not copied); replayed rows get -1
+// (the replay writes them to the activation planes) and their X is gathered from its segment
+// into the dispatch plane (MXFP8: quantised along H). One wave per row.
 struct StageArgs {
   const MTile* restore;
   const int32_t* restore_slot;
@@ -300,12 +313,8 @@ struct StageArgs {
   const int32_t* counts;
   const int32_t* perm;
   const uint16_t* const* x_seg;
-  const uint8_t* ring;
-  int64_t ring_share;   // bytes per XCD share
-  int64_t aofs, asb;    // offset of the activation slots inside a share, bytes per slot
-  int capa;             // activation slots per share
   uint8_t* xd;          // dispatch plane [rows_max] (codes then scales in MXFP8)
-  ActPlanes act;        // g|u and h planes [rows_max]
+  int32_t* code;        // [rows_max] row-source codes (ActSource), written here
   int64_t rows_max;
   int H, I, K, T, dtype;
   int64_t NK;
@@ -320,7 +329,12 @@ __global__ __launch_bounds__(256) void k_bwd_stage(StageArgs a) {
     const int t = int(it / (kTileM / 16)), chunk = int(it % (kTileM / 16));
     const bool rest = t < nr;
     const MTile tl = rest ? a.restore[t] : a.replay[t - nr];
-    if (!rest && mx && a.H <= 8 * kRowBatchChunks) {
+    if (threadIdx.x < 16 && chunk * 16 + int(threadIdx.x) < tl.nrows) {
+      const int i = chunk * 16 + int(threadIdx.x);
+      a.code[tl.row0 + i] = rest ? ((a.restore_slot[t] << 8) | i) : -1;
+    }
+    if (rest) continue;
+    if (mx && a.H <= 8 * kRowBatchChunks) {
       // MXFP8 replay gather: the wave's rows i0, i0 + 4, ... quantised with the next row's
       // loads in flight; lane j looks up the source of the wave's j-th row.
       const int i0 = chunk * 16 + wave, iend = min(tl.nrows, chunk * 16 + 16);
@@ -346,31 +360,14 @@ __global__ __launch_bounds__(256) void k_bwd_stage(StageArgs a) {
     }
     for (int i = chunk * 16 + wave; i < min(tl.nrows, chunk * 16 + 16); i += 4) {
       const int64_t row = tl.row0 + i;
-      if (rest) {
-        const int sl = a.restore_slot[t];
-        uint8_t* slot = const_cast<uint8_t*>(a.ring) + int64_t(sl / a.capa) * a.ring_share +
-                        a.aofs + int64_t(sl % a.capa) * a.asb;
-        const ActPlanes sp = act_planes(slot, kTileM, a.H, a.I, a.dtype, false);
-        copy_row_bf16(sp.gu + int64_t(i) * 2 * a.I, a.act.gu + row * 2 * a.I, 2 * a.I, lane);
-        if (mx) {
-          // I codes (as I/2 16-bit units) and I/32 scale bytes
-          copy_row_bf16(reinterpret_cast<const uint16_t*>(sp.h + int64_t(i) * a.I),
-                        reinterpret_cast<uint16_t*>(a.act.h + row * a.I), a.I / 2, lane);
-          for (int b = lane; b < a.I / 32; b += 64) a.act.hs[row * (a.I / 32) + b] = sp.hs[int64_t(i) * (a.I / 32) + b];
-        } else {
-          copy_row_bf16(reinterpret_cast<const uint16_t*>(sp.h) + int64_t(i) * a.I,
-                        reinterpret_cast<uint16_t*>(a.act.h) + row * a.I, a.I, lane);
-        }
-      } else {
-        const int32_t pair = a.perm[row];
-        const uint16_t* src = nullptr;
-        if (pair >= 0 && pair < a.NK) {
-          const int64_t n = pair / a.K;
-          src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.H);
-        }
-        if (mx) quant_row_mx(src, a.xd + row * a.H, a.xd + a.rows_max * a.H + row * (a.H / 32), a.H, lane);
-        else copy_row_bf16(src, reinterpret_cast<uint16_t*>(a.xd) + row * a.H, a.H, lane);
+      const int32_t pair = a.perm[row];
+      const uint16_t* src = nullptr;
+      if (pair >= 0 && pair < a.NK) {
+        const int64_t n = pair / a.K;
+        src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.H);
       }
+      if (mx) quant_row_mx(src, a.xd + row * a.H, a.xd + a.rows_max * a.H + row * (a.H / 32), a.H, lane);
+      else copy_row_bf16(src, reinterpret_cast<uint16_t*>(a.xd) + row * a.H, a.H, lane);
     }
   }
 }
@@ -398,7 +395,7 @@ struct BwdArgs {
   const uint8_t* d_s;      // MXFP8 scales [rows][H/32]
   const uint8_t* wdt;      // Wd^T [El][I][H] (BF16 or codes)
   const uint8_t* wdt_s;
-  ActPlanes act;           // g|u and h of the forward (replayed)
+  ActSource act;           // g|u and h of the forward (ring slot or replayed plane, per row)
   uint16_t* dgu;           // out: dg|du BF16 [rows][2I]
   float* dp_part;          // out: [rows][I/256]
   // dx GEMM
@@ -566,13 +563,8 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
     st.counts = counts;
     st.perm = perm;
     st.x_seg = reinterpret_cast<const uint16_t* const*>(b.x_seg);
-    st.ring = b.ring;
-    st.ring_share = L.ring_share;
-    st.aofs = int64_t(L.ring_capx) * L.xsb;
-    st.asb = L.asb;
-    st.capa = L.ring_capa > 0 ? L.ring_capa : 1;
     st.xd = b.xd;
-    st.act = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
+    st.code = b.actsrc;
     st.rows_max = L.rows_max;
     st.H = H; st.I = I; st.K = L.K; st.T = L.T; st.dtype = L.dtype;
     st.NK = L.NK;
@@ -600,18 +592,27 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
   const uint16_t* const* ds = reinterpret_cast<const uint16_t* const*>(b.dout_seg);
   const int64_t ld = L.rp_max;
+  // where the backward reads each row's g|u and h (ring slot or replayed plane)
+  const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
+  ActSource asrc{};
+  asrc.act = ap;
+  asrc.ring = b.ring;
+  asrc.ring_share = L.ring_share;
+  asrc.aofs = int64_t(L.ring_capx) * L.xsb;
+  asrc.asb = L.asb;
+  asrc.capa = L.ring_capa > 0 ? L.ring_capa : 1;
+  asrc.code = b.actsrc;
   auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
                 int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst,
-                uint16_t* rows_out = nullptr) {
+                uint16_t* rows_out = nullptr, bool from_act = false) {
     TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
-                    ld, F, L.K, L.T, El, rows_out};
+                    ld, F, L.K, L.T, El, rows_out, int(from_act), asrc};
     hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
   };
-  const ActPlanes ap = act_planes(b.act, L.rows_max, H, I, L.dtype, false);
   tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt);                         // X^T
   tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt,
      mx ? nullptr : reinterpret_cast<uint16_t*>(b.d));                              // (p D)^T (+ D)
-  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht);          // h^T
+  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht, nullptr, true);  // h^T
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   BwdArgs a{};
@@ -625,7 +626,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.d_s = mx ? b.dq + L.rows_max * H : nullptr;
   a.wdt = mx ? b.w.wdt_q : reinterpret_cast<const uint8_t*>(b.wdt);
   a.wdt_s = mx ? b.w.wdt_s : nullptr;
-  a.act = ap;
+  a.act = asrc;
   a.dgu = b.dgu;
   a.dp_part = b.dp_part;
   a.dgu_a = mx ? b.dguq : reinterpret_cast<const uint8_t*>(b.dgu);

@@ -280,6 +280,7 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
   b.hdr2 = reinterpret_cast<int32_t*>(ws + L.b_hdr2);
   b.xd = ws + L.b_xd;
   b.act = ws + L.b_act;
+  b.actsrc = reinterpret_cast<int32_t*>(ws + L.b_actsrc);
   b.d = ws + L.b_d;
   b.dq = ws + L.b_dq;
   b.dgu = reinterpret_cast<uint16_t*>(ws + L.b_dgu);

@@ -83,7 +83,7 @@ struct Layout {
   int64_t rp_max;
   int64_t b_hdr2, b_xd, b_act, b_d, b_dq, b_dgu, b_dguq, b_dp, b_wdt, b_wgt, b_wut;
   int64_t b_xt, b_dt, b_dgt, b_dut, b_ht, b_qxt, b_qdt, b_qdgt, b_qdut, b_qht;
-  int64_t b_restore, b_replay, b_rsl, b_counts, b_bytes;
+  int64_t b_restore, b_replay, b_rsl, b_counts, b_actsrc, b_bytes;
 };
 
 // Bytes of an activation row of width `w` elements in the activation format: BF16, or
@@ -175,6 +175,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_replay = take(16 * L.tiles_max);
   L.b_rsl = take(4 * L.tiles_max);
   L.b_counts = take(4 * (4 + 2 * kXcds));   // plan counts, then two work-queue counter sets
+  L.b_actsrc = take(4 * rm);                 // where each row's g|u and h live (ActSource)
   L.b_bytes = off;
   return L;
 }
@@ -202,6 +203,37 @@ __host__ __device__ inline ActPlanes act_planes(uint8_t* base, int64_t rows, int
   if (dtype == MOK_BF16) { q += rows * I * 2; }
   else { q += rows * I; p.hs = q; }
   return p;
+}
+
+// Where the backward reads each expert-ordered row's g|u and h: rows of a tile the forward left
+// resident in a ring activation slot are read there (code = slot << 8 | row inside the tile,
+// slot = XCD * capa + slot of that XCD); replayed rows (code < 0) from the backward's own
+// activation planes.
+struct ActSource {
+  ActPlanes act;             // backward activation planes [rows_max]
+  const uint8_t* ring;       // the forward's ring (may be null when every code is < 0)
+  int64_t ring_share;        // bytes per XCD share
+  int64_t aofs, asb;         // activation slots: offset inside a share, bytes per slot
+  int capa;                  // activation slots per share
+  const int32_t* code;       // [rows_max]
+};
+
+struct ActRow {
+  const uint16_t* gu;        // BF16 [2I]
+  const uint8_t* h;          // BF16 [I] or codes [I]
+  const uint8_t* hs;         // MXFP8 scales [I/32] (null in BF16)
+};
+
+__device__ inline ActRow act_row(const ActSource& s, int64_t row, int32_t code, int H, int I,
+                                 int dtype) {
+  const int64_t hb = dtype == MOK_BF16 ? 2 * int64_t(I) : int64_t(I);
+  if (code < 0)
+    return ActRow{s.act.gu + row * 2 * I, s.act.h + row * hb, s.act.hs ? s.act.hs + row * (I / 32) : nullptr};
+  const int slot = code >> 8, lr = code & 255;
+  uint8_t* base = const_cast<uint8_t*>(s.ring) + int64_t(slot / s.capa) * s.ring_share + s.aofs +
+                  int64_t(slot % s.capa) * s.asb;
+  const ActPlanes sp = act_planes(base, kTileM, H, I, dtype, false);
+  return ActRow{sp.gu + int64_t(lr) * 2 * I, sp.h + lr * hb, sp.hs ? sp.hs + int64_t(lr) * (I / 32) : nullptr};
 }
 
 // One m-tile of a grouped GEMM: rows [row0, row0 + nrows) of expert e, inside minibatch j.
@@ -260,6 +292,7 @@ struct BwdBuffers {
   uint16_t *xt, *dt, *dgt, *dut, *ht;
   uint8_t *q_xt, *q_dt, *q_dgt, *q_dut, *q_ht;
   uint8_t* ring;      // the forward's ring (null: replay every row)
+  int32_t* actsrc;    // [rows_max] row-source codes of the activations (ActSource)
 };
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
 
