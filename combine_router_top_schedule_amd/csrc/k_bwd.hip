@@ -156,9 +156,9 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
       s_row[tid] = li < s_cnt[e] ? s_off[e] + li : -1;
     }
     __syncthreads();
-    // load: 64 rows x 16 chunks of 8 features
+    // load: kTrCols rows x 16 chunks of 8 features
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kTrCols / 16; ++i) {
       const int idx = tid + 256 * i, r = idx >> 4, ch = idx & 15;
       const uint8_t* src = s_src[r];
       uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -192,10 +192,10 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
       for (int k = 0; k < 4; ++k) dst[k] = w[k];
     }
     __syncthreads();
-    // store: 128 features x 8 chunks of 8 columns
+    // store: 128 features x kTrCols/8 chunks of 8 columns (runs of 2 * kTrCols bytes per row)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, f = idx >> 3, cc = idx & 7;
+    for (int i = 0; i < kTrCols / 16; ++i) {
+      const int idx = tid + 256 * i, f = idx / (kTrCols / 8), cc = idx % (kTrCols / 8);
       u32x4 out;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
 
 // Backward set-up, one wave, no host synchronisation:
 //  - split the forward's tiles into those whose ring slot still holds them (their g|u and h are
-//    copied back) and those to replay (X gathered again, gate/up recomputed), both in forward
+//    read in place) and those to replay (X gathered again, gate/up recomputed), both in forward
 //    tile order (ballot compaction, so the lists are deterministic); without ring state (staged
 //    forward, or no ring passed) every row is replayed, in per-expert tiles;
 //  - the backward GEMMs' tile table: per-expert tiles of at most kTileM rows (no minibatch cuts);
