@@ -226,7 +226,7 @@ __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t 
                                         int e, int c0, const uint8_t* dgu, const uint8_t* dgu_s,
                                         const uint8_t* wgt, const uint8_t* wgt_s,
                                         const uint8_t* wut, const uint8_t* wut_s,
-                                        const int32_t* perm, uint16_t* slots) {
+                                        const PushTarget& pt) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
@@ -244,10 +244,9 @@ __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t 
     B.s0 = make_rsrc(wgt_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
     B.s1 = make_rsrc(wut_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
   }
-  const int32_t my_pair = tid < nrows ? perm[row0 + tid] : 0;
   f32x16 acc[4][4];
   gemm_tile<MX>(sm, A, B, arow / kStageRowBytes, acc, wm, wn, lane);
-  push_epilogue(sm, acc, nrows, c0, s.H, my_pair, slots);
+  push_epilogue<kPushRec>(sm, acc, nrows, c0, s.H, 0, pt, row0);
 }
 
 // Weight-gradient tile: out[m0 + m][n0 + n] = sum over the expert's padded columns c of

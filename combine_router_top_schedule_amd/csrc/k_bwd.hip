@@ -405,7 +405,7 @@ struct BwdArgs {
   const uint8_t* wgt_s;
   const uint8_t* wut;      // Wu^T [El][H][I]
   const uint8_t* wut_s;
-  uint16_t* slots;
+  PushTarget push;         // dx rows: pair slots, or dX of a token's only local pair
   // weight gradients: up to three jobs dW[e] = Ta[:, cols of e] . Tb[:, cols of e]^T
   WJob jobs[3];
   int njobs;
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gemms(BwdArgs a) {
                      const_cast<uint8_t*>(a.dgu_s), a.dp_part);
         else
           dx_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.dgu_a, a.dgu_s, a.wgt,
-                      a.wgt_s, a.wut, a.wut_s, a.perm, a.slots);
+                      a.wgt_s, a.wut, a.wut_s, a.push);
       } else {
         int j = 0, rem = t - n_p;
         for (; j < a.njobs; ++j) {
@@ -635,7 +635,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.wgt_s = mx ? b.w.wgt_s : nullptr;
   a.wut = mx ? b.w.wut_q : reinterpret_cast<const uint8_t*>(b.wut);
   a.wut_s = mx ? b.w.wut_s : nullptr;
-  a.slots = b.slots;
+  a.push = PushTarget{b.slots, b.push};
   a.ld = ld;
   a.El = El;
   a.queue = counts + 4;
@@ -660,7 +660,10 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   else hipLaunchKernelGGL((k_bwd_gemms<false, 0>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   trace_after(MOK_TRACE_BWD_GEMM1, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 6. dg^T, du^T; phase 1: dx GEMM pushed to the slots, dWg and dWu
+  // 6. dg^T, du^T; phase 1: dx GEMM pushed to the slots (a token's only local pair straight to
+  //    its dX row), dWg and dWu
+  if ((err = launch_push_rows(L, b.saved, b.slots, b.dx_seg, nullptr, b.push, s)) != hipSuccess)
+    return err;
   const uint8_t* dgu8 = reinterpret_cast<const uint8_t*>(b.dgu);
   tr(nullptr, nullptr, dgu8, nullptr, 2 * I, 0, I, b.dgt, b.q_dgt);                   // dg^T
   tr(nullptr, nullptr, dgu8, nullptr, 2 * I, I, I, b.dut, b.q_dut);                   // du^T
@@ -676,7 +679,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // 7. the unweighted fixed-order dX merge, the router-weight gradient per pair, and dlogits
   //    when every expert is local
-  if ((err = launch_combine(L, b.saved, b.topk_idx, nullptr, b.slots, b.dx_seg, s)) != hipSuccess)
+  if ((err = launch_combine(L, b.saved, b.topk_idx, nullptr, b.slots, b.dx_seg, true, s)) != hipSuccess)
     return err;
   hipLaunchKernelGGL(k_dp_finalize, dim3(grid_cap(L.rows_max / 256 + 1, 4096)), dim3(256), 0, s,
                      hdr, perm, b.dp_part, int(cdiv(I, kTileN)), b.dp, L.rows_max);

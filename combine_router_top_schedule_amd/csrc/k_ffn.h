@@ -131,17 +131,33 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
   __syncthreads();
 }
 
+// Where the push epilogue sends a tile's rows. kPushSlots: every row raw to slots[pair], the
+// pair ids coming from the caller. kPushRec: per the rows' push records (PushRec), which send
+// a token's only local pair straight to its output row.
+enum PushMode : int { kPushSlots = 0, kPushRec = 1 };
+
+struct PushTarget {
+  uint16_t* slots;
+  const PushRec* rec;   // [rows], kPushRec
+};
+
 // Push epilogue shared by the down GEMM and the dx GEMM: stage the BF16 tile in LDS, then
-// write whole rows (512 B, 16 B per lane) to the receive slot of each row's pair.
-// `my_pair` is the pair id of tile row threadIdx.x (loaded by the caller before the K loop, so
-// its latency is hidden and no wait on outstanding stores is needed here).
+// write whole rows (512 B, 16 B per lane) to each row's destination (see PushTarget).
+// kPushSlots: `my_pair` is the pair id of tile row threadIdx.x, loaded by the caller before the
+// K loop so its latency is hidden. kPushRec: the row's record is loaded here, unconditionally
+// (clamped row index), and first used after the LDS staging, so its latency is hidden there;
+// nothing of it is live across the K loop.
+template <int MODE>
 __device__ __forceinline__ void push_epilogue(GemmLds& sm, const f32x16 (&acc)[4][4], int nrows,
-                                              int c0, int H, int32_t my_pair, uint16_t* slots) {
+                                              int c0, int H, int32_t my_pair,
+                                              const PushTarget& pt, int64_t row0) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   uint16_t* t = reinterpret_cast<uint16_t*>(sm.a[0]);
-  int32_t* s_perm = reinterpret_cast<int32_t*>(sm.as[0]);
-  s_perm[tid] = my_pair;
+  uint16_t** s_dst = reinterpret_cast<uint16_t**>(sm.as[0]);
+  float* s_w = reinterpret_cast<float*>(sm.bs[0]);
+  PushRec rec{};
+  if (MODE == kPushRec) rec = pt.rec[row0 + min(tid, nrows - 1)];
   {
     uint16_t* tl = t + opaque((wm * 128 + 4 * (lane >> 5)) * 256 + wn * 128 + (lane & 31));
 #pragma unroll
@@ -152,26 +168,39 @@ __device__ __forceinline__ void push_epilogue(GemmLds& sm, const f32x16 (&acc)[4
         for (int v = 0; v < 16; ++v)
           tl[(i * 32 + 8 * (v >> 2) + (v & 3)) * 256 + j * 32] = f2bf(acc[i][j][v]);
   }
+  s_dst[tid] = MODE == kPushRec ? rec.dst : pt.slots + int64_t(my_pair) * H;
+  s_w[tid] = MODE == kPushRec ? rec.w : -1.f;
   __syncthreads();
   {
     const int half = lane >> 5, c = lane & 31;
     const bool colok = c0 + c * 8 < H;
     for (int r = wave * 2 + half; r < nrows; r += 8) {
-      const int32_t pair = s_perm[r];
-      const u32x4 val = *reinterpret_cast<const u32x4*>(t + r * 256 + c * 8);
-      if (colok) *reinterpret_cast<u32x4*>(slots + int64_t(pair) * H + c0 + c * 8) = val;
+      uint16_t* d = s_dst[r];
+      const float rw = s_w[r];
+      u32x4 val = *reinterpret_cast<const u32x4*>(t + r * 256 + c * 8);
+      if (rw >= 0.f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          val[i] = pack_bf2(fmaf(rw, __uint_as_float(val[i] << 16), 0.f),
+                            fmaf(rw, __uint_as_float(val[i] & 0xFFFF0000u), 0.f));
+      }
+      // The pointer came through LDS: name its address space, or the store becomes a flat
+      // store, which every later LDS read would wait for.
+      typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+      if (colok) *(global_u32x4*)(d + c0 + c * 8) = val;
     }
   }
   __syncthreads();
 }
 
 // y = h Wd^T over the 256 output columns [c0, c0+256) of expert e; the epilogue pushes each
-// row to its token's receive slot: slots[perm[row]][c] = bf16(y).
-template <bool MX>
+// row to its token's receive slot, slots[perm[row]][c] = bf16(y), or (kPushRec: a token's only
+// local pair) writes the token's output row.
+template <bool MX, int MODE>
 __device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
                                           const ActPlanes& pl, int64_t prow0, int64_t row0,
                                           int nrows, int e, int c0, const int32_t* perm,
-                                          uint16_t* slots) {
+                                          const PushTarget& pt) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
@@ -189,11 +218,11 @@ __device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const 
     A.s0 = A.s1 = make_rsrc(pl.hs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
     B.s0 = B.s1 = make_rsrc(w.wd_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
   }
-  const int32_t my_pair = tid < nrows ? perm[row0 + tid] : 0;
+  const int32_t my_pair = MODE == kPushSlots && tid < nrows ? perm[row0 + tid] : 0;
   f32x16 acc[4][4];
   gemm_tile<MX>(sm, A, B, hrow / kStageRowBytes, acc, wm, wn, lane);
 
-  push_epilogue(sm, acc, nrows, c0, s.H, my_pair, slots);
+  push_epilogue<MODE>(sm, acc, nrows, c0, s.H, my_pair, pt, row0);
 }
 
 }  // namespace mok

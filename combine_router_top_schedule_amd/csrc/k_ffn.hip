@@ -42,8 +42,8 @@ __global__ __launch_bounds__(256, 1) void k_down_staged(FfnStagedArgs a) {
     int mt, nt;
     tile_coords(t, mtiles, ntn, mt, nt);
     const MTile tl = a.tiles[mt];
-    down_tile<MX>(sm, a.s, a.w, a.pl, tl.row0, tl.row0, tl.nrows, tl.e, nt * kTileN, a.perm,
-                  a.slots);
+    down_tile<MX, kPushSlots>(sm, a.s, a.w, a.pl, tl.row0, tl.row0, tl.nrows, tl.e,
+                              nt * kTileN, a.perm, PushTarget{a.slots, nullptr});
   }
 }
 

@@ -17,8 +17,11 @@
 // round-robin: gather slots hold a row tile's X rows until its gate/up tiles are done;
 // activation slots hold its g|u and h until its down tiles are done, and after the kernel the
 // last capa of them stay for the backward's reverse walk. Splitting the two lets one ring keep
-// g|u and h of many more row tiles than whole-tile slots would. Down-GEMM results are pushed to
-// the pair slots; the weighted merge runs as the next kernel on the stream.
+// g|u and h of many more row tiles than whole-tile slots would. A down-GEMM row whose pair is
+// its token's only local pair (nearly all rows when a GPU holds a few experts of many) becomes
+// the token's output row at once, bf16(p * bf16(y)), the merge over one term; the other rows
+// are pushed to the pair slots and the weighted merge of the tokens with several local pairs
+// runs as the next kernel on the stream.
 //
 // Work order and deadlock freedom: all workgroups are co-resident (cooperative launch, one per
 // CU). The first `lag` row tiles of an XCD (lag = 2 with at least 3 activation slots per XCD,
@@ -52,7 +55,8 @@ struct FusedArgs {
   int capx, capa;            // gather slots / activation slots per XCD
   FfnShape s;
   FfnWeights w;
-  uint16_t* slots;
+  PushTarget push;           // down-GEMM rows: pair slots, or the output row of a token's only
+                             // local pair
   int32_t* cnt;              // [kCntWords + 3 * tiles_max]
   int32_t* err;
   int32_t* rhdr;             // ring state for the backward (in saved): header,
@@ -335,8 +339,8 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
     } else {
       if (!wait_geq(gu_done + mt, ngu, a.err, a.spin_limit)) return;
       l1_invalidate();
-      down_tile<MX>(sm, a.s, a.w, pl, 0, tl.row0, tl.nrows, tl.e, (k - ngu) * kTileN, a.perm,
-                    a.slots);
+      down_tile<MX, kPushRec>(sm, a.s, a.w, pl, 0, tl.row0, tl.nrows, tl.e, (k - ngu) * kTileN,
+                              a.perm, a.push);
       signal(dn_done + mt);
     }
   }
@@ -354,7 +358,8 @@ int fused_slots_per_xcd(const Layout& L) { return L.ring_capa; }
 
 hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
                             const void* const* x_seg, const mok_weights& w, uint8_t* ring,
-                            uint16_t* slots, uint8_t* ws, hipStream_t s) {
+                            uint16_t* slots, void* const* out_seg, const float* p, uint8_t* ws,
+                            hipStream_t s) {
   static bool attr_done = false;
   hipError_t err;
   if (!attr_done) {
@@ -400,7 +405,9 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
   else a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),
                         static_cast<const uint8_t*>(w.wd), nullptr, nullptr, nullptr};
-  a.slots = slots;
+  PushRec* rec = reinterpret_cast<PushRec*>(ws + L.ws_push);
+  if ((err = launch_push_rows(L, saved, slots, out_seg, p, rec, s)) != hipSuccess) return err;
+  a.push = PushTarget{slots, rec};
   a.cnt = cnt;
   a.err = reinterpret_cast<int32_t*>(ws) + kWsError;
   a.tiles_max = L.tiles_max;

@@ -72,11 +72,14 @@ __global__ __launch_bounds__(256) void k_dispatch(const int32_t* hdr, const int3
 }
 
 // Final weighted merge ("把 MoE 通信延迟从 103μs 压到 18μs", section 04): for every touched
-// token, out[n] = bf16( sum over k ascending, idx[n,k] local, of p[n,k] * y[n*K+k] ).
+// token, out[n] = bf16( sum over k ascending, idx[n,k] local, of p[n,k] * y[n*K+k] ). With
+// skip_sole, tokens with one local pair are left out (the fused paths write those rows from
+// the GEMM epilogue with the same arithmetic).
 __global__ __launch_bounds__(256) void k_combine(const int32_t* hdr, const int32_t* touched,
                                                  const int32_t* idx, const float* p,
                                                  const uint16_t* slots, uint16_t* const* out_seg,
-                                                 int H, int K, int S, int T, int e0, int El) {
+                                                 int H, int K, int S, int T, int e0, int El,
+                                                 int skip_sole) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = (int64_t(gridDim.x) * blockDim.x) >> 6;
@@ -85,7 +88,33 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* hdr, const int32
   for (int64_t u = wave; u < U; u += nwaves) {
     const int64_t n = touched[u];
     if (n < 0 || n >= N) continue;
-    merge_row(n, idx, p, slots, out_seg[n / T] + (n % T) * int64_t(H), H, K, e0, El, lane);
+    merge_row(n, idx, p, slots, out_seg[n / T] + (n % T) * int64_t(H), H, K, e0, El, skip_sole,
+              lane);
+  }
+}
+
+// Push record of every expert-ordered row (see PushRec); pad rows (code -1) get a raw record
+// no tile uses.
+__global__ __launch_bounds__(256) void k_push_rows(const int32_t* hdr, const int32_t* pcode,
+                                                   uint16_t* slots, uint16_t* const* seg,
+                                                   const float* p, PushRec* rec,
+                                                   int64_t rows_max, int H, int K, int T) {
+  const int64_t rows = min(int64_t(hdr[kHdrRows]), rows_max);
+  for (int64_t r = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; r < rows;
+       r += int64_t(gridDim.x) * blockDim.x) {
+    const int32_t code = pcode[r];
+    PushRec o{slots, -1.f, 0};
+    if (code >= 0) {
+      const int32_t pair = code & ~kSoleFlag;
+      if (code & kSoleFlag) {
+        const int n = pair / K;
+        o.dst = seg[n / T] + int64_t(n % T) * H;
+        o.w = p ? p[pair] : 1.f;
+      } else {
+        o.dst = slots + int64_t(pair) * H;
+      }
+    }
+    rec[r] = o;
   }
 }
 
@@ -174,12 +203,23 @@ hipError_t launch_dispatch(const Layout& L, const uint8_t* saved, const void* co
 }
 
 hipError_t launch_combine(const Layout& L, const uint8_t* saved, const int32_t* idx, const float* p,
-                          const uint16_t* slots, void* const* out_seg, hipStream_t s) {
+                          const uint16_t* slots, void* const* out_seg, bool skip_sole,
+                          hipStream_t s) {
   const int cap = 8 * (device_cus() > 0 ? device_cus() : 256);
   hipLaunchKernelGGL(k_combine, dim3(grid_for(L.N, 4, cap)), dim3(256), 0, s,
                      reinterpret_cast<const int32_t*>(saved),
                      reinterpret_cast<const int32_t*>(saved + L.sv_touched), idx, p, slots,
-                     reinterpret_cast<uint16_t* const*>(out_seg), L.H, L.K, L.S, L.T, L.e0, L.El);
+                     reinterpret_cast<uint16_t* const*>(out_seg), L.H, L.K, L.S, L.T, L.e0, L.El,
+                     int(skip_sole));
+  return hipGetLastError();
+}
+
+hipError_t launch_push_rows(const Layout& L, const uint8_t* saved, uint16_t* slots,
+                            void* const* seg, const float* p, PushRec* rec, hipStream_t s) {
+  hipLaunchKernelGGL(k_push_rows, dim3(grid_for(L.rows_max, 256, 1024)), dim3(256), 0, s,
+                     reinterpret_cast<const int32_t*>(saved),
+                     reinterpret_cast<const int32_t*>(saved + L.sv_pcode), slots,
+                     reinterpret_cast<uint16_t* const*>(seg), p, rec, L.rows_max, L.H, L.K, L.T);
   return hipGetLastError();
 }
 

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
         int k = 0;
         for (int q = 0; q < a.K; ++q)
           if (a.idx[n * a.K + q] == a.e0 + e) k = q;
-        a.rank[n * a.K + k] = r;
+        a.rank[n * a.K + k] = r | (__popcll(mymask) == 1 ? kSoleFlag : 0);
       } else if (r < a.N) {
         a.touched[r] = int32_t(n);
       }
@@ -250,6 +250,8 @@ struct PlaceArgs {
   int32_t* hdr;
   int32_t* perm;
   int32_t* tokpos;
+  int32_t* pcode;        // [rows_max]: perm | kSoleFlag when the pair is its token's only local
+                         // pair
   int64_t NK, rows_max;
   int K, e0, El, row_align;
 };
@@ -279,7 +281,10 @@ __global__ __launch_bounds__(256) void k_place(PlaceArgs a) {
     for (int q = threadIdx.x; q < a.El * a.row_align; q += blockDim.x) {
       int e = q / a.row_align, i = q % a.row_align;
       int r = s_off[e] + s_cnt[e] + i;
-      if (r < s_off[e + 1]) a.perm[r] = -1;
+      if (r < s_off[e + 1]) {
+        a.perm[r] = -1;
+        a.pcode[r] = -1;
+      }
     }
   }
   for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < a.NK;
@@ -288,10 +293,14 @@ __global__ __launch_bounds__(256) void k_place(PlaceArgs a) {
     if (le >= 0 && le < a.El) {
       // A rank outside the expert's range only follows a failed look-back (error word set);
       // never write outside the table.
-      const int rank = a.tokpos[q];
+      const int word = a.tokpos[q];
+      const int rank = word & ~kSoleFlag;
       const int row = s_off[le] + rank;
-      const bool ok = rank >= 0 && rank < s_cnt[le] && row < a.rows_max;
-      if (ok) a.perm[row] = int32_t(q);
+      const bool ok = word >= 0 && rank < s_cnt[le] && row < a.rows_max;
+      if (ok) {
+        a.perm[row] = int32_t(q);
+        a.pcode[row] = int32_t(q) | (word & kSoleFlag);
+      }
       a.tokpos[q] = ok ? row : -1;
     } else {
       a.tokpos[q] = -1;
@@ -361,8 +370,9 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   PlaceArgs pa{idx, hdr, reinterpret_cast<int32_t*>(saved + L.sv_perm),
-               reinterpret_cast<int32_t*>(saved + L.sv_tokpos), L.NK, L.rows_max, L.K, L.e0,
-               L.El, L.row_align};
+               reinterpret_cast<int32_t*>(saved + L.sv_tokpos),
+               reinterpret_cast<int32_t*>(saved + L.sv_pcode), L.NK,
+               L.rows_max, L.K, L.e0, L.El, L.row_align};
   int pblocks = int(cdiv(L.NK, 256));
   if (pblocks > 4096) pblocks = 4096;
   hipLaunchKernelGGL(k_place, dim3(pblocks), dim3(256), 0, s, pa);

@@ -187,7 +187,7 @@ mok_status mok_combine(const mok_desc* desc, const void* saved_dev, const int32_
   const Layout L = layout_of(*desc);
   return hip_status(launch_combine(L, static_cast<const uint8_t*>(saved_dev), topk_idx_dev,
                                    topk_p_dev, static_cast<const uint16_t*>(slots_dev), out_seg_dev,
-                                   as_stream(stream)));
+                                   false, as_stream(stream)));
 }
 
 mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void* src_dev,
@@ -238,10 +238,10 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
   hipError_t e = launch_router(L, logits_dev, topk_idx_dev, topk_p_dev, saved, ws, s);
   if (e == hipSuccess)
     e = launch_layer_fwd(L, *desc, saved, x_seg_dev, *w, static_cast<uint8_t*>(ring_dev),
-                         static_cast<uint16_t*>(slots_dev), ws, s);
+                         static_cast<uint16_t*>(slots_dev), out_seg_dev, topk_p_dev, ws, s);
   if (e == hipSuccess)
     e = launch_combine(L, saved, topk_idx_dev, topk_p_dev, static_cast<const uint16_t*>(slots_dev),
-                       out_seg_dev, s);
+                       out_seg_dev, true, s);
   return hip_status(e);
 }
 
@@ -281,6 +281,7 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
   b.xd = ws + L.b_xd;
   b.act = ws + L.b_act;
   b.actsrc = reinterpret_cast<int32_t*>(ws + L.b_actsrc);
+  b.push = reinterpret_cast<PushRec*>(ws + L.ws_push);
   b.d = ws + L.b_d;
   b.dq = ws + L.b_dq;
   b.dgu = reinterpret_cast<uint16_t*>(ws + L.b_dgu);

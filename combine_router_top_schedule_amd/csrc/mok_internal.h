@@ -23,6 +23,21 @@ constexpr int kRingXSlots = 3;      // gather slots per XCD share of the fused-f
 __host__ __device__ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Marks a token's only local pair: set in the rank words the router passes to k_place and in
+// the push codes (pair id | flag) it writes per row. Ranks and pair ids stay below it
+// (N*K < 2^30).
+constexpr int32_t kSoleFlag = 1 << 30;
+
+// Where the push epilogue of the down GEMM or the dx GEMM sends one expert-ordered row (one
+// 16-byte load per row): w < 0: the raw BF16 row to dst (the pair's slot); else dst is the
+// token's own output row and receives bf16(w * float(bf16 row)), the merge over one term, for
+// a token whose only local pair this is.
+struct alignas(16) PushRec {
+  uint16_t* dst;
+  float w;
+  int32_t pad;
+};
+
 // ---- saved (schedule table) header, int32 words ----------------------------------------
 enum SavedHeader : int {
   kHdrP = 0,        // local pairs
@@ -65,14 +80,14 @@ struct Layout {
   int64_t N, NK, rows_max;
   int row_align;
   // saved
-  int64_t sv_perm, sv_tokpos, sv_touched, sv_bytes;
+  int64_t sv_perm, sv_tokpos, sv_touched, sv_pcode, sv_bytes;
   int64_t sv_rhdr, sv_rtiles, sv_rslot, sv_rowner;
   // fused-forward ring, one share per XCD: gather slots (X of one row tile) and activation
   // slots (g|u and h of one row tile)
   int64_t ring_share, xsb, asb;
   int ring_capx, ring_capa;
   // ws
-  int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_bytes;
+  int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_push, ws_bytes;
   int topk_blocks;
   int64_t tiles_max, J_max;
   // activation row bytes: X | GU | Hact
@@ -125,6 +140,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.sv_perm = off; off = align_up(off + 4 * L.rows_max, 256);
   L.sv_tokpos = off; off = align_up(off + 4 * L.NK, 256);
   L.sv_touched = off; off = align_up(off + 4 * L.N, 256);
+  L.sv_pcode = off; off = align_up(off + 4 * L.rows_max, 256);   // perm | kSoleFlag, see k_place
   L.sv_rhdr = off; off = align_up(off + 4 * kRhWords, 256);
   L.sv_rtiles = off; off = align_up(off + 16 * L.tiles_max, 256);
   L.sv_rslot = off; off = align_up(off + 4 * L.tiles_max, 256);
@@ -137,6 +153,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
   L.ws_counters = off; off = align_up(off + 4 * (64 + (3 + kXcds) * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
+  L.ws_push = off; off = align_up(off + 16 * L.rows_max, 256);   // PushRec per row
   L.ws_bytes = off;
   // staged
   L.xd_bytes = align_up(L.rows_max * L.x_row_bytes, 256);
@@ -256,8 +273,15 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
 hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s);
 hipError_t launch_dispatch(const Layout& L, const uint8_t* saved, const void* const* x_seg,
                            uint8_t* xd, hipStream_t s);
+// skip_sole: leave out tokens with a single local pair (their row was written by the GEMM
+// epilogue that produced it).
 hipError_t launch_combine(const Layout& L, const uint8_t* saved, const int32_t* idx, const float* p,
-                          const uint16_t* slots, void* const* out_seg, hipStream_t s);
+                          const uint16_t* slots, void* const* out_seg, bool skip_sole,
+                          hipStream_t s);
+// Push records of the rows [0, rows): pairs flagged kSoleFlag in the schedule's push codes go
+// to their token's row of seg with weight p[pair] (1 when p is null); the others to the slots.
+hipError_t launch_push_rows(const Layout& L, const uint8_t* saved, uint16_t* slots,
+                            void* const* seg, const float* p, PushRec* rec, hipStream_t s);
 hipError_t launch_quantize_mx(int batch, int rows, int cols, const uint16_t* src, int transpose,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_ffn_staged(const Layout& L, const uint8_t* saved, const uint8_t* xd,
@@ -293,6 +317,7 @@ struct BwdBuffers {
   uint8_t *q_xt, *q_dt, *q_dgt, *q_dut, *q_ht;
   uint8_t* ring;      // the forward's ring (null: replay every row)
   int32_t* actsrc;    // [rows_max] row-source codes of the activations (ActSource)
+  PushRec* push;      // [rows_max] dx GEMM push records
 };
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
 
@@ -301,7 +326,8 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
 int fused_slots_per_xcd(const Layout& L);
 hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
                             const void* const* x_seg, const mok_weights& w, uint8_t* ring,
-                            uint16_t* slots, uint8_t* ws, hipStream_t s);
+                            uint16_t* slots, void* const* out_seg, const float* p, uint8_t* ws,
+                            hipStream_t s);
 
 int device_cus();
 

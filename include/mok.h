@@ -196,7 +196,10 @@ mok_status mok_combine(const mok_desc* desc, const void* saved_dev, const int32_
  * dispatch/combine workers and GEMM workers, coordinated through counters in HBM with no
  * host synchronisation; tokens flow through the fixed-size ring in minibatches of M rows
  * ("把 MoE 通信延迟从 103μs 压到 18μs", section 03 parts ② and ③; "Mixture-of-Kittens (MoK)",
- * section on the ring token buffer). Outputs as mok_schedule + mok_combine. ring_bytes must
+ * section on the ring token buffer). Outputs as mok_schedule + mok_combine, except that
+ * slots_dev is scratch here: the down GEMM writes the output row of a token with a single
+ * local pair itself (bf16(p * bf16(y)), the merge over one term), and only pairs of tokens
+ * with several local pairs pass through the slots. ring_bytes must
  * be at least mok_sizes.ring_min_bytes (else MOK_ERR_RING); the ring keeps g|u and h of the
  * last R = mok_sizes.ring_slots row tiles (256 expert-ordered rows each) for mok_layer_bwd. */
 mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
@@ -211,8 +214,9 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
  * Technical Details). Per minibatch: pull dOut rows (reverse combine), a = dOut Wd_e with
  * dp = <a, h>, dh = p a and SwiGLU backward fused in the epilogue (the router-weight
  * gradient inside SwiGLU backward, "Mixture-of-Kittens (MoK)", benchmark section),
- * dx = dg Wg_e + du Wu_e pushed to slots[pair id], and the weight gradients. Then the dX
- * merge over k ascending and, when E_loc == E, dlogits.
+ * dx = dg Wg_e + du Wu_e pushed to slots[pair id] (a token with a single local pair gets its
+ * dX row written directly), and the weight gradients. Then the dX merge over k ascending of the
+ * tokens with several local pairs and, when E_loc == E, dlogits.
  *   dp_dev       fp32 [N][K], written at local pairs only
  *   dlogits_dev  fp32 [N][E] or NULL; must be NULL unless E_loc == E
  *   g            weight gradients, fully overwritten

@@ -31,13 +31,26 @@ def _staged(case):
     return case.out.clone()
 
 
+def _local_pair_counts(case, fw):
+    cfg = case.cfg
+    local = (fw.idx >= cfg.e0) & (fw.idx < cfg.e0 + cfg.E_loc)
+    return local.sum(axis=1)
+
+
+@pytest.mark.parametrize("e0,E_loc", [(0, 8), (2, 3)])
 @pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
-def test_fused_forward_tiny_matches_oracle_and_staged(dtype):
-    cfg = datagen.CONFIGS["tiny"].replace(dtype=dtype, M=32,
+def test_fused_forward_tiny_matches_oracle_and_staged(dtype, e0, E_loc):
+    """With experts 2..4 of 8 local, some tokens have one local pair (their output row is
+    written by the down-GEMM epilogue) and some two (merged from the slots); the fused result
+    equals the staged path's, which merges every token from the slots, bit for bit."""
+    cfg = datagen.CONFIGS["tiny"].replace(dtype=dtype, M=32, e0=e0, E_loc=E_loc,
                                           x_std=1.0 if dtype == "mxfp8" else 0.02)
     case = Case(cfg, fused=True)
     fused = _fused(case)
     fw = case.oracle_forward()
+    if E_loc < cfg.E:
+        per_token = _local_pair_counts(case, fw)
+        assert (per_token == 1).any() and (per_token > 1).any()
     got = case.out_rows(fw.sched.touched)
     if dtype == "bf16":
         assert max_rel_err(got, fw.out) <= BF16_TOL
