@@ -103,8 +103,11 @@ __device__ __forceinline__ int wave_id() {
 // which holds the logical chunk (L%8) ^ f(row) of the swizzled layout, where
 // f(row) = (L/8) ^ (c & 1) because 64w + 8c is a multiple of 8.
 __device__ __forceinline__ void issue_stage(const Operand& op, uint8_t* lds, uint32_t* lds_s, int kt,
-                                            bool mx) {
-  const int w = wave_id(), L = threadIdx.x & 63;
+                                            bool mx, int w) {
+  // The lane's offsets are recomputed per stage (a few VALU operations) rather than hoisted out
+  // of the K loop, where 8 per operand would stay live and, in MXFP8, be spilled. `w` is the
+  // wave index, computed once by the caller (a uniform value).
+  const int L = opaque(int(threadIdx.x) & 63);
   const int lchunk0 = (L & 7) ^ (L >> 3);
   const bool second = kt >= op.ksplit;                 // K split across two sources
   if (second) kt -= op.ksplit;
@@ -217,8 +220,9 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   if (ksteps <= 0) return;
-  issue_stage(A, sm.a[0], sm.as[0], 0, MX);
-  issue_stage(B, sm.b[0], sm.bs[0], 0, MX);
+  const int w = wave_id();
+  issue_stage(A, sm.a[0], sm.as[0], 0, MX, w);
+  issue_stage(B, sm.b[0], sm.bs[0], 0, MX, w);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frag f[2];
@@ -231,13 +235,13 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
     // competing with one slice's fragment reads (measured +9 %). E4M3 (2 slices): both before
     // slice 0, which leaves the whole stage to cover their latency.
     if (more && MX) {
-      issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX);
-      issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX);
+      issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX, w);
+      issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX, w);
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      if (!MX && more && kk == 0) issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX);
-      if (!MX && more && kk == 1) issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX);
+      if (!MX && more && kk == 0) issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX, w);
+      if (!MX && more && kk == 1) issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX, w);
       // Scheduling fences keep each phase whole: the compiler would otherwise interleave the
       // MFMAs of slice kk with the fragment reads of slice kk+1 and wait on those reads.
       __builtin_amdgcn_sched_barrier(0);
