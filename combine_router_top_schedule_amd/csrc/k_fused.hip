@@ -412,10 +412,10 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   a.err = reinterpret_cast<int32_t*>(ws) + kWsError;
   a.tiles_max = L.tiles_max;
   const int cus = device_cus() > 0 ? device_cus() : 256;
-  // Dispatch CUs: 2 per XCD for BF16 copies; 4 per XCD for MXFP8, whose dispatch workers
-  // also quantise every row (measured on the Kimi-K2 MXFP8 workload: 8.48 ms with 16, 7.14 ms
-  // with 32, 7.63 ms with 48).
-  const int comm_total = d.comm_cus > 0 ? d.comm_cus : (mx ? 32 : 16);
+  // Dispatch CUs: 2 per XCD for BF16 copies; 3 per XCD for MXFP8, whose dispatch workers
+  // also quantise every row (measured on the Kimi-K2 MXFP8 workload: 8.92 ms with 16, 6.83 ms
+  // with 24, 6.88 ms with 32, 7.13 ms with 40, 7.36 ms with 48).
+  const int comm_total = d.comm_cus > 0 ? d.comm_cus : (mx ? 24 : 16);
   a.comm_per_xcd = comm_total / kMaxXcd > 0 ? comm_total / kMaxXcd : 1;
   a.K = L.K;
   a.T = L.T;

@@ -76,7 +76,7 @@ typedef struct {
   int32_t num_local_experts;   /* E_loc: 1..64, e0 + E_loc <= E                           */
   int32_t minibatch_tokens;    /* M: ring minibatch rows (MXFP8: multiple of 32); 0 = default */
   int32_t comm_cus;            /* CUs given to dispatch/combine in the fused kernels;
-                                  0 = library default (16 for BF16; 32 for MXFP8, whose
+                                  0 = library default (16 for BF16; 24 for MXFP8, whose
                                   dispatch also quantises every row)                       */
   int64_t ring_bytes;          /* size of the caller's ring token buffer                  */
   int32_t dtype;               /* mok_dtype                                               */
