@@ -34,7 +34,8 @@ struct RouterArgs {
   int32_t* hdr;          // saved header
   int32_t* rank;         // tokpos, used here as the within-expert rank of each local pair
   int32_t* touched;
-  uint32_t* state;       // [blocks][El + 1] look-back words
+  int32_t* multi;        // touched tokens with more than one local pair, ascending
+  uint32_t* state;       // [blocks][El + 2] look-back words
   int32_t* ticket;
   int32_t* err;
   int64_t N;
@@ -81,8 +82,8 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   __shared__ int s_b;
   __shared__ float s_l[2][kTopkTokensPerBlock][33];
   __shared__ uint64_t s_mask[kTopkTokensPerBlock];
-  __shared__ int s_wcnt[4][kMaxLocalExperts + 1];
-  __shared__ int s_excl[kMaxLocalExperts + 1];
+  __shared__ int s_wcnt[4][kMaxLocalExperts + 2];
+  __shared__ int s_excl[kMaxLocalExperts + 2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (tid == 0) s_b = atomicAdd(a.ticket, 1);   // dispatch-ordered block id for the look-back
@@ -166,11 +167,16 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   s_mask[tid] = mask;
   __syncthreads();
 
-  // ---- per-block counts per local expert (value El counts touched tokens) ----
+  // ---- per-block counts per local expert (value El counts touched tokens, El + 1 those with
+  // more than one local pair) ----
   const uint64_t mymask = s_mask[tid];
   const uint64_t lt = (1ull << lane) - 1;
-  for (int e = 0; e <= a.El; ++e) {
-    bool bit = e < a.El ? ((mymask >> e) & 1) : (mymask != 0);
+  const int nc = a.El + 2;   // counted values
+  auto counted = [&](int e) -> bool {
+    return e < a.El ? ((mymask >> e) & 1) : e == a.El ? mymask != 0 : __popcll(mymask) > 1;
+  };
+  for (int e = 0; e < nc; ++e) {
+    bool bit = counted(e);
     uint64_t bal = __ballot(bit);
     if (lane == 0) s_wcnt[wave][e] = __popcll(bal);
   }
@@ -181,18 +187,18 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   // and inspects predecessors 64 at a time (lane i looks at block base - i): the nearest
   // inclusive prefix ends the walk; aggregates before it are summed; an unpublished
   // predecessor makes the wave re-read the window (bounded).
-  if (tid <= a.El) {
+  if (tid < nc) {
     const uint32_t agg = uint32_t(s_wcnt[0][tid] + s_wcnt[1][tid] + s_wcnt[2][tid] + s_wcnt[3][tid]);
-    st_relaxed_u(a.state + int64_t(b) * (a.El + 1) + tid, (b == 0 ? kFlagInc : kFlagAgg) | agg);
+    st_relaxed_u(a.state + int64_t(b) * nc + tid, (b == 0 ? kFlagInc : kFlagAgg) | agg);
   }
-  for (int e = wave; e <= a.El; e += 4) {
+  for (int e = wave; e < nc; e += 4) {
     const uint32_t agg = uint32_t(s_wcnt[0][e] + s_wcnt[1][e] + s_wcnt[2][e] + s_wcnt[3][e]);
     uint32_t excl = 0;
     int base = b - 1;
     int spins = 0;
     while (base >= 0) {
       const int j = base - lane;
-      const uint32_t w = j >= 0 ? ld_relaxed_u(a.state + int64_t(j) * (a.El + 1) + e) : kFlagInc;
+      const uint32_t w = j >= 0 ? ld_relaxed_u(a.state + int64_t(j) * nc + e) : kFlagInc;
       const uint32_t flag = w & ~kValMask;
       const uint64_t inc = __ballot(flag == kFlagInc);
       const uint64_t inv = __ballot(flag == 0);
@@ -211,22 +217,22 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
       base -= 64;
     }
     if (lane == 0) {
-      if (b > 0) st_relaxed_u(a.state + int64_t(b) * (a.El + 1) + e, kFlagInc | (excl + agg));
+      if (b > 0) st_relaxed_u(a.state + int64_t(b) * nc + e, kFlagInc | (excl + agg));
       s_excl[e] = int(excl);
       if (b == a.nblocks - 1) {
         // Last block: inclusive values are the totals.
         const int total = int(excl + agg);
         if (e < a.El) a.hdr[kHdrCounts + e] = total;
-        else a.hdr[kHdrU] = total;
+        else a.hdr[e == a.El ? kHdrU : kHdrUm] = total;
       }
     }
   }
   __syncthreads();
 
-  // ---- ranks of this block's pairs, and the touched-token list ----
+  // ---- ranks of this block's pairs, and the touched-token lists ----
   const int64_t n = n_base + tid;
-  for (int e = 0; e <= a.El; ++e) {
-    bool bit = e < a.El ? ((mymask >> e) & 1) : (mymask != 0);
+  for (int e = 0; e < nc; ++e) {
+    bool bit = counted(e);
     uint64_t bal = __ballot(bit);
     if (bit) {
       int r = s_excl[e] + __popcll(bal & lt);
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
           if (a.idx[n * a.K + q] == a.e0 + e) k = q;
         a.rank[n * a.K + k] = r | (__popcll(mymask) == 1 ? kSoleFlag : 0);
       } else if (r < a.N) {
-        a.touched[r] = int32_t(n);
+        (e == a.El ? a.touched : a.multi)[r] = int32_t(n);
       }
     }
   }
@@ -351,7 +357,7 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
   const FillRange fills[] = {
       {reinterpret_cast<uint32_t*>(wsh), kWsWords, 0u},
       {reinterpret_cast<uint32_t*>(saved + L.sv_rhdr), kRhWords, 0u},
-      {state, int64_t(L.topk_blocks) * (L.El + 1), 0u},
+      {state, int64_t(L.topk_blocks) * (L.El + 2), 0u},
       {reinterpret_cast<uint32_t*>(hdr), kHdrWords, 0u},
   };
   hipError_t err = launch_fill_ranges(fills, 4, s);
@@ -359,6 +365,7 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
   RouterArgs a{logits, idx, p, hdr,
                reinterpret_cast<int32_t*>(saved + L.sv_tokpos),
                reinterpret_cast<int32_t*>(saved + L.sv_touched),
+               reinterpret_cast<int32_t*>(saved + L.sv_multi),
                state, wsh + kWsTicket, wsh + kWsError,
                L.N, L.E, L.K, L.e0, L.El, L.row_align, L.topk_blocks};
   // top-KM list with KM >= K; its first K entries are the top-K

@@ -43,6 +43,7 @@ enum SavedHeader : int {
   kHdrP = 0,        // local pairs
   kHdrRows = 1,     // expert-order rows (P + per-expert padding in MXFP8 mode)
   kHdrU = 2,        // touched tokens
+  kHdrUm = 3,       // touched tokens with more than one local pair
   kHdrCounts = 16,  // [E_loc]
   kHdrOffsets = 96, // [E_loc + 1]
   kHdrWords = 192,
@@ -80,7 +81,7 @@ struct Layout {
   int64_t N, NK, rows_max;
   int row_align;
   // saved
-  int64_t sv_perm, sv_tokpos, sv_touched, sv_pcode, sv_bytes;
+  int64_t sv_perm, sv_tokpos, sv_touched, sv_multi, sv_pcode, sv_bytes;
   int64_t sv_rhdr, sv_rtiles, sv_rslot, sv_rowner;
   // fused-forward ring, one share per XCD: gather slots (X of one row tile) and activation
   // slots (g|u and h of one row tile)
@@ -140,6 +141,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.sv_perm = off; off = align_up(off + 4 * L.rows_max, 256);
   L.sv_tokpos = off; off = align_up(off + 4 * L.NK, 256);
   L.sv_touched = off; off = align_up(off + 4 * L.N, 256);
+  L.sv_multi = off; off = align_up(off + 4 * L.N, 256);   // tokens with several local pairs
   L.sv_pcode = off; off = align_up(off + 4 * L.rows_max, 256);   // perm | kSoleFlag, see k_place
   L.sv_rhdr = off; off = align_up(off + 4 * kRhWords, 256);
   L.sv_rtiles = off; off = align_up(off + 16 * L.tiles_max, 256);
@@ -149,7 +151,7 @@ inline Layout make_layout(const mok_desc& d) {
   // ws
   L.topk_blocks = int(cdiv(L.N, kTopkTokensPerBlock));
   off = 256;
-  L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 1), 256);
+  L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 2), 256);
   L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
   L.ws_counters = off; off = align_up(off + 4 * (64 + (3 + kXcds) * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);

@@ -172,10 +172,10 @@ __device__ __forceinline__ void quant_rows_mx_2(int nrows, int H, int lane, Src 
 // local, of w_k * slots[n*K+k] ), w_k = p[n,k] (or 1 when p == nullptr). fp32 accumulation,
 // one fused multiply-add per term in k order, so the result is bit-reproducible. The token's
 // K indices and weights are read once (lane k), and a pass keeps 16 chunks of 16 bytes per
-// lane of every term in flight. skip_sole: do nothing for a token with a single local pair.
+// lane of every term in flight.
 __device__ __forceinline__ void merge_row(int64_t n, const int32_t* idx, const float* p,
                                          const uint16_t* slots, uint16_t* dst, int H, int K, int e0,
-                                         int El, bool skip_sole, int lane) {
+                                         int El, int lane) {
   int my_le = -1;
   float my_w = 0.f;
   if (lane < K) {
@@ -183,7 +183,6 @@ __device__ __forceinline__ void merge_row(int64_t n, const int32_t* idx, const f
     my_w = p ? p[n * K + lane] : 1.f;
   }
   const uint64_t local = __ballot(my_le >= 0 && my_le < El);
-  if (skip_sole && __popcll(local) == 1) return;
   const int nch = H / 8;
   for (int c0 = 0; c0 < nch; c0 += 64 * 16) {
     float acc[16][8];
