@@ -33,6 +33,9 @@ def _check_schedule(case, row_align=1):
     hdr, perm, tokpos, touched = case.layer.table()
     hdr = hdr.numpy()
     assert hdr[0] == s_ref.P and hdr[1] == s_ref.rows and hdr[2] == len(s_ref.touched)
+    # header word 3: touched tokens with more than one local pair (the fused merges' list)
+    local = ((idx_ref >= cfg.e0) & (idx_ref < cfg.e0 + cfg.E_loc)).sum(axis=1)
+    assert hdr[3] == int((local > 1).sum())
     assert np.array_equal(hdr[16:16 + cfg.E_loc], s_ref.counts)
     assert np.array_equal(hdr[96:96 + cfg.E_loc + 1], s_ref.offsets)
     assert np.array_equal(perm.numpy()[:s_ref.rows], s_ref.perm)
