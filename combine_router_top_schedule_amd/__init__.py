@@ -44,7 +44,8 @@ class MokSizes(ctypes.Structure):
                 ("minibatch", ctypes.c_int32), ("slot_bytes", ctypes.c_int64),
                 ("perm_offset", ctypes.c_int64), ("tokpos_offset", ctypes.c_int64),
                 ("touched_offset", ctypes.c_int64), ("x_slot_bytes", ctypes.c_int64),
-                ("ring_min_bytes", ctypes.c_int64)]
+                ("ring_min_bytes", ctypes.c_int64), ("tiles_offset", ctypes.c_int64),
+                ("tiles_max", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -64,6 +65,9 @@ _SIGS = {
     "mok_abi_version": (ctypes.c_int, []),
     "mok_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "mok_query_sizes": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.POINTER(MokSizes)]),
+    "mok_workspace_size": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t),
+                                          ctypes.POINTER(ctypes.c_size_t)]),
     "mok_two_wave_floor": (ctypes.c_int64, [ctypes.c_int32] * 4),
     "mok_schedule": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P, _P]),
     "mok_dispatch": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P]),
@@ -132,6 +136,14 @@ def query_sizes(d: MokDesc) -> MokSizes:
     s = MokSizes()
     _check("mok_query_sizes", lib().mok_query_sizes(ctypes.byref(d), ctypes.byref(s)))
     return s
+
+
+def workspace_size(d: MokDesc):
+    """(ws_bytes, saved_bytes, slot_bytes) of the fused entry points."""
+    ws, sv, sl = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check("mok_workspace_size", lib().mok_workspace_size(ctypes.byref(d), ctypes.byref(ws),
+                                                          ctypes.byref(sv), ctypes.byref(sl)))
+    return int(ws.value), int(sv.value), int(sl.value)
 
 
 def two_wave_floor(cus: int, tile_m: int, tile_n: int, intermediate: int) -> int:

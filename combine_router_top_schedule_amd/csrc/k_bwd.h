@@ -75,28 +75,49 @@ __device__ __forceinline__ void a_stage_store(const AStage& st, uint16_t* lg, ui
   }
 }
 
+// MXFP8 weight-gradient operands dg^T and du^T, written by the a-GEMM epilogue: codes
+// [I][cols] blocked along tokens (32 rows of one expert per block), scales [I][cols / 32] at
+// codes + I * ld. An expert's token columns start at a multiple of 128 (zero padding after its
+// rows), so a 32-row block of a tile that starts inside the expert's padded range never mixes
+// experts.
+struct TokQuant {
+  uint8_t* dg;          // codes of dg^T (scales at dg + I * ld)
+  uint8_t* du;
+  int64_t ld;           // host bound on the padded token columns
+  int64_t cols;         // padded token columns in use (device-side total)
+  int64_t colbase;      // token column of the tile's row 0
+  int padlim;           // rows of the tile inside the expert's padded range
+};
+
 // Compute one staged 32-row block (i, a template argument so the accumulator stays in
-// registers): dg, du in place of g, u in LDS, dp partials, then dg | du rows out.
+// registers): dg, du, dp partials, then dg | du rows out.
+// BF16: dg, du replace g, u in LDS (BF16) and leave as BF16 rows.
+// MXFP8: dg and du are quantised from their fp32 values twice, with no BF16 rounding in
+// between: along I for the dx GEMM (the 32 lanes of a half-wave hold one 32-column block of a
+// row; codes go to the low byte of the g / u LDS slots, the block's scale code to the high
+// byte of its first slot) and along tokens for the weight gradients (a column's 32 rows of the
+// block sit in lanes l and l ^ 32; codes of 4 consecutive rows leave as one dword).
 template <bool MX, int i>
 __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], const FfnShape& s,
                                                  int64_t row0, int nrows, int colw,
                                                  uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s,
-                                                 float* s_dp,
+                                                 const TokQuant& tq, float* s_dp,
                                                  uint16_t* lg, uint16_t* lu, const uint16_t* lh,
                                                  const float* lpg, int wm, int wn, int lane) {
     const int rbase = wm * 128 + i * 32;                                // tile row of lg row 0
+    float part[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int lr = acc_row(v, lane);                                  // row inside the block
-      const int r = rbase + lr;
-      const bool rok = r < nrows;
-      const float pg = lpg[lr];
-      float part = 0.f;
+    for (int v = 0; v < 16; ++v) part[v] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int lc = j * 32 + (lane & 31);
-        const int c = colw + lc;
-        const bool ok = rok && c < s.I;
+    for (int j = 0; j < 4; ++j) {
+      const int lc = j * 32 + (lane & 31);
+      const int c = colw + lc;
+      float dgr[16], dur[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int lr = acc_row(v, lane);                                // row inside the block
+        const bool ok = rbase + lr < nrows && c < s.I;
+        const float pg = lpg[lr];
         const float av = acc[i][j][v];
         const float g = bf2f(lg[lr * 128 + lc]);
         const float u = bf2f(lu[lr * 128 + lc]);
@@ -105,19 +126,70 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
         const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
         const float duv = dh * g * sg;
-        // dg and du replace g and u in place (each element is read and written by this lane)
-        lg[lr * 128 + lc] = f2bf(dgv);
-        lu[lr * 128 + lc] = f2bf(duv);
-        if (ok) part = fmaf(av, h, part);
-      }
-      // sum over the 32 columns of this half-wave, then over the two wn waves
+        if (ok) part[v] = fmaf(av, h, part[v]);
+        if (MX) {
+          float ag = fabsf(dgv), au = fabsf(duv);
 #pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-      if ((lane & 31) == 0) s_dp[wn * 256 + r] = part;
+          for (int off = 16; off >= 1; off >>= 1) {
+            ag = fmaxf(ag, __shfl_xor(ag, off, 64));
+            au = fmaxf(au, __shfl_xor(au, off, 64));
+          }
+          const int eg = mx_block_exp(ag), eu = mx_block_exp(au);
+          const uint32_t lead = (lane & 31) == 0;
+          lg[lr * 128 + lc] = uint16_t((e4m3x2(dgv * exp2i(-eg), 0.f) & 0xFFu) | (lead * uint32_t(eg + 127) << 8));
+          lu[lr * 128 + lc] = uint16_t((e4m3x2(duv * exp2i(-eu), 0.f) & 0xFFu) | (lead * uint32_t(eu + 127) << 8));
+          dgr[v] = dgv;
+          dur[v] = duv;
+        } else {
+          // dg and du replace g and u in place (each element is read and written by this lane)
+          lg[lr * 128 + lc] = f2bf(dgv);
+          lu[lr * 128 + lc] = f2bf(duv);
+        }
+      }
+      if (MX) {
+        // Along tokens: this lane holds rows 8t + 4h + (0..3), t = 0..3, h = lane / 32, of
+        // column c; lane ^ 32 the others. Rows past the tile's valid rows hold 0 (zero operand
+        // rows, zero gate), which is the padding of the expert's last block.
+        float ag = 0.f, au = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          ag = fmaxf(ag, fabsf(dgr[v]));
+          au = fmaxf(au, fabsf(dur[v]));
+        }
+        ag = fmaxf(ag, __shfl_xor(ag, 32, 64));
+        au = fmaxf(au, __shfl_xor(au, 32, 64));
+        const int eg = mx_block_exp(ag), eu = mx_block_exp(au);
+        const float ig = exp2i(-eg), iu = exp2i(-eu);
+        if (c < s.I && rbase < tq.padlim) {
+          const int64_t col = tq.colbase + rbase;
+          uint8_t* pg_ = tq.dg + int64_t(c) * tq.cols + col + 4 * (lane >> 5);
+          uint8_t* pu_ = tq.du + int64_t(c) * tq.cols + col + 4 * (lane >> 5);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            *reinterpret_cast<uint32_t*>(pg_ + 8 * t) =
+                e4m3x2(dgr[4 * t] * ig, dgr[4 * t + 1] * ig) | (e4m3x2(dgr[4 * t + 2] * ig, dgr[4 * t + 3] * ig) << 16);
+            *reinterpret_cast<uint32_t*>(pu_ + 8 * t) =
+                e4m3x2(dur[4 * t] * iu, dur[4 * t + 1] * iu) | (e4m3x2(dur[4 * t + 2] * iu, dur[4 * t + 3] * iu) << 16);
+          }
+          if (lane < 32) {
+            tq.dg[int64_t(s.I) * tq.ld + int64_t(c) * (tq.cols / 32) + col / 32] = uint8_t(eg + 127);
+            tq.du[int64_t(s.I) * tq.ld + int64_t(c) * (tq.cols / 32) + col / 32] = uint8_t(eu + 127);
+          }
+        }
+      }
+    }
+    // dp partials: sum over the 32 columns of this half-wave (then the two wn waves' halves are
+    // added when the tile's partials leave)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float pv = part[v];
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) pv += __shfl_xor(pv, off, 64);
+      if ((lane & 31) == 0) s_dp[wn * 256 + rbase + acc_row(v, lane)] = pv;
     }
     // (a wave's LDS accesses complete in order: no wait before reading dg | du back)
     __builtin_amdgcn_wave_barrier();
-    // dg | du rows out with 16-byte stores, 16 lanes per row
+    // dg | du rows out with 16-byte stores (BF16) or 8-byte code stores (MXFP8), 16 lanes per row
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
@@ -125,24 +197,24 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
       const u32x4 gv = *reinterpret_cast<const u32x4*>(lg + rr * 128 + cc);
       const u32x4 uv = *reinterpret_cast<const u32x4*>(lu + rr * 128 + cc);
       const int64_t row = row0 + rbase + rr;
-      if (wr) {
+      if (!wr) continue;
+      if (MX) {
+        // low bytes of the 8 slots are the codes; the first slot of a 32-column block also
+        // carries the block's scale code in its high byte
+        auto codes = [](const u32x4& w) {
+          return uint2{(w[0] & 0xFFu) | ((w[0] >> 8) & 0xFF00u) | ((w[1] & 0xFFu) << 16) | ((w[1] & 0xFF0000u) << 8),
+                       (w[2] & 0xFFu) | ((w[2] >> 8) & 0xFF00u) | ((w[3] & 0xFFu) << 16) | ((w[3] & 0xFF0000u) << 8)};
+        };
+        *reinterpret_cast<uint2*>(dgq + row * 2 * s.I + colw + cc) = codes(gv);
+        *reinterpret_cast<uint2*>(dgq + row * 2 * s.I + s.I + colw + cc) = codes(uv);
+        if ((lane & 3) == 0) {
+          dgq_s[row * (2 * s.I / 32) + (colw + cc) / 32] = uint8_t(gv[0] >> 8);
+          dgq_s[row * (2 * s.I / 32) + (s.I + colw + cc) / 32] = uint8_t(uv[0] >> 8);
+        }
+      } else {
         uint16_t* dst = dgu + row * 2 * s.I + colw + cc;
         *reinterpret_cast<u32x4*>(dst) = gv;
         *reinterpret_cast<u32x4*>(dst + s.I) = uv;
-      }
-      if (MX) {
-        // dg | du quantised along I for the dx GEMM: 4 lanes = one 32-column block
-        uint32_t sg, su;
-        const uint2 cg = mx_quant8_group4(gv, &sg);
-        const uint2 cu = mx_quant8_group4(uv, &su);
-        if (wr) {
-          *reinterpret_cast<uint2*>(dgq + row * 2 * s.I + colw + cc) = cg;
-          *reinterpret_cast<uint2*>(dgq + row * 2 * s.I + s.I + colw + cc) = cu;
-          if ((lane & 3) == 0) {
-            dgq_s[row * (2 * s.I / 32) + (colw + cc) / 32] = uint8_t(sg);
-            dgq_s[row * (2 * s.I / 32) + (s.I + colw + cc) / 32] = uint8_t(su);
-          }
-        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -151,13 +223,20 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
 // a = D Wd_e for the 256 intermediate columns [c0, c0+256) of expert e, rows [row0, row0+nrows)
 // of the expert-ordered stream (plane rows of `act` and of D). Epilogue per element (row, i):
 //   dh = p a, dg = dh u s(g) (1 + g (1 - s(g))), du = dh g s(g)     -> dgu[row][i], [I + i]
+//     (MXFP8: codes dgq[row][i], [I + i] blocked along I, and dg^T, du^T blocked along tokens)
 //   dp partial = sum over this tile's columns of a h (fixed tree)   -> dp_part[row][c0/256]
+// The epilogue's LDS carve-out is laid out for exactly 4 waves: 24 KB per wave in the first
+// three stage buffers, dp partials, gates and row-source codes in the fourth.
+static_assert(kThreads == 256, "a_tile's LDS regions assume 4 waves");
+static_assert(4 * 24576 <= 3 * kStageBytes, "per-wave regions must end before the fourth stage buffer");
+static_assert(6144 + 4 * 128 * 4 <= kStageBytes, "dp partials, gates and codes fit one stage buffer");
 template <bool MX>
 __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t row0, int nrows,
                                        int e, int c0, const uint8_t* d, const uint8_t* d_s,
                                        const uint8_t* wdt, const uint8_t* wdt_s,
                                        const ActSource& act, const int32_t* perm, const float* p,
-                                       uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s, float* dp_part) {
+                                       uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s,
+                                       const TokQuant& tq, float* dp_part) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
@@ -204,7 +283,7 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
     if (I_ < 3) a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act,         \
                                  lcode + (I_ + 1) * 32, lane);                                   \
     __builtin_amdgcn_wave_barrier();                                                             \
-    a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, dgq, dgq_s, s_dp, lg, lu, lh,        \
+    a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, dgq, dgq_s, tq, s_dp, lg, lu, lh,    \
                              lpg + I_ * 32, wm,                                                  \
                              wn, lane);                                                          \
   }

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
           for (int k = 0; k < 4; ++k) w[k] = v[k];
           if (a.rows_out)
             *reinterpret_cast<u32x4*>(a.rows_out + int64_t(s_row[r]) * a.F + f0 + ch * 8) = v;
-          if (a.p) {
+          if (a.p && !a.qdst) {   // BF16 operand; MXFP8 applies the gate in fp32 below
             const float g = s_gate[r];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -202,9 +202,20 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
         out[k] = uint32_t(t[(cc * 8 + 2 * k) * kTrPitch + f]) |
                  (uint32_t(t[(cc * 8 + 2 * k + 1) * kTrPitch + f]) << 16);
       if (a.qdst) {
-        // blocks of 32 padded columns (4 lanes); expert ranges start at multiples of 128
+        // blocks of 32 padded columns (4 lanes); expert ranges start at multiples of 128. A
+        // gated operand (p * D) is formed in fp32 and quantised from there.
+        float fv[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          fv[2 * k] = bf2f(uint16_t(out[k]));
+          fv[2 * k + 1] = bf2f(uint16_t(out[k] >> 16));
+        }
+        if (a.p) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) fv[k] *= s_gate[cc * 8 + k];
+        }
         uint32_t sc;
-        const uint2 codes = mx_quant8_group4(out, &sc);
+        const uint2 codes = mx_quant8_group4_f(fv, &sc);
         *reinterpret_cast<uint2*>(a.qdst + int64_t(f0 + f) * cols + c0 + cc * 8) = codes;
         if ((cc & 3) == 0)
           a.qdst[int64_t(a.F) * a.ld + int64_t(f0 + f) * (cols / 32) + (c0 + cc * 8) / 32] = uint8_t(sc);
@@ -228,10 +239,12 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
 //    columns [colpad[e], colpad[e] + count[e]), colpad[e] a multiple of kPadRows, the rest of its
 //    rounded-up range zero; hdr2[kB2RowsPad] = total padded columns;
 //  - zeroed work-queue counters of the two GEMM launches.
-// El <= 64, so lane e owns expert e.
+// El <= 64, so lane e owns expert e. The ring record is used only if it is whole: its slot
+// count matches this ring, and every recorded tile has a slot of this ring and lies inside its
+// expert's rows; otherwise every row is replayed (the result is the same either way).
 __global__ __launch_bounds__(64) void k_bwd_plan(const int32_t* hdr, const int32_t* rhdr,
                                                  const MTile* rtiles, const int32_t* rslot,
-                                                 const int32_t* rowner, int have_ring,
+                                                 const int32_t* rowner, int have_ring, int capa,
                                                  MTile* restore, int32_t* restore_slot,
                                                  MTile* replay, int32_t* counts, MTile* tiles,
                                                  int32_t* ntiles, int32_t* hdr2, int El,
@@ -255,8 +268,30 @@ __global__ __launch_bounds__(64) void k_bwd_plan(const int32_t* hdr, const int32
   const int t_tot = __shfl(t_ex, 63, 64), p_tot = __shfl(p_ex, 63, 64);
   t_ex -= nt_e;
   p_ex -= pad_e;
+  // the forward's ring record, validated
+  int nt = have_ring ? rhdr[kRhTiles] : 0;
+  if (nt < 0 || nt > tiles_max || (nt > 0 && rhdr[kRhCapt] != capa)) nt = 0;
+  {
+    const int nslots = kXcds * capa;
+    bool bad = false;
+    for (int base = 0; base < nt; base += 64) {
+      const int mt = base + lane;
+      MTile t{0, 0, 0, 0};
+      int sl = 0;
+      if (mt < nt) {
+        t = rtiles[mt];
+        sl = rslot[mt];
+      }
+      // (every lane takes part in the shuffles)
+      const bool eok = t.e >= 0 && t.e < El;
+      const int eo = __shfl(off, eok ? t.e : 0, 64), ec = __shfl(cnt, eok ? t.e : 0, 64);
+      const bool ok = mt >= nt || (eok && sl >= 0 && sl < nslots && t.nrows >= 1 &&
+                                   t.nrows <= kTileM && t.row0 >= eo && t.row0 + t.nrows <= eo + ec);
+      bad = bad || __ballot(!ok) != 0;
+    }
+    if (bad) nt = 0;
+  }
   // per-expert tiles: the GEMM tile table, and the replay list when there is no ring state
-  const int nt = have_ring ? rhdr[kRhTiles] : 0;
   if (lane < El) {
     for (int q = 0; q < nt_e && t_ex + q < tiles_max; ++q) {
       const MTile t{0, lane, off + q * kTileM, min(kTileM, cnt - q * kTileM)};
@@ -386,6 +421,7 @@ struct WJob {
 struct BwdArgs {
   const MTile* tiles;
   const int32_t* ntiles;
+  const int32_t* hdr;      // schedule header (expert offsets)
   const int32_t* perm;
   const float* p;
   const int32_t* hdr2;
@@ -396,7 +432,9 @@ struct BwdArgs {
   const uint8_t* wdt;      // Wd^T [El][I][H] (BF16 or codes)
   const uint8_t* wdt_s;
   ActSource act;           // g|u and h of the forward (ring slot or replayed plane, per row)
-  uint16_t* dgu;           // out: dg|du BF16 [rows][2I]
+  uint16_t* dgu;           // out: dg|du BF16 [rows][2I] (BF16 mode)
+  uint8_t* q_dgt;          // out (MXFP8): dg^T, du^T blocked along tokens, codes then scales
+  uint8_t* q_dut;
   float* dp_part;          // out: [rows][I/256]
   // dx GEMM
   const uint8_t* dgu_a;    // dg|du as the dx GEMM reads it: BF16 or codes [rows][2I]
@@ -457,11 +495,19 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gemms(BwdArgs a) {
         int mt, nt;
         tile_coords(t, mtiles, ntn, mt, nt);
         const MTile tl = a.tiles[mt];
-        if (PHASE == 0)
+        if (PHASE == 0) {
+          TokQuant tq{};
+          if (MX) {
+            // token column of the tile's first row in the per-expert padded planes
+            const int rel = tl.row0 - a.hdr[kHdrOffsets + tl.e];
+            const int cp = a.hdr2[kB2ColPad + tl.e];
+            tq = TokQuant{a.q_dgt, a.q_dut, a.ld, a.hdr2[kB2RowsPad], int64_t(cp) + rel,
+                          a.hdr2[kB2ColPad + tl.e + 1] - cp - rel};
+          }
           a_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.d, a.d_s, a.wdt, a.wdt_s,
                      a.act, a.perm, a.p, a.dgu, const_cast<uint8_t*>(a.dgu_a),
-                     const_cast<uint8_t*>(a.dgu_s), a.dp_part);
-        else
+                     const_cast<uint8_t*>(a.dgu_s), tq, a.dp_part);
+        } else
           dx_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.dgu_a, a.dgu_s, a.wgt,
                       a.wgt_s, a.wut, a.wut_s, a.push);
       } else {
@@ -524,15 +570,15 @@ int grid_cap(int64_t items, int cap) {
 }  // namespace
 
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) {
-  static bool attr_done = false;
-  hipError_t err;
-  if (!attr_done) {
-    if ((err = allow_big_lds(k_bwd_gemms<false, 0>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_bwd_gemms<true, 0>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_bwd_gemms<false, 1>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_bwd_gemms<true, 1>)) != hipSuccess) return err;
-    attr_done = true;
-  }
+  static std::atomic<bool> attr_done[kMaxDevices];
+  hipError_t err = once_per_device(attr_done, [] {
+    hipError_t e;
+    if ((e = allow_big_lds(k_bwd_gemms<false, 0>)) != hipSuccess) return e;
+    if ((e = allow_big_lds(k_bwd_gemms<true, 0>)) != hipSuccess) return e;
+    if ((e = allow_big_lds(k_bwd_gemms<false, 1>)) != hipSuccess) return e;
+    return allow_big_lds(k_bwd_gemms<true, 1>);
+  });
+  if (err != hipSuccess) return err;
   const bool mx = L.dtype == MOK_MXFP8;
   const int G = device_cus() > 0 ? device_cus() : 256;
   const int H = L.H, I = L.I, El = L.El;
@@ -551,7 +597,8 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
                      reinterpret_cast<const MTile*>(b.saved + L.sv_rtiles),
                      reinterpret_cast<const int32_t*>(b.saved + L.sv_rslot),
                      reinterpret_cast<const int32_t*>(b.saved + L.sv_rowner),
-                     int(b.ring != nullptr && L.ring_capa > 0), restore, rsl, replay, counts,
+                     int(b.ring != nullptr && L.ring_capa > 0), L.ring_capa, restore, rsl,
+                     replay, counts,
                      reinterpret_cast<MTile*>(b.ws + L.ws_tiles),
                      reinterpret_cast<int32_t*>(b.ws) + kWsNumTiles, b.hdr2, El, L.tiles_max);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -618,7 +665,10 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   BwdArgs a{};
   a.tiles = reinterpret_cast<const MTile*>(b.ws + L.ws_tiles);
   a.ntiles = reinterpret_cast<const int32_t*>(b.ws) + kWsNumTiles;
+  a.hdr = hdr;
   a.perm = perm;
+  a.q_dgt = b.q_dgt;
+  a.q_dut = b.q_dut;
   a.p = b.topk_p;
   a.hdr2 = b.hdr2;
   a.s = FfnShape{H, I};
@@ -660,14 +710,17 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   else hipLaunchKernelGGL((k_bwd_gemms<false, 0>), dim3(G), dim3(kThreads), kGemmLdsBytes, s, a);
   trace_after(MOK_TRACE_BWD_GEMM1, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 6. dg^T, du^T; phase 1: dx GEMM pushed to the slots (a token's only local pair straight to
-  //    its dX row), dWg and dWu
+  // 6. dg^T, du^T (BF16; the MXFP8 a-GEMM epilogue wrote them, quantised along tokens from
+  //    fp32); phase 1: dx GEMM pushed to the slots (a token's only local pair straight to its
+  //    dX row), dWg and dWu
   if ((err = launch_push_rows(L, b.saved, b.slots, b.dx_seg, nullptr, b.push, s)) != hipSuccess)
     return err;
-  const uint8_t* dgu8 = reinterpret_cast<const uint8_t*>(b.dgu);
-  tr(nullptr, nullptr, dgu8, nullptr, 2 * I, 0, I, b.dgt, b.q_dgt);                   // dg^T
-  tr(nullptr, nullptr, dgu8, nullptr, 2 * I, I, I, b.dut, b.q_dut);                   // du^T
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (!mx) {
+    const uint8_t* dgu8 = reinterpret_cast<const uint8_t*>(b.dgu);
+    tr(nullptr, nullptr, dgu8, nullptr, 2 * I, 0, I, b.dgt, nullptr);                 // dg^T
+    tr(nullptr, nullptr, dgu8, nullptr, 2 * I, I, I, b.dut, nullptr);                 // du^T
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   a.njobs = 2;
   job(a.jobs[0], b.dgt, b.xt, b.q_dgt, b.q_xt, I, H, b.g.dwg);
   job(a.jobs[1], b.dut, b.xt, b.q_dut, b.q_xt, I, H, b.g.dwu);

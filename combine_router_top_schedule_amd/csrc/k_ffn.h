@@ -147,6 +147,12 @@ struct PushTarget {
 // K loop so its latency is hidden. kPushRec: the row's record is loaded here, unconditionally
 // (clamped row index), and first used after the LDS staging, so its latency is hidden there;
 // nothing of it is live across the K loop.
+// The epilogue keeps one destination pointer and one weight per thread in the MXFP8 scale
+// buffers, and the BF16 tile in the stage buffers.
+static_assert(kThreads * sizeof(void*) <= sizeof(GemmLds::as), "push destinations fit as[]");
+static_assert(kThreads * sizeof(float) <= sizeof(GemmLds::bs[0]), "push weights fit bs[0]");
+static_assert(kTileM * kTileN * 2 <= 4 * kStageBytes, "BF16 tile fits the stage buffers");
+
 template <int MODE>
 __device__ __forceinline__ void push_epilogue(GemmLds& sm, const f32x16 (&acc)[4][4], int nrows,
                                               int c0, int H, int32_t my_pair,

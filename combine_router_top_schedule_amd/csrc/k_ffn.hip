@@ -56,17 +56,15 @@ hipError_t allow_big_lds(F* f) {
 }  // namespace
 
 namespace {
-bool g_attr_done = false;
-
 hipError_t ffn_init() {
-  if (g_attr_done) return hipSuccess;
-  hipError_t e;
-  if ((e = allow_big_lds(k_gateup_staged<false>)) != hipSuccess) return e;
-  if ((e = allow_big_lds(k_gateup_staged<true>)) != hipSuccess) return e;
-  if ((e = allow_big_lds(k_down_staged<false>)) != hipSuccess) return e;
-  if ((e = allow_big_lds(k_down_staged<true>)) != hipSuccess) return e;
-  g_attr_done = true;
-  return hipSuccess;
+  static std::atomic<bool> attr_done[kMaxDevices];
+  return once_per_device(attr_done, [] {
+    hipError_t e;
+    if ((e = allow_big_lds(k_gateup_staged<false>)) != hipSuccess) return e;
+    if ((e = allow_big_lds(k_gateup_staged<true>)) != hipSuccess) return e;
+    if ((e = allow_big_lds(k_down_staged<false>)) != hipSuccess) return e;
+    return allow_big_lds(k_down_staged<true>);
+  });
 }
 
 FfnStagedArgs staged_args(const Layout& L, const uint8_t* saved, const uint8_t* xd,

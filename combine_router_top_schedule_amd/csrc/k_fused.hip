@@ -74,7 +74,8 @@ struct FusedArgs {
 // ended up with (-1 until known) and per XCD the next GEMM item. After them: landed / gu_done /
 // dn_done per tile, then per XCD the tile id of its q-th row tile (-1 until known).
 enum CntWords : int {
-  kCntArrived = 0, kCntReg = 8, kCntEnd = 16, kCntNext = 24, kCntItem = 32, kCntWords = 64
+  kCntArrived = 0, kCntReg = 8, kCntEnd = 16, kCntNext = 24, kCntItem = 32, kCntExit = 40,
+  kCntWords = 64
 };
 
 __device__ __forceinline__ int xcc_id() {
@@ -137,11 +138,11 @@ __device__ __forceinline__ void signal(int32_t* p) {
   if (threadIdx.x == 0) add_relaxed(p, 1);
 }
 
+// The work of one workgroup. Every exit is taken by the whole workgroup (the values deciding
+// it come through LDS or from one thread's atomic), so the caller's exit protocol runs once.
 template <bool MX>
-__global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
-  __shared__ int s_x, s_local, s_n[kMaxXcd];
+__device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) {
+  __shared__ int s_x, s_local, s_n[kMaxXcd], s_fail;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
   // ---- registration: which XCD am I on, and how many workgroups share it ----
@@ -156,9 +157,10 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
       __builtin_amdgcn_s_sleep(2);
     }
     for (int i = 0; i < kMaxXcd; ++i) s_n[i] = ld_relaxed(a.cnt + kCntReg + i);
+    s_fail = ld_relaxed(a.err) != 0;
   }
   __syncthreads();
-  if (ld_relaxed(a.err) != 0) return;
+  if (s_fail) return;
   const int x = s_x, local = s_local;
   // active XCDs: those with at least one comm and one GEMM worker
   int nact = 0, ax = -1;
@@ -192,10 +194,6 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
     return pl;
   };
 
-  if (ax == 0 && local == 0 && tid == 0) {
-    a.rhdr[kRhTiles] = nt;
-    a.rhdr[kRhCapt] = a.capa;
-  }
   // The tile id of this XCD's q-th row tile: workgroup 0 takes it from the global counter and
   // publishes it (row tiles are taken when this XCD has a free slot, so faster XCDs take more
   // of them); the others wait for the publication. Returns >= nt when there is none, -1 after
@@ -346,6 +344,27 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   }
 }
 
+// Persistent forward kernel: the workgroup's work, then the exit protocol. The ring record the
+// backward reads (which row tile each activation slot holds) is published only by the last
+// workgroup to finish, and only when no workgroup reported an error: after a failed bounded
+// wait the record may name tiles that were never taken, and the backward must not trust it.
+template <bool MX>
+__global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
+  layer_fwd_body<MX>(a, sm);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(a.cnt + kCntExit, 1, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    if (done == int(gridDim.x) - 1 && ld_relaxed(a.err) == 0) {
+      a.rhdr[kRhCapt] = a.capa;
+      a.rhdr[kRhTiles] = *a.ntiles;
+    }
+  }
+}
+
 template <class F>
 hipError_t allow_big_lds(F* f) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(f),
@@ -360,13 +379,12 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
                             const void* const* x_seg, const mok_weights& w, uint8_t* ring,
                             uint16_t* slots, void* const* out_seg, const float* p, uint8_t* ws,
                             hipStream_t s) {
-  static bool attr_done = false;
-  hipError_t err;
-  if (!attr_done) {
-    if ((err = allow_big_lds(k_layer_fwd<false>)) != hipSuccess) return err;
-    if ((err = allow_big_lds(k_layer_fwd<true>)) != hipSuccess) return err;
-    attr_done = true;
-  }
+  static std::atomic<bool> attr_done[kMaxDevices];
+  hipError_t err = once_per_device(attr_done, [] {
+    const hipError_t e = allow_big_lds(k_layer_fwd<false>);
+    return e != hipSuccess ? e : allow_big_lds(k_layer_fwd<true>);
+  });
+  if (err != hipSuccess) return err;
   if ((err = launch_tiles(L, L.M, saved, ws, s)) != hipSuccess) return err;
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.ws_counters);
   const bool mx = L.dtype == MOK_MXFP8;

@@ -160,14 +160,18 @@ int grid_for(int64_t work_items, int per_block, int cap) {
 
 }  // namespace
 
+// Compute units of the current device, cached per device id (0 if unknown).
 int device_cus() {
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
-    cus = prop.multiProcessorCount;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices && cus > 0) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

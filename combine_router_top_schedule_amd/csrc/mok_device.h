@@ -70,17 +70,11 @@ __device__ __forceinline__ uint32_t mx_quant32(const float* v, uint32_t* out8) {
   return uint32_t(e + 127);
 }
 
-// Quantise 8 BF16 values (packed in v) held by each lane of an aligned group of 4 consecutive
-// lanes, which together form one 32-element MX block: same rule as mx_quant32 (block amax
-// over the 4 lanes by shuffles). Returns the 8 codes; *scode gets the block's scale code.
-// Every lane of the wave must call it.
-__device__ __forceinline__ uint2 mx_quant8_group4(const u32x4& v, uint32_t* scode) {
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(v[i] << 16);
-    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
-  }
+// Quantise 8 fp32 values held by each lane of an aligned group of 4 consecutive lanes, which
+// together form one 32-element MX block: same rule as mx_quant32 (block amax over the 4 lanes
+// by shuffles). Returns the 8 codes; *scode gets the block's scale code. Every lane of the wave
+// must call it.
+__device__ __forceinline__ uint2 mx_quant8_group4_f(const float (&f)[8], uint32_t* scode) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
@@ -91,6 +85,17 @@ __device__ __forceinline__ uint2 mx_quant8_group4(const u32x4& v, uint32_t* scod
   *scode = uint32_t(e + 127);
   return uint2{e4m3x2(f[0] * inv, f[1] * inv) | (e4m3x2(f[2] * inv, f[3] * inv) << 16),
                e4m3x2(f[4] * inv, f[5] * inv) | (e4m3x2(f[6] * inv, f[7] * inv) << 16)};
+}
+
+// The same for 8 BF16 values packed in v.
+__device__ __forceinline__ uint2 mx_quant8_group4(const u32x4& v, uint32_t* scode) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+  return mx_quant8_group4_f(f, scode);
 }
 
 // ---- agent-scope signalling ---------------------------------------------------------------

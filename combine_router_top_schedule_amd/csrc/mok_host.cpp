@@ -132,6 +132,20 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   sizes->touched_offset = L.sv_touched;
   sizes->x_slot_bytes = L.xsb;
   sizes->ring_min_bytes = int64_t(kXcds) * (kRingXSlots * L.xsb + 2 * L.asb);
+  sizes->tiles_offset = L.ws_tiles;
+  sizes->tiles_max = L.tiles_max;
+  return MOK_OK;
+}
+
+mok_status mok_workspace_size(const mok_desc* desc, size_t* ws_bytes, size_t* saved_bytes,
+                              size_t* slot_bytes) {
+  if (!ws_bytes || !saved_bytes || !slot_bytes) return MOK_ERR_NULL;
+  mok_sizes sz{};
+  const mok_status st = mok_query_sizes(desc, &sz);
+  if (st != MOK_OK) return st;
+  *ws_bytes = sz.bwd_ws_bytes;
+  *saved_bytes = sz.saved_bytes;
+  *slot_bytes = sz.slots_bytes;
   return MOK_OK;
 }
 

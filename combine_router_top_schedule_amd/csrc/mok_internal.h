@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/mok.h"
 
 namespace mok {
@@ -173,7 +175,7 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_act = take(L.act_bytes);
   L.b_d = take(mx ? 0 : rm * H * 2);      // BF16 D (MXFP8 gathers straight into b_dq)
   L.b_dq = take(mx ? rm * (H + H / 32) : 0);
-  L.b_dgu = take(rm * 2 * I * 2);
+  L.b_dgu = take(mx ? 0 : rm * 2 * I * 2);   // BF16 dg|du (MXFP8 writes codes only)
   L.b_dguq = take(mx ? rm * (2 * I + 2 * I / 32) : 0);
   L.b_dp = take(rm * (I / kTileN + 1) * 4);
   L.b_wdt = take(mx ? 0 : int64_t(L.El) * H * I * 2);
@@ -332,6 +334,20 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
                             hipStream_t s);
 
 int device_cus();
+
+// One-time set-up per device (kernel attributes are set for the device that is current when
+// the first call on it happens). `done` holds one flag per device id below kMaxDevices; other
+// ids run the set-up every time.
+constexpr int kMaxDevices = 64;
+template <class F>
+hipError_t once_per_device(std::atomic<bool> (&done)[kMaxDevices], F&& setup) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = setup();
+  if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 // Measurement hook (mok_trace_kernel): events recorded around one kernel group.
 struct TraceHook {

@@ -113,6 +113,14 @@ class MokLayer:
     def header(self):
         return self.saved[:1024].view(torch.int32).cpu()
 
+    def tiles(self):
+        """The grouped-GEMM tile table the last forward used: int32 [n][4] rows
+        (minibatch, local expert, first row, rows), copied to the host."""
+        s = self.sizes
+        n = int(self.ws[8:12].view(torch.int32).item())
+        off = int(s.tiles_offset)
+        return self.ws[off:off + 16 * n].view(torch.int32).reshape(n, 4).cpu()
+
     def table(self):
         """(header, perm, tokpos, touched) of the schedule table, copied to the host."""
         s = self.sizes

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOK_ABI_VERSION 2
+#define MOK_ABI_VERSION 3
 
 typedef enum {
   MOK_OK = 0,
@@ -111,6 +111,12 @@ typedef struct {
   int64_t x_slot_bytes;   /* bytes of one gather slot of the ring (X rows of 256 tokens)      */
   int64_t ring_min_bytes; /* smallest ring_bytes the fused path accepts (two activation slots
                              per XCD share)                                                  */
+  /* The grouped-GEMM tile table inside `ws`, written by mok_expert_ffn and mok_layer_fwd:
+   * int32 quads {minibatch j, local expert, first expert-order row, rows}, ordered by j, then
+   * expert, then row; tiles never straddle an expert or a minibatch. Its length is int32 word
+   * 2 of ws. */
+  int64_t tiles_offset;
+  int64_t tiles_max;
 } mok_sizes;
 
 /* Expert weights (device pointers). BF16 mode uses wg/wu/wd only. MXFP8 mode uses E4M3 codes
@@ -141,6 +147,13 @@ const char* mok_status_str(mok_status s);
 
 /* Validate `desc` and report every buffer size. Host only; launches nothing. */
 mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes);
+
+/* The three sizes a caller of the fused entry points needs, in the form the layer's scope
+ * states them: *ws_bytes = workspace of mok_layer_fwd and mok_layer_bwd (the backward's, which
+ * is the larger), *saved_bytes = the schedule table and ring record, *slot_bytes = the
+ * push/receive buffer (N*K rows of H BF16). Host only; same validation as mok_query_sizes. */
+mok_status mok_workspace_size(const mok_desc* desc, size_t* ws_bytes, size_t* saved_bytes,
+                              size_t* slot_bytes);
 
 /* Two-wave minibatch floor: the smallest minibatch for which the gate/up grouped GEMM
  * (N = 2*I columns) gives every one of `cus` compute units at least two tiles of

@@ -357,6 +357,48 @@ def backward(fw: Forward, dout_fn, W: Weights, K: int, e0: int, E_loc: int,
     return Backward(dx, dp, dwg, dwu, dwd, dlogits, a, dg, du)
 
 
+def expert_wgrad_rows(x_rows: np.ndarray, dout_rows: np.ndarray, p_rows: np.ndarray, W: Weights,
+                      e: int, gi, hi, workers: int = 1):
+    """Rows ``gi`` of dWg_e and dWu_e and rows ``hi`` of dWd_e, from expert e's rows alone.
+
+    x_rows, dout_rows: [R][H] the values of the source rows of expert e's pairs in schedule
+    order (ascending token id), p_rows: [R] their gates. Same definitions as ``backward`` (O9-O12),
+    restricted to the requested rows: row i of dWg_e and dWu_e needs column i of dg and du only,
+    and row j of dWd_e column j of p*D and the whole h. In MXFP8 mode the weight-gradient
+    operands are blocked along tokens, so quantising one column alone gives the same values as
+    quantising the whole operand. ``workers`` parallelises the quantiser over slices.
+    Returns (dWg rows [len(gi)][H], dWu rows, dWd rows [len(hi)][I])."""
+    mxm = W.dtype != "bf16"
+    gi, hi = np.asarray(gi), np.asarray(hi)
+    xd = mx.fake_quant(x_rows, axis=1, workers=workers) if mxm else x_rows
+    Wg, Wu = W.fwd_gate()[e], W.fwd_up()[e]
+    D = mx.fake_quant(dout_rows, axis=1, workers=workers) if mxm else dout_rows
+    # dg, du at columns gi (O10)
+    g = xd @ Wg[gi].T
+    u = xd @ Wu[gi].T
+    a = D @ W.bwd_down()[e][:, gi]
+    dh = p_rows[:, None] * a
+    sg = sigmoid(g)
+    dg = dh * u * sg * (1.0 + g * (1.0 - sg))
+    du = dh * g * sg
+    # the whole h of the expert's rows (O5-O6)
+    gf = xd @ Wg.T
+    hf = silu(gf) * (xd @ Wu.T)
+    if mxm:
+        hf = mx.fake_quant(_q32(hf), axis=1, workers=workers)
+    pD = p_rows[:, None] * dout_rows[:, hi]
+    if mxm:
+        xs = mx.fake_quant_rows_padded(x_rows, workers=workers)
+        dwg = mx.fake_quant_rows_padded(_q32(dg)).T @ xs
+        dwu = mx.fake_quant_rows_padded(_q32(du)).T @ xs
+        dwd = mx.fake_quant_rows_padded(_q32(pD)).T @ mx.fake_quant_rows_padded(hf, workers=workers)
+    else:
+        dwg = dg.T @ xd
+        dwu = du.T @ xd
+        dwd = pD.T @ hf
+    return dwg, dwu, dwd
+
+
 def loss(fw: Forward, dout: np.ndarray) -> float:
     """L = sum over touched tokens of <dOut[n], out[n]> (dout indexed by token id)."""
     return float((dout[fw.sched.touched] * fw.out).sum())

@@ -99,13 +99,34 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, axis: int = -1) -> np.ndar
     return np.moveaxis(out.reshape(cm.shape), -1, axis)
 
 
-def fake_quant(v: np.ndarray, axis: int = -1) -> np.ndarray:
-    """dequantize(quantize(v)) along ``axis``."""
-    c, s = quantize(v, axis)
-    return dequantize(c, s, axis)
+def _sliced(fn, v: np.ndarray, axis: int, workers: int) -> np.ndarray:
+    """Apply ``fn`` (which blocks along ``axis``) to slices of ``v`` along another axis, in
+    ``workers`` threads. Every block lies inside one slice, so the result is the same as one
+    call on the whole array; numpy releases the interpreter lock inside its loops."""
+    axis = axis % v.ndim
+    if workers <= 1 or v.ndim < 2:
+        return fn(v)
+    other = 0 if axis != 0 else 1
+    n = v.shape[other]
+    bounds = np.linspace(0, n, min(workers, n) + 1).astype(int)
+    parts = [np.take(v, np.arange(a, b), axis=other) for a, b in zip(bounds[:-1], bounds[1:])]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(parts)) as ex:
+        return np.concatenate(list(ex.map(fn, parts)), axis=other)
 
 
-def fake_quant_rows_padded(v: np.ndarray) -> np.ndarray:
+def fake_quant(v: np.ndarray, axis: int = -1, workers: int = 1) -> np.ndarray:
+    """dequantize(quantize(v)) along ``axis`` (``workers`` > 1: in parallel slices)."""
+    v = np.asarray(v, dtype=np.float64)
+
+    def one(a):
+        c, s = quantize(a, axis)
+        return dequantize(c, s, axis)
+
+    return _sliced(one, v, axis, workers)
+
+
+def fake_quant_rows_padded(v: np.ndarray, workers: int = 1) -> np.ndarray:
     """Quantise a [rows][cols] operand in blocks of 32 along rows, zero-padding the last block.
 
     Used for weight-gradient GEMMs, whose reduction axis is the token axis of one expert.
@@ -114,4 +135,4 @@ def fake_quant_rows_padded(v: np.ndarray) -> np.ndarray:
     r = v.shape[0]
     pad = (-r) % BLOCK
     vp = np.concatenate([v, np.zeros((pad,) + v.shape[1:])], axis=0) if pad else v
-    return fake_quant(vp, axis=0)[:r]
+    return fake_quant(vp, axis=0, workers=workers)[:r]

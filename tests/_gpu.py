@@ -27,9 +27,10 @@ class Case:
     """Device inputs and a MokLayer for one datagen config."""
 
     def __init__(self, cfg: datagen.Config, M=None, ring_bytes=None, staged=True, fused=False,
-                 with_dout=False, logits=None, flags=0):
+                 with_dout=False, logits=None, flags=0, comm_cus=0):
         self.cfg = cfg
-        self.d = mok.desc_from_config(cfg, M=M, ring_bytes=ring_bytes, flags=flags)
+        self.d = mok.desc_from_config(cfg, M=M, ring_bytes=ring_bytes, flags=flags,
+                                      comm_cus=comm_cus)
         self.layer = MokLayer(self.d, staged=staged, fused=fused)
         self.logits_h = datagen.logits(cfg) if logits is None else logits
         self.x_h = datagen.x_all(cfg)
@@ -128,3 +129,53 @@ class BwdCase(Case):
         fw = fw or self.oracle_forward()
         W = self.oracle_weights()
         return fw, mo.backward(fw, mo.bf16_rows(self.dout_h), W, cfg.K, cfg.e0, cfg.E_loc, cfg.E)
+
+
+class ArrayCase:
+    """A layer on explicit arrays (float64 values exactly representable in BF16): one segment of
+    N tokens, all experts [0, E_loc) local. Runs the staged or the fused forward and the
+    backward; results come back as float64 arrays."""
+
+    def __init__(self, x, dout, logits, wg, wu, wd, K, dtype="mxfp8", M=64, fused=False):
+        from tests import mx_cases as mc
+        N, H = x.shape
+        E_loc, I, _ = wg.shape
+        E = logits.shape[1]
+        self.N, self.H, self.I, self.K, self.E, self.E_loc = N, H, I, K, E, E_loc
+        d0 = mok.desc(H, E, K, I, 1, N, 0, E_loc, M, 0, dtype)
+        ring = mok.query_sizes(d0).ring_min_bytes if fused else 0
+        self.d = mok.desc(H, E, K, I, 1, N, 0, E_loc, M, ring, dtype)
+        self.fused = fused
+        self.layer = MokLayer(self.d, staged=not fused, fused=fused)
+        bits = lambda a: dev_u16(mc.bf16_bits(a))
+        self.x, self.dout = bits(x), bits(dout)
+        self.logits = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
+        self.wg, self.wu, self.wd = bits(wg), bits(wu), bits(wd)
+        self.layer.set_weights(self.wg, self.wu, self.wd)
+        self.out = torch.zeros((N, H), dtype=torch.int16, device="cuda")
+        self.dx = torch.zeros_like(self.out)
+        self.x_seg, self.out_seg, self.dout_seg, self.dx_seg = (
+            self.layer.segs(t) for t in (self.x, self.out, self.dout, self.dx))
+        self.dp = torch.zeros(N * K, dtype=torch.float32, device="cuda")
+        self.dlogits = (torch.zeros((N, E), dtype=torch.float32, device="cuda")
+                        if E_loc == E else None)
+        self.dwg = torch.zeros((E_loc, I, H), dtype=torch.float32, device="cuda")
+        self.dwu = torch.zeros_like(self.dwg)
+        self.dwd = torch.zeros((E_loc, H, I), dtype=torch.float32, device="cuda")
+        self.bws = torch.empty(int(self.layer.sizes.bwd_ws_bytes), dtype=torch.uint8, device="cuda")
+
+    def run(self):
+        L = self.layer
+        if self.fused:
+            L.forward(self.x_seg, self.logits, self.out_seg)
+        else:
+            L.forward_staged(self.x_seg, self.logits, self.out_seg)
+        mok.mok_layer_bwd(self.d, self.dout_seg, self.x_seg, L.w, L.idx, L.p, L.saved, L.ring,
+                          L.slots, self.dx_seg, self.dp, self.dlogits, self.dwg, self.dwu,
+                          self.dwd, self.bws)
+        torch.cuda.synchronize()
+        assert mok.mok_device_status(L.ws) == 0
+        f64 = lambda t: t.cpu().numpy().astype(np.float64)
+        return dict(out=bf16_to_f64(host_u16(self.out)), dx=bf16_to_f64(host_u16(self.dx)),
+                    dwg=f64(self.dwg), dwu=f64(self.dwu), dwd=f64(self.dwd),
+                    dp=f64(self.dp).reshape(self.N, self.K))

@@ -13,6 +13,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import combine_router_top_schedule_amd as mok
+from oracle import moe_oracle as mo
 from tests._gpu import BF16_TOL, MX_TOL, Case, frob_rel_err, host_u16, max_rel_err
 
 
@@ -130,3 +131,85 @@ def test_fused_forward_withheld_signal_times_out():
     case = Case(cfg, fused=True, flags=mok.MOK_FLAG_SKIP_ONE_SIGNAL)
     case.layer.forward(case.x_seg, case.logits, case.out_seg)
     assert mok.mok_device_status(case.layer.ws) == 8
+
+
+def _expected_tiles(sched, M):
+    """The oracle's minibatch cut (rows [jM, (j+1)M) of the expert-ordered stream, one ring
+    slot each) intersected with each expert's rows, in GEMM tiles of at most 256 rows: tiles
+    never straddle an expert or a minibatch. Ordered by minibatch, then expert, then row."""
+    out = []
+    for j in range(sched.J):
+        rows = mo.minibatch_rows(sched, j)
+        for e in range(len(sched.counts)):
+            lo, hi = int(sched.offsets[e]), int(sched.offsets[e]) + int(sched.counts[e])
+            r0, r1 = max(rows.start, lo), min(rows.stop, hi)
+            for q in range(r0, r1, 256):
+                out.append((j, e, q, min(256, r1 - q)))
+    return np.array(out, dtype=np.int64).reshape(-1, 4)
+
+
+@pytest.mark.parametrize("name,M,dtype", [("tiny4", 64, "bf16"), ("tiny4", 96, "mxfp8"),
+                                          ("dsv3", 2368, "bf16")])
+def test_tile_table_is_the_oracles_minibatch_cut(name, M, dtype):
+    cfg = (datagen.CONFIGS["tiny"].replace(S=4, T=256, x_std=1.0) if name == "tiny4"
+           else datagen.CONFIGS[name]).replace(M=M, dtype=dtype)
+    case = Case(cfg, fused=True)
+    _fused(case)
+    got = case.layer.tiles().numpy().astype(np.int64)
+    idx, _ = mo.topk_gating(case.logits_h, cfg.K)
+    sched = mo.schedule(idx, cfg.e0, cfg.E_loc, M, 32 if dtype == "mxfp8" else 1)
+    exp = _expected_tiles(sched, M)
+    print(f"  {len(got)} tiles over {sched.J} minibatches")
+    assert np.array_equal(got, exp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_results_do_not_depend_on_the_cu_split(dtype):
+    """The share of compute units given to dispatch changes only who does the work: forward and
+    backward outputs are bit-identical for every split."""
+    from tests._gpu import BwdCase
+    cfg = datagen.CONFIGS["tiny"].replace(S=4, T=512, H=1024, I=512, M=128, x_std=1.0, dtype=dtype)
+    ring = 2 * mok.query_sizes(mok.desc_from_config(cfg)).ring_min_bytes
+    ref = None
+    for cus in (8, 16, 40, 96):
+        case = BwdCase(cfg, fused=True, comm_cus=cus, ring_bytes=ring)
+        case.run(fused=True)
+        res = case.grads() + [case.out.clone()]
+        if ref is None:
+            ref = res
+        else:
+            for a, b in zip(ref, res):
+                assert torch.equal(a, b), cus
+
+
+def test_layer_calls_do_not_synchronise_with_the_host():
+    """mok_layer_fwd and mok_layer_bwd only enqueue work: queued behind a long GPU sleep, both
+    host calls return while the stream is still busy, and the results are those of an
+    unobstructed run."""
+    import time
+    from tests._gpu import BwdCase
+    cfg = datagen.CONFIGS["tiny"].replace(S=4, T=256, M=64, x_std=1.0)
+    case = BwdCase(cfg, fused=True)
+    case.run(fused=True)
+    ref = case.grads() + [case.out.clone()]
+    # calibrate torch.cuda._sleep's cycle count to about 0.5 s
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(); torch.cuda._sleep(10_000_000); b.record(); torch.cuda.synchronize()
+    cycles = int(10_000_000 * 500.0 / max(a.elapsed_time(b), 1e-3))
+    L = case.layer
+    torch.cuda._sleep(cycles)
+    t0 = time.perf_counter()
+    L.forward(case.x_seg, case.logits, case.out_seg)
+    mok.mok_layer_bwd(case.d, case.dout_seg, case.x_seg, L.w, L.idx, L.p, L.saved, L.ring,
+                      L.slots, case.dx_seg, case.dp, case.dlogits, case.dwg, case.dwu, case.dwd,
+                      case.bws)
+    host_s = time.perf_counter() - t0
+    done = torch.cuda.Event()
+    done.record()
+    busy = not done.query()
+    torch.cuda.synchronize()
+    print(f"  host time of both calls {host_s * 1e3:.2f} ms behind a ~500 ms GPU sleep")
+    assert busy and host_s < 0.25
+    assert mok.mok_device_status(L.ws) == 0
+    for x, y in zip(ref, case.grads() + [case.out.clone()]):
+        assert torch.equal(x, y)

@@ -181,3 +181,11 @@ def test_quantised_operands_come_from_fp32_values():
         assert 272 < v * 512 < 273
         assert mx.fake_quant(np.full(32, bf(v)))[0] == 0.5
         assert mx.fake_quant(np.full(32, np.float32(v)).astype(np.float64))[0] == 0.5625
+
+
+def test_parallel_quantiser_slices_give_identical_values():
+    v = np.random.default_rng(3).standard_normal((100, 96)) * np.exp2(np.arange(96) % 7)
+    for axis in (0, 1):
+        assert np.array_equal(mx.fake_quant(v[:96 if axis == 0 else 100], axis=axis, workers=5),
+                              mx.fake_quant(v[:96 if axis == 0 else 100], axis=axis))
+    assert np.array_equal(mx.fake_quant_rows_padded(v, workers=3), mx.fake_quant_rows_padded(v))

@@ -434,3 +434,29 @@ def test_mxfp8_backward_close_to_bf16_backward():
         assert rel(getattr(bm, name), getattr(bb, name)) < 0.08, name
     # dlogits = p (dp - sum p dp) subtracts nearly equal terms, which magnifies the error.
     assert rel(bm.dlogits, bb.dlogits) < 0.2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_expert_wgrad_rows_match_full_backward(dtype):
+    """The per-expert sampled weight-gradient rows (used to check full-size runs) equal the
+    corresponding rows of the whole backward, for every expert of a multi-expert layer with
+    ragged per-expert row counts."""
+    cfg = datagen.CONFIGS["tiny"].replace(S=2, T=96, E=8, K=3, e0=2, E_loc=3, x_std=1.0,
+                                          dtype=dtype)
+    X = mo.decode_bf16(datagen.x_all(cfg))
+    dO = mo.decode_bf16(datagen.dout_all(cfg))
+    L = datagen.logits(cfg)
+    W = mo.weights_from_bits(datagen.weights(cfg), dtype)
+    align = 32 if dtype == "mxfp8" else 1
+    fw = mo.forward(lambda r: X[r], L, W, cfg.K, cfg.e0, cfg.E_loc, 64, align)
+    bw = mo.backward(fw, lambda r: dO[r], W, cfg.K, cfg.e0, cfg.E_loc, cfg.E)
+    gi = np.array([0, 5, 77, cfg.I - 1]); hi = np.array([1, 64, cfg.H - 1])
+    for e in range(cfg.E_loc):
+        lo, c = int(fw.sched.offsets[e]), int(fw.sched.counts[e])
+        pairs = fw.sched.perm[lo:lo + c]
+        n = pairs // cfg.K
+        p_rows = fw.p.reshape(-1)[pairs]
+        dwg, dwu, dwd = mo.expert_wgrad_rows(X[n], dO[n], p_rows, W, e, gi, hi, workers=2)
+        assert np.allclose(dwg, bw.dwg[e][gi], rtol=1e-12, atol=1e-14)
+        assert np.allclose(dwu, bw.dwu[e][gi], rtol=1e-12, atol=1e-14)
+        assert np.allclose(dwd, bw.dwd[e][hi], rtol=1e-12, atol=1e-14)
