@@ -82,8 +82,12 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kMaxXcd - 1);  // HW_REG_XCC_ID
 }
 
-// Invalidate this CU's vector L1 so later loads see data other CUs of the XCD stored to L2.
-__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
+// Acquire at agent scope after a counter wait, so later loads see what other CUs of the XCD
+// stored to L2: on gfx950 this invalidates the CU's vector L1 (buffer_inv sc1). A
+// workgroup-scope invalidate (buffer_inv sc0) is not enough: a CU that stored rows of a ring
+// slot earlier (every workgroup gathers the first row tiles) kept those lines in its L1 and
+// read them back, stale, when the slot held a later tile.
+__device__ __forceinline__ void l1_invalidate() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Thread 0 waits until *p >= target (bounded); returns false (for the whole workgroup) if the
 // wait failed or another worker already reported an error.
