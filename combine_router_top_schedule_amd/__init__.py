@@ -22,7 +22,8 @@ MOK_BF16, MOK_MXFP8 = 0, 1
 MOK_FLAG_SKIP_ONE_SIGNAL = 0x1
 STATUS = {0: "MOK_OK", 1: "MOK_ERR_NULL", 2: "MOK_ERR_SHAPE", 3: "MOK_ERR_DTYPE",
           4: "MOK_ERR_ALIGN", 5: "MOK_ERR_WORKSPACE", 6: "MOK_ERR_RING", 7: "MOK_ERR_HIP",
-          8: "MOK_ERR_DEVICE_TIMEOUT", 9: "MOK_ERR_UNSUPPORTED"}
+          8: "MOK_ERR_DEVICE_TIMEOUT", 9: "MOK_ERR_UNSUPPORTED", 10: "MOK_ERR_SCRATCH"}
+MOK_SCRATCH_BYTES = 1 << 20
 
 
 class MokDesc(ctypes.Structure):
@@ -70,6 +71,7 @@ _SIGS = {
                                           ctypes.POINTER(ctypes.c_size_t)]),
     "mok_two_wave_floor": (ctypes.c_int64, [ctypes.c_int32] * 4),
     "mok_schedule": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P, _P]),
+    "mok_schedule_noalloc": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P]),
     "mok_dispatch": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P]),
     "mok_expert_ffn": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
                                       _P, _P, _P, _P]),
@@ -197,6 +199,13 @@ def mok_schedule(d: MokDesc, logits, topk_idx, topk_p, saved, ws, stream=None):
     _need_cuda(logits, topk_idx, topk_p, saved, ws)
     _check("mok_schedule", lib().mok_schedule(ctypes.byref(d), _ptr(logits), _ptr(topk_idx),
                                               _ptr(topk_p), _ptr(saved), _ptr(ws), _stream(stream)))
+
+
+def mok_schedule_noalloc(d: MokDesc, logits, topk_idx, topk_p, saved, stream=None):
+    _need_cuda(logits, topk_idx, topk_p, saved)
+    _check("mok_schedule_noalloc", lib().mok_schedule_noalloc(ctypes.byref(d), _ptr(logits),
+                                                              _ptr(topk_idx), _ptr(topk_p),
+                                                              _ptr(saved), _stream(stream)))
 
 
 def mok_dispatch(d: MokDesc, saved, x_seg, xd, ws, stream=None):

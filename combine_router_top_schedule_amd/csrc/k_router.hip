@@ -253,6 +253,7 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
 // so they are read in k_place (a later launch on the same stream).
 struct PlaceArgs {
   const int32_t* idx;
+  const int32_t* err;    // the router's error word (workspace)
   int32_t* hdr;
   int32_t* perm;
   int32_t* tokpos;
@@ -279,6 +280,7 @@ __global__ __launch_bounds__(256) void k_place(PlaceArgs a) {
       for (int e = 0; e <= a.El; ++e) a.hdr[kHdrOffsets + e] = s_off[e];
       a.hdr[kHdrP] = P;
       a.hdr[kHdrRows] = off;
+      a.hdr[kHdrStatus] = *a.err;
     }
   }
   __syncthreads();
@@ -376,7 +378,7 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
   else hipLaunchKernelGGL(k_topk_scan<16>, dim3(L.topk_blocks), dim3(256), 0, s, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  PlaceArgs pa{idx, hdr, reinterpret_cast<int32_t*>(saved + L.sv_perm),
+  PlaceArgs pa{idx, wsh + kWsError, hdr, reinterpret_cast<int32_t*>(saved + L.sv_perm),
                reinterpret_cast<int32_t*>(saved + L.sv_tokpos),
                reinterpret_cast<int32_t*>(saved + L.sv_pcode), L.NK,
                L.rows_max, L.K, L.e0, L.El, L.row_align};
@@ -384,6 +386,30 @@ hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, flo
   if (pblocks > 4096) pblocks = 4096;
   hipLaunchKernelGGL(k_place, dim3(pblocks), dim3(256), 0, s, pa);
   return hipGetLastError();
+}
+
+// ---- the router without a caller workspace ---------------------------------------------------
+// Its scratch (error word, scan ticket, look-back states) lives in this array, one copy per
+// device, kept until the process ends. Host code never passes `scratch` itself to a kernel (on
+// the host it names a stand-in, not device memory): it passes the address hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[MOK_SCRATCH_BYTES];
+
+mok_status launch_router_noalloc(const Layout& L, const float* logits, int32_t* idx, float* p,
+                                 uint8_t* saved, hipStream_t s) {
+  if (router_ws_bytes(L) > int64_t(MOK_SCRATCH_BYTES)) return MOK_ERR_SCRATCH;
+  static std::atomic<uint8_t*> ptr[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOK_ERR_HIP;
+  uint8_t* base = ptr[dev].load(std::memory_order_acquire);
+  if (!base) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MOK_ERR_HIP;
+    base = static_cast<uint8_t*>(q);
+    ptr[dev].store(base, std::memory_order_release);
+  }
+  // launch_router clears the header, the scan ticket and the look-back states it uses.
+  return launch_router(L, logits, idx, p, saved, base, s) == hipSuccess ? MOK_OK : MOK_ERR_HIP;
 }
 
 hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s) {

@@ -90,6 +90,7 @@ const char* mok_status_str(mok_status s) {
     case MOK_ERR_HIP: return "HIP runtime or launch failure";
     case MOK_ERR_DEVICE_TIMEOUT: return "device-side bounded wait expired";
     case MOK_ERR_UNSUPPORTED: return "unsupported";
+    case MOK_ERR_SCRATCH: return "shape needs more than the static scratch of mok_schedule_noalloc";
   }
   return "unknown status";
 }
@@ -161,6 +162,18 @@ mok_status mok_schedule(const mok_desc* desc, const float* logits_dev, int32_t* 
   // nothing in the ring for the backward)
   return hip_status(launch_router(L, logits_dev, topk_idx_dev, topk_p_dev,
                                   static_cast<uint8_t*>(saved_dev), static_cast<uint8_t*>(ws_dev), s));
+}
+
+mok_status mok_schedule_noalloc(const mok_desc* desc, const float* logits_dev,
+                                int32_t* topk_idx_dev, float* topk_p_dev, void* saved_dev,
+                                void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!logits_dev || !topk_idx_dev || !topk_p_dev || !saved_dev) return MOK_ERR_NULL;
+  if (!aligned16(logits_dev) || !aligned16(saved_dev)) return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  return launch_router_noalloc(L, logits_dev, topk_idx_dev, topk_p_dev,
+                               static_cast<uint8_t*>(saved_dev), as_stream(stream));
 }
 
 mok_status mok_dispatch(const mok_desc* desc, const void* saved_dev, const void* const* x_seg_dev,

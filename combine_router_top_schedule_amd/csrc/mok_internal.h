@@ -46,6 +46,7 @@ enum SavedHeader : int {
   kHdrRows = 1,     // expert-order rows (P + per-expert padding in MXFP8 mode)
   kHdrU = 2,        // touched tokens
   kHdrUm = 3,       // touched tokens with more than one local pair
+  kHdrStatus = 4,   // copy of the router's device-side status (0 if its scan finished)
   kHdrCounts = 16,  // [E_loc]
   kHdrOffsets = 96, // [E_loc + 1]
   kHdrWords = 192,
@@ -275,6 +276,14 @@ hipError_t launch_fill_ranges(const FillRange* r, int count, hipStream_t s);
 hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, float* p,
                          uint8_t* saved, uint8_t* ws, hipStream_t s);
 hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s);
+// Bytes of the workspace the router alone uses (header and look-back scan state).
+inline int64_t router_ws_bytes(const Layout& L) {
+  return L.ws_state + align_up(4 * int64_t(L.topk_blocks) * (L.El + 2), 256);
+}
+// The router with its workspace in the library's static per-device scratch (no allocation):
+// MOK_ERR_SCRATCH when router_ws_bytes exceeds it.
+mok_status launch_router_noalloc(const Layout& L, const float* logits, int32_t* idx, float* p,
+                                 uint8_t* saved, hipStream_t s);
 hipError_t launch_dispatch(const Layout& L, const uint8_t* saved, const void* const* x_seg,
                            uint8_t* xd, hipStream_t s);
 // skip_sole: leave out tokens with a single local pair (their row was written by the GEMM

@@ -53,7 +53,9 @@ typedef enum {
   MOK_ERR_RING = 6,            /* ring_bytes below mok_sizes.ring_min_bytes              */
   MOK_ERR_HIP = 7,             /* a HIP runtime call or kernel launch failed             */
   MOK_ERR_DEVICE_TIMEOUT = 8,  /* a device-side bounded wait ran out (see ws error word) */
-  MOK_ERR_UNSUPPORTED = 9      /* not supported on this device                           */
+  MOK_ERR_UNSUPPORTED = 9,     /* not supported on this device                           */
+  MOK_ERR_SCRATCH = 10         /* the shape needs more than the static scratch of
+                                  mok_schedule_noalloc (MOK_SCRATCH_BYTES)                 */
 } mok_status;
 
 typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
@@ -104,6 +106,7 @@ typedef struct {
   int64_t slot_bytes;    /* bytes of one activation slot (g|u and h of 256 rows)            */
   /* Layout of the schedule table inside `saved` (byte offsets). Words 0..191 are a header:
    * [0] P (local pairs), [1] rows (P plus MXFP8 padding), [2] U (touched tokens),
+   * [3] touched tokens with several local pairs, [4] the router's device-side status,
    * [16 + e] count of local expert e, [96 + e] first row of expert e (e = 0..E_loc). */
   int64_t perm_offset;    /* int32 [rows_max]: expert-order row -> pair id (-1: pad row)     */
   int64_t tokpos_offset;  /* int32 [N*K]: pair id -> row (-1: not local)                     */
@@ -173,6 +176,24 @@ int64_t mok_two_wave_floor(int32_t cus, int32_t tile_m, int32_t tile_n, int32_t 
  *   ws_dev       scratch (ws_bytes) */
 mok_status mok_schedule(const mok_desc* desc, const float* logits_dev, int32_t* topk_idx_dev,
                         float* topk_p_dev, void* saved_dev, void* ws_dev, void* stream);
+
+/* mok_schedule for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same outputs, bit for bit, with
+ * the router's scratch (its error word and the look-back scan state, 4 * ceil(N/256) *
+ * (E_loc + 2) bytes plus 256) taken from a static array of MOK_SCRATCH_BYTES that the library
+ * holds on each device it runs on until the process ends, instead of a caller's workspace.
+ *   - No allocation or free happens in the call. The first call on a device looks the array up
+ *     (hipGetSymbolAddress) with that device current.
+ *   - Returns MOK_ERR_SCRATCH, before launching anything, when N and E_loc need more scratch.
+ *   - Every call on one device shares that device's array: calls that overlap in time on one
+ *     device (other streams, other host threads) race and give undefined results; calls ordered
+ *     on one stream are fine. The call clears what it needs before use.
+ *   - A device-side failure (the scan's bounded wait) is recorded in int32 word 4 of saved_dev's
+ *     header (mok_device_status, which reads a workspace, does not see it). */
+#define MOK_SCRATCH_BYTES (1u << 20)
+mok_status mok_schedule_noalloc(const mok_desc* desc, const float* logits_dev,
+                                int32_t* topk_idx_dev, float* topk_p_dev, void* saved_dev,
+                                void* stream);
 
 /* Pull dispatch, staged form: the receiving side reads every routed token row from its
  * source segment and writes it in expert order ("Mixture-of-Kittens (MoK)", section on pull

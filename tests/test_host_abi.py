@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_status_strings():
     assert mok.abi_version() == 3
-    for code in range(10):
+    for code in range(11):
         assert mok.lib().mok_status_str(code)
 
 
