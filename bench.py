@@ -19,6 +19,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -30,51 +31,81 @@ PEAK_BF16_TFLOPS = 2516.6       # dense BF16 MFMA: 256 CU x 2.4 GHz x 4096 flop/
 PEAK_MXFP8_TFLOPS = 5033.2
 PEAK_HBM_GBS = 8000.0
 
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic_layer_fwd_dsv3_bf16.md")
 CSRC = os.path.join(HERE, "combine_router_top_schedule_amd", "csrc")
+HEADER = os.path.join("..", "..", "include", "mok.h")
+
+# The three GEMM launches of a step, with the sources each is compiled from (its file and every
+# header it includes) and the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of its HBM
+# traffic on the DeepSeek-V3 BF16 workload. A stored figure is used only while the kernel's
+# sources hash to the digest recorded with it.
+KERNELS = {
+    "k_layer_fwd": dict(trace=1, flop_per_phi=6.0,
+                        what="fused forward: dispatch, gate/up + SwiGLU, down + push",
+                        sources=("k_fused.hip", "k_ffn.h", "k_gemm.h", "mok_rows.h",
+                                 "mok_device.h", "mok_internal.h", HEADER),
+                        traffic="traffic_layer_fwd_dsv3_bf16.md"),
+    "k_bwd_gemms<0>": dict(trace=2, flop_per_phi=4.0,
+                           what="a-GEMM with dp + SwiGLU backward, and dW_down",
+                           sources=("k_bwd.hip", "k_bwd.h", "k_ffn.h", "k_gemm.h", "mok_rows.h",
+                                    "mok_device.h", "mok_internal.h", HEADER),
+                           traffic="traffic_bwd_gemm1_dsv3_bf16.md"),
+    "k_bwd_gemms<1>": dict(trace=3, flop_per_phi=8.0,
+                           what="dx GEMM + push, and dW_gate, dW_up",
+                           sources=("k_bwd.hip", "k_bwd.h", "k_ffn.h", "k_gemm.h", "mok_rows.h",
+                                    "mok_device.h", "mok_internal.h", HEADER),
+                           traffic="traffic_bwd_gemm2_dsv3_bf16.md"),
+}
 
 
-# The sources the fused forward kernel (k_layer_fwd) is compiled from: its file and every header
-# it includes. A stored HBM-traffic figure for that kernel is valid only for these.
-FUSED_FWD_SOURCES = ("k_fused.hip", "k_ffn.h", "k_gemm.h", "mok_rows.h", "mok_device.h",
-                     "mok_internal.h", os.path.join("..", "..", "include", "mok.h"))
-
-
-def csrc_digest() -> str:
-    """Digest of the fused forward kernel's sources."""
+def csrc_digest(sources) -> str:
+    """Digest of a kernel's sources."""
     h = hashlib.sha256()
-    for name in FUSED_FWD_SOURCES:
+    for name in sources:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(os.path.basename(name).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch of the fused forward kernel from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when it is absent or was taken on other kernel sources."""
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from its committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when it is absent or was taken on other kernel sources."""
+    k = KERNELS[kernel]
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(os.path.join(HERE, "profiles", k["traffic"])).read()
     except OSError:
         return None
     m = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
     d = re.search(r"^csrc_digest:\s*([0-9a-f]+)", text, re.M)
-    if not m or not d or d.group(1) != csrc_digest():
+    if not m or not d or d.group(1) != csrc_digest(k["sources"]):
         return None
     return int(m.group(1))
 
 
-def cpu_baseline(cfg, target_s: float = 12.0) -> dict:
-    """The oracle (fp64 numpy) forward + backward on the tokens of the first n source segments,
-    on this host's cores. n is sized from a one-segment run so that the timed sample takes about
-    `target_s`; n segments are n/S of a step's work, so oracle tokens/s = T * n / (S * t)."""
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        m = re.search(r"^Model name:\s*(.+)$", out, re.M)
+        return m.group(1).strip() if m else "unknown"
+    except Exception:
+        return "unknown"
+
+
+def cpu_baseline(cfg, target_s: float = 4.0) -> dict:
+    """The oracle (fp64 numpy, untuned) forward + backward on the tokens of the first n source
+    segments, on this host's cores: n is sized from a one-segment run so one timed run takes about
+    `target_s`, and the value is the median of 3 runs (n segments are n/S of a step's work, so
+    oracle tokens/s = T * n / (S * t)). Then one run of one segment with the BLAS pool held to a
+    single thread."""
     import math
+    import statistics
     import numpy as np
     import datagen
     from oracle import moe_oracle as mo
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         cores = os.cpu_count() or 1
     W = mo.weights_from_bits(datagen.weights(cfg), cfg.dtype)
     align = 32 if cfg.dtype == "mxfp8" else 1
@@ -91,13 +122,24 @@ def cpu_baseline(cfg, target_s: float = 12.0) -> dict:
 
     n = 1
     t, pairs = run(1)
-    while t < target_s and n < cfg.S:
-        n = min(cfg.S, max(2 * n, math.ceil(n * target_s / max(t, 1e-3))))
+    if t < target_s and cfg.S > 1:
+        n = min(cfg.S, max(2, math.ceil(target_s / max(t, 1e-3))))
+    times = []
+    for _ in range(3):
         t, pairs = run(n)
+        times.append(t)
+    t = statistics.median(times)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1, _ = run(1)
+        one = round(cfg.T / (cfg.S * t1), 3)
     return {"value": round(cfg.T * n / (cfg.S * t), 3), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "one_thread_value": one,
             "sample": f"oracle fwd+bwd on source segments 0..{n - 1} of {cfg.S} ({n * cfg.T} "
-                      f"tokens, {pairs} local pairs) in {t:.2f} s = {n}/{cfg.S} of a step"}
+                      f"tokens, {pairs} local pairs): median of 3 runs "
+                      f"{', '.join(f'{x:.2f}' for x in times)} s = {n}/{cfg.S} of a step; "
+                      f"one_thread_value: segment 0 alone with one BLAS thread"}
 
 
 def main() -> int:
@@ -111,6 +153,8 @@ def main() -> int:
                     help="override the workload's minibatch rows M (ring granularity)")
     ap.add_argument("--forward-only", action="store_true",
                     help="time mok_layer_fwd alone (minibatch sweeps); not the headline metric")
+    ap.add_argument("--tune", action="store_true",
+                    help="run mok_autotune first (minibatch and dispatch-CU split for this shape)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is one "
@@ -169,6 +213,13 @@ def main() -> int:
         if not args.forward_only:
             L.backward(dout_seg, x_seg, dx_seg, dp, dlogits, dwg, dwu, dwd)
 
+    tuning = None
+    if args.tune:
+        print("[bench] autotune", file=sys.stderr, flush=True)
+        tuned, best, table = L.autotune(x_seg, logits, out_seg, reps=3)
+        tuning = {"minibatch": tuned.minibatch_tokens, "comm_cus": tuned.comm_cus,
+                  "fwd_ms": round(best, 4),
+                  "table": [[m, c, round(t, 4)] for m, c, t in table]}
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -206,27 +257,36 @@ def main() -> int:
     if st != 0:
         raise RuntimeError(f"device status {mok.STATUS.get(st, st)} after the timed steps")
 
-    # ---- after the timed region: the other kernel groups, one untimed step each ----
-    groups = {}
-    for name, kid in (() if args.forward_only else
-                      (("a_gemm_and_dwd", mok.MOK_TRACE_BWD_GEMM1),
-                       ("dx_gemm_and_dwg_dwu", mok.MOK_TRACE_BWD_GEMM2))):
-        (a, b), = events(1)
-        mok.mok_trace_kernel(kid, a, b)
-        step()
-        torch.cuda.synchronize()
-        mok.mok_trace_kernel(mok.MOK_TRACE_NONE)
-        groups[name] = round(a.elapsed_time(b), 4)
+    # ---- after the timed region: the two backward GEMM launches, each over K more steps ----
+    kernel_ms = {"k_layer_fwd": fused_ms}
+    if not args.forward_only:
+        for name in ("k_bwd_gemms<0>", "k_bwd_gemms<1>"):
+            ev = events(K)
+            for i in range(K):
+                mok.mok_trace_kernel(KERNELS[name]["trace"], *ev[i])
+                step()
+            torch.cuda.synchronize()
+            mok.mok_trace_kernel(mok.MOK_TRACE_NONE)
+            kernel_ms[name] = sum(a.elapsed_time(b) for a, b in ev) / K
+            del ev
 
     P = int(L.header()[0])
     HI = cfg.H * cfg.I
-    fwd_flop = 6.0 * P * HI
     step_flop = (6.0 if args.forward_only else 18.0) * P * HI
     peak = PEAK_MXFP8_TFLOPS if mx else PEAK_BF16_TFLOPS
-    achieved = fwd_flop / (fused_ms * 1e-3) / 1e12
-    # the committed counter summary covers the default DeepSeek-V3 BF16 run only
-    traffic = stored_traffic() if (args.workload == "dsv3" and not args.minibatch
-                                   and not args.forward_only) else None
+    # the committed counter summaries cover the default DeepSeek-V3 BF16 run only
+    default_run = args.workload == "dsv3" and not args.minibatch and not args.forward_only
+    kernels = {}
+    for name, t in kernel_ms.items():
+        k = KERNELS[name]
+        ach = k["flop_per_phi"] * P * HI / (t * 1e-3) / 1e12
+        traffic = stored_traffic(name) if default_run else None
+        kernels[name] = {"what": k["what"], "avg_ms": round(t, 4), "tflops": round(ach, 1),
+                         "frac_of_mfma_peak": round(ach / peak, 4), "traffic_bytes": traffic,
+                         "hbm_frac": (round(traffic / (t * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)
+                                      if traffic else None)}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    dk = kernels[dominant]
     tokens_s = cfg.T / (ms * 1e-3)
     line = {
         "metric": ("MoE layer tokens/sec fwd only on 1 MI355X (minibatch sweep)" if args.forward_only
@@ -248,15 +308,25 @@ def main() -> int:
                    "local_experts": cfg.E_loc, "segments": cfg.S,
                    "tokens_per_segment": cfg.T, "minibatch": cfg.M,
                    "ring_mib": cfg.ring_bytes >> 20, "pairs": P},
-        "roofline": {"bound": "mfma", "kernel": "k_layer_fwd (fused forward)",
-                     "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "roofline": {"bound": "mfma", "kernel": f"{dominant} ({dk['what']})",
+                     "achieved": dk["tflops"], "peak": peak, "unit": "TFLOP/s",
+                     "frac": dk["frac_of_mfma_peak"], "traffic": dk["traffic_bytes"],
+                     "traffic_hbm_frac": dk["hbm_frac"]},
         "detail": {"pairs_per_s": round(P / (ms * 1e-3), 1),
                    "step_tflops": round(step_flop / (ms * 1e-3) / 1e12, 1),
                    "step_frac_of_mfma_peak": round(step_flop / (ms * 1e-3) / 1e12 / peak, 4),
-                   "fused_fwd_ms": round(fused_ms, 4), "bwd_group_ms": groups,
-                   "wall_s": round(wall, 3)},
+                   "kernels": kernels, "wall_s": round(wall, 3)},
     }
+    if tuning:
+        line["detail"]["autotune"] = tuning
+        line["config"]["minibatch"] = tuning["minibatch"]
+        line["config"]["comm_cus"] = tuning["comm_cus"]
+    # release what this run created on the device before the interpreter exits (the library's
+    # trace hook is already off): events, buffers and the layer
+    del kev, t0, t1
+    del L, x, dout, logits, out, dx, dp, dlogits, dwg, dwu, dwd, x_seg, out_seg, dout_seg, dx_seg
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline and not args.forward_only:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg)

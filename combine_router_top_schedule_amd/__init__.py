@@ -57,6 +57,11 @@ class MokWeights(ctypes.Structure):
                                   "wd_s", "wgt_q", "wgt_s", "wut_q", "wut_s", "wdt_q", "wdt_s")]
 
 
+class MokTuneResult(ctypes.Structure):
+    _fields_ = [("minibatch_tokens", ctypes.c_int32), ("comm_cus", ctypes.c_int32),
+                ("ms", ctypes.c_float)]
+
+
 class MokWeightGrads(ctypes.Structure):
     _fields_ = [("dwg", _P), ("dwu", _P), ("dwd", _P)]
 
@@ -84,6 +89,11 @@ _SIGS = {
     "mok_quantize_mx": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
                                        ctypes.c_int32, _P, _P, _P]),
     "mok_device_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
+    "mok_autotune": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
+                                    _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                    ctypes.POINTER(MokDesc), ctypes.POINTER(ctypes.c_float),
+                                    ctypes.POINTER(MokTuneResult), ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32)]),
     "mok_device_cus": (ctypes.c_int32, []),
     "mok_trace_kernel": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
 }
@@ -255,6 +265,23 @@ def mok_quantize_mx(src, transpose: bool, codes, scales, stream=None):
     batch, rows, cols = (1,) + shape if len(shape) == 2 else shape
     _check("mok_quantize_mx", lib().mok_quantize_mx(batch, rows, cols, _ptr(src), int(transpose),
                                                     _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def mok_autotune(d: MokDesc, x_seg, logits, w: MokWeights, out_seg, topk_idx, topk_p, saved,
+                 ring, slots, ws, reps: int = 3, stream=None):
+    """Returns (tuned descriptor, best ms, [(minibatch, comm_cus, ms), ...])."""
+    _need_cuda(x_seg, logits, out_seg, topk_idx, topk_p, saved, ring, slots, ws)
+    tuned, best = MokDesc(), ctypes.c_float()
+    res = (MokTuneResult * 64)()
+    n = ctypes.c_int32(0)
+    _check("mok_autotune", lib().mok_autotune(ctypes.byref(d), _ptr(x_seg), _ptr(logits),
+                                              ctypes.byref(w), _ptr(out_seg), _ptr(topk_idx),
+                                              _ptr(topk_p), _ptr(saved), _ptr(ring), _ptr(slots),
+                                              _ptr(ws), _stream(stream), int(reps),
+                                              ctypes.byref(tuned), ctypes.byref(best), res, 64,
+                                              ctypes.byref(n)))
+    return tuned, float(best.value), [(r.minibatch_tokens, r.comm_cus, float(r.ms))
+                                      for r in res[:n.value]]
 
 
 def mok_device_status(ws, stream=None) -> int:

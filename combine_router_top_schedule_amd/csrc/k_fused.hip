@@ -357,11 +357,13 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   GemmLds& sm = *reinterpret_cast<GemmLds*>(smem);
   layer_fwd_body<MX>(a, sm);
+  // The error word is only ever written by device-scope atomics, which have completed once the
+  // writer's vmcnt reaches zero; so when the exit count is full, every failure is in the word.
+  // (No release is needed: the ring record's plain stores are read by later kernels.)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int done = __hip_atomic_fetch_add(a.cnt + kCntExit, 1, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+    const int done = add_relaxed(a.cnt + kCntExit, 1);
     if (done == int(gridDim.x) - 1 && ld_relaxed(a.err) == 0) {
       a.rhdr[kRhCapt] = a.capa;
       a.rhdr[kRhTiles] = *a.ntiles;

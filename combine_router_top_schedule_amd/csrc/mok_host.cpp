@@ -3,8 +3,10 @@
 // except mok_device_status synchronises or reads device memory back.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "mok_internal.h"
 
@@ -332,3 +334,79 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
 }
 
 }  // extern "C"
+
+extern "C" mok_status mok_autotune(const mok_desc* desc, const void* const* x_seg_dev,
+                                   const float* logits_dev, const mok_weights* w,
+                                   void* const* out_seg_dev, int32_t* topk_idx_dev,
+                                   float* topk_p_dev, void* saved_dev, void* ring_dev,
+                                   void* slots_dev, void* ws_dev, void* stream, int32_t reps,
+                                   mok_desc* tuned, float* best_ms, mok_tune_result* results,
+                                   int32_t max_results, int32_t* n_results) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!tuned || !best_ms) return MOK_ERR_NULL;
+  if (reps < 1 || reps > 1000 || max_results < 0) return MOK_ERR_SHAPE;
+  if (results && max_results > 0 && !n_results) return MOK_ERR_NULL;
+  const Layout L0 = layout_of(*desc);
+  const int M0 = L0.M;
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t all_rows = align_up(L0.rows_max, 32);
+  std::vector<int> ms_cand = {M0};
+  for (int64_t m : {int64_t(2) * M0, int64_t(4) * M0, all_rows})
+    if (m > ms_cand.back() && m <= (int64_t(1) << 30)) ms_cand.push_back(int(m));
+  std::vector<int> cu_cand;
+  for (int c : {8, 16, 24, 32, 48})
+    if (c < cus / 2) cu_cand.push_back(c);
+  if (cu_cand.empty()) cu_cand.push_back(kXcds);
+  hipStream_t s = as_stream(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return MOK_ERR_HIP;
+  }
+  mok_status out = MOK_OK;
+  float best = -1.f;
+  mok_desc best_d = *desc;
+  int32_t n = 0;
+  for (int m : ms_cand) {
+    for (int c : cu_cand) {
+      mok_desc d = *desc;
+      d.minibatch_tokens = m;
+      d.comm_cus = c;
+      std::vector<float> times;
+      for (int r = 0; r <= reps && out == MOK_OK; ++r) {
+        if (hipEventRecord(e0, s) != hipSuccess) { out = MOK_ERR_HIP; break; }
+        out = mok_layer_fwd(&d, x_seg_dev, logits_dev, w, out_seg_dev, topk_idx_dev, topk_p_dev,
+                            saved_dev, ring_dev, slots_dev, ws_dev, stream);
+        if (out != MOK_OK) break;
+        if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {
+          out = MOK_ERR_HIP;
+          break;
+        }
+        mok_status dev = MOK_OK;
+        if ((out = mok_device_status(ws_dev, stream, &dev)) != MOK_OK) break;
+        if (dev != MOK_OK) { out = dev; break; }
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, e0, e1) != hipSuccess) { out = MOK_ERR_HIP; break; }
+        if (r > 0) times.push_back(t);   // the first call is a warm-up
+      }
+      if (out != MOK_OK) break;
+      std::sort(times.begin(), times.end());
+      const float med = times[times.size() / 2];
+      if (results && n < max_results) results[n] = mok_tune_result{m, c, med};
+      ++n;
+      if (best < 0.f || med < best) {
+        best = med;
+        best_d = d;
+      }
+    }
+    if (out != MOK_OK) break;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (out != MOK_OK) return out;
+  *tuned = best_d;
+  *best_ms = best;
+  if (n_results) *n_results = std::min(n, max_results);
+  return MOK_OK;
+}

@@ -6,9 +6,9 @@ from typing import Optional
 
 import torch
 
-from . import (MOK_MXFP8, desc, mok_combine, mok_dispatch, mok_expert_ffn, mok_layer_bwd,
-               mok_layer_fwd, mok_quantize_mx, mok_schedule, query_sizes, seg_table,
-               weights_struct)
+from . import (MOK_MXFP8, desc, mok_autotune, mok_combine, mok_dispatch, mok_expert_ffn,
+               mok_layer_bwd, mok_layer_fwd, mok_quantize_mx, mok_schedule, query_sizes,
+               seg_table, weights_struct)
 
 
 def _bytes(n, device):
@@ -101,6 +101,16 @@ class MokLayer:
     def forward(self, x_seg, logits, out_seg):
         mok_layer_fwd(self.d, x_seg, logits, self.w, out_seg, self.idx, self.p, self.saved,
                       self.ring, self.slots, self.ws)
+
+    def autotune(self, x_seg, logits, out_seg, reps: int = 3, apply: bool = True):
+        """Time the fused forward over candidate minibatch sizes and dispatch-CU counts (this
+        layer's buffers fit every candidate) and, with `apply`, use the fastest from now on.
+        Returns (tuned descriptor, best ms, all measurements)."""
+        tuned, best, table = mok_autotune(self.d, x_seg, logits, self.w, out_seg, self.idx,
+                                          self.p, self.saved, self.ring, self.slots, self.ws, reps)
+        if apply:
+            self.d = tuned
+        return tuned, best, table
 
     def backward(self, dout_seg, x_seg, dx_seg, dp, dlogits, dwg, dwu, dwd):
         """Backward of the last forward (reads the schedule table, ring and slots it left)."""

@@ -18,7 +18,7 @@
  *   mok_trace_kernel; calls on different streams with different buffers are independent.
  * - Streams: every call is asynchronous and stream-ordered on `stream` (a hipStream_t passed
  *   as void*; NULL is the default stream). No call synchronises the host or copies device
- *   data to the host, except mok_device_status.
+ *   data to the host, except mok_device_status and the tuner mok_autotune.
  * - Errors: argument errors are detected on the host and returned before anything is
  *   launched. A failed launch returns MOK_ERR_HIP. A device-side failure (a bounded wait that
  *   ran out) is recorded in the workspace's error word and reported by mok_device_status.
@@ -278,7 +278,37 @@ mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void
                            int32_t transpose, uint8_t* codes_dev, uint8_t* scales_dev,
                            void* stream);
 
-/* Waits for `stream`, then reads the workspace error word. The only synchronising call. */
+/* One measured configuration of mok_autotune. */
+typedef struct {
+  int32_t minibatch_tokens;   /* M tried                                                      */
+  int32_t comm_cus;           /* dispatch CUs tried                                           */
+  float ms;                   /* median time of mok_layer_fwd over the repetitions            */
+} mok_tune_result;
+
+/* Per-shape tuner of the fused forward's minibatch size and compute-unit split: the pages note
+ * that a different hidden size, top-k or expert count needs a different minibatch and a
+ * different number of communication SMs ("把 MoE 通信延迟从 103μs 压到 18μs", section 05;
+ * section 03 part ② on the minibatch trade-off). Runs mok_layer_fwd, on the caller's inputs and
+ * buffers (sized for `desc`), for every candidate pair
+ *   comm_cus in {8, 16, 24, 32, 48} (clipped to the device), and
+ *   minibatch_tokens in {M, 2M, 4M, all rows} (M = desc's minibatch after its default; larger
+ *   minibatches never need larger buffers),
+ * `reps` times each (after one warm-up call), and writes the fastest into *tuned (a copy of desc
+ * with those two fields set) and its median time into *best_ms. If `results` is not NULL, up to
+ * `max_results` measured candidates are written there and their count to *n_results.
+ * Outputs of the layer do not depend on the choice (the same bit-identical results for every
+ * candidate). Unlike every other call this one SYNCHRONISES the host with `stream` (it
+ * measures): call it once per shape, outside timed regions and graph capture. It allocates no
+ * device memory (HIP events only). A device-side failure aborts with its status. */
+mok_status mok_autotune(const mok_desc* desc, const void* const* x_seg_dev,
+                        const float* logits_dev, const mok_weights* w, void* const* out_seg_dev,
+                        int32_t* topk_idx_dev, float* topk_p_dev, void* saved_dev, void* ring_dev,
+                        void* slots_dev, void* ws_dev, void* stream, int32_t reps,
+                        mok_desc* tuned, float* best_ms, mok_tune_result* results,
+                        int32_t max_results, int32_t* n_results);
+
+/* Waits for `stream`, then reads the workspace error word. The only synchronising call apart
+ * from mok_autotune. */
 mok_status mok_device_status(const void* ws_dev, void* stream, mok_status* out);
 
 /* Number of compute units of the current device (0 if unknown). */

@@ -213,3 +213,30 @@ def test_layer_calls_do_not_synchronise_with_the_host():
     assert mok.mok_device_status(L.ws) == 0
     for x, y in zip(ref, case.grads() + [case.out.clone()]):
         assert torch.equal(x, y)
+
+
+def test_autotune_measures_every_candidate_and_all_give_the_same_output():
+    """mok_autotune times the fused forward over minibatch sizes M, 2M, 4M, all rows and
+    dispatch-CU counts 8 .. 48, returns the fastest, and every candidate produces the same output
+    bit for bit (the choice changes speed only)."""
+    from combine_router_top_schedule_amd.layer import MokLayer
+    cfg = datagen.CONFIGS["tiny"].replace(S=4, T=512, H=1024, I=512, M=128, x_std=1.0)
+    ring = 2 * mok.query_sizes(mok.desc_from_config(cfg)).ring_min_bytes
+    case = Case(cfg, fused=True, ring_bytes=ring)
+    ref = _fused(case)
+    tuned, best, table = case.layer.autotune(case.x_seg, case.logits, case.out_seg, reps=2,
+                                             apply=False)
+    print(f"  tuned M={tuned.minibatch_tokens} comm_cus={tuned.comm_cus} {best:.3f} ms; {table}")
+    Ms = sorted({m for m, _, _ in table})
+    assert Ms[0] == 128 and Ms[1:3] == [256, 512] and len(table) == len(Ms) * 5
+    assert (tuned.minibatch_tokens, tuned.comm_cus) in {(m, c) for m, c, _ in table}
+    assert best == min(t for _, _, t in table)
+    for m, c, _ in table:
+        layer = MokLayer(mok.desc_from_config(cfg, M=m, ring_bytes=ring, comm_cus=c),
+                         staged=False, fused=True)
+        layer.set_weights(case.wg, case.wu, case.wd)
+        case.out.zero_()
+        layer.forward(case.x_seg, case.logits, case.out_seg)
+        torch.cuda.synchronize()
+        assert mok.mok_device_status(layer.ws) == 0
+        assert torch.equal(case.out, ref), (m, c)
