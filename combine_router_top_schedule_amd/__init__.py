@@ -83,6 +83,11 @@ _SIGS = {
     "mok_combine": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P, _P, _P]),
     "mok_layer_fwd": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
                                      _P, _P, _P, _P, _P, _P, _P, _P]),
+    "mok_macro_ws_size": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_size_t)]),
+    "mok_layer_fwd_macro": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.c_int32, _P, _P,
+                                           ctypes.POINTER(MokWeights), _P, _P, _P, _P, _P, _P,
+                                           _P, _P]),
     "mok_layer_bwd": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
                                      _P, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.POINTER(MokWeightGrads), _P, _P]),
@@ -245,6 +250,29 @@ def mok_layer_fwd(d: MokDesc, x_seg, logits, w: MokWeights, out_seg, topk_idx, t
                                                 ctypes.byref(w), _ptr(out_seg), _ptr(topk_idx),
                                                 _ptr(topk_p), _ptr(saved), _ptr(ring),
                                                 _ptr(slots), _ptr(ws), _stream(stream)))
+
+
+def macro_ws_size(d: MokDesc, num_macro: int) -> int:
+    n = ctypes.c_size_t()
+    _check("mok_macro_ws_size", lib().mok_macro_ws_size(ctypes.byref(d), int(num_macro),
+                                                        ctypes.byref(n)))
+    return int(n.value)
+
+
+def mok_layer_fwd_macro(d: MokDesc, x_segs, logits, w: MokWeights, out_segs, topk_idx, topk_p,
+                        saved, ring, slots, ws, stream=None):
+    """Lists (one entry per macrobatch) for every per-call argument."""
+    B = len(x_segs)
+    for lst in (logits, out_segs, topk_idx, topk_p, saved, slots):
+        if len(lst) != B:
+            raise ValueError("one entry per macrobatch in every list")
+        _need_cuda(*lst)
+    _need_cuda(*x_segs, ring, ws)
+    arr = lambda ts: (ctypes.c_void_p * B)(*[_ptr(t) for t in ts])
+    _check("mok_layer_fwd_macro", lib().mok_layer_fwd_macro(
+        ctypes.byref(d), B, arr(x_segs), arr(logits), ctypes.byref(w), arr(out_segs),
+        arr(topk_idx), arr(topk_p), arr(saved), _ptr(ring), arr(slots), _ptr(ws),
+        _stream(stream)))
 
 
 def mok_layer_bwd(d: MokDesc, dout_seg, x_seg, w: MokWeights, topk_idx, topk_p, saved, ring,

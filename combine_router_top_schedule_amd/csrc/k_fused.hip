@@ -43,29 +43,38 @@ namespace {
 
 constexpr int kMaxXcd = kXcds;
 
-struct FusedArgs {
-  const int32_t* hdr;
+// One macrobatch (one layer call) of a launch: its schedule table, tile table, token segments,
+// push records and the ring record it leaves for its backward.
+struct MacroArgs {
   const int32_t* perm;
   const MTile* tiles;
-  const int32_t* ntiles;
+  const int32_t* ntiles;     // device word: tiles in this macrobatch's table
   const uint16_t* const* x_seg;
+  PushTarget push;           // down-GEMM rows: pair slots, or the output row of a token's only
+                             // local pair
+  int32_t* rhdr;             // ring state for the backward (in saved): header,
+  MTile* rtiles;             //   copy of the tile table,
+  int32_t* rslot;            //   activation slot id (x * capa + slot) of every tile,
+  int32_t* rowner;           //   the tile of this macrobatch that last used every slot (-1:
+                             //   the slot's last tile belongs to another macrobatch)
+};
+
+struct FusedArgs {
   uint8_t* ring;
   int64_t ring_share;        // bytes of the ring owned by one XCD
   int64_t xsb, asb;          // bytes of one gather slot / one activation slot
   int capx, capa;            // gather slots / activation slots per XCD
   FfnShape s;
   FfnWeights w;
-  PushTarget push;           // down-GEMM rows: pair slots, or the output row of a token's only
-                             // local pair
-  int32_t* cnt;              // [kCntWords + 3 * tiles_max]
+  int32_t* cnt;              // [kCntWords + (3 + kXcds) * B * tiles_max]
   int32_t* err;
-  int32_t* rhdr;             // ring state for the backward (in saved): header,
-  MTile* rtiles;             //   copy of the tile table,
-  int32_t* rslot;            //   activation slot id (x * capa + slot) of every tile,
-  int32_t* rowner;           //   last tile written to every slot
-  int64_t tiles_max;
+  int64_t tiles_max;         // per macrobatch
+  int B;                     // macrobatches, each a whole layer call; their row tiles form one
+                             // list in macrobatch order
+  MacroArgs mb[kMaxMacro];
   int comm_per_xcd;
   int K, T, dtype;
+  int64_t NK;
   int spin_limit;
   uint32_t flags;
 };
@@ -177,13 +186,31 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
   if (ax < 0) return;
   const int nx = s_n[x];
   const int C = min(a.comm_per_xcd, nx - 1);
-  const int nt = *a.ntiles;
+  // Row tiles of all macrobatches form one list: global tile g is tile g - s_first[b] of
+  // macrobatch b, for the b with s_first[b] <= g < s_first[b + 1].
+  __shared__ int s_first[kMaxMacro + 1];
+  if (tid == 0) {
+    int f = 0;
+    for (int b = 0; b < a.B; ++b) {
+      s_first[b] = f;
+      f += min(*a.mb[b].ntiles, int(a.tiles_max));
+    }
+    s_first[a.B] = f;
+  }
+  __syncthreads();
+  const int nt = s_first[a.B];
+  const int64_t gmax = a.tiles_max * a.B;           // bound on global tile ids
+  auto macro_of = [&](int g) {
+    int b = 0;
+    while (b + 1 < a.B && s_first[b + 1] <= g) ++b;
+    return b;
+  };
   const int ngu = a.s.I / 128;
   const int ndn = (a.s.H + kTileN - 1) / kTileN;
   int32_t* landed = a.cnt + kCntWords;
-  int32_t* gu_done = landed + a.tiles_max;
-  int32_t* dn_done = gu_done + a.tiles_max;
-  int32_t* xq = dn_done + a.tiles_max + int64_t(x) * a.tiles_max;   // this XCD's tile ids
+  int32_t* gu_done = landed + gmax;
+  int32_t* dn_done = gu_done + gmax;
+  int32_t* xq = dn_done + gmax + int64_t(x) * gmax;   // this XCD's tile ids
   int32_t* xend = a.cnt + kCntEnd + x;
   uint8_t* share = a.ring + int64_t(x) * a.ring_share;
   // Planes of this XCD's q-th row tile: X in gather slot q % capx, g|u and h in activation
@@ -204,7 +231,7 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
   // an error.
   __shared__ int s_mt;
   auto take_tile = [&](int q) -> int {
-    if (local != 0) return tile_of(xq, xend, q, a.tiles_max, a.err, a.spin_limit);
+    if (local != 0) return tile_of(xq, xend, q, gmax, a.err, a.spin_limit);
     if (tid == 0) {
       int t = add_relaxed(a.cnt + kCntNext, 1);
       if (t >= nt) {
@@ -212,11 +239,13 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
         __hip_atomic_store(xend, q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         // One thread per XCD records its tiles in order, so each slot's owner ends as the
-        // last tile that used it.
+        // last tile that used it (and only that tile's macrobatch claims the slot).
         const int slot = x * a.capa + q % a.capa;
-        a.rtiles[t] = a.tiles[t];
-        a.rslot[t] = slot;
-        a.rowner[slot] = t;
+        const int b = macro_of(t), tb = t - s_first[b];
+        const MacroArgs& m = a.mb[b];
+        m.rtiles[tb] = m.tiles[tb];
+        m.rslot[tb] = slot;
+        for (int o = 0; o < a.B; ++o) a.mb[o].rowner[slot] = o == b ? tb : -1;
         __hip_atomic_store(xq + q, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       s_mt = t;
@@ -230,14 +259,19 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
   // workgroup in landed[mt]. Lane j looks up row j's source first (one round of dependent
   // loads per tile instead of one per row).
   auto gather = [&](int q, int mt, int r0, int rstep) {
-    const MTile tl = a.tiles[mt];
+    const int b = macro_of(mt);
+    const MacroArgs& m = a.mb[b];
+    const MTile tl = m.tiles[mt - s_first[b]];
     const ActPlanes pl = planes(q);
     const uint16_t* my_src = nullptr;
     {
       const int r = r0 + lane * rstep;
       if (lane * rstep < kTileM && r < tl.nrows) {
-        const int64_t n = a.perm[tl.row0 + r] / a.K;
-        my_src = a.x_seg[n / a.T] + (n % a.T) * int64_t(a.s.H);
+        const int32_t pair = m.perm[tl.row0 + r];
+        if (pair >= 0 && pair < a.NK) {      // (a pad row, or a failed schedule: zeros)
+          const int64_t n = pair / a.K;
+          my_src = m.x_seg[n / a.T] + (n % a.T) * int64_t(a.s.H);
+        }
       }
     }
     const uint64_t sp = reinterpret_cast<uint64_t>(my_src);
@@ -314,7 +348,7 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
       k = it % ngu;
     } else {
       const int blk = (it - lag * ngu) / per_tile, off = (it - lag * ngu) % per_tile;
-      const int tb = tile_of(xq, xend, blk, a.tiles_max, a.err, a.spin_limit);
+      const int tb = tile_of(xq, xend, blk, gmax, a.err, a.spin_limit);
       if (tb < 0) return;
       if (tb >= nt) break;                            // no down work left: done
       if (off < ngu) {
@@ -325,13 +359,14 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
         k = off;
       }
     }
-    const int mt = tile_of(xq, xend, q, a.tiles_max, a.err, a.spin_limit);
+    const int mt = tile_of(xq, xend, q, gmax, a.err, a.spin_limit);
     if (mt < 0) return;
     if (mt >= nt) {
       if (q == 0) break;                              // this XCD got no row tile at all
       continue;                                       // no such row tile: nothing to do
     }
-    const MTile tl = a.tiles[mt];
+    const int b = macro_of(mt);
+    const MTile tl = a.mb[b].tiles[mt - s_first[b]];
     const ActPlanes pl = planes(q);
     if (k < ngu) {
       if (!wait_geq(landed + mt, q < lag ? nx : C, a.err, a.spin_limit)) return;
@@ -342,7 +377,7 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
       if (!wait_geq(gu_done + mt, ngu, a.err, a.spin_limit)) return;
       l1_invalidate();
       down_tile<MX, kPushRec>(sm, a.s, a.w, pl, 0, tl.row0, tl.nrows, tl.e, (k - ngu) * kTileN,
-                              a.perm, a.push);
+                              a.mb[b].perm, a.mb[b].push);
       signal(dn_done + mt);
     }
   }
@@ -365,8 +400,10 @@ __global__ __launch_bounds__(256, 1) void k_layer_fwd(FusedArgs a) {
   if (threadIdx.x == 0) {
     const int done = add_relaxed(a.cnt + kCntExit, 1);
     if (done == int(gridDim.x) - 1 && ld_relaxed(a.err) == 0) {
-      a.rhdr[kRhCapt] = a.capa;
-      a.rhdr[kRhTiles] = *a.ntiles;
+      for (int b = 0; b < a.B; ++b) {
+        a.mb[b].rhdr[kRhCapt] = a.capa;
+        a.mb[b].rhdr[kRhTiles] = min(*a.mb[b].ntiles, int(a.tiles_max));
+      }
     }
   }
 }
@@ -381,57 +418,75 @@ hipError_t allow_big_lds(F* f) {
 
 int fused_slots_per_xcd(const Layout& L) { return L.ring_capa; }
 
-hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
-                            const void* const* x_seg, const mok_weights& w, uint8_t* ring,
-                            uint16_t* slots, void* const* out_seg, const float* p, uint8_t* ws,
-                            hipStream_t s) {
+hipError_t launch_layer_fwd_macro(const Layout& L, const mok_desc& d, int B,
+                                  const MacroBuffers* mb, const mok_weights& w, uint8_t* ring,
+                                  uint8_t* ws, hipStream_t s) {
+  if (B < 1 || B > kMaxMacro) return hipErrorInvalidValue;
   static std::atomic<bool> attr_done[kMaxDevices];
   hipError_t err = once_per_device(attr_done, [] {
     const hipError_t e = allow_big_lds(k_layer_fwd<false>);
     return e != hipSuccess ? e : allow_big_lds(k_layer_fwd<true>);
   });
   if (err != hipSuccess) return err;
-  if ((err = launch_tiles(L, L.M, saved, ws, s)) != hipSuccess) return err;
-  int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.ws_counters);
+  const MacroWs mw = macro_ws(L, B);
   const bool mx = L.dtype == MOK_MXFP8;
   FusedArgs a{};
-  a.hdr = reinterpret_cast<const int32_t*>(saved);
-  a.perm = reinterpret_cast<const int32_t*>(saved + L.sv_perm);
-  a.tiles = reinterpret_cast<const MTile*>(ws + L.ws_tiles);
-  a.ntiles = reinterpret_cast<const int32_t*>(ws) + kWsNumTiles;
-  a.x_seg = reinterpret_cast<const uint16_t* const*>(x_seg);
+  a.B = B;
+  // Per macrobatch: router and schedule table (errors of earlier routers are kept). All routers
+  // run first: each clears the workspace header, where macrobatch 0's tile count lives.
+  for (int b = 0; b < B; ++b)
+    if ((err = launch_router(L, mb[b].logits, mb[b].idx, mb[b].p, mb[b].saved, ws, s, b == 0)) !=
+        hipSuccess)
+      return err;
+  // Then per macrobatch: tile table and push records (a token's only local pair goes straight
+  // to its output row).
+  for (int b = 0; b < B; ++b) {
+    uint8_t* sv = mb[b].saved;
+    MTile* tiles = reinterpret_cast<MTile*>(ws + mw.tiles[b]);
+    int32_t* ntiles = reinterpret_cast<int32_t*>(ws + mw.ntiles[b]);
+    if ((err = launch_tiles_to(L, L.M, sv, tiles, ntiles, s)) != hipSuccess) return err;
+    PushRec* rec = reinterpret_cast<PushRec*>(ws + mw.push[b]);
+    if ((err = launch_push_rows(L, sv, mb[b].slots, mb[b].out_seg, mb[b].p, rec, s)) != hipSuccess)
+      return err;
+    MacroArgs& m = a.mb[b];
+    m.perm = reinterpret_cast<const int32_t*>(sv + L.sv_perm);
+    m.tiles = tiles;
+    m.ntiles = ntiles;
+    m.x_seg = reinterpret_cast<const uint16_t* const*>(mb[b].x_seg);
+    m.push = PushTarget{mb[b].slots, rec};
+    m.rhdr = reinterpret_cast<int32_t*>(sv + L.sv_rhdr);
+    m.rtiles = reinterpret_cast<MTile*>(sv + L.sv_rtiles);
+    m.rslot = reinterpret_cast<int32_t*>(sv + L.sv_rslot);
+    m.rowner = reinterpret_cast<int32_t*>(sv + L.sv_rowner);
+  }
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + mw.counters);
+  const int64_t gmax = int64_t(B) * L.tiles_max;
+  // One launch sets the counters: zero, except the per-XCD tile counts (kCntEnd, -1 until
+  // known) and the per-XCD tile ids that follow the per-tile counters (-1 until taken); and no
+  // tile of any macrobatch is resident in any activation slot until the kernel records it.
+  {
+    uint32_t* c = reinterpret_cast<uint32_t*>(cnt);
+    FillRange fills[4 + kMaxMacro] = {
+        {c, kCntEnd, 0u},
+        {c + kCntEnd, kMaxXcd, 0xFFFFFFFFu},
+        {c + kCntEnd + kMaxXcd, kCntWords - kCntEnd - kMaxXcd + 3 * gmax, 0u},
+        {c + kCntWords + 3 * gmax, int64_t(kMaxXcd) * gmax, 0xFFFFFFFFu},
+    };
+    for (int b = 0; b < B; ++b)
+      fills[4 + b] = FillRange{reinterpret_cast<uint32_t*>(a.mb[b].rowner),
+                               int64_t(kXcds) * L.ring_capa, 0xFFFFFFFFu};
+    if ((err = launch_fill_ranges(fills, 4 + B, s)) != hipSuccess) return err;
+  }
   a.ring = ring;
   a.ring_share = L.ring_share;
   a.xsb = L.xsb;
   a.asb = L.asb;
   a.capx = L.ring_capx;
   a.capa = L.ring_capa;
-  uint8_t* sv = const_cast<uint8_t*>(saved);
-  a.rhdr = reinterpret_cast<int32_t*>(sv + L.sv_rhdr);
-  a.rtiles = reinterpret_cast<MTile*>(sv + L.sv_rtiles);
-  a.rslot = reinterpret_cast<int32_t*>(sv + L.sv_rslot);
-  a.rowner = reinterpret_cast<int32_t*>(sv + L.sv_rowner);
-  // One launch sets the counters: zero, except the per-XCD tile counts (kCntEnd, -1 until
-  // known) and the per-XCD tile ids that follow the per-tile counters (-1 until taken); and no
-  // tile is resident in any activation slot until the kernel records it.
-  {
-    uint32_t* c = reinterpret_cast<uint32_t*>(cnt);
-    const FillRange fills[] = {
-        {c, kCntEnd, 0u},
-        {c + kCntEnd, kMaxXcd, 0xFFFFFFFFu},
-        {c + kCntEnd + kMaxXcd, kCntWords - kCntEnd - kMaxXcd + 3 * L.tiles_max, 0u},
-        {c + kCntWords + 3 * L.tiles_max, int64_t(kMaxXcd) * L.tiles_max, 0xFFFFFFFFu},
-        {reinterpret_cast<uint32_t*>(a.rowner), int64_t(kXcds) * L.ring_capa, 0xFFFFFFFFu},
-    };
-    if ((err = launch_fill_ranges(fills, 5, s)) != hipSuccess) return err;
-  }
   a.s = FfnShape{L.H, L.I};
   if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
   else a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),
                         static_cast<const uint8_t*>(w.wd), nullptr, nullptr, nullptr};
-  PushRec* rec = reinterpret_cast<PushRec*>(ws + L.ws_push);
-  if ((err = launch_push_rows(L, saved, slots, out_seg, p, rec, s)) != hipSuccess) return err;
-  a.push = PushTarget{slots, rec};
   a.cnt = cnt;
   a.err = reinterpret_cast<int32_t*>(ws) + kWsError;
   a.tiles_max = L.tiles_max;
@@ -444,6 +499,7 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   a.K = L.K;
   a.T = L.T;
   a.dtype = L.dtype;
+  a.NK = L.NK;
   a.flags = d.flags;
   a.spin_limit = (d.flags & MOK_FLAG_SKIP_ONE_SIGNAL) ? (1 << 12) : (1 << 24);
   void* args[] = {&a};
@@ -452,7 +508,14 @@ hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* s
   trace_before(MOK_TRACE_FUSED_FWD, s);
   err = hipLaunchCooperativeKernel(fn, dim3(cus), dim3(kThreads), args, kGemmLdsBytes, s);
   trace_after(MOK_TRACE_FUSED_FWD, s);
-  return err;
+  if (err != hipSuccess) return err;
+  // The weighted merge of each macrobatch's tokens with several local pairs (the others' rows
+  // were written by the down-GEMM epilogue).
+  for (int b = 0; b < B; ++b)
+    if ((err = launch_combine(L, mb[b].saved, mb[b].idx, mb[b].p, mb[b].slots, mb[b].out_seg,
+                              true, s)) != hipSuccess)
+      return err;
+  return hipSuccess;
 }
 
 }  // namespace mok

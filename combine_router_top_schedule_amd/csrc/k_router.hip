@@ -349,15 +349,16 @@ __global__ __launch_bounds__(64) void k_tiles(const int32_t* hdr, MTile* tiles, 
 }  // namespace
 
 hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, float* p,
-                         uint8_t* saved, uint8_t* ws, hipStream_t s) {
+                         uint8_t* saved, uint8_t* ws, hipStream_t s, bool clear_error) {
   int32_t* hdr = reinterpret_cast<int32_t*>(saved);
   int32_t* wsh = reinterpret_cast<int32_t*>(ws);
   uint32_t* state = reinterpret_cast<uint32_t*>(ws + L.ws_state);
-  // One launch clears the workspace header (error word, scan ticket), the ring record header
-  // (nothing resident until a fused forward writes it), the look-back scan state and the
-  // schedule header.
+  // One launch clears the workspace header (error word unless asked to keep it, scan ticket),
+  // the ring record header (nothing resident until a fused forward writes it), the look-back
+  // scan state and the schedule header.
+  const int keep = clear_error ? 0 : 1;   // kWsError is word 0
   const FillRange fills[] = {
-      {reinterpret_cast<uint32_t*>(wsh), kWsWords, 0u},
+      {reinterpret_cast<uint32_t*>(wsh) + keep, kWsWords - keep, 0u},
       {reinterpret_cast<uint32_t*>(saved + L.sv_rhdr), kRhWords, 0u},
       {state, int64_t(L.topk_blocks) * (L.El + 2), 0u},
       {reinterpret_cast<uint32_t*>(hdr), kHdrWords, 0u},
@@ -412,12 +413,16 @@ mok_status launch_router_noalloc(const Layout& L, const float* logits, int32_t* 
   return launch_router(L, logits, idx, p, saved, base, s) == hipSuccess ? MOK_OK : MOK_ERR_HIP;
 }
 
-hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s) {
-  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(64), 0, s,
-                     reinterpret_cast<const int32_t*>(saved),
-                     reinterpret_cast<MTile*>(ws + L.ws_tiles),
-                     reinterpret_cast<int32_t*>(ws) + kWsNumTiles, L.El, M, L.tiles_max);
+hipError_t launch_tiles_to(const Layout& L, int M, const uint8_t* saved, MTile* tiles,
+                           int32_t* ntiles, hipStream_t s) {
+  hipLaunchKernelGGL(k_tiles, dim3(1), dim3(64), 0, s, reinterpret_cast<const int32_t*>(saved),
+                     tiles, ntiles, L.El, M, L.tiles_max);
   return hipGetLastError();
+}
+
+hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s) {
+  return launch_tiles_to(L, M, saved, reinterpret_cast<MTile*>(ws + L.ws_tiles),
+                         reinterpret_cast<int32_t*>(ws) + kWsNumTiles, s);
 }
 
 }  // namespace mok

@@ -261,17 +261,56 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
     return MOK_ERR_ALIGN;
   const Layout L = layout_of(*desc);
   if (fused_slots_per_xcd(L) < 2) return MOK_ERR_RING;
-  hipStream_t s = as_stream(stream);
-  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  uint8_t* saved = static_cast<uint8_t*>(saved_dev);
-  hipError_t e = launch_router(L, logits_dev, topk_idx_dev, topk_p_dev, saved, ws, s);
-  if (e == hipSuccess)
-    e = launch_layer_fwd(L, *desc, saved, x_seg_dev, *w, static_cast<uint8_t*>(ring_dev),
-                         static_cast<uint16_t*>(slots_dev), out_seg_dev, topk_p_dev, ws, s);
-  if (e == hipSuccess)
-    e = launch_combine(L, saved, topk_idx_dev, topk_p_dev, static_cast<const uint16_t*>(slots_dev),
-                       out_seg_dev, true, s);
-  return hip_status(e);
+  const MacroBuffers mb{x_seg_dev, logits_dev, out_seg_dev, topk_idx_dev, topk_p_dev,
+                        static_cast<uint8_t*>(saved_dev), static_cast<uint16_t*>(slots_dev)};
+  return hip_status(launch_layer_fwd_macro(L, *desc, 1, &mb, *w, static_cast<uint8_t*>(ring_dev),
+                                           static_cast<uint8_t*>(ws_dev), as_stream(stream)));
+}
+
+mok_status mok_macro_ws_size(const mok_desc* desc, int32_t num_macro, size_t* ws_bytes) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!ws_bytes) return MOK_ERR_NULL;
+  if (num_macro < 1 || num_macro > kMaxMacro) return MOK_ERR_SHAPE;
+  *ws_bytes = size_t(macro_ws(layout_of(*desc), num_macro).bytes);
+  return MOK_OK;
+}
+
+mok_status mok_layer_fwd_macro(const mok_desc* desc, int32_t num_macro,
+                               const void* const* const* x_seg_dev, const float* const* logits_dev,
+                               const mok_weights* w, void* const* const* out_seg_dev,
+                               int32_t* const* topk_idx_dev, float* const* topk_p_dev,
+                               void* const* saved_dev, void* ring_dev, void* const* slots_dev,
+                               void* ws_dev, void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (num_macro < 1 || num_macro > kMaxMacro) return MOK_ERR_SHAPE;
+  if (!x_seg_dev || !logits_dev || !w || !out_seg_dev || !topk_idx_dev || !topk_p_dev ||
+      !saved_dev || !ring_dev || !slots_dev || !ws_dev)
+    return MOK_ERR_NULL;
+  st = check_weights(desc, w, false);
+  if (st != MOK_OK) return st;
+  if (!aligned16(ring_dev) || !aligned16(ws_dev)) return MOK_ERR_ALIGN;
+  MacroBuffers mb[kMaxMacro];
+  for (int b = 0; b < num_macro; ++b) {
+    if (!x_seg_dev[b] || !logits_dev[b] || !out_seg_dev[b] || !topk_idx_dev[b] || !topk_p_dev[b] ||
+        !saved_dev[b] || !slots_dev[b])
+      return MOK_ERR_NULL;
+    if (!aligned16(logits_dev[b]) || !aligned16(saved_dev[b]) || !aligned16(slots_dev[b]))
+      return MOK_ERR_ALIGN;
+    for (int o = 0; o < b; ++o)
+      if (saved_dev[o] == saved_dev[b] || slots_dev[o] == slots_dev[b] ||
+          out_seg_dev[o] == out_seg_dev[b] || topk_idx_dev[o] == topk_idx_dev[b])
+        return MOK_ERR_SHAPE;   // each macrobatch needs its own outputs
+    mb[b] = MacroBuffers{x_seg_dev[b], logits_dev[b], out_seg_dev[b], topk_idx_dev[b],
+                         topk_p_dev[b], static_cast<uint8_t*>(saved_dev[b]),
+                         static_cast<uint16_t*>(slots_dev[b])};
+  }
+  const Layout L = layout_of(*desc);
+  if (fused_slots_per_xcd(L) < 2) return MOK_ERR_RING;
+  return hip_status(launch_layer_fwd_macro(L, *desc, num_macro, mb, *w,
+                                           static_cast<uint8_t*>(ring_dev),
+                                           static_cast<uint8_t*>(ws_dev), as_stream(stream)));
 }
 
 mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,

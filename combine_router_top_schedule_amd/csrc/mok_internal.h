@@ -21,6 +21,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;            // XCDs per MI355X device (each with its own L2)
 constexpr int kRingXSlots = 3;      // gather slots per XCD share of the fused-forward ring
+constexpr int kMaxMacro = 8;        // macrobatches (layer calls) one fused launch can run
 
 __host__ __device__ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -271,11 +272,16 @@ struct FillRange {
   int64_t n;
   uint32_t v;
 };
-constexpr int kMaxFillRanges = 8;
+constexpr int kMaxFillRanges = 16;
 hipError_t launch_fill_ranges(const FillRange* r, int count, hipStream_t s);
+// clear_error = false keeps a failure an earlier call recorded in the error word (the
+// routers of several macrobatches of one fused launch).
 hipError_t launch_router(const Layout& L, const float* logits, int32_t* idx, float* p,
-                         uint8_t* saved, uint8_t* ws, hipStream_t s);
+                         uint8_t* saved, uint8_t* ws, hipStream_t s, bool clear_error = true);
 hipError_t launch_tiles(const Layout& L, int M, const uint8_t* saved, uint8_t* ws, hipStream_t s);
+// The same into an explicit table and count word.
+hipError_t launch_tiles_to(const Layout& L, int M, const uint8_t* saved, MTile* tiles,
+                           int32_t* ntiles, hipStream_t s);
 // Bytes of the workspace the router alone uses (header and look-back scan state).
 inline int64_t router_ws_bytes(const Layout& L) {
   return L.ws_state + align_up(4 * int64_t(L.topk_blocks) * (L.El + 2), 256);
@@ -337,10 +343,51 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
 // Fused forward (k_fused.hip): the ring is split into one share per XCD, each cut into tile
 // slots of 256 expert-ordered rows (X | g,u | h).
 int fused_slots_per_xcd(const Layout& L);
-hipError_t launch_layer_fwd(const Layout& L, const mok_desc& d, const uint8_t* saved,
-                            const void* const* x_seg, const mok_weights& w, uint8_t* ring,
-                            uint16_t* slots, void* const* out_seg, const float* p, uint8_t* ws,
-                            hipStream_t s);
+
+// Buffers of one macrobatch (one layer call) of a fused forward launch.
+struct MacroBuffers {
+  const void* const* x_seg;
+  const float* logits;
+  void* const* out_seg;
+  int32_t* idx;
+  float* p;
+  uint8_t* saved;
+  uint16_t* slots;
+};
+
+// Workspace of a fused forward over B macrobatches (byte offsets from the ws start). B = 1 is the
+// single-call layout: tile table, push records and counters where Layout puts them.
+struct MacroWs {
+  int64_t counters;
+  int64_t tiles[kMaxMacro], ntiles[kMaxMacro], push[kMaxMacro];
+  int64_t bytes;
+};
+inline MacroWs macro_ws(const Layout& L, int B) {
+  MacroWs m{};
+  int64_t off = align_up(L.ws_bytes, 256);
+  if (B <= 1) {
+    m.counters = L.ws_counters;
+  } else {
+    m.counters = off;
+    off = align_up(off + 4 * (64 + (3 + kXcds) * int64_t(B) * L.tiles_max), 256);
+  }
+  m.tiles[0] = L.ws_tiles;
+  m.ntiles[0] = 4 * int64_t(kWsNumTiles);
+  m.push[0] = L.ws_push;
+  for (int b = 1; b < B; ++b) {
+    m.ntiles[b] = off; off += 256;
+    m.tiles[b] = off; off = align_up(off + 16 * L.tiles_max, 256);
+    m.push[b] = off; off = align_up(off + 16 * L.rows_max, 256);
+  }
+  m.bytes = B <= 1 ? L.ws_bytes : off;
+  return m;
+}
+
+// Router, tile tables and push records of every macrobatch, then one persistent launch over all
+// of their row tiles, then each macrobatch's merge of tokens with several local pairs.
+hipError_t launch_layer_fwd_macro(const Layout& L, const mok_desc& d, int B,
+                                  const MacroBuffers* mb, const mok_weights& w, uint8_t* ring,
+                                  uint8_t* ws, hipStream_t s);
 
 int device_cus();
 

@@ -33,12 +33,13 @@ __device__ __forceinline__ void copy_row_bf16(const uint16_t* src, uint16_t* dst
 // Rows of at most 64 x 16 chunks of 16 bytes (H <= 8192 BF16) fit one register batch per lane.
 constexpr int kRowBatchChunks = 64 * 16;
 
+// (src == nullptr loads zeros)
 __device__ __forceinline__ void load_row16(const uint16_t* src, u32x4 (&v)[16], int nch, int lane) {
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int c = q * 64 + lane;
-    v[q] = c < nch ? __builtin_nontemporal_load(s + c) : u32x4{0, 0, 0, 0};
+    v[q] = (src && c < nch) ? __builtin_nontemporal_load(s + c) : u32x4{0, 0, 0, 0};
   }
 }
 

@@ -242,6 +242,30 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
                          void* saved_dev, void* ring_dev, void* slots_dev, void* ws_dev,
                          void* stream);
 
+/* Macrobatch interleave: `num_macro` consecutive layer calls (1..8 macrobatches, each with its
+ * own tokens, logits, outputs, schedule table and slots, the same weights) in one persistent
+ * launch. The pages' ring buffer interleaves dispatch and combine at macrobatch boundaries: the
+ * previous macrobatch's combine and the next one's dispatch run at the same time
+ * ("Mixture-of-Kittens (MoK)", ring token buffer section; "Cursor Open-Sources
+ * Mixture-of-Kittens (MoK)", Technical Details; "把 MoE 通信延迟从 103μs 压到 18μs", section 03
+ * part ③). Here the row tiles of all macrobatches form one list taken in macrobatch order, so
+ * macrobatch b+1 is pulled and computed while macrobatch b's last tiles finish and push their
+ * results; then each macrobatch's merge of tokens with several local pairs runs.
+ *   x_seg_dev, logits_dev, out_seg_dev, topk_idx_dev, topk_p_dev, saved_dev, slots_dev: HOST
+ *     arrays of num_macro entries, each what mok_layer_fwd takes for that call (distinct
+ *     outputs per macrobatch);
+ *   ring_dev: one ring, as for mok_layer_fwd; ws_dev: mok_macro_ws_size(desc, num_macro) bytes.
+ * Every output equals, bit for bit, that of num_macro separate mok_layer_fwd calls. Each saved
+ * table records the ring slots its own tiles still hold at the end, so mok_layer_bwd of any
+ * macrobatch (in any order, ring untouched in between) reuses them. */
+mok_status mok_macro_ws_size(const mok_desc* desc, int32_t num_macro, size_t* ws_bytes);
+mok_status mok_layer_fwd_macro(const mok_desc* desc, int32_t num_macro,
+                               const void* const* const* x_seg_dev, const float* const* logits_dev,
+                               const mok_weights* w, void* const* const* out_seg_dev,
+                               int32_t* const* topk_idx_dev, float* const* topk_p_dev,
+                               void* const* saved_dev, void* ring_dev, void* const* slots_dev,
+                               void* ws_dev, void* stream);
+
 /* Fused backward of L = sum_n <dOut[n], out[n]>, walking the ring in reverse so the
  * minibatches still resident after the forward are not replayed ("Mixture-of-Kittens (MoK)",
  * section on the ring token buffer; "Cursor Open-Sources Mixture-of-Kittens (MoK)",
