@@ -77,6 +77,9 @@ _SIGS = {
     "mok_two_wave_floor": (ctypes.c_int64, [ctypes.c_int32] * 4),
     "mok_schedule": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P, _P]),
     "mok_schedule_noalloc": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P]),
+    "mok_router_fwd": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P]),
+    "mok_router_ws_size": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "mok_router_bwd": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P, _P, _P]),
     "mok_dispatch": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, _P, _P, _P]),
     "mok_expert_ffn": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
                                       _P, _P, _P, _P]),
@@ -221,6 +224,25 @@ def mok_schedule_noalloc(d: MokDesc, logits, topk_idx, topk_p, saved, stream=Non
     _check("mok_schedule_noalloc", lib().mok_schedule_noalloc(ctypes.byref(d), _ptr(logits),
                                                               _ptr(topk_idx), _ptr(topk_p),
                                                               _ptr(saved), _stream(stream)))
+
+
+def mok_router_fwd(d: MokDesc, x_seg, wr, logits, stream=None):
+    _need_cuda(x_seg, wr, logits)
+    _check("mok_router_fwd", lib().mok_router_fwd(ctypes.byref(d), _ptr(x_seg), _ptr(wr),
+                                                  _ptr(logits), _stream(stream)))
+
+
+def router_ws_size(d: MokDesc) -> int:
+    n = ctypes.c_size_t()
+    _check("mok_router_ws_size", lib().mok_router_ws_size(ctypes.byref(d), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mok_router_bwd(d: MokDesc, x_seg, wr, dlogits, dwr, dx_seg, ws, stream=None):
+    _need_cuda(x_seg, wr, dlogits, dwr, dx_seg, ws)
+    _check("mok_router_bwd", lib().mok_router_bwd(ctypes.byref(d), _ptr(x_seg), _ptr(wr),
+                                                  _ptr(dlogits), _ptr(dwr), _ptr(dx_seg),
+                                                  _ptr(ws), _stream(stream)))
 
 
 def mok_dispatch(d: MokDesc, saved, x_seg, xd, ws, stream=None):

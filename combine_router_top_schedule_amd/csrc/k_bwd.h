@@ -328,6 +328,39 @@ __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t 
   push_epilogue<kPushRec>(sm, acc, nrows, c0, s.H, 0, pt, row0);
 }
 
+// Write an fp32 tile: out[m * ld + n] = acc for m < ma, n < nb. The tile leaves through LDS in
+// two passes of 128 rows: the two waves holding those rows (wm == pass) stage their 128 x 128
+// blocks in the stage buffers ([128][256] fp32, 128 KB), then every wave writes whole 1 KB rows
+// with 16-byte stores (storing 4 bytes per lane straight from the accumulators is many times
+// slower when many tiles end together). nb and ld are multiples of 4, so a lane's 4 columns
+// are all in range or all out. The caller's K loop has ended (stage buffers free).
+__device__ __forceinline__ void store_tile_f32(GemmLds& sm, const f32x16 (&acc)[4][4], float* out,
+                                               int64_t ld, int ma, int nb) {
+  const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  float* t = reinterpret_cast<float*>(sm.a[0]);
+  for (int pass = 0; pass < 2; ++pass) {
+    if (wm == pass) {
+      float* tl = t + opaque(4 * (lane >> 5) * 256 + wn * 128 + (lane & 31));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            tl[(i * 32 + 8 * (v >> 2) + (v & 3)) * 256 + j * 32] = acc[i][j][v];
+    }
+    __syncthreads();
+    for (int r = wave; r < 128; r += 4) {
+      const int m = pass * 128 + r;
+      if (m < ma && lane * 4 < nb)
+        *reinterpret_cast<f32x4*>(out + int64_t(m) * ld + lane * 4) =
+            *reinterpret_cast<const f32x4*>(t + r * 256 + lane * 4);
+    }
+    __syncthreads();
+  }
+}
+
 // Weight-gradient tile: out[m0 + m][n0 + n] = sum over the expert's padded columns c of
 // Ta[m0 + m][c] Tb[n0 + n][c]; fp32 output [Fa][Fb] (fully overwritten). ld = row pitch of Ta
 // and Tb (elements; their MXFP8 scale rows have ld / 32 bytes).
@@ -361,32 +394,7 @@ __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   }
-  // The fp32 tile leaves through LDS in two passes of 128 rows: the two waves holding those
-  // rows (wm == pass) stage their 128 x 128 blocks in the stage buffers ([128][256] fp32,
-  // 128 KB), then every wave writes whole 1 KB rows with 16-byte stores. Storing 4 bytes per
-  // lane straight from the accumulators is many times slower when many tiles end together.
-  // nb is a multiple of 32 (H and I are), so a lane's 4 columns are all in range or all out.
-  float* t = reinterpret_cast<float*>(sm.a[0]);
-  for (int pass = 0; pass < 2; ++pass) {
-    if (wm == pass) {
-      float* tl = t + opaque(4 * (lane >> 5) * 256 + wn * 128 + (lane & 31));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            tl[(i * 32 + 8 * (v >> 2) + (v & 3)) * 256 + j * 32] = acc[i][j][v];
-    }
-    __syncthreads();
-    for (int r = wave; r < 128; r += 4) {
-      const int m = pass * 128 + r;
-      if (m < ma && lane * 4 < nb)
-        *reinterpret_cast<f32x4*>(out + int64_t(m0 + m) * Fb + n0 + lane * 4) =
-            *reinterpret_cast<const f32x4*>(t + r * 256 + lane * 4);
-    }
-    __syncthreads();
-  }
+  store_tile_f32(sm, acc, out + int64_t(m0) * Fb + n0, Fb, ma, nb);
 }
 
 }  // namespace mok

@@ -449,3 +449,43 @@ extern "C" mok_status mok_autotune(const mok_desc* desc, const void* const* x_se
   if (n_results) *n_results = std::min(n, max_results);
   return MOK_OK;
 }
+
+extern "C" {
+
+mok_status mok_router_fwd(const mok_desc* desc, const void* const* x_seg_dev, const void* wr_dev,
+                          float* logits_dev, void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!x_seg_dev || !wr_dev || !logits_dev) return MOK_ERR_NULL;
+  if (desc->num_experts % 4) return MOK_ERR_SHAPE;
+  if (!aligned16(wr_dev) || !aligned16(logits_dev)) return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  return hip_status(launch_router_fwd(L, x_seg_dev, static_cast<const uint16_t*>(wr_dev),
+                                      logits_dev, as_stream(stream)));
+}
+
+mok_status mok_router_ws_size(const mok_desc* desc, size_t* ws_bytes) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!ws_bytes) return MOK_ERR_NULL;
+  *ws_bytes = size_t(router_ws(layout_of(*desc)).bytes);
+  return MOK_OK;
+}
+
+mok_status mok_router_bwd(const mok_desc* desc, const void* const* x_seg_dev, const void* wr_dev,
+                          const float* dlogits_dev, float* dwr_dev, void* const* dx_seg_dev,
+                          void* ws_dev, void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!x_seg_dev || !wr_dev || !dlogits_dev || !dwr_dev || !dx_seg_dev || !ws_dev)
+    return MOK_ERR_NULL;
+  if (desc->num_experts % 4) return MOK_ERR_SHAPE;
+  if (!aligned16(wr_dev) || !aligned16(dlogits_dev) || !aligned16(dwr_dev) || !aligned16(ws_dev))
+    return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  return hip_status(launch_router_bwd(L, x_seg_dev, static_cast<const uint16_t*>(wr_dev),
+                                      dlogits_dev, dwr_dev, dx_seg_dev,
+                                      static_cast<uint8_t*>(ws_dev), as_stream(stream)));
+}
+
+}  // extern "C"

@@ -389,6 +389,20 @@ hipError_t launch_layer_fwd_macro(const Layout& L, const mok_desc& d, int B,
                                   const MacroBuffers* mb, const mok_weights& w, uint8_t* ring,
                                   uint8_t* ws, hipStream_t s);
 
+// Router gate projection (k_routerg.hip): workspace of the backward (byte offsets), with the
+// token axis padded to Np and the expert axis to Ep (multiples of a 64-element K stage).
+struct RouterWs {
+  int64_t Np;
+  int Ep;
+  int64_t dl16, dlt, xt, wrt, bytes;
+};
+RouterWs router_ws(const Layout& L);
+hipError_t launch_router_fwd(const Layout& L, const void* const* x_seg, const uint16_t* wr,
+                             float* logits, hipStream_t s);
+hipError_t launch_router_bwd(const Layout& L, const void* const* x_seg, const uint16_t* wr,
+                             const float* dlogits, float* dwr, void* const* dx_seg, uint8_t* ws,
+                             hipStream_t s);
+
 int device_cus();
 
 // One-time set-up per device (kernel attributes are set for the device that is current when

@@ -24,7 +24,7 @@ from typing import Optional
 import numpy as np
 
 # Stream ids: one per tensor kind.
-_LOGITS, _X, _WG, _WU, _WD, _DOUT = 1, 2, 3, 4, 5, 6
+_LOGITS, _X, _WG, _WU, _WD, _DOUT, _WR = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -195,3 +195,14 @@ def weights(cfg: Config) -> dict:
             mats.append(f32_to_bf16_bits(z))
         out[name] = np.stack(mats)
     return out
+
+
+def router_weight(cfg: Config, std: Optional[float] = None) -> np.ndarray:
+    """Router gate weights as BF16 bits [E][H] (the reduction axis contiguous), ~N(0, std^2);
+    by default std = logit_std / (x_std * sqrt(H)), so the logits X W_r^T have the spread of the
+    workload's direct logits."""
+    if std is None:
+        std = cfg.logit_std / (cfg.x_std * np.sqrt(cfg.H))
+    z = _rng(cfg, _WR, 0).standard_normal((cfg.E, cfg.H), dtype=np.float32)
+    z *= np.float32(std)
+    return f32_to_bf16_bits(z)

@@ -195,6 +195,27 @@ mok_status mok_schedule_noalloc(const mok_desc* desc, const float* logits_dev,
                                 int32_t* topk_idx_dev, float* topk_p_dev, void* saved_dev,
                                 void* stream);
 
+/* The router's gate projection, the step before top-k: logits[n][e] = sum_h X[n][h] W_r[e][h]
+ * for every token n of the segments (fp32 [N][E], BF16 operands, fp32 accumulation in a fixed
+ * order). The result feeds mok_schedule / mok_layer_fwd. The router-weight gradient is part of
+ * the layer ("Mixture-of-Kittens (MoK)", benchmark section; "Cursor Open-Sources
+ * Mixture-of-Kittens (MoK)", Technical Details).
+ *   wr_dev  BF16 [E][H] (the reduction axis contiguous); E must be a multiple of 4. */
+mok_status mok_router_fwd(const mok_desc* desc, const void* const* x_seg_dev, const void* wr_dev,
+                          float* logits_dev, void* stream);
+
+/* Backward of the gate projection, given dlogits (from mok_layer_bwd when every expert is
+ * local, or completed at the source in expert parallelism):
+ *   dwr_dev  fp32 [E][H], overwritten: dW_r = dlogits^T X;
+ *   dx_seg   BF16 token rows, updated in place: dX[n] = bf16(float(dX[n]) + dlogits[n] W_r)
+ *            for every token n (write or zero dX first);
+ *   ws_dev   mok_router_ws_size bytes (X^T, dlogits^T, W_r^T, zero-padded).
+ * dlogits enter the contraction rounded to BF16. */
+mok_status mok_router_ws_size(const mok_desc* desc, size_t* ws_bytes);
+mok_status mok_router_bwd(const mok_desc* desc, const void* const* x_seg_dev, const void* wr_dev,
+                          const float* dlogits_dev, float* dwr_dev, void* const* dx_seg_dev,
+                          void* ws_dev, void* stream);
+
 /* Pull dispatch, staged form: the receiving side reads every routed token row from its
  * source segment and writes it in expert order ("Mixture-of-Kittens (MoK)", section on pull
  * dispatch; "把 MoE 通信延迟从 103μs 压到 18μs", section 03 part ①). In MXFP8 mode each row is

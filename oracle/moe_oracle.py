@@ -45,6 +45,25 @@ def decode_bf16(bits: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------------------------
+# O0: the router's gate projection, the step before top-k, and its backward. The pages compute
+# the router-weight gradient as part of the layer, SonicMoE-style, inside SwiGLU backward
+# ("Mixture-of-Kittens (MoK)", benchmark section; "Cursor Open-Sources Mixture-of-Kittens
+# (MoK)", Technical Details): dp comes out of SwiGLU backward, the top-k softmax backward turns
+# it into dlogits (O13), and the projection's chain rule carries dlogits into W_r and X.
+
+def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
+    """logits[n, e] = sum_h x[n, h] wr[e, h] (fp64); wr is [E][H]."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(wr, dtype=np.float64).T
+
+
+def router_backward(x: np.ndarray, wr: np.ndarray, dlogits: np.ndarray):
+    """Chain rule of the projection: dW_r = dlogits^T x ([E][H]) and the router's share of the
+    input gradient, dlogits wr ([N][H])."""
+    dl = np.asarray(dlogits, dtype=np.float64)
+    return dl.T @ np.asarray(x, dtype=np.float64), dl @ np.asarray(wr, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------------------------
 # O1 + O2: router top-k and gating.
 # The router picks K experts per token anew every step, which is why per-expert loads are
 # dynamic ("把 MoE 通信延迟从 103μs 压到 18μs", section 02).

@@ -460,3 +460,46 @@ def test_expert_wgrad_rows_match_full_backward(dtype):
         assert np.allclose(dwg, bw.dwg[e][gi], rtol=1e-12, atol=1e-14)
         assert np.allclose(dwu, bw.dwu[e][gi], rtol=1e-12, atol=1e-14)
         assert np.allclose(dwd, bw.dwd[e][hi], rtol=1e-12, atol=1e-14)
+
+
+def test_router_projection_gradients_match_finite_differences():
+    """With logits = X W_r^T feeding the layer (every expert local, so dlogits is complete), the
+    gradients of L = sum <dOut, out> are dW_r = dlogits^T X and dX = dX_layer + dlogits W_r:
+    checked by central differences in fp64 on the tiny workload."""
+    cfg = datagen.CONFIGS["tiny"]
+    X = mo.decode_bf16(datagen.x_all(cfg))
+    Wr = mo.decode_bf16(datagen.router_weight(cfg))
+    w = datagen.weights(cfg)
+    Wg, Wu, Wd = (mo.decode_bf16(w[k]) for k in ("wg", "wu", "wd"))
+    dO = mo.decode_bf16(datagen.dout_all(cfg))
+    K, E = cfg.K, cfg.E
+    L = mo.router_logits(X, Wr)
+    assert 0.5 < L.std() < 2.0                         # the spread the workload's logits have
+    Ls = np.sort(L, axis=1)[:, ::-1]
+    assert (Ls[:, K - 1] - Ls[:, K]).min() > 1e-4      # no near-tie: top-k is locally constant
+    fw, bw = _run_oracle(X, L, Wg, Wu, Wd, dO, K, 0, E, E)
+    dwr, dxr = mo.router_backward(X, Wr, bw.dlogits)
+    assert np.array_equal(fw.sched.touched, np.arange(cfg.N))
+    dx_total = bw.dx + dxr
+    f = lambda: _loss(X, mo.router_logits(X, Wr), Wg, Wu, Wd, dO, K, 0, E)
+    eps = 1e-6
+    rng = np.random.default_rng(11)
+
+    def fd(arr, pos):
+        old = arr[pos]
+        arr[pos] = old + eps; lp = f()
+        arr[pos] = old - eps; lm = f()
+        arr[pos] = old
+        return (lp - lm) / (2 * eps)
+
+    checks = []
+    for _ in range(16):
+        pos = (int(rng.integers(E)), int(rng.integers(cfg.H)))
+        checks.append((fd(Wr, pos), dwr[pos]))
+    for _ in range(16):
+        pos = (int(rng.integers(cfg.N)), int(rng.integers(cfg.H)))
+        checks.append((fd(X, pos), dx_total[pos]))
+    for fdv, an in checks:
+        assert abs(fdv - an) <= 1e-6 * max(abs(an), 1e-3), (fdv, an)
+    # the projection's share matters: without it dX would be off
+    assert np.abs(dxr).max() > 1e-3 * np.abs(bw.dx).max()
