@@ -155,6 +155,9 @@ def main() -> int:
                     help="time mok_layer_fwd alone (minibatch sweeps); not the headline metric")
     ap.add_argument("--tune", action="store_true",
                     help="run mok_autotune first (minibatch and dispatch-CU split for this shape)")
+    ap.add_argument("--trace", action="store_true",
+                    help="after the timed steps, run one forward with the phase trace on "
+                         "(MOK_FLAG_TRACE) and report its summary under detail.fused_trace")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is one "
@@ -321,6 +324,21 @@ def main() -> int:
         line["detail"]["autotune"] = tuning
         line["config"]["minibatch"] = tuning["minibatch"]
         line["config"]["comm_cus"] = tuning["comm_cus"]
+    if args.trace:
+        # one more forward on a layer whose descriptor asks for the phase trace (outside the
+        # timed region; the trace costs a few clock reads and one record store per item)
+        from combine_router_top_schedule_amd import trace
+        dt = mok.desc_from_config(cfg, flags=mok.MOK_FLAG_TRACE)
+        if tuning:
+            dt.minibatch_tokens, dt.comm_cus = tuning["minibatch"], tuning["comm_cus"]
+        Lt = MokLayer(dt, device=dev, staged=False, fused=True)
+        Lt.w = L.w
+        for _ in range(2):
+            Lt.forward(x_seg, logits, out_seg)
+        torch.cuda.synchronize()
+        rec, count = trace.read(Lt.ws, Lt.sizes)
+        line["detail"]["fused_trace"] = dict(trace.summarize(rec), dropped=int(count - len(rec)))
+        del Lt
     # release what this run created on the device before the interpreter exits (the library's
     # trace hook is already off): events, buffers and the layer
     del kev, t0, t1

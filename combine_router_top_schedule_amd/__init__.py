@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(HERE, "libmok.so")
 
 MOK_BF16, MOK_MXFP8 = 0, 1
 MOK_FLAG_SKIP_ONE_SIGNAL = 0x1
+MOK_FLAG_TRACE = 0x2
+MOK_FLAG_POISON = 0x4
 STATUS = {0: "MOK_OK", 1: "MOK_ERR_NULL", 2: "MOK_ERR_SHAPE", 3: "MOK_ERR_DTYPE",
           4: "MOK_ERR_ALIGN", 5: "MOK_ERR_WORKSPACE", 6: "MOK_ERR_RING", 7: "MOK_ERR_HIP",
           8: "MOK_ERR_DEVICE_TIMEOUT", 9: "MOK_ERR_UNSUPPORTED", 10: "MOK_ERR_SCRATCH"}
@@ -46,7 +48,8 @@ class MokSizes(ctypes.Structure):
                 ("perm_offset", ctypes.c_int64), ("tokpos_offset", ctypes.c_int64),
                 ("touched_offset", ctypes.c_int64), ("x_slot_bytes", ctypes.c_int64),
                 ("ring_min_bytes", ctypes.c_int64), ("tiles_offset", ctypes.c_int64),
-                ("tiles_max", ctypes.c_int64)]
+                ("tiles_max", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
+                ("trace_records", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p

@@ -77,6 +77,9 @@ struct FusedArgs {
   int64_t NK;
   int spin_limit;
   uint32_t flags;
+  TraceRec* trace;           // MOK_FLAG_TRACE: phase records (null without it)
+  int64_t trace_max;
+  int32_t* trace_count;
 };
 
 // Counter words: registration, the global row-tile counter, per XCD the number of row tiles it
@@ -149,6 +152,58 @@ __device__ __forceinline__ void signal(int32_t* p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) add_relaxed(p, 1);
+}
+
+// Constant-rate clock for the phase trace (100 MHz on gfx950).
+__device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Thread 0 appends one phase record (MOK_FLAG_TRACE); records past the capacity are counted
+// but dropped.
+__device__ __forceinline__ void trace_item(const FusedArgs& a, int kind, int x, int b, int tile,
+                                           int item, uint64_t t_wait, uint64_t t_begin) {
+  if (a.trace == nullptr || threadIdx.x != 0) return;
+  const uint64_t t_end = trace_clock();
+  const int i = add_relaxed(a.trace_count, 1);
+  if (i < a.trace_max) {
+    TraceRec r;
+    r.wg = int(blockIdx.x);
+    r.info = kind | (x << 8) | (b << 16);
+    r.tile = tile;
+    r.item = item;
+    r.t_wait = t_wait;
+    r.t_begin = t_begin;
+    r.t_end = t_end;
+    r.pad = 0;
+    a.trace[i] = r;
+  }
+}
+
+// MOK_FLAG_POISON: fill rows r0, r0 + rstep, ... (< kTileM) of a gather slot's X plane (and
+// its MXFP8 scales) and of an activation slot's g|u, h planes with 0xFF bytes (NaN in BF16,
+// E4M3 and UE8M0), so a read of a released slot before its next tile's data is written shows
+// up as NaN. Rows are split exactly as the gather splits them, so each row's poison precedes
+// its gathered bytes in one wave's program order (with a vmcnt wait between them).
+__device__ void poison_rows(const ActPlanes& px, const ActPlanes& pa, bool gather_slot,
+                            bool act_slot, int H, int I, bool mx, int r0, int rstep, int lane) {
+  auto fill = [&](uint8_t* p, int64_t bytes) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(p);
+    const int64_t nw = bytes / 4;
+    for (int64_t i = lane; i < nw; i += 64) w[i] = 0xFFFFFFFFu;
+    for (int64_t i = nw * 4 + lane; i < bytes; i += 64) p[i] = 0xFFu;
+  };
+  const int64_t xrow = mx ? H : 2 * int64_t(H);
+  const int64_t hrow = mx ? I : 2 * int64_t(I);
+  for (int r = r0; r < kTileM; r += rstep) {
+    if (gather_slot) {
+      fill(px.x + r * xrow, xrow);
+      if (mx) fill(px.xs + int64_t(r) * (H / 32), H / 32);
+    }
+    if (act_slot) {
+      fill(reinterpret_cast<uint8_t*>(pa.gu) + int64_t(r) * 4 * I, 4 * int64_t(I));
+      fill(pa.h + r * hrow, hrow);
+      if (mx) fill(pa.hs + int64_t(r) * (I / 32), I / 32);
+    }
+  }
 }
 
 // The work of one workgroup. Every exit is taken by the whole workgroup (the values deciding
@@ -306,13 +361,23 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
   const int lag = a.capa > 2 ? 2 : 1;                 // lag < capx: the prologue never waits
   bool ended = false;
   for (int q = 0; q < lag; ++q) {
+    const uint64_t tw = trace_clock();
     const int mt = take_tile(q);
     if (mt < 0) return;
     if (mt >= nt) {
       ended = true;
       break;
     }
+    const uint64_t tb = trace_clock();
+    if (a.flags & MOK_FLAG_POISON) {
+      const ActPlanes pl = planes(q);
+      poison_rows(pl, pl, true, true, a.s.H, a.s.I, MX, local * 4 + wave, 4 * nx, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     gather(q, mt, local * 4 + wave, 4 * nx);
+    const int b = macro_of(mt);
+    trace_item(a, kTrPrologueGather, x, b, mt - s_first[b], q, tw, tb);
   }
 
   if (local < C) {
@@ -320,6 +385,7 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
     // once its gate/up tiles are done, and the activation slot of tile q - capa once its down
     // tiles are done.
     for (int q = lag; !ended; ++q) {
+      const uint64_t tw = trace_clock();
       if (q >= a.capx && !wait_geq(gu_done + ld_relaxed(xq + q - a.capx), ngu, a.err, a.spin_limit))
         return;
       if (q >= a.capa && !wait_geq(dn_done + ld_relaxed(xq + q - a.capa), ndn, a.err, a.spin_limit))
@@ -327,7 +393,18 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
       const int mt = take_tile(q);
       if (mt < 0) return;
       if (mt >= nt) break;
+      const uint64_t tb = trace_clock();
+      if (a.flags & MOK_FLAG_POISON) {
+        // the slots' previous tiles are done with them (the waits above): poison this
+        // workgroup's rows of both before the new tile's bytes arrive
+        const ActPlanes pl = planes(q);
+        poison_rows(pl, pl, true, q >= a.capa, a.s.H, a.s.I, MX, local * 4 + wave, 4 * C, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
       gather(q, mt, local * 4 + wave, 4 * C);
+      const int b = macro_of(mt);
+      trace_item(a, kTrGather, x, b, mt - s_first[b], q, tw, tb);
     }
     return;
   }
@@ -368,17 +445,22 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
     const int b = macro_of(mt);
     const MTile tl = a.mb[b].tiles[mt - s_first[b]];
     const ActPlanes pl = planes(q);
+    const uint64_t tw = trace_clock();
     if (k < ngu) {
       if (!wait_geq(landed + mt, q < lag ? nx : C, a.err, a.spin_limit)) return;
       l1_invalidate();
+      const uint64_t tb = trace_clock();
       gateup_tile<MX>(sm, a.s, a.w, pl, 0, tl.nrows, tl.e, k * 128);
       signal(gu_done + mt);
+      trace_item(a, kTrGateUp, x, b, mt - s_first[b], it, tw, tb);
     } else {
       if (!wait_geq(gu_done + mt, ngu, a.err, a.spin_limit)) return;
       l1_invalidate();
+      const uint64_t tb = trace_clock();
       down_tile<MX, kPushRec>(sm, a.s, a.w, pl, 0, tl.row0, tl.nrows, tl.e, (k - ngu) * kTileN,
                               a.mb[b].perm, a.mb[b].push);
       signal(dn_done + mt);
+      trace_item(a, kTrDown, x, b, mt - s_first[b], it, tw, tb);
     }
   }
 }
@@ -501,6 +583,11 @@ hipError_t launch_layer_fwd_macro(const Layout& L, const mok_desc& d, int B,
   a.dtype = L.dtype;
   a.NK = L.NK;
   a.flags = d.flags;
+  if ((d.flags & MOK_FLAG_TRACE) && L.trace_max > 0) {
+    a.trace = reinterpret_cast<TraceRec*>(ws + L.ws_trace);
+    a.trace_max = L.trace_max;
+    a.trace_count = reinterpret_cast<int32_t*>(ws) + kWsTraceCount;
+  }
   a.spin_limit = (d.flags & MOK_FLAG_SKIP_ONE_SIGNAL) ? (1 << 12) : (1 << 24);
   void* args[] = {&a};
   const void* fn = mx ? reinterpret_cast<const void*>(k_layer_fwd<true>)

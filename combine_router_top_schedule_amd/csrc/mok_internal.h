@@ -41,6 +41,18 @@ struct alignas(16) PushRec {
   int32_t pad;
 };
 
+// One phase-trace record (MOK_FLAG_TRACE): which workgroup ran which item of which row tile, and
+// when (s_memrealtime ticks, a 100 MHz clock): t_wait when it started waiting for the item's
+// inputs, t_begin when they were there, t_end when its results were signalled.
+enum TraceKind : int { kTrPrologueGather = 1, kTrGather = 2, kTrGateUp = 3, kTrDown = 4 };
+struct TraceRec {
+  int32_t wg;        // workgroup (blockIdx.x)
+  int32_t info;      // kind | xcd << 8 | macrobatch << 16
+  int32_t tile;      // row tile within its macrobatch
+  int32_t item;      // the XCD's item number (GEMM items), or its row-tile index (gathers)
+  uint64_t t_wait, t_begin, t_end, pad;
+};
+
 // ---- saved (schedule table) header, int32 words ----------------------------------------
 enum SavedHeader : int {
   kHdrP = 0,        // local pairs
@@ -58,6 +70,7 @@ enum WsHeader : int {
   kWsError = 0,     // mok_status of the first device-side failure, 0 if none
   kWsTicket = 1,    // dynamic block id for the router's single-pass scan
   kWsNumTiles = 2,  // m-tiles in the tile table
+  kWsTraceCount = 3,  // phase-trace records written (MOK_FLAG_TRACE)
   kWsWords = 64,
 };
 
@@ -92,7 +105,8 @@ struct Layout {
   int64_t ring_share, xsb, asb;
   int ring_capx, ring_capa;
   // ws
-  int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_push, ws_bytes;
+  int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_push, ws_trace, ws_bytes;
+  int64_t trace_max;   // phase-trace records (MOK_FLAG_TRACE; 0 without it)
   int topk_blocks;
   int64_t tiles_max, J_max;
   // activation row bytes: X | GU | Hact
@@ -160,6 +174,12 @@ inline Layout make_layout(const mok_desc& d) {
   L.ws_counters = off; off = align_up(off + 4 * (64 + (3 + kXcds) * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
   L.ws_push = off; off = align_up(off + 16 * L.rows_max, 256);   // PushRec per row
+  // phase trace: a record per fused-forward item (gate/up and down tiles, gathers), for up to
+  // kMaxMacro macrobatches and 64 gathering workgroups per row tile
+  L.trace_max = (d.flags & MOK_FLAG_TRACE)
+                    ? int64_t(kMaxMacro) * L.tiles_max * (L.I / 128 + cdiv(L.H, kTileN) + 64)
+                    : 0;
+  L.ws_trace = off; off = align_up(off + int64_t(sizeof(TraceRec)) * L.trace_max, 256);
   L.ws_bytes = off;
   // staged
   L.xd_bytes = align_up(L.rows_max * L.x_row_bytes, 256);

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOK_ABI_VERSION 3
+#define MOK_ABI_VERSION 4
 
 typedef enum {
   MOK_OK = 0,
@@ -60,9 +60,32 @@ typedef enum {
 
 typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
 
-/* Debug flags (mok_desc.flags). */
+/* Debug flags (mok_desc.flags). None changes a result. */
 #define MOK_FLAG_SKIP_ONE_SIGNAL 0x1u  /* test only: withhold one ring signal so the bounded
                                           wait must expire and report a device timeout     */
+#define MOK_FLAG_TRACE 0x2u            /* the fused forward records one mok_trace_record per
+                                          item (gathers, gate/up and down tiles) in the
+                                          workspace: mok_sizes.trace_offset, up to
+                                          trace_records of them (the count is int32 word 3 of
+                                          ws; records past the capacity are dropped). The
+                                          workspace grows by the trace region.               */
+#define MOK_FLAG_POISON 0x4u           /* the fused forward fills a ring slot with NaN bytes
+                                          (0xFF) when it is released, before the slot's next
+                                          tile is gathered: any read of a released slot shows
+                                          up as NaN in the outputs                           */
+
+/* One phase-trace record (MOK_FLAG_TRACE). Times are s_memrealtime ticks (100 MHz). */
+typedef struct {
+  int32_t workgroup;
+  int32_t info;        /* kind (1 prologue gather, 2 gather, 3 gate/up tile, 4 down tile) |
+                          xcd << 8 | macrobatch << 16                                      */
+  int32_t tile;        /* row tile within its macrobatch                                 */
+  int32_t item;        /* the XCD's GEMM item number, or its row-tile index for gathers   */
+  uint64_t t_wait;     /* started waiting for the item's inputs                          */
+  uint64_t t_begin;    /* inputs there, work starts                                      */
+  uint64_t t_end;      /* results stored and signalled                                    */
+  uint64_t reserved;
+} mok_trace_record;
 
 /* Shapes and tunables of the layer, as the pages state it: hidden size, expert count, top-k,
  * expert intermediate size, BF16 or MXFP8 ("Mixture-of-Kittens (MoK)", benchmark section;
@@ -120,6 +143,8 @@ typedef struct {
    * 2 of ws. */
   int64_t tiles_offset;
   int64_t tiles_max;
+  int64_t trace_offset;   /* MOK_FLAG_TRACE: byte offset of the records inside ws (else 0)  */
+  int64_t trace_records;  /* capacity in records (0 without MOK_FLAG_TRACE)                 */
 } mok_sizes;
 
 /* Expert weights (device pointers). BF16 mode uses wg/wu/wd only. MXFP8 mode uses E4M3 codes

@@ -240,3 +240,49 @@ def test_autotune_measures_every_candidate_and_all_give_the_same_output():
         torch.cuda.synchronize()
         assert mok.mok_device_status(layer.ws) == 0
         assert torch.equal(case.out, ref), (m, c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_trace_and_poison_flags_leave_results_unchanged(dtype):
+    """MOK_FLAG_POISON fills every ring slot with NaN bytes when a new row tile takes it, before
+    that tile's rows arrive; MOK_FLAG_TRACE records each item of the fused forward. Neither
+    changes a bit of the forward or backward outputs (so no item read a slot before its data was
+    there), and the trace holds every item of every row tile exactly once, with times ordered as
+    the counters order them: a tile's gate/up items start after its gathers started, its down
+    items after all of its gate/up items started."""
+    from combine_router_top_schedule_amd import trace
+    from tests._gpu import BwdCase
+    # ~64 row tiles through the smallest ring: every slot is reused several times
+    cfg = datagen.CONFIGS["tiny"].replace(S=4, T=256, M=64, x_std=1.0, dtype=dtype)
+    ring = mok.query_sizes(mok.desc_from_config(cfg)).ring_min_bytes
+    ref = BwdCase(cfg, fused=True, ring_bytes=ring)
+    ref.run(fused=True)
+    want = [ref.out.clone()] + ref.grads()
+    ngu, ndn = cfg.I // 128, -(-cfg.H // 256)
+    for flags in (mok.MOK_FLAG_POISON, mok.MOK_FLAG_TRACE,
+                  mok.MOK_FLAG_POISON | mok.MOK_FLAG_TRACE):
+        case = BwdCase(cfg, fused=True, ring_bytes=ring, flags=flags)
+        case.run(fused=True)
+        for a, b in zip(want, [case.out.clone()] + case.grads()):
+            assert torch.equal(a, b), flags
+        if not flags & mok.MOK_FLAG_TRACE:
+            continue
+        L = case.layer
+        rec, count = trace.read(L.ws, L.sizes)
+        assert count == len(rec) > 0
+        kind, xcd, macro = trace.fields(rec)
+        assert (macro == 0).all()
+        assert (rec["t_wait"] <= rec["t_begin"]).all() and (rec["t_begin"] <= rec["t_end"]).all()
+        ntiles = len(L.tiles())
+        for t in range(ntiles):
+            m = rec["tile"] == t
+            gathers = m & (kind <= 2)
+            gu, dn = m & (kind == 3), m & (kind == 4)
+            assert gathers.any() and gu.sum() == ngu and dn.sum() == ndn, t
+            assert len(np.unique(xcd[m])) == 1, t          # a row tile stays on one XCD
+            assert rec["t_begin"][gu].min() >= rec["t_begin"][gathers].max(), t
+            assert rec["t_begin"][dn].min() >= rec["t_begin"][gu].max(), t
+        assert set(np.unique(rec["tile"])) == set(range(ntiles))
+        s = trace.summarize(rec)
+        print(f"  {dtype} flags {flags}: {s['records']} records, {s['span_us']} us, GEMM workers "
+              f"busy {s['gemm_busy_frac']:.2f}, waiting {s['gemm_wait_frac']:.2f}")

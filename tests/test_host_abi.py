@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert mok.abi_version() == 3
+    assert mok.abi_version() == 4
     for code in range(11):
         assert mok.lib().mok_status_str(code)
 
