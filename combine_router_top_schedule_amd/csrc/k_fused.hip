@@ -12,8 +12,9 @@
 // counter whenever it has free ring slots, so the row tiles spread over the XCDs by speed. A
 // row tile (<= 256 expert-ordered rows of one expert inside one minibatch) is produced and
 // consumed inside one XCD, so its ring bytes stay coherent in that XCD's L2: producers complete
-// their stores before bumping a counter, and a consumer invalidates only its CU's L1 after
-// seeing the counter. Each XCD owns a fixed share of the ring, cut into two kinds of slots used
+// their stores before bumping a counter, and consumers read ring rows with agent-scope loads
+// that miss in their CU's L1 (a slot is reused for one row tile after another, so an L1 line
+// kept from an earlier tile would be stale). Each XCD owns a fixed share of the ring, cut into two kinds of slots used
 // round-robin: gather slots hold a row tile's X rows until its gate/up tiles are done;
 // activation slots hold its g|u and h until its down tiles are done, and after the kernel the
 // last capa of them stay for the backward's reverse walk. Splitting the two lets one ring keep
@@ -94,12 +95,11 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & (kMaxXcd - 1);  // HW_REG_XCC_ID
 }
 
-// Acquire at agent scope after a counter wait, so later loads see what other CUs of the XCD
-// stored to L2: on gfx950 this invalidates the CU's vector L1 (buffer_inv sc1). A
-// workgroup-scope invalidate (buffer_inv sc0) is not enough: a CU that stored rows of a ring
-// slot earlier (every workgroup gathers the first row tiles) kept those lines in its L1 and
-// read them back, stale, when the slot held a later tile.
-__device__ __forceinline__ void l1_invalidate() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// After a counter wait no cache maintenance is needed: every read of ring rows is a GEMM
+// A-operand stage load, issued at agent scope (sc1), so it misses in the CU's L1 and sees what
+// other CUs of the XCD stored to L2. (A workgroup-scope invalidate is not enough: a CU that
+// read or stored rows of a ring slot for an earlier tile can keep those lines in its L1; an
+// agent-scope acquire after each wait, buffer_inv sc1, is correct but measured 1-2 % slower.)
 
 // Thread 0 waits until *p >= target (bounded); returns false (for the whole workgroup) if the
 // wait failed or another worker already reported an error.
@@ -448,14 +448,12 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
     const uint64_t tw = trace_clock();
     if (k < ngu) {
       if (!wait_geq(landed + mt, q < lag ? nx : C, a.err, a.spin_limit)) return;
-      l1_invalidate();
       const uint64_t tb = trace_clock();
       gateup_tile<MX>(sm, a.s, a.w, pl, 0, tl.nrows, tl.e, k * 128);
       signal(gu_done + mt);
       trace_item(a, kTrGateUp, x, b, mt - s_first[b], it, tw, tb);
     } else {
       if (!wait_geq(gu_done + mt, ngu, a.err, a.spin_limit)) return;
-      l1_invalidate();
       const uint64_t tb = trace_clock();
       down_tile<MX, kPushRec>(sm, a.s, a.w, pl, 0, tl.row0, tl.nrows, tl.e, (k - ngu) * kTileN,
                               a.mb[b].perm, a.mb[b].push);

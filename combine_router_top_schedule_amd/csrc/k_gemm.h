@@ -97,11 +97,19 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
 }
 
+// Cache policy of a stage load. kLoadAgent (sc1): agent scope, the load misses in the CU's L1
+// and is served by the XCD's L2. A-operand rows can be rows another CU of the XCD stored
+// during the same launch (ring slots of the fused forward, reused for one row tile after
+// another), and an L1 line kept from an earlier read of the same address would be stale;
+// the A tile of a workgroup is read once per stage, so bypassing L1 costs nothing (measured).
+constexpr int kLoadDefault = 0, kLoadAgent = 16;
+
 // Issue the loads of stage kt (128 bytes of every row, and in MXFP8 mode the 4 scale bytes of
 // every row) into one LDS stage. Wave w covers rows 64w .. 64w+63: 8 loads of 8 rows x 128
 // bytes. Lane L of load c lands at LDS offset 16*L: row 64w + 8c + L/8, physical chunk L%8,
 // which holds the logical chunk (L%8) ^ f(row) of the swizzled layout, where
 // f(row) = (L/8) ^ (c & 1) because 64w + 8c is a multiple of 8.
+template <int POLICY>
 __device__ __forceinline__ void issue_stage(const Operand& op, uint8_t* lds, uint32_t* lds_s, int kt,
                                             bool mx, int w) {
   // The lane's offsets are recomputed per stage (a few VALU operations) rather than hoisted out
@@ -120,12 +128,12 @@ __device__ __forceinline__ void issue_stage(const Operand& op, uint8_t* lds, uin
     const int lchunk = lchunk0 ^ (c & 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + (w * 64 + 8 * c) * kStageRowBytes),
                                              16, lrow * op.stride + kt * kStageRowBytes + lchunk * 16,
-                                             0, 0, 0);
+                                             0, 0, POLICY);
   }
   if (mx) {
     const __amdgpu_buffer_rsrc_t rs = odd ? op.s1 : op.s0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_s + w * 64), 4,
-                                             (rbase + L) * op.sstride + kt * 4, 0, 0, 0);
+                                             (rbase + L) * op.sstride + kt * 4, 0, 0, POLICY);
   }
 }
 
@@ -221,8 +229,8 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   if (ksteps <= 0) return;
   const int w = wave_id();
-  issue_stage(A, sm.a[0], sm.as[0], 0, MX, w);
-  issue_stage(B, sm.b[0], sm.bs[0], 0, MX, w);
+  issue_stage<kLoadAgent>(A, sm.a[0], sm.as[0], 0, MX, w);
+  issue_stage<kLoadDefault>(B, sm.b[0], sm.bs[0], 0, MX, w);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frag f[2];
@@ -235,13 +243,13 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
     // competing with one slice's fragment reads (measured +9 %). E4M3 (2 slices): both before
     // slice 0, which leaves the whole stage to cover their latency.
     if (more && MX) {
-      issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX, w);
-      issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX, w);
+      issue_stage<kLoadAgent>(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX, w);
+      issue_stage<kLoadDefault>(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX, w);
     }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      if (!MX && more && kk == 0) issue_stage(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX, w);
-      if (!MX && more && kk == 1) issue_stage(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX, w);
+      if (!MX && more && kk == 0) issue_stage<kLoadAgent>(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, MX, w);
+      if (!MX && more && kk == 1) issue_stage<kLoadDefault>(B, sm.b[cur ^ 1], sm.bs[cur ^ 1], kt + 1, MX, w);
       // Scheduling fences keep each phase whole: the compiler would otherwise interleave the
       // MFMAs of slice kk with the fragment reads of slice kk+1 and wait on those reads.
       __builtin_amdgcn_sched_barrier(0);
