@@ -57,7 +57,8 @@ _P = ctypes.c_void_p
 
 class MokWeights(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("wg", "wu", "wd", "wg_q", "wg_s", "wu_q", "wu_s", "wd_q",
-                                  "wd_s", "wgt_q", "wgt_s", "wut_q", "wut_s", "wdt_q", "wdt_s")]
+                                  "wd_s", "wgt_q", "wgt_s", "wut_q", "wut_s", "wdt_q", "wdt_s",
+                                  "wg_t", "wu_t", "wd_t")]
 
 
 class MokTuneResult(ctypes.Structure):
@@ -99,6 +100,8 @@ _SIGS = {
                                      ctypes.POINTER(MokWeightGrads), _P, _P]),
     "mok_quantize_mx": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
                                        ctypes.c_int32, _P, _P, _P]),
+    "mok_transpose_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                          _P]),
     "mok_device_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
     "mok_autotune": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
                                     _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
@@ -318,6 +321,15 @@ def mok_quantize_mx(src, transpose: bool, codes, scales, stream=None):
     batch, rows, cols = (1,) + shape if len(shape) == 2 else shape
     _check("mok_quantize_mx", lib().mok_quantize_mx(batch, rows, cols, _ptr(src), int(transpose),
                                                     _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def mok_transpose_bf16(src, dst, stream=None):
+    """BF16 [batch][rows][cols] (or [rows][cols]) -> dst [batch][cols][rows]."""
+    _need_cuda(src, dst)
+    shape = tuple(src.shape)
+    batch, rows, cols = (1,) + shape if len(shape) == 2 else shape
+    _check("mok_transpose_bf16", lib().mok_transpose_bf16(batch, rows, cols, _ptr(src), _ptr(dst),
+                                                          _stream(stream)))
 
 
 def mok_autotune(d: MokDesc, x_seg, logits, w: MokWeights, out_seg, topk_idx, topk_p, saved,

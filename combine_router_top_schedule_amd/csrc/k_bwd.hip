@@ -569,6 +569,13 @@ int grid_cap(int64_t items, int cap) {
 
 }  // namespace
 
+hipError_t launch_transpose_w(const uint16_t* src, uint16_t* dst, int batch, int R, int C,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(batch) * R * C / 8192, 8192)), dim3(256), 0, s,
+                     src, dst, batch, R, C);
+  return hipGetLastError();
+}
+
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) {
   static std::atomic<bool> attr_done[kMaxDevices];
   hipError_t err = once_per_device(attr_done, [] {
@@ -624,16 +631,18 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   //    (MXFP8: the gather quantises along H on the way, like the forward dispatch)
   //    (BF16: D is written by the (p D)^T gather-transpose below, which reads the same rows)
   if (mx && (err = launch_dispatch(L, b.saved, b.dout_seg, b.dq, s)) != hipSuccess) return err;
-  // 3. transposed BF16 weights for the backward GEMMs
-  if (!mx) {
-    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 8192, 8192)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(b.w.wd), b.wdt, El, H, I);
-    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 8192, 8192)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(b.w.wg), b.wgt, El, I, H);
-    hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(El) * H * I / 8192, 8192)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(b.w.wu), b.wut, El, I, H);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  // 3. transposed BF16 weights for the backward GEMMs: the caller's (made once per weight
+  //    update), or made here into the workspace
+  const bool given_t = !mx && b.w.wg_t && b.w.wu_t && b.w.wd_t;
+  if (!mx && !given_t) {
+    if ((err = launch_transpose_w(static_cast<const uint16_t*>(b.w.wd), b.wdt, El, H, I, s)) != hipSuccess ||
+        (err = launch_transpose_w(static_cast<const uint16_t*>(b.w.wg), b.wgt, El, I, H, s)) != hipSuccess ||
+        (err = launch_transpose_w(static_cast<const uint16_t*>(b.w.wu), b.wut, El, I, H, s)) != hipSuccess)
+      return err;
   }
+  const uint8_t* wdt_bf = reinterpret_cast<const uint8_t*>(given_t ? b.w.wd_t : b.wdt);
+  const uint8_t* wgt_bf = reinterpret_cast<const uint8_t*>(given_t ? b.w.wg_t : b.wgt);
+  const uint8_t* wut_bf = reinterpret_cast<const uint8_t*>(given_t ? b.w.wu_t : b.wut);
   // 4. weight-gradient operand planes that do not need dg|du: per-expert column ranges, X^T,
   //    (p D)^T and h^T (MXFP8: quantised along tokens as they are written)
   const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
@@ -674,16 +683,16 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.s = FfnShape{H, I};
   a.d = mx ? b.dq : b.d;
   a.d_s = mx ? b.dq + L.rows_max * H : nullptr;
-  a.wdt = mx ? b.w.wdt_q : reinterpret_cast<const uint8_t*>(b.wdt);
+  a.wdt = mx ? b.w.wdt_q : wdt_bf;
   a.wdt_s = mx ? b.w.wdt_s : nullptr;
   a.act = asrc;
   a.dgu = b.dgu;
   a.dp_part = b.dp_part;
   a.dgu_a = mx ? b.dguq : reinterpret_cast<const uint8_t*>(b.dgu);
   a.dgu_s = mx ? b.dguq + L.rows_max * 2 * I : nullptr;
-  a.wgt = mx ? b.w.wgt_q : reinterpret_cast<const uint8_t*>(b.wgt);
+  a.wgt = mx ? b.w.wgt_q : wgt_bf;
   a.wgt_s = mx ? b.w.wgt_s : nullptr;
-  a.wut = mx ? b.w.wut_q : reinterpret_cast<const uint8_t*>(b.wut);
+  a.wut = mx ? b.w.wut_q : wut_bf;
   a.wut_s = mx ? b.w.wut_s : nullptr;
   a.push = PushTarget{b.slots, b.push};
   a.ld = ld;

@@ -53,6 +53,13 @@ mok_status check_weights(const mok_desc* d, const mok_weights* w, bool backward)
   if (d->dtype == MOK_BF16) {
     if (!w->wg || !w->wu || !w->wd) return MOK_ERR_NULL;
     if (!aligned16(w->wg) || !aligned16(w->wu) || !aligned16(w->wd)) return MOK_ERR_ALIGN;
+    if (backward) {
+      // the transposed weights come as a set, or not at all
+      const int given = (w->wg_t != nullptr) + (w->wu_t != nullptr) + (w->wd_t != nullptr);
+      if (given != 0 && given != 3) return MOK_ERR_NULL;
+      if (given == 3 && (!aligned16(w->wg_t) || !aligned16(w->wu_t) || !aligned16(w->wd_t)))
+        return MOK_ERR_ALIGN;
+    }
   } else {
     if (!w->wg_q || !w->wg_s || !w->wu_q || !w->wu_s || !w->wd_q || !w->wd_s) return MOK_ERR_DTYPE;
     if (!aligned16(w->wg_q) || !aligned16(w->wu_q) || !aligned16(w->wd_q)) return MOK_ERR_ALIGN;
@@ -231,6 +238,19 @@ mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void
   if (!aligned16(codes_dev)) return MOK_ERR_ALIGN;
   return hip_status(launch_quantize_mx(batch, rows, cols, static_cast<const uint16_t*>(src_dev),
                                        transpose, codes_dev, scales_dev, as_stream(stream)));
+}
+
+mok_status mok_transpose_bf16(int32_t batch, int32_t rows, int32_t cols, const void* src_dev,
+                              void* dst_dev, void* stream) {
+  if (!src_dev || !dst_dev) return MOK_ERR_NULL;
+  if (batch < 1 || rows < 64 || cols < 128 || rows % 64 || cols % 128) return MOK_ERR_SHAPE;
+  if (!aligned16(src_dev) || !aligned16(dst_dev)) return MOK_ERR_ALIGN;
+  const int64_t bytes = int64_t(batch) * rows * cols * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src_dev), b = reinterpret_cast<uintptr_t>(dst_dev);
+  if (a < b + bytes && b < a + bytes) return MOK_ERR_SHAPE;   // overlapping buffers
+  return hip_status(launch_transpose_w(static_cast<const uint16_t*>(src_dev),
+                                       static_cast<uint16_t*>(dst_dev), batch, rows, cols,
+                                       as_stream(stream)));
 }
 
 mok_status mok_device_status(const void* ws_dev, void* stream, mok_status* out) {

@@ -359,6 +359,9 @@ struct BwdBuffers {
   PushRec* push;      // [rows_max] dx GEMM push records
 };
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
+// W [batch][R][C] -> [batch][C][R], BF16; R a multiple of 64, C a multiple of 128.
+hipError_t launch_transpose_w(const uint16_t* src, uint16_t* dst, int batch, int R, int C,
+                              hipStream_t s);
 
 // Fused forward (k_fused.hip): the ring is split into one share per XCD, each cut into tile
 // slots of 256 expert-ordered rows (X | g,u | h).

@@ -161,6 +161,11 @@ typedef struct {
   const void* wd;
   const uint8_t *wg_q, *wg_s, *wu_q, *wu_s, *wd_q, *wd_s;
   const uint8_t *wgt_q, *wgt_s, *wut_q, *wut_s, *wdt_q, *wdt_s;
+  /* BF16 backward, optional: the transposed weights Wg^T, Wu^T [E_loc][H][I] and Wd^T
+   * [E_loc][I][H] (the backward GEMMs reduce over the other axis of each weight), made once per
+   * weight update with mok_transpose_bf16. When all three are set mok_layer_bwd reads them;
+   * when all three are NULL it transposes into its workspace on every call (3 launches). */
+  const void *wg_t, *wu_t, *wd_t;
 } mok_weights;
 
 /* Weight gradients, fp32, same layouts as the BF16 weights. Fully overwritten. */
@@ -347,6 +352,13 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
 mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void* src_dev,
                            int32_t transpose, uint8_t* codes_dev, uint8_t* scales_dev,
                            void* stream);
+
+/* BF16 transpose of `batch` matrices [rows][cols] -> [cols][rows] (rows a multiple of 64, cols
+ * a multiple of 128; 16-byte aligned device pointers, src and dst not overlapping). Makes the
+ * backward blocking of BF16 weights (mok_weights.wg_t, wu_t, wd_t) once per weight update, the
+ * counterpart of mok_quantize_mx's transposed MXFP8 blocking. Stream-ordered, no host sync. */
+mok_status mok_transpose_bf16(int32_t batch, int32_t rows, int32_t cols, const void* src_dev,
+                              void* dst_dev, void* stream);
 
 /* One measured configuration of mok_autotune. */
 typedef struct {

@@ -226,3 +226,23 @@ def test_backward_after_timed_out_forward_replays_every_row():
     good.run(fused=False)
     for a, b in zip(bad.grads(), good.grads()):
         assert torch.equal(a, b)
+
+
+def test_backward_with_caller_transposed_weights_equals_per_call_transposes():
+    """BF16: the backward reading transposed weights made once by mok_transpose_bf16 (the
+    layer's default) gives bit for bit the outputs of the backward that transposes the weights
+    into its workspace on every call; mok_transpose_bf16 equals torch's transpose exactly."""
+    cfg = datagen.CONFIGS["tiny"].replace(S=3, T=512, H=1024, E=16, K=4, I=384, e0=4, E_loc=4,
+                                          x_std=1.0)
+    case = BwdCase(cfg)
+    assert case.layer.w.wg_t and case.layer.w.wu_t and case.layer.w.wd_t
+    case.run()
+    with_t = case.grads()
+    wd_t = torch.empty((cfg.E_loc, cfg.I, cfg.H), dtype=case.wd.dtype, device="cuda")
+    mok.mok_transpose_bf16(case.wd, wd_t)
+    assert torch.equal(wd_t, case.wd.transpose(1, 2).contiguous())
+    case.layer.set_weights(case.wg, case.wu, case.wd, transposed=False)
+    assert not case.layer.w.wg_t
+    case.run()
+    for a, b in zip(with_t, case.grads()):
+        assert torch.equal(a, b)
