@@ -142,6 +142,69 @@ def cpu_baseline(cfg, target_s: float = 4.0) -> dict:
                       f"one_thread_value: segment 0 alone with one BLAS thread"}
 
 
+def staged_line(args, cfg, L, mok, torch, x_seg, logits, out_seg) -> dict:
+    """The staged forward, timed whole and with HIP events around its pull-dispatch gather and
+    its merge (every touched token), each against the HBM peak with its algorithmic bytes:
+    dispatch reads and writes every local pair's row (plus the row map), the merge reads every
+    pair's pushed row and each touched token's indices and gates and writes its output row."""
+    def step():
+        L.forward_staged(x_seg, logits, out_seg)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(K):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    hdr = L.header()
+    P, rows, U = int(hdr[0]), int(hdr[1]), int(hdr[2])
+    mx = cfg.dtype == "mxfp8"
+    row_out = cfg.H + cfg.H // 32 if mx else 2 * cfg.H
+    work = {"k_dispatch": (mok.MOK_TRACE_DISPATCH, P * cfg.H * 2 + P * row_out + rows * 4,
+                           "pull-dispatch gather (P rows read from the segments, written in "
+                           "expert order" + (", quantised" if mx else "") + ")"),
+            "k_combine": (mok.MOK_TRACE_COMBINE, P * cfg.H * 2 + U * cfg.H * 2 + U * cfg.K * 8,
+                          "weighted merge of every touched token (P pushed rows read, U output "
+                          "rows written)")}
+    kernels = {}
+    for name, (tr, nbytes, what) in work.items():
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        for i in range(K):
+            mok.mok_trace_kernel(tr, *ev[i])
+            step()
+        torch.cuda.synchronize()
+        mok.mok_trace_kernel(mok.MOK_TRACE_NONE)
+        t = sum(a.elapsed_time(b) for a, b in ev) / K
+        gbs = nbytes / (t * 1e-3) / 1e9
+        kernels[name] = {"what": what, "avg_ms": round(t, 4), "bytes": int(nbytes),
+                         "gb_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    return {
+        "metric": "MoE layer tokens/sec fwd, staged path (dispatch and merge bandwidth)",
+        "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded PCG64: X ~ N(0,1), logits ~ N(0,1), W ~ N(0,0.02^2))",
+        "config": {"workload": f"{cfg.name} local share, staged fwd", "hidden": cfg.H,
+                   "experts": cfg.E, "top_k": cfg.K, "intermediate": cfg.I,
+                   "local_experts": cfg.E_loc, "segments": cfg.S, "tokens_per_segment": cfg.T,
+                   "minibatch": cfg.M, "pairs": P, "touched_tokens": U},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gb_s"],
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kernels[dom]["hbm_frac"],
+                     "traffic": None},
+        "detail": {"kernels": kernels},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +218,10 @@ def main() -> int:
                     help="time mok_layer_fwd alone (minibatch sweeps); not the headline metric")
     ap.add_argument("--tune", action="store_true",
                     help="run mok_autotune first (minibatch and dispatch-CU split for this shape)")
+    ap.add_argument("--staged", action="store_true",
+                    help="time the staged forward (mok_schedule, mok_dispatch, mok_expert_ffn, "
+                         "mok_combine over every touched token) and report the dispatch gather "
+                         "and the merge against HBM bandwidth; not the headline metric")
     ap.add_argument("--trace", action="store_true",
                     help="after the timed steps, run one forward with the phase trace on "
                          "(MOK_FLAG_TRACE) and report its summary under detail.fused_trace")
@@ -186,7 +253,7 @@ def main() -> int:
 
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     d = mok.desc_from_config(cfg)
-    L = MokLayer(d, device=dev, staged=False, fused=True)
+    L = MokLayer(d, device=dev, staged=args.staged, fused=not args.staged)
     buf = np.empty((cfg.N, cfg.H), dtype=np.uint16)
     x = up(datagen.x_all(cfg, buf))
     dout = up(datagen.dout_all(cfg, buf))
@@ -215,6 +282,13 @@ def main() -> int:
         L.forward(x_seg, logits, out_seg)
         if not args.forward_only:
             L.backward(dout_seg, x_seg, dx_seg, dp, dlogits, dwg, dwu, dwd)
+
+    if args.staged:
+        line = staged_line(args, cfg, L, mok, torch, x_seg, logits, out_seg)
+        del L, x, dout, logits, out, dx, x_seg, out_seg, dout_seg, dx_seg
+        torch.cuda.synchronize()
+        print(json.dumps(line), flush=True)
+        return 0
 
     tuning = None
     if args.tune:

@@ -112,7 +112,8 @@ _SIGS = {
     "mok_trace_kernel": (ctypes.c_int, [ctypes.c_int32, _P, _P]),
 }
 
-MOK_TRACE_NONE, MOK_TRACE_FUSED_FWD, MOK_TRACE_BWD_GEMM1, MOK_TRACE_BWD_GEMM2 = range(4)
+(MOK_TRACE_NONE, MOK_TRACE_FUSED_FWD, MOK_TRACE_BWD_GEMM1, MOK_TRACE_BWD_GEMM2, MOK_TRACE_DISPATCH,
+ MOK_TRACE_COMBINE) = range(6)
 
 _lib = None
 

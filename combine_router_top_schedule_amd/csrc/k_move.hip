@@ -198,11 +198,13 @@ hipError_t launch_fill_ranges(const FillRange* r, int count, hipStream_t s) {
 hipError_t launch_dispatch(const Layout& L, const uint8_t* saved, const void* const* x_seg,
                            uint8_t* xd, hipStream_t s) {
   const int cap = 8 * (device_cus() > 0 ? device_cus() : 256);
+  trace_before(MOK_TRACE_DISPATCH, s);
   hipLaunchKernelGGL(k_dispatch, dim3(grid_for(L.rows_max, 4, cap)), dim3(256), 0, s,
                      reinterpret_cast<const int32_t*>(saved),
                      reinterpret_cast<const int32_t*>(saved + L.sv_perm),
                      reinterpret_cast<const uint16_t* const*>(x_seg), xd, L.rows_max, L.H, L.K,
                      L.S, L.T, L.dtype);
+  trace_after(MOK_TRACE_DISPATCH, s);
   return hipGetLastError();
 }
 
@@ -210,12 +212,14 @@ hipError_t launch_combine(const Layout& L, const uint8_t* saved, const int32_t* 
                           const uint16_t* slots, void* const* out_seg, bool skip_sole,
                           hipStream_t s) {
   const int cap = 8 * (device_cus() > 0 ? device_cus() : 256);
+  trace_before(MOK_TRACE_COMBINE, s);
   hipLaunchKernelGGL(k_combine, dim3(grid_for(L.N, 4, cap)), dim3(256), 0, s,
                      reinterpret_cast<const int32_t*>(saved), skip_sole ? kHdrUm : kHdrU,
                      reinterpret_cast<const int32_t*>(saved + (skip_sole ? L.sv_multi
                                                                          : L.sv_touched)),
                      idx, p, slots, reinterpret_cast<uint16_t* const*>(out_seg), L.H, L.K, L.S,
                      L.T, L.e0, L.El);
+  trace_after(MOK_TRACE_COMBINE, s);
   return hipGetLastError();
 }
 

@@ -114,7 +114,7 @@ int64_t mok_two_wave_floor(int32_t cus, int32_t tile_m, int32_t tile_n, int32_t 
 int32_t mok_device_cus(void) { return device_cus(); }
 
 mok_status mok_trace_kernel(int32_t kernel, void* before, void* after) {
-  if (kernel < MOK_TRACE_NONE || kernel > MOK_TRACE_BWD_GEMM2) return MOK_ERR_SHAPE;
+  if (kernel < MOK_TRACE_NONE || kernel > MOK_TRACE_COMBINE) return MOK_ERR_SHAPE;
   g_trace.kernel = (before && after) ? kernel : MOK_TRACE_NONE;
   g_trace.before = reinterpret_cast<hipEvent_t>(before);
   g_trace.after = reinterpret_cast<hipEvent_t>(after);

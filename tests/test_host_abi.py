@@ -89,3 +89,12 @@ def test_two_wave_floor_matches_pages_figure():
     # MI355X, 256 CUs: 256 x 256 tiles -> 8192 tokens; 128 x 128 -> 2048.
     assert mok.two_wave_floor(256, 256, 256, 2048) == 8192
     assert mok.two_wave_floor(256, 128, 128, 2048) == 2048
+
+
+def test_measurement_hook_kernel_ids():
+    # fused forward, the two backward GEMM launches, the dispatch gather and the merge;
+    # null events switch the hook off
+    for k in range(6):
+        mok.mok_trace_kernel(k)
+    with pytest.raises(mok.MokError):
+        mok.mok_trace_kernel(6)
