@@ -89,6 +89,36 @@ struct TokQuant {
   int padlim;           // rows of the tile inside the expert's padded range
 };
 
+// Reduce-scatter of |x| over the 32 lanes of a half-wave: lane l holds 16 values x[v] (one per
+// accumulator row v, its own column); on return it holds, for the row index
+// scatter_row(l) = 8 b4 + 4 b3 + 2 b2 + b1 (b = bits of l), the largest |x| over all 32 lanes
+// of its half-wave (lanes l and l ^ 1 hold the same row). Exchanges 8 + 4 + 2 + 1 + 1 values.
+__device__ __forceinline__ int scatter_row(int lane) {
+  return ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1);
+}
+__device__ __forceinline__ float half_wave_row_amax(const float (&x)[16], int lane) {
+  float m8[8], m4[4], m2[2];
+  const bool b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float keep = fabsf(b4 ? x[k + 8] : x[k]), send = fabsf(b4 ? x[k] : x[k + 8]);
+    m8[k] = fmaxf(keep, __shfl_xor(send, 16, 64));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = b3 ? m8[k + 4] : m8[k], send = b3 ? m8[k] : m8[k + 4];
+    m4[k] = fmaxf(keep, __shfl_xor(send, 8, 64));
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = b2 ? m4[k + 2] : m4[k], send = b2 ? m4[k] : m4[k + 2];
+    m2[k] = fmaxf(keep, __shfl_xor(send, 4, 64));
+  }
+  const float keep = b1 ? m2[1] : m2[0], send = b1 ? m2[0] : m2[1];
+  const float m1 = fmaxf(keep, __shfl_xor(send, 2, 64));
+  return fmaxf(m1, __shfl_xor(m1, 1, 64));
+}
+
 // Compute one staged 32-row block (i, a template argument so the accumulator stays in
 // registers): dg, du, dp partials, then dg | du rows out.
 // BF16: dg, du replace g, u in LDS (BF16) and leave as BF16 rows.
@@ -103,7 +133,8 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
                                                  uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s,
                                                  const TokQuant& tq, float* s_dp,
                                                  uint16_t* lg, uint16_t* lu, const uint16_t* lh,
-                                                 const float* lpg, int wm, int wn, int lane) {
+                                                 const float* lpg, float* lam, int wm, int wn,
+                                                 int lane) {
     const int rbase = wm * 128 + i * 32;                                // tile row of lg row 0
     float part[16];
 #pragma unroll
@@ -128,16 +159,6 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         const float duv = dh * g * sg;
         if (ok) part[v] = fmaf(av, h, part[v]);
         if (MX) {
-          float ag = fabsf(dgv), au = fabsf(duv);
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) {
-            ag = fmaxf(ag, __shfl_xor(ag, off, 64));
-            au = fmaxf(au, __shfl_xor(au, off, 64));
-          }
-          const int eg = mx_block_exp(ag), eu = mx_block_exp(au);
-          const uint32_t lead = (lane & 31) == 0;
-          lg[lr * 128 + lc] = uint16_t((e4m3x2(dgv * exp2i(-eg), 0.f) & 0xFFu) | (lead * uint32_t(eg + 127) << 8));
-          lu[lr * 128 + lc] = uint16_t((e4m3x2(duv * exp2i(-eu), 0.f) & 0xFFu) | (lead * uint32_t(eu + 127) << 8));
           dgr[v] = dgv;
           dur[v] = duv;
         } else {
@@ -147,6 +168,27 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         }
       }
       if (MX) {
+        // Along I: the amax of each of the half-wave's 16 rows over its 32 columns, by a
+        // reduce-scatter over the 32 lanes (16 exchanges per operand instead of 5 per element),
+        // published through the wave's 256 bytes of LDS and read back by every lane.
+        const int hw = lane >> 5;
+        const float rg = half_wave_row_amax(dgr, lane), ru = half_wave_row_amax(dur, lane);
+        if ((lane & 1) == 0) {
+          const int k = scatter_row(lane);
+          lam[hw * 32 + k] = rg;
+          lam[hw * 32 + 16 + k] = ru;
+        }
+        __builtin_amdgcn_wave_barrier();   // (a wave's LDS accesses complete in order)
+        const uint32_t lead = (lane & 31) == 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = acc_row(v, lane);
+          const int eg = mx_block_exp(lam[hw * 32 + v]), eu = mx_block_exp(lam[hw * 32 + 16 + v]);
+          lg[lr * 128 + lc] = uint16_t((e4m3x2(dgr[v] * exp2i(-eg), 0.f) & 0xFFu) | (lead * uint32_t(eg + 127) << 8));
+          lu[lr * 128 + lc] = uint16_t((e4m3x2(dur[v] * exp2i(-eu), 0.f) & 0xFFu) | (lead * uint32_t(eu + 127) << 8));
+        }
+        __builtin_amdgcn_wave_barrier();   // lam is rewritten for the next j
+
         // Along tokens: this lane holds rows 8t + 4h + (0..3), t = 0..3, h = lane / 32, of
         // column c; lane ^ 32 the others. Rows past the tile's valid rows hold 0 (zero operand
         // rows, zero gate), which is the padding of the expert's last block.
@@ -160,17 +202,25 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         au = fmaxf(au, __shfl_xor(au, 32, 64));
         const int eg = mx_block_exp(ag), eu = mx_block_exp(au);
         const float ig = exp2i(-eg), iu = exp2i(-eu);
+        // Codes of rows 8t + 4h .. +3 as dword t; the two lanes of a column swap two dwords so
+        // lane h holds rows 16h .. 16h+15 in order and writes them with one 16-byte store.
+        uint32_t wg4[4], wu4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          wg4[t] = e4m3x2(dgr[4 * t] * ig, dgr[4 * t + 1] * ig) | (e4m3x2(dgr[4 * t + 2] * ig, dgr[4 * t + 3] * ig) << 16);
+          wu4[t] = e4m3x2(dur[4 * t] * iu, dur[4 * t + 1] * iu) | (e4m3x2(dur[4 * t + 2] * iu, dur[4 * t + 3] * iu) << 16);
+        }
+        const bool hi = (lane >> 5) != 0;
+        const uint32_t g0 = __shfl_xor(hi ? wg4[0] : wg4[2], 32, 64);
+        const uint32_t g1 = __shfl_xor(hi ? wg4[1] : wg4[3], 32, 64);
+        const uint32_t u0 = __shfl_xor(hi ? wu4[0] : wu4[2], 32, 64);
+        const uint32_t u1 = __shfl_xor(hi ? wu4[1] : wu4[3], 32, 64);
+        const u32x4 og = hi ? u32x4{g0, wg4[2], g1, wg4[3]} : u32x4{wg4[0], g0, wg4[1], g1};
+        const u32x4 ou = hi ? u32x4{u0, wu4[2], u1, wu4[3]} : u32x4{wu4[0], u0, wu4[1], u1};
         if (c < s.I && rbase < tq.padlim) {
           const int64_t col = tq.colbase + rbase;
-          uint8_t* pg_ = tq.dg + int64_t(c) * tq.cols + col + 4 * (lane >> 5);
-          uint8_t* pu_ = tq.du + int64_t(c) * tq.cols + col + 4 * (lane >> 5);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            *reinterpret_cast<uint32_t*>(pg_ + 8 * t) =
-                e4m3x2(dgr[4 * t] * ig, dgr[4 * t + 1] * ig) | (e4m3x2(dgr[4 * t + 2] * ig, dgr[4 * t + 3] * ig) << 16);
-            *reinterpret_cast<uint32_t*>(pu_ + 8 * t) =
-                e4m3x2(dur[4 * t] * iu, dur[4 * t + 1] * iu) | (e4m3x2(dur[4 * t + 2] * iu, dur[4 * t + 3] * iu) << 16);
-          }
+          *reinterpret_cast<u32x4*>(tq.dg + int64_t(c) * tq.cols + col + 16 * (lane >> 5)) = og;
+          *reinterpret_cast<u32x4*>(tq.du + int64_t(c) * tq.cols + col + 16 * (lane >> 5)) = ou;
           if (lane < 32) {
             tq.dg[int64_t(s.I) * tq.ld + int64_t(c) * (tq.cols / 32) + col / 32] = uint8_t(eg + 127);
             tq.du[int64_t(s.I) * tq.ld + int64_t(c) * (tq.cols / 32) + col / 32] = uint8_t(eu + 127);
@@ -226,10 +276,12 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
 //     (MXFP8: codes dgq[row][i], [I + i] blocked along I, and dg^T, du^T blocked along tokens)
 //   dp partial = sum over this tile's columns of a h (fixed tree)   -> dp_part[row][c0/256]
 // The epilogue's LDS carve-out is laid out for exactly 4 waves: 24 KB per wave in the first
-// three stage buffers, dp partials, gates and row-source codes in the fourth.
+// three stage buffers, dp partials, gates, row-source codes and (MXFP8) the row amaxes along I
+// in the fourth.
 static_assert(kThreads == 256, "a_tile's LDS regions assume 4 waves");
 static_assert(4 * 24576 <= 3 * kStageBytes, "per-wave regions must end before the fourth stage buffer");
-static_assert(6144 + 4 * 128 * 4 <= kStageBytes, "dp partials, gates and codes fit one stage buffer");
+static_assert(6144 + 4 * 128 * 4 <= 8192, "dp partials, gates and codes end before the amaxes");
+static_assert(8192 + 4 * 64 * 4 <= kStageBytes, "the row amaxes fit the fourth stage buffer");
 template <bool MX>
 __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t row0, int nrows,
                                        int e, int c0, const uint8_t* d, const uint8_t* d_s,
@@ -266,6 +318,7 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   const int colw = c0 + wn * 128;                                       // wave's first column
   float* lpg = reinterpret_cast<float*>(sm.b[1] + 4096) + wave * 128;    // gates of the wave's rows
   int32_t* lcode = reinterpret_cast<int32_t*>(sm.b[1] + 6144) + wave * 128;  // their sources
+  float* lam = reinterpret_cast<float*>(sm.b[1] + 8192) + wave * 64;   // MXFP8 row amaxes along I
   // gates and row-source codes of the wave's 128 rows (lane l: row wm*128 + l, l < 128 over
   // two halves)
   for (int l = lane; l < 128; l += 64) {
@@ -284,8 +337,7 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
                                  lcode + (I_ + 1) * 32, lane);                                   \
     __builtin_amdgcn_wave_barrier();                                                             \
     a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, dgq, dgq_s, tq, s_dp, lg, lu, lh,    \
-                             lpg + I_ * 32, wm,                                                  \
-                             wn, lane);                                                          \
+                             lpg + I_ * 32, lam, wm, wn, lane);                                  \
   }
   MOK_A_BLOCK(0)
   MOK_A_BLOCK(1)
