@@ -89,36 +89,6 @@ struct TokQuant {
   int padlim;           // rows of the tile inside the expert's padded range
 };
 
-// Reduce-scatter of |x| over the 32 lanes of a half-wave: lane l holds 16 values x[v] (one per
-// accumulator row v, its own column); on return it holds, for the row index
-// scatter_row(l) = 8 b4 + 4 b3 + 2 b2 + b1 (b = bits of l), the largest |x| over all 32 lanes
-// of its half-wave (lanes l and l ^ 1 hold the same row). Exchanges 8 + 4 + 2 + 1 + 1 values.
-__device__ __forceinline__ int scatter_row(int lane) {
-  return ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1);
-}
-__device__ __forceinline__ float half_wave_row_amax(const float (&x)[16], int lane) {
-  float m8[8], m4[4], m2[2];
-  const bool b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float keep = fabsf(b4 ? x[k + 8] : x[k]), send = fabsf(b4 ? x[k] : x[k + 8]);
-    m8[k] = fmaxf(keep, __shfl_xor(send, 16, 64));
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float keep = b3 ? m8[k + 4] : m8[k], send = b3 ? m8[k] : m8[k + 4];
-    m4[k] = fmaxf(keep, __shfl_xor(send, 8, 64));
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float keep = b2 ? m4[k + 2] : m4[k], send = b2 ? m4[k] : m4[k + 2];
-    m2[k] = fmaxf(keep, __shfl_xor(send, 4, 64));
-  }
-  const float keep = b1 ? m2[1] : m2[0], send = b1 ? m2[0] : m2[1];
-  const float m1 = fmaxf(keep, __shfl_xor(send, 2, 64));
-  return fmaxf(m1, __shfl_xor(m1, 1, 64));
-}
-
 // Compute one staged 32-row block (i, a template argument so the accumulator stays in
 // registers): dg, du, dp partials, then dg | du rows out.
 // BF16: dg, du replace g, u in LDS (BF16) and leave as BF16 rows.

@@ -20,6 +20,36 @@ struct FfnShape {
   int H, I;
 };
 
+// Reduce-scatter of |x| over the 32 lanes of a half-wave: lane l holds 16 values x[v] (one per
+// accumulator row v, its own column); on return it holds, for the row index
+// scatter_row(l) = 8 b4 + 4 b3 + 2 b2 + b1 (b = bits of l), the largest |x| over all 32 lanes
+// of its half-wave (lanes l and l ^ 1 hold the same row). Exchanges 8 + 4 + 2 + 1 + 1 values.
+__device__ __forceinline__ int scatter_row(int lane) {
+  return ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1);
+}
+__device__ __forceinline__ float half_wave_row_amax(const float (&x)[16], int lane) {
+  float m8[8], m4[4], m2[2];
+  const bool b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float keep = fabsf(b4 ? x[k + 8] : x[k]), send = fabsf(b4 ? x[k] : x[k + 8]);
+    m8[k] = fmaxf(keep, __shfl_xor(send, 16, 64));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = b3 ? m8[k + 4] : m8[k], send = b3 ? m8[k] : m8[k + 4];
+    m4[k] = fmaxf(keep, __shfl_xor(send, 8, 64));
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = b2 ? m4[k + 2] : m4[k], send = b2 ? m4[k] : m4[k + 2];
+    m2[k] = fmaxf(keep, __shfl_xor(send, 4, 64));
+  }
+  const float keep = b1 ? m2[1] : m2[0], send = b1 ? m2[0] : m2[1];
+  const float m1 = fmaxf(keep, __shfl_xor(send, 2, 64));
+  return fmaxf(m1, __shfl_xor(m1, 1, 64));
+}
+
 // g|u = x [Wg;Wu]^T over the 128 h-columns [i0, i0+128) of expert e; SwiGLU h = silu(g) u.
 // B tile rows interleave 64-row blocks of Wg and Wu (block q even: Wg, odd: Wu, both for
 // i = i0 + (q/2)*64 + row%64), so wave (wm, wn) holds g in column blocks 0,1 and the matching
@@ -86,29 +116,40 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
   uint32_t* ts = reinterpret_cast<uint32_t*>(sm.b[0]);   // MXFP8 scales, one word per row
   const int rl = opaque(wm * 128 + 4 * (lane >> 5));
   const int cl = opaque(wn * 64 + (lane & 31));
+  // MXFP8: h is quantised along I; the 32 lanes of a half-wave hold one 32-column block of 16
+  // rows. The rows' amaxes come from a reduce-scatter over the half-wave, published through
+  // 128 bytes of the wave's LDS (in the fourth stage buffer, free in this phase).
+  float* lam = reinterpret_cast<float*>(sm.b[1]) + wave * 32;
+  const int hw = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jg = 0; jg < 2; ++jg) {
       const int col = cl + jg * 32;
+      float hv[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float g = acc[i][jg][v];
+        const float u = acc[i][jg + 2][v];
+        hv[v] = g / (1.f + expf(-g)) * u;
+      }
+      if (MX) {
+        const float rh = half_wave_row_amax(hv, lane);
+        if ((lane & 1) == 0) lam[hw * 16 + scatter_row(lane)] = rh;
+        __builtin_amdgcn_wave_barrier();   // (a wave's LDS accesses complete in order)
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = rl + i * 32 + 8 * (v >> 2) + (v & 3);
-        const float g = acc[i][jg][v];
-        const float u = acc[i][jg + 2][v];
-        const float h = g / (1.f + expf(-g)) * u;
         if (MX) {
-          // Quantise h along I: the 32 lanes of this half-wave hold one MX block of row r.
-          float amax = fabsf(h);
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-          const int ex = mx_block_exp(amax);
-          tb[r * 128 + col] = uint8_t(e4m3x2(h * exp2i(-ex), 0.f) & 0xFFu);
+          const int ex = mx_block_exp(lam[hw * 16 + v]);
+          tb[r * 128 + col] = uint8_t(e4m3x2(hv[v] * exp2i(-ex), 0.f) & 0xFFu);
           if ((lane & 31) == 0) reinterpret_cast<uint8_t*>(ts)[r * 4 + (col >> 5)] = uint8_t(ex + 127);
         } else {
-          t[r * 128 + col] = f2bf(h);
+          t[r * 128 + col] = f2bf(hv[v]);
         }
       }
+      if (MX) __builtin_amdgcn_wave_barrier();   // lam is rewritten for the next block
     }
   __syncthreads();
   if (MX) {
