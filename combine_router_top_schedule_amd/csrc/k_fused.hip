@@ -154,6 +154,22 @@ __device__ __forceinline__ void signal(int32_t* p) {
   if (threadIdx.x == 0) add_relaxed(p, 1);
 }
 
+// MXFP8 gather of a dispatch worker's rows: row j's source pointer is lane j's `sp`; its codes
+// go to codes + j * rstep * H, its scales to scales + j * rstep * H / 32. Not inlined: the
+// persistent kernel's GEMM paths hold the register file near its limit, and the quantiser's
+// two rows in flight spilled when allocated together with them; as a call it gets its own
+// allocation (the caller keeps almost nothing live across it).
+__device__ __noinline__ void gather_rows_mx(int nr, int H, int lane, uint64_t sp, uint8_t* codes,
+                                            uint8_t* scales, int rstep) {
+  auto src_of = [&](int j) {
+    const uint32_t lo = __shfl(uint32_t(sp), j, 64), hi = __shfl(uint32_t(sp >> 32), j, 64);
+    return reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
+  };
+  quant_rows_mx_2(
+      nr, H, lane, src_of, [&](int j) { return codes + int64_t(j) * rstep * H; },
+      [&](int j) { return scales + int64_t(j) * rstep * (H / 32); });
+}
+
 // Constant-rate clock for the phase trace (100 MHz on gfx950).
 __device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -341,10 +357,8 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
       });
     } else if (MX && a.s.H <= 8 * kRowBatchChunks) {
       const int nr = r0 < tl.nrows ? (tl.nrows - r0 + rstep - 1) / rstep : 0;
-      quant_rows_mx_2(
-          nr, a.s.H, lane, src_of,
-          [&](int j) { return pl.x + int64_t(r0 + j * rstep) * a.s.H; },
-          [&](int j) { return pl.xs + int64_t(r0 + j * rstep) * (a.s.H / 32); });
+      gather_rows_mx(nr, a.s.H, lane, sp, pl.x + int64_t(r0) * a.s.H,
+                     pl.xs + int64_t(r0) * (a.s.H / 32), rstep);
     } else {
       for (int j = 0; r0 + j * rstep < tl.nrows; ++j) {
         const int r = r0 + j * rstep;

@@ -109,41 +109,31 @@ __device__ __forceinline__ void quant_row_mx(const uint16_t* src, uint8_t* codes
   }
 }
 
-// Rows of at most 256 MX blocks (H <= 8192): lane l owns blocks l, l+64, l+128, l+192, whose
-// 64 bytes each it loads (src == nullptr loads zeros) ...
-__device__ __forceinline__ void mx_row_load(const uint16_t* src, u32x4 (&raw)[4][4], int nblk,
+// Rows of at most 8192 BF16 values, MXFP8 along the row: lane l loads the 16-byte chunks
+// l, l + 64, ... (as load_row16), so every load instruction reads 1 KB of consecutive bytes,
+// and an aligned group of 4 lanes holds one 32-element MX block (src == nullptr loads zeros).
+// The codes leave as 8 bytes per lane (512 consecutive bytes per instruction), the scale from
+// the group's first lane. Same rule as quant_row_mx.
+__device__ __forceinline__ void mx_row_load(const uint16_t* src, u32x4 (&raw)[16], int nch,
                                             int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int b = j * 64 + lane;
-    const u32x4* s = reinterpret_cast<const u32x4*>(src + int64_t(b) * 32);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      raw[j][q] = (src && b < nblk) ? __builtin_nontemporal_load(s + q) : u32x4{0, 0, 0, 0};
-  }
+  load_row16(src, raw, nch, lane);
 }
 
-// ... and quantises and stores (the rule of quant_row_mx).
-__device__ __forceinline__ void mx_row_store(const u32x4 (&raw)[4][4], uint8_t* codes,
-                                             uint8_t* scales, int nblk, int lane) {
+__device__ __forceinline__ void mx_row_store(const u32x4 (&raw)[16], uint8_t* codes,
+                                             uint8_t* scales, int nch, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int b = j * 64 + lane;
-    if (b >= nblk) continue;
-    float v[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[q * 8 + 2 * i] = __uint_as_float(raw[j][q][i] << 16);
-        v[q * 8 + 2 * i + 1] = __uint_as_float(raw[j][q][i] & 0xFFFF0000u);
-      }
-    uint32_t c8[8];
-    const uint32_t sc = mx_quant32(v, c8);
-    u32x4* d = reinterpret_cast<u32x4*>(codes + b * 32);
-    d[0] = u32x4{c8[0], c8[1], c8[2], c8[3]};
-    d[1] = u32x4{c8[4], c8[5], c8[6], c8[7]};
-    scales[b] = uint8_t(sc);
+  for (int q = 0; q < 16; ++q) {
+    if (q * 64 >= nch) break;                     // (uniform)
+    const int c = q * 64 + lane;
+    uint32_t sc;
+    const uint2 cw = mx_quant8_group4(raw[q], &sc);   // every lane: the block amax shuffles
+    if (c < nch) {
+      *reinterpret_cast<uint2*>(codes + int64_t(c) * 8) = cw;
+      if ((lane & 3) == 0) scales[c >> 2] = uint8_t(sc);
+    }
+    // one chunk at a time: interleaving the 16 chunks' arithmetic would hold all of their
+    // temporaries at once (spills in the fused forward kernel, which inlines this)
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -153,18 +143,18 @@ __device__ __forceinline__ void mx_row_store(const u32x4 (&raw)[4][4], uint8_t* 
 template <class Src, class Codes, class Scales>
 __device__ __forceinline__ void quant_rows_mx_2(int nrows, int H, int lane, Src src_of,
                                                 Codes codes_of, Scales scales_of) {
-  const int nblk = H / 32;
-  u32x4 ra[4][4], rb[4][4];
+  const int nch = H / 8;
+  u32x4 ra[16], rb[16];
   if (nrows <= 0) return;
-  mx_row_load(src_of(0), ra, nblk, lane);
+  mx_row_load(src_of(0), ra, nch, lane);
   for (int j = 0;; j += 2) {
     const bool has1 = j + 1 < nrows;
-    if (has1) mx_row_load(src_of(j + 1), rb, nblk, lane);
-    mx_row_store(ra, codes_of(j), scales_of(j), nblk, lane);
+    if (has1) mx_row_load(src_of(j + 1), rb, nch, lane);
+    mx_row_store(ra, codes_of(j), scales_of(j), nch, lane);
     if (!has1) break;
     const bool has2 = j + 2 < nrows;
-    if (has2) mx_row_load(src_of(j + 2), ra, nblk, lane);
-    mx_row_store(rb, codes_of(j + 1), scales_of(j + 1), nblk, lane);
+    if (has2) mx_row_load(src_of(j + 2), ra, nch, lane);
+    mx_row_store(rb, codes_of(j + 1), scales_of(j + 1), nch, lane);
     if (!has2) break;
   }
 }
