@@ -49,7 +49,7 @@ class MokSizes(ctypes.Structure):
                 ("touched_offset", ctypes.c_int64), ("x_slot_bytes", ctypes.c_int64),
                 ("ring_min_bytes", ctypes.c_int64), ("tiles_offset", ctypes.c_int64),
                 ("tiles_max", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
-                ("trace_records", ctypes.c_int64)]
+                ("trace_records", ctypes.c_int64), ("h_slot_bytes", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p

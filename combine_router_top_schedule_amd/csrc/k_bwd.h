@@ -7,25 +7,22 @@
 
 namespace mok {
 
-// E4M3 code -> float (finite codes; the quantiser never produces NaN).
+// E4M3 code -> float (finite codes; the quantiser never produces NaN): gfx950's conversion
+// instruction, which decodes the OCP E4M3 format (checked against the format's definition for
+// all 254 finite codes).
 __device__ __forceinline__ float e4m3_value(uint8_t c) {
-  const int ex = (c >> 3) & 0xF, m = c & 7;
-  const float mag = ex == 0 ? float(m) * 0.001953125f                       // m/8 * 2^-6
-                            : (1.f + float(m) * 0.125f) * exp2i(ex - 7);
-  return (c & 0x80) ? -mag : mag;
+  return __builtin_amdgcn_cvt_f32_fp8(int(c), 0);
 }
 
-// g, u and h of one 32-row x 128-column block of the a-GEMM epilogue, as loaded from where the
+// g and u of one 32-row x 128-column block of the a-GEMM epilogue, as loaded from where the
 // rows live (ring slot or activation plane): 16 lanes x 16 bytes cover a row, 4 rows per load.
 // Held in registers so the next block's loads are in flight while the current block is computed.
 struct AStage {
   u32x4 g[8], u[8];
-  u32x4 h[8];          // BF16 values; MXFP8: 8 codes in .x/.y and the block scale code in .z
 };
 
 // lcode: the row-source codes of the block's 32 rows (LDS). Rows past the tile or columns past
 // I load zeros (their values are never stored).
-template <bool MX>
 __device__ __forceinline__ void a_stage_load(AStage& st, const FfnShape& s, int64_t row0,
                                              int nrows, int colw, int rbase,
                                              const ActSource& src, const int32_t* lcode, int lane) {
@@ -33,45 +30,24 @@ __device__ __forceinline__ void a_stage_load(AStage& st, const FfnShape& s, int6
   for (int q = 0; q < 8; ++q) {
     const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
     const bool ok = rbase + rr < nrows && colw + cc < s.I;
-    st.g[q] = st.u[q] = st.h[q] = u32x4{0u, 0u, 0u, 0u};
+    st.g[q] = st.u[q] = u32x4{0u, 0u, 0u, 0u};
     if (ok) {
-      const ActRow ar = act_row(src, row0 + rbase + rr, lcode[rr], s.H, s.I, MX ? MOK_MXFP8 : MOK_BF16);
+      const uint16_t* gu = act_gu_row(src, row0 + rbase + rr, lcode[rr], s.I);
       const int col = colw + cc;
-      st.g[q] = *reinterpret_cast<const u32x4*>(ar.gu + col);
-      st.u[q] = *reinterpret_cast<const u32x4*>(ar.gu + s.I + col);
-      if (MX) {
-        const uint2 hv = *reinterpret_cast<const uint2*>(ar.h + col);
-        st.h[q] = u32x4{hv.x, hv.y, uint32_t(ar.hs[col / 32]), 0u};
-      } else {
-        st.h[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(ar.h) + col);
-      }
+      st.g[q] = *reinterpret_cast<const u32x4*>(gu + col);
+      st.u[q] = *reinterpret_cast<const u32x4*>(gu + s.I + col);
     }
   }
 }
 
-// Write a loaded block into the wave's LDS region (MXFP8 h decoded to BF16, exact).
-template <bool MX>
+// Write a loaded block into the wave's LDS region.
 __device__ __forceinline__ void a_stage_store(const AStage& st, uint16_t* lg, uint16_t* lu,
-                                              uint16_t* lh, int lane) {
+                                              int lane) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
     *reinterpret_cast<u32x4*>(lg + rr * 128 + cc) = st.g[q];
     *reinterpret_cast<u32x4*>(lu + rr * 128 + cc) = st.u[q];
-    if (MX) {
-      const float scale = exp2i(int(st.h[q][2]) - 127);
-      u32x4 packed;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w = k < 2 ? st.h[q][0] : st.h[q][1];
-        const int sh = (k & 1) * 16;
-        packed[k] = pack_bf2(e4m3_value(uint8_t(w >> sh)) * scale,
-                             e4m3_value(uint8_t(w >> (sh + 8))) * scale);
-      }
-      *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) = packed;
-    } else {
-      *reinterpret_cast<u32x4*>(lh + rr * 128 + cc) = st.h[q];
-    }
   }
 }
 
@@ -102,7 +78,7 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
                                                  int64_t row0, int nrows, int colw,
                                                  uint16_t* dgu, uint8_t* dgq, uint8_t* dgq_s,
                                                  const TokQuant& tq, float* s_dp,
-                                                 uint16_t* lg, uint16_t* lu, const uint16_t* lh,
+                                                 uint16_t* lg, uint16_t* lu,
                                                  const float* lpg, float* lam, int wm, int wn,
                                                  int lane) {
     const int rbase = wm * 128 + i * 32;                                // tile row of lg row 0
@@ -113,49 +89,65 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
     for (int j = 0; j < 4; ++j) {
       const int lc = j * 32 + (lane & 31);
       const int c = colw + lc;
-      float dgr[16], dur[16];
+      float dgr[16], dur[16], hv[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int lr = acc_row(v, lane);                                // row inside the block
-        const bool ok = rbase + lr < nrows && c < s.I;
         const float pg = lpg[lr];
         const float av = acc[i][j][v];
         const float g = bf2f(lg[lr * 128 + lc]);
         const float u = bf2f(lu[lr * 128 + lc]);
-        const float h = bf2f(lh[lr * 128 + lc]);
-        const float dh = pg * av;
         const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
+        // the forward's h, recomputed from the stored g and u (through the forward's own helper:
+        // sharing sg with it here made the compiler spill inside the K loop)
+        const float hf = swiglu_bf(g, u);
+        const float dh = pg * av;
         const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
         const float duv = dh * g * sg;
-        if (ok) part[v] = fmaf(av, h, part[v]);
         if (MX) {
           dgr[v] = dgv;
           dur[v] = duv;
+          hv[v] = hf;
         } else {
-          // dg and du replace g and u in place (each element is read and written by this lane)
+          // dg and du replace g and u in place (each element is read and written by this lane);
+          // the dp partial takes h as the down GEMM did, rounded to BF16
           lg[lr * 128 + lc] = f2bf(dgv);
           lu[lr * 128 + lc] = f2bf(duv);
+          if (rbase + lr < nrows && c < s.I) part[v] = fmaf(av, bf2f(f2bf(hf)), part[v]);
         }
       }
+      const int hw = lane >> 5;
       if (MX) {
-        // Along I: the amax of each of the half-wave's 16 rows over its 32 columns, by a
-        // reduce-scatter over the 32 lanes (16 exchanges per operand instead of 5 per element),
-        // published through the wave's 256 bytes of LDS and read back by every lane.
-        const int hw = lane >> 5;
+        // Along I: the amax of each of the half-wave's 16 rows over its 32 columns (for dg, du
+        // and h), by a reduce-scatter over the 32 lanes (16 exchanges per operand instead of 5
+        // per element), published through the wave's 384 bytes of LDS and read back by every
+        // lane.
         const float rg = half_wave_row_amax(dgr, lane), ru = half_wave_row_amax(dur, lane);
+        const float rh = half_wave_row_amax(hv, lane);
         if ((lane & 1) == 0) {
           const int k = scatter_row(lane);
-          lam[hw * 32 + k] = rg;
-          lam[hw * 32 + 16 + k] = ru;
+          lam[hw * 48 + k] = rg;
+          lam[hw * 48 + 16 + k] = ru;
+          lam[hw * 48 + 32 + k] = rh;
         }
         __builtin_amdgcn_wave_barrier();   // (a wave's LDS accesses complete in order)
         const uint32_t lead = (lane & 31) == 0;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int lr = acc_row(v, lane);
-          const int eg = mx_block_exp(lam[hw * 32 + v]), eu = mx_block_exp(lam[hw * 32 + 16 + v]);
+          const int eg = mx_block_exp(lam[hw * 48 + v]), eu = mx_block_exp(lam[hw * 48 + 16 + v]);
           lg[lr * 128 + lc] = uint16_t((e4m3x2(dgr[v] * exp2i(-eg), 0.f) & 0xFFu) | (lead * uint32_t(eg + 127) << 8));
           lu[lr * 128 + lc] = uint16_t((e4m3x2(dur[v] * exp2i(-eu), 0.f) & 0xFFu) | (lead * uint32_t(eu + 127) << 8));
+        }
+      }
+      if (MX) {
+        // dp partial with h as the down GEMM used it: quantised along I and decoded (exact)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = acc_row(v, lane);
+          const int eh = mx_block_exp(lam[hw * 48 + 32 + v]);
+          const float hq = e4m3_value(uint8_t(e4m3x2(hv[v] * exp2i(-eh), 0.f) & 0xFFu)) * exp2i(eh);
+          if (rbase + lr < nrows && c < s.I) part[v] = fmaf(acc[i][j][v], hq, part[v]);
         }
         __builtin_amdgcn_wave_barrier();   // lam is rewritten for the next j
 
@@ -245,13 +237,13 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
 //   dh = p a, dg = dh u s(g) (1 + g (1 - s(g))), du = dh g s(g)     -> dgu[row][i], [I + i]
 //     (MXFP8: codes dgq[row][i], [I + i] blocked along I, and dg^T, du^T blocked along tokens)
 //   dp partial = sum over this tile's columns of a h (fixed tree)   -> dp_part[row][c0/256]
-// The epilogue's LDS carve-out is laid out for exactly 4 waves: 24 KB per wave in the first
+// The epilogue's LDS carve-out is laid out for exactly 4 waves: 16 KB per wave in the first
 // three stage buffers, dp partials, gates, row-source codes and (MXFP8) the row amaxes along I
 // in the fourth.
 static_assert(kThreads == 256, "a_tile's LDS regions assume 4 waves");
-static_assert(4 * 24576 <= 3 * kStageBytes, "per-wave regions must end before the fourth stage buffer");
+static_assert(4 * 16384 <= 3 * kStageBytes, "per-wave regions must end before the fourth stage buffer");
 static_assert(6144 + 4 * 128 * 4 <= 8192, "dp partials, gates and codes end before the amaxes");
-static_assert(8192 + 4 * 64 * 4 <= kStageBytes, "the row amaxes fit the fourth stage buffer");
+static_assert(8192 + 4 * 96 * 4 <= kStageBytes, "the row amaxes fit the fourth stage buffer");
 template <bool MX>
 __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t row0, int nrows,
                                        int e, int c0, const uint8_t* d, const uint8_t* d_s,
@@ -281,14 +273,13 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   // decoded on the way).
   const int nparts = (s.I + kTileN - 1) / kTileN;
   float* s_dp = reinterpret_cast<float*>(sm.b[1]);                      // [2][256]
-  uint8_t* wreg = sm.a[0] + wave * 24576;                               // 24 KB per wave
+  uint8_t* wreg = sm.a[0] + wave * 16384;                               // 16 KB per wave
   uint16_t* lg = reinterpret_cast<uint16_t*>(wreg);                     // [32][128] BF16
   uint16_t* lu = lg + 32 * 128;
-  uint16_t* lh = lu + 32 * 128;   // BF16 (exact for decoded E4M3 values too)
   const int colw = c0 + wn * 128;                                       // wave's first column
   float* lpg = reinterpret_cast<float*>(sm.b[1] + 4096) + wave * 128;    // gates of the wave's rows
   int32_t* lcode = reinterpret_cast<int32_t*>(sm.b[1] + 6144) + wave * 128;  // their sources
-  float* lam = reinterpret_cast<float*>(sm.b[1] + 8192) + wave * 64;   // MXFP8 row amaxes along I
+  float* lam = reinterpret_cast<float*>(sm.b[1] + 8192) + wave * 96;   // MXFP8 row amaxes along I
   // gates and row-source codes of the wave's 128 rows (lane l: row wm*128 + l, l < 128 over
   // two halves)
   for (int l = lane; l < 128; l += 64) {
@@ -298,15 +289,15 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   }
   __builtin_amdgcn_wave_barrier();
   AStage st;
-  a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128, act, lcode, lane);
+  a_stage_load(st, s, row0, nrows, colw, wm * 128, act, lcode, lane);
 #define MOK_A_BLOCK(I_)                                                                          \
   {                                                                                              \
     __builtin_amdgcn_s_waitcnt(0);                                                               \
-    a_stage_store<MX>(st, lg, lu, lh, lane);                                                     \
-    if (I_ < 3) a_stage_load<MX>(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act,         \
-                                 lcode + (I_ + 1) * 32, lane);                                   \
+    a_stage_store(st, lg, lu, lane);                                                             \
+    if (I_ < 3) a_stage_load(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act,             \
+                             lcode + (I_ + 1) * 32, lane);                                       \
     __builtin_amdgcn_wave_barrier();                                                             \
-    a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, dgq, dgq_s, tq, s_dp, lg, lu, lh,    \
+    a_epilogue_block<MX, I_>(acc, s, row0, nrows, colw, dgu, dgq, dgq_s, tq, s_dp, lg, lu,        \
                              lpg + I_ * 32, lam, wm, wn, lane);                                  \
   }
   MOK_A_BLOCK(0)

@@ -86,8 +86,10 @@ struct TransposeArgs {
   // Non-null (BF16 rows from segments): every source row is also copied, unscaled, to
   // rows_out[its expert-ordered row][F] (the dOut gather D of the backward, read once for both).
   uint16_t* rows_out;
-  // from_act: rows are the h of the activations, read where each row lives (ActSource; the
-  // plane fields are unused)
+  // from_act: rows are h, recomputed from the g|u of the activations, read where each row
+  // lives (ActSource); h is formed as the forward formed it and then taken as the down GEMM
+  // used it: rounded to BF16, or (plane_s non-null) quantised to MXFP8 along the features and
+  // decoded. (The plane fields are otherwise unused.)
   int from_act;
   ActSource act;
 };
@@ -135,13 +137,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
           src = reinterpret_cast<const uint8_t*>(a.seg[n / a.T] + (n % a.T) * int64_t(a.F) + f0);
           if (a.p) gate = a.p[pair];
         } else if (a.from_act) {
-          const ActRow ar = act_row(a.act, row, a.act.code[row], 0, a.F, mxp ? MOK_MXFP8 : MOK_BF16);
-          if (mxp) {
-            src = ar.h + f0;
-            sc4 = *reinterpret_cast<const uint32_t*>(ar.hs + f0 / 32);
-          } else {
-            src = ar.h + int64_t(f0) * 2;
-          }
+          src = reinterpret_cast<const uint8_t*>(act_gu_row(a.act, row, a.act.code[row], a.F) + f0);
         } else if (mxp) {
           src = a.plane + row * a.plane_stride + a.plane_col0 + f0;
           sc4 = *reinterpret_cast<const uint32_t*>(a.plane_s + row * (a.plane_stride / 32) +
@@ -162,7 +158,34 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
       const int idx = tid + 256 * i, r = idx >> 4, ch = idx & 15;
       const uint8_t* src = s_src[r];
       uint32_t w[4] = {0u, 0u, 0u, 0u};
-      if (src) {
+      if (a.from_act) {
+        // g at src, u F values further; every lane takes part (the MXFP8 block amax is a
+        // 4-lane shuffle), rows without a source as zeros
+        u32x4 gv = {0u, 0u, 0u, 0u}, uv = {0u, 0u, 0u, 0u};
+        if (src) {
+          gv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ch * 16));
+          uv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + int64_t(a.F) * 2 + ch * 16));
+        }
+        float hv[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hv[2 * k] = swiglu_bf(bf2f(uint16_t(gv[k])), bf2f(uint16_t(uv[k])));
+          hv[2 * k + 1] = swiglu_bf(bf2f(uint16_t(gv[k] >> 16)), bf2f(uint16_t(uv[k] >> 16)));
+        }
+        if (mxp) {
+          uint32_t sc;
+          const uint2 cw = mx_quant8_group4_f(hv, &sc);
+          const float scale = exp2i(int(sc) - 127);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t c2 = (k < 2 ? cw.x : cw.y) >> ((k & 1) * 16);
+            w[k] = pack_bf2(e4m3_value(uint8_t(c2)) * scale, e4m3_value(uint8_t(c2 >> 8)) * scale);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = pack_bf2(hv[2 * k], hv[2 * k + 1]);
+        }
+      } else if (src) {
         if (mxp) {
           const uint64_t c64 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(src + ch * 8));
           const uint2 c8 = make_uint2(uint32_t(c64), uint32_t(c64 >> 32));
@@ -654,7 +677,7 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   asrc.act = ap;
   asrc.ring = b.ring;
   asrc.ring_share = L.ring_share;
-  asrc.aofs = int64_t(L.ring_capx) * L.xsb;
+  asrc.aofs = int64_t(L.ring_capx) * L.xsb + int64_t(L.ring_caph) * L.hsb;
   asrc.asb = L.asb;
   asrc.capa = L.ring_capa > 0 ? L.ring_capa : 1;
   asrc.code = b.actsrc;

@@ -50,14 +50,34 @@ __device__ __forceinline__ float half_wave_row_amax(const float (&x)[16], int la
   return fmaxf(m1, __shfl_xor(m1, 1, 64));
 }
 
-// g|u = x [Wg;Wu]^T over the 128 h-columns [i0, i0+128) of expert e; SwiGLU h = silu(g) u.
-// B tile rows interleave 64-row blocks of Wg and Wu (block q even: Wg, odd: Wu, both for
-// i = i0 + (q/2)*64 + row%64), so wave (wm, wn) holds g in column blocks 0,1 and the matching
-// u in column blocks 2,3, lane for lane.
-template <bool MX>
-__device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
+// SwiGLU of the stored (BF16-rounded) g and u, h = g s(g) u with s(g) = 1 / (1 + e^-g) from the
+// hardware exp and reciprocal: the forward and the backward's recomputation (which needs s(g)
+// for dg and du anyway) form h with these same instructions, so they agree bit for bit.
+// (Neither has an add fed by a multiply, so no context can fuse two of their operations.)
+__device__ __forceinline__ float sigmoid_hw(float g) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
+__device__ __forceinline__ float swiglu_of(float gb, float sg, float ub) {
+  return gb * sg * ub;
+}
+__device__ __forceinline__ float swiglu_bf(float g, float u) {
+  const float gb = bf2f(f2bf(g)), ub = bf2f(f2bf(u));
+  return swiglu_of(gb, sigmoid_hw(gb), ub);
+}
+
+// g|u = x [Wg;Wu]^T over the 128 h-columns [i0, i0+128) of expert e; SwiGLU h = silu(g) u of
+// the BF16-rounded g and u. B tile rows interleave 64-row blocks of Wg and Wu (block q even:
+// Wg, odd: Wu, both for i = i0 + (q/2)*64 + row%64), so wave (wm, wn) holds g in column
+// blocks 0,1 and the matching u in column blocks 2,3, lane for lane.
+// before_h() runs (workgroup-uniform) after g|u is stored and before h is; when it returns
+// false the tile stops there and returns false (the fused forward waits there for h's slot).
+struct AlwaysReady {
+  __device__ bool operator()() const { return true; }
+};
+template <bool MX, class BeforeH = AlwaysReady>
+__device__ __forceinline__ bool gateup_tile(GemmLds& sm, const FfnShape& s, const FfnWeights& w,
                                             const ActPlanes& pl, int64_t prow0, int nrows, int e,
-                                            int i0) {
+                                            int i0, BeforeH before_h = BeforeH()) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;                              // bytes per element
@@ -112,6 +132,7 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
     }
   }
   __syncthreads();
+  if (!before_h()) return false;
   uint8_t* tb = sm.a[0];
   uint32_t* ts = reinterpret_cast<uint32_t*>(sm.b[0]);   // MXFP8 scales, one word per row
   const int rl = opaque(wm * 128 + 4 * (lane >> 5));
@@ -128,11 +149,7 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
       const int col = cl + jg * 32;
       float hv[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float g = acc[i][jg][v];
-        const float u = acc[i][jg + 2][v];
-        hv[v] = g / (1.f + expf(-g)) * u;
-      }
+      for (int v = 0; v < 16; ++v) hv[v] = swiglu_bf(acc[i][jg][v], acc[i][jg + 2][v]);
       if (MX) {
         const float rh = half_wave_row_amax(hv, lane);
         if ((lane & 1) == 0) lam[hw * 16 + scatter_row(lane)] = rh;
@@ -170,6 +187,7 @@ __device__ __forceinline__ void gateup_tile(GemmLds& sm, const FfnShape& s, cons
     }
   }
   __syncthreads();
+  return true;
 }
 
 // Where the push epilogue sends a tile's rows. kPushSlots: every row raw to slots[pair], the

@@ -14,11 +14,12 @@
 // consumed inside one XCD, so its ring bytes stay coherent in that XCD's L2: producers complete
 // their stores before bumping a counter, and consumers read ring rows with agent-scope loads
 // that miss in their CU's L1 (a slot is reused for one row tile after another, so an L1 line
-// kept from an earlier tile would be stale). Each XCD owns a fixed share of the ring, cut into two kinds of slots used
-// round-robin: gather slots hold a row tile's X rows until its gate/up tiles are done;
-// activation slots hold its g|u and h until its down tiles are done, and after the kernel the
-// last capa of them stay for the backward's reverse walk. Splitting the two lets one ring keep
-// g|u and h of many more row tiles than whole-tile slots would. A down-GEMM row whose pair is
+// kept from an earlier tile would be stale). Each XCD owns a fixed share of the ring, cut into
+// three kinds of slots used round-robin: gather slots hold a row tile's X rows until its
+// gate/up tiles are done; h slots hold its h until its down tiles are done; activation slots
+// hold its g|u, which only the backward reads, and after the kernel the last capa of them stay
+// for the backward's reverse walk (it recomputes h from g|u). Splitting them lets one ring keep
+// the g|u of many more row tiles than whole-tile slots would. A down-GEMM row whose pair is
 // its token's only local pair (nearly all rows when a GPU holds a few experts of many) becomes
 // the token's output row at once, bf16(p * bf16(y)), the merge over one term; the other rows
 // are pushed to the pair slots and the weighted merge of the tokens with several local pairs
@@ -33,9 +34,11 @@
 // after its gate/up tiles and rarely wait for them. A GEMM worker that finishes an item takes
 // the next number from the XCD's item counter, so items are handed out in increasing order to
 // whichever worker is free. Every wait is on a lower-numbered item, already held by a running
-// worker: dn(q) on gu(q), and gu(q) on the gather of tile q, whose slot was freed by
-// dn(q - capa) and gu(q - capx), both numbered below gu(q) because capa > lag. Every wait is
-// bounded; an expired wait sets the error word and all workers drain.
+// worker: dn(q) on gu(q), and gu(q) on the gather of tile q, whose slots were freed by
+// dn(q - capa) and gu(q - capx), both numbered below gu(q) because capa > lag; before storing h,
+// gu(q) also waits for dn(q - caph), the last reader of its h slot, numbered below gu(q)
+// because caph > lag. Every wait is bounded; an expired wait sets the error word and all
+// workers drain.
 #include "k_ffn.h"
 #include "mok_rows.h"
 
@@ -63,8 +66,8 @@ struct MacroArgs {
 struct FusedArgs {
   uint8_t* ring;
   int64_t ring_share;        // bytes of the ring owned by one XCD
-  int64_t xsb, asb;          // bytes of one gather slot / one activation slot
-  int capx, capa;            // gather slots / activation slots per XCD
+  int64_t xsb, hsb, asb;     // bytes of one gather slot / h slot / activation slot
+  int capx, caph, capa;      // gather slots / h slots / activation slots per XCD
   FfnShape s;
   FfnWeights w;
   int32_t* cnt;              // [kCntWords + (3 + kXcds) * B * tiles_max]
@@ -195,12 +198,13 @@ __device__ __forceinline__ void trace_item(const FusedArgs& a, int kind, int x, 
 }
 
 // MOK_FLAG_POISON: fill rows r0, r0 + rstep, ... (< kTileM) of a gather slot's X plane (and
-// its MXFP8 scales) and of an activation slot's g|u, h planes with 0xFF bytes (NaN in BF16,
-// E4M3 and UE8M0), so a read of a released slot before its next tile's data is written shows
-// up as NaN. Rows are split exactly as the gather splits them, so each row's poison precedes
-// its gathered bytes in one wave's program order (with a vmcnt wait between them).
-__device__ void poison_rows(const ActPlanes& px, const ActPlanes& pa, bool gather_slot,
-                            bool act_slot, int H, int I, bool mx, int r0, int rstep, int lane) {
+// its MXFP8 scales), an activation slot's g|u and an h slot's h (and scales) with 0xFF bytes
+// (NaN in BF16, E4M3 and UE8M0), so a read of a released slot before its next tile's data is
+// written shows up as NaN. Rows are split exactly as the gather splits them, so each row's
+// poison precedes its gathered bytes in one wave's program order (with a vmcnt wait between
+// them).
+__device__ void poison_rows(const ActPlanes& pl, bool gather_slot, bool gu_slot, bool h_slot,
+                            int H, int I, bool mx, int r0, int rstep, int lane) {
   auto fill = [&](uint8_t* p, int64_t bytes) {
     uint32_t* w = reinterpret_cast<uint32_t*>(p);
     const int64_t nw = bytes / 4;
@@ -211,13 +215,13 @@ __device__ void poison_rows(const ActPlanes& px, const ActPlanes& pa, bool gathe
   const int64_t hrow = mx ? I : 2 * int64_t(I);
   for (int r = r0; r < kTileM; r += rstep) {
     if (gather_slot) {
-      fill(px.x + r * xrow, xrow);
-      if (mx) fill(px.xs + int64_t(r) * (H / 32), H / 32);
+      fill(pl.x + r * xrow, xrow);
+      if (mx) fill(pl.xs + int64_t(r) * (H / 32), H / 32);
     }
-    if (act_slot) {
-      fill(reinterpret_cast<uint8_t*>(pa.gu) + int64_t(r) * 4 * I, 4 * int64_t(I));
-      fill(pa.h + r * hrow, hrow);
-      if (mx) fill(pa.hs + int64_t(r) * (I / 32), I / 32);
+    if (gu_slot) fill(reinterpret_cast<uint8_t*>(pl.gu) + int64_t(r) * 4 * I, 4 * int64_t(I));
+    if (h_slot) {
+      fill(pl.h + r * hrow, hrow);
+      if (mx) fill(pl.hs + int64_t(r) * (I / 32), I / 32);
     }
   }
 }
@@ -284,15 +288,16 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
   int32_t* xq = dn_done + gmax + int64_t(x) * gmax;   // this XCD's tile ids
   int32_t* xend = a.cnt + kCntEnd + x;
   uint8_t* share = a.ring + int64_t(x) * a.ring_share;
-  // Planes of this XCD's q-th row tile: X in gather slot q % capx, g|u and h in activation
-  // slot q % capa.
+  // Planes of this XCD's q-th row tile: X in gather slot q % capx, h in h slot q % caph, g|u in
+  // activation slot q % capa.
   auto planes = [&](int q) {
-    ActPlanes pl = act_planes(share + a.capx * a.xsb + int64_t(q % a.capa) * a.asb, kTileM, a.s.H,
-                              a.s.I, a.dtype, false);
-    const ActPlanes px = act_planes(share + int64_t(q % a.capx) * a.xsb, kTileM, a.s.H, a.s.I,
-                                    a.dtype, true);
-    pl.x = px.x;
-    pl.xs = px.xs;
+    ActPlanes pl{};
+    pl.x = share + int64_t(q % a.capx) * a.xsb;
+    pl.xs = a.dtype == MOK_BF16 ? nullptr : pl.x + int64_t(kTileM) * a.s.H;
+    pl.h = share + a.capx * a.xsb + int64_t(q % a.caph) * a.hsb;
+    pl.hs = a.dtype == MOK_BF16 ? nullptr : pl.h + int64_t(kTileM) * a.s.I;
+    pl.gu = reinterpret_cast<uint16_t*>(share + a.capx * a.xsb + a.caph * a.hsb +
+                                        int64_t(q % a.capa) * a.asb);
     return pl;
   };
 
@@ -385,7 +390,7 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
     const uint64_t tb = trace_clock();
     if (a.flags & MOK_FLAG_POISON) {
       const ActPlanes pl = planes(q);
-      poison_rows(pl, pl, true, true, a.s.H, a.s.I, MX, local * 4 + wave, 4 * nx, lane);
+      poison_rows(pl, true, true, true, a.s.H, a.s.I, MX, local * 4 + wave, 4 * nx, lane);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -409,10 +414,16 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
       if (mt >= nt) break;
       const uint64_t tb = trace_clock();
       if (a.flags & MOK_FLAG_POISON) {
-        // the slots' previous tiles are done with them (the waits above): poison this
-        // workgroup's rows of both before the new tile's bytes arrive
+        // The gather and activation slots' previous tiles are done with them (the waits
+        // above); the h slot's once that tile's down items are done (a wait the gate/up items
+        // otherwise make themselves, just before they store h). Poison this workgroup's rows
+        // of all three before the new tile's bytes arrive.
+        if (q >= a.caph &&
+            !wait_geq(dn_done + ld_relaxed(xq + q - a.caph), ndn, a.err, a.spin_limit))
+          return;
         const ActPlanes pl = planes(q);
-        poison_rows(pl, pl, true, q >= a.capa, a.s.H, a.s.I, MX, local * 4 + wave, 4 * C, lane);
+        poison_rows(pl, true, q >= a.capa, q >= a.caph, a.s.H, a.s.I, MX, local * 4 + wave,
+                    4 * C, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
@@ -463,7 +474,16 @@ __device__ __forceinline__ void layer_fwd_body(const FusedArgs& a, GemmLds& sm) 
     if (k < ngu) {
       if (!wait_geq(landed + mt, q < lag ? nx : C, a.err, a.spin_limit)) return;
       const uint64_t tb = trace_clock();
-      gateup_tile<MX>(sm, a.s, a.w, pl, 0, tl.nrows, tl.e, k * 128);
+      // h goes to h slot q % caph once the down items of the tile that used it before are
+      // done (that tile is q - caph: its down items are numbered below this item)
+      // (the tile id comes through tile_of: this workgroup may never have seen tile q - caph)
+      const bool ok = gateup_tile<MX>(sm, a.s, a.w, pl, 0, tl.nrows, tl.e, k * 128, [&]() {
+        if (q < a.caph) return true;
+        const int tp = tile_of(xq, xend, q - a.caph, gmax, a.err, a.spin_limit);
+        if (tp < 0) return false;
+        return tp >= nt || wait_geq(dn_done + tp, ndn, a.err, a.spin_limit);
+      });
+      if (!ok) return;
       signal(gu_done + mt);
       trace_item(a, kTrGateUp, x, b, mt - s_first[b], it, tw, tb);
     } else {
@@ -574,8 +594,10 @@ hipError_t launch_layer_fwd_macro(const Layout& L, const mok_desc& d, int B,
   a.ring = ring;
   a.ring_share = L.ring_share;
   a.xsb = L.xsb;
+  a.hsb = L.hsb;
   a.asb = L.asb;
   a.capx = L.ring_capx;
+  a.caph = L.ring_caph;
   a.capa = L.ring_capa;
   a.s = FfnShape{L.H, L.I};
   if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};

@@ -141,11 +141,12 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   sizes->tokpos_offset = L.sv_tokpos;
   sizes->touched_offset = L.sv_touched;
   sizes->x_slot_bytes = L.xsb;
-  sizes->ring_min_bytes = int64_t(kXcds) * (kRingXSlots * L.xsb + 2 * L.asb);
+  sizes->ring_min_bytes = int64_t(kXcds) * (kRingXSlots * L.xsb + kRingHSlots * L.hsb + 2 * L.asb);
   sizes->tiles_offset = L.ws_tiles;
   sizes->tiles_max = L.tiles_max;
   sizes->trace_offset = L.trace_max > 0 ? L.ws_trace : 0;
   sizes->trace_records = L.trace_max;
+  sizes->h_slot_bytes = L.hsb;
   return MOK_OK;
 }
 

@@ -21,6 +21,7 @@ constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;            // XCDs per MI355X device (each with its own L2)
 constexpr int kRingXSlots = 3;      // gather slots per XCD share of the fused-forward ring
+constexpr int kRingHSlots = 3;      // h slots per XCD share (more than the forward's lag of 2)
 constexpr int kMaxMacro = 8;        // macrobatches (layer calls) one fused launch can run
 
 __host__ __device__ inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -100,10 +101,10 @@ struct Layout {
   // saved
   int64_t sv_perm, sv_tokpos, sv_touched, sv_multi, sv_pcode, sv_bytes;
   int64_t sv_rhdr, sv_rtiles, sv_rslot, sv_rowner;
-  // fused-forward ring, one share per XCD: gather slots (X of one row tile) and activation
-  // slots (g|u and h of one row tile)
-  int64_t ring_share, xsb, asb;
-  int ring_capx, ring_capa;
+  // fused-forward ring, one share per XCD: gather slots (X of one row tile), h slots (h of
+  // one row tile) and activation slots (g|u of one row tile)
+  int64_t ring_share, xsb, hsb, asb;
+  int ring_capx, ring_caph, ring_capa;
   // ws
   int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_push, ws_trace, ws_bytes;
   int64_t trace_max;   // phase-trace records (MOK_FLAG_TRACE; 0 without it)
@@ -144,14 +145,17 @@ inline Layout make_layout(const mok_desc& d) {
   L.gu_row_bytes = int64_t(2) * L.I * 2;
   L.h_row_bytes = act_row_bytes(L.I, L.dtype);
   // fused-forward ring: one share per XCD = kRingXSlots gather slots (the X rows of a row tile,
-  // needed until its gate/up tiles are done) followed by activation slots (its g|u and h,
-  // needed until its down tiles are done, and kept for the backward afterwards)
+  // needed until its gate/up tiles are done), kRingHSlots h slots (its h, needed until its down
+  // tiles are done), then activation slots (its g|u, written by the gate/up tiles and kept for
+  // the backward, which recomputes h from it)
   L.xsb = align_up(int64_t(kTileM) * L.x_row_bytes, 256);
-  L.asb = align_up(int64_t(kTileM) * (L.gu_row_bytes + L.h_row_bytes), 256);
+  L.hsb = align_up(int64_t(kTileM) * L.h_row_bytes, 256);
+  L.asb = align_up(int64_t(kTileM) * L.gu_row_bytes, 256);
   L.ring_share = d.ring_bytes / kXcds / 256 * 256;
   L.ring_capx = kRingXSlots;
+  L.ring_caph = kRingHSlots;
   {
-    const int64_t rest = L.ring_share - kRingXSlots * L.xsb;
+    const int64_t rest = L.ring_share - kRingXSlots * L.xsb - kRingHSlots * L.hsb;
     L.ring_capa = rest > 0 ? int(rest / L.asb) : 0;
   }
   // saved
@@ -248,10 +252,10 @@ __host__ __device__ inline ActPlanes act_planes(uint8_t* base, int64_t rows, int
   return p;
 }
 
-// Where the backward reads each expert-ordered row's g|u and h: rows of a tile the forward left
+// Where the backward reads each expert-ordered row's g|u: rows of a tile the forward left
 // resident in a ring activation slot are read there (code = slot << 8 | row inside the tile,
 // slot = XCD * capa + slot of that XCD); replayed rows (code < 0) from the backward's own
-// activation planes.
+// activation planes. (h is recomputed from g|u wherever the backward needs it.)
 struct ActSource {
   ActPlanes act;             // backward activation planes [rows_max]
   const uint8_t* ring;       // the forward's ring (may be null when every code is < 0)
@@ -261,22 +265,13 @@ struct ActSource {
   const int32_t* code;       // [rows_max]
 };
 
-struct ActRow {
-  const uint16_t* gu;        // BF16 [2I]
-  const uint8_t* h;          // BF16 [I] or codes [I]
-  const uint8_t* hs;         // MXFP8 scales [I/32] (null in BF16)
-};
-
-__device__ inline ActRow act_row(const ActSource& s, int64_t row, int32_t code, int H, int I,
-                                 int dtype) {
-  const int64_t hb = dtype == MOK_BF16 ? 2 * int64_t(I) : int64_t(I);
-  if (code < 0)
-    return ActRow{s.act.gu + row * 2 * I, s.act.h + row * hb, s.act.hs ? s.act.hs + row * (I / 32) : nullptr};
+// The g|u row (BF16 [2I]: g in [0, I), u in [I, 2I)) of an expert-ordered row.
+__device__ inline const uint16_t* act_gu_row(const ActSource& s, int64_t row, int32_t code, int I) {
+  if (code < 0) return s.act.gu + row * 2 * I;
   const int slot = code >> 8, lr = code & 255;
-  uint8_t* base = const_cast<uint8_t*>(s.ring) + int64_t(slot / s.capa) * s.ring_share + s.aofs +
-                  int64_t(slot % s.capa) * s.asb;
-  const ActPlanes sp = act_planes(base, kTileM, H, I, dtype, false);
-  return ActRow{sp.gu + int64_t(lr) * 2 * I, sp.h + lr * hb, sp.hs ? sp.hs + int64_t(lr) * (I / 32) : nullptr};
+  const uint8_t* base = s.ring + int64_t(slot / s.capa) * s.ring_share + s.aofs +
+                        int64_t(slot % s.capa) * s.asb;
+  return reinterpret_cast<const uint16_t*>(base) + int64_t(lr) * 2 * I;
 }
 
 // One m-tile of a grouped GEMM: rows [row0, row0 + nrows) of expert e, inside minibatch j.

@@ -68,7 +68,7 @@ ZIPF_ALPHA_KIMI = 0.2
 CONFIGS = {
     # 64 tokens, hidden 128, 8 experts, top-2, intermediate 256, all experts local.
     "tiny": Config("tiny", S=1, T=64, H=128, E=8, K=2, I=256, e0=0, E_loc=8, M=16,
-                   ring_bytes=8 * MiB,
+                   ring_bytes=16 * MiB,
                    x_std=0.02, w_std=0.02, logit_std=1.0, dout_std=1.0),
     # DeepSeek-V3-shaped local share: experts 0..3 of 256, 64 x 2048 source tokens.
     "dsv3": Config("dsv3", S=64, T=2048, H=7168, E=256, K=8, I=2048, e0=0, E_loc=4,

@@ -123,10 +123,10 @@ typedef struct {
   size_t wq_bytes;       /* MXFP8: one quantised weight tensor (codes + scales)             */
   int64_t rows_max;      /* bound on expert-order rows                                       */
   int32_t ring_slots;    /* R: activation slots of the fused-path ring, i.e. row tiles whose
-                            g|u and h the backward finds resident (8 XCD shares, each
-                            3 gather slots then R/8 activation slots)                        */
+                            g|u the backward finds resident (8 XCD shares, each 3 gather
+                            slots, 3 h slots, then R/8 activation slots)                     */
   int32_t minibatch;     /* M actually used (after the default is applied)                  */
-  int64_t slot_bytes;    /* bytes of one activation slot (g|u and h of 256 rows)            */
+  int64_t slot_bytes;    /* bytes of one activation slot (g|u of 256 rows)                  */
   /* Layout of the schedule table inside `saved` (byte offsets). Words 0..191 are a header:
    * [0] P (local pairs), [1] rows (P plus MXFP8 padding), [2] U (touched tokens),
    * [3] touched tokens with several local pairs, [4] the router's device-side status,
@@ -136,7 +136,7 @@ typedef struct {
   int64_t touched_offset; /* int32 [N]: tokens with a local pair, ascending (first U valid)  */
   int64_t x_slot_bytes;   /* bytes of one gather slot of the ring (X rows of 256 tokens)      */
   int64_t ring_min_bytes; /* smallest ring_bytes the fused path accepts (two activation slots
-                             per XCD share)                                                  */
+                             per XCD share after its gather and h slots)                    */
   /* The grouped-GEMM tile table inside `ws`, written by mok_expert_ffn and mok_layer_fwd:
    * int32 quads {minibatch j, local expert, first expert-order row, rows}, ordered by j, then
    * expert, then row; tiles never straddle an expert or a minibatch. Its length is int32 word
@@ -145,6 +145,8 @@ typedef struct {
   int64_t tiles_max;
   int64_t trace_offset;   /* MOK_FLAG_TRACE: byte offset of the records inside ws (else 0)  */
   int64_t trace_records;  /* capacity in records (0 without MOK_FLAG_TRACE)                 */
+  int64_t h_slot_bytes;   /* bytes of one h slot of the ring (h of 256 rows: BF16, or MXFP8
+                             codes and scales along I)                                      */
 } mok_sizes;
 
 /* Expert weights (device pointers). BF16 mode uses wg/wu/wd only. MXFP8 mode uses E4M3 codes
@@ -285,8 +287,10 @@ mok_status mok_combine(const mok_desc* desc, const void* saved_dev, const int32_
  * slots_dev is scratch here: the down GEMM writes the output row of a token with a single
  * local pair itself (bf16(p * bf16(y)), the merge over one term), and only pairs of tokens
  * with several local pairs pass through the slots. ring_bytes must
- * be at least mok_sizes.ring_min_bytes (else MOK_ERR_RING); the ring keeps g|u and h of the
- * last R = mok_sizes.ring_slots row tiles (256 expert-ordered rows each) for mok_layer_bwd. */
+ * be at least mok_sizes.ring_min_bytes (else MOK_ERR_RING); the ring keeps g|u of the last
+ * R = mok_sizes.ring_slots row tiles (256 expert-ordered rows each) for mok_layer_bwd.
+ * SwiGLU: h = silu(g) u is formed from the BF16-rounded g and u that the ring keeps, so the
+ * backward recomputes exactly the h the down GEMM used. */
 mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
                          const float* logits_dev, const mok_weights* w,
                          void* const* out_seg_dev, int32_t* topk_idx_dev, float* topk_p_dev,

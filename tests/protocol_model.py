@@ -7,16 +7,18 @@ the first C workgroups of the XCD are dispatch workers (they take the XCD's next
 global counter once its gather slot and activation slot are free, gather it, and count
 themselves in landed[t]) and the others are GEMM workers (they take the XCD's next item number
 from the XCD's item counter: gate/up items of the first `lag` tiles, then blocks [gate/up of tile
-q + lag, down of tile q]). Waits: gate/up of tile t waits for landed[t]; down of tile t for
+q + lag, down of tile q]). Waits: gate/up of tile t waits for landed[t], and before it stores h
+for dn_done of the XCD's (q - caph)-th tile (the last reader of its h slot); down of tile t for
 gu_done[t]; the dispatch of the XCD's q-th tile for gu_done of its (q - capx)-th tile (gather
 slot) and dn_done of its (q - capa)-th (activation slot). Counters and the per-XCD tile list
 are shared integers under one lock (the kernel's atomics).
 
-Slot contents are tracked explicitly: a gather writes "tile t" into its gather slot, a gate/up
-item checks that the gather slot still holds its tile when it starts and when it ends and writes
-"tile t" into the activation slot, a down item checks the activation slot likewise. A protocol
-error (a slot overwritten while an item of the previous tile still reads it, an item run twice,
-a wait on a higher-numbered item, a wait that never ends) raises in the thread that sees it.
+Slot contents are tracked explicitly: a gather writes "tile t" into its gather slot; a gate/up
+item checks that the gather slot still holds its tile when it starts and when it ends, writes
+"tile t" into the activation slot (g|u, read only by the backward) and then into the h slot; a
+down item checks that the h slot holds its tile when it starts and when it ends. A protocol
+error (a slot overwritten while an item of the previous tile still reads or writes it, an item
+run twice, a wait that never ends) raises in the thread that sees it.
 
 Test infrastructure only: nothing in the library imports it.
 """
@@ -42,6 +44,7 @@ class Params:
     ndn: int = 2                # down items per row tile
     capx: int = 3               # gather slots per XCD
     capa: int = 3               # activation slots per XCD
+    caph: int = 3               # h slots per XCD
     tiles: Tuple[int, ...] = (11,)   # row tiles per macrobatch
     max_delay: float = 0.0005   # random sleep per step (seconds)
     timeout: float = 20.0       # a wait longer than this is a deadlock
@@ -62,6 +65,7 @@ class State:
     dn_done: Dict[int, int] = field(default_factory=dict)
     gather_slot: Dict[Tuple[int, int], int] = field(default_factory=dict)   # (x, s) -> tile
     act_slot: Dict[Tuple[int, int], int] = field(default_factory=dict)
+    h_slot: Dict[Tuple[int, int], int] = field(default_factory=dict)
     done_items: Dict[Tuple[int, str, int], int] = field(default_factory=dict)
     rowner: Dict[Tuple[int, int], Tuple[int, int]] = field(default_factory=dict)  # slot -> (b, t)
     failures: List[str] = field(default_factory=list)
@@ -211,35 +215,45 @@ def _workgroup(st: State, wid: int):
             st.done_items[key] = it
         if kind == "gu":
             _wait(st, lambda: st.landed.get(t, 0) >= (nx if q < lag else C), f"landed {t}")
-            gs, as_ = (x, q % p.capx), (x, q % p.capa)
+            gs, as_, hs = (x, q % p.capx), (x, q % p.capa), (x, q % p.caph)
             with st.lock:
                 if st.gather_slot.get(gs) != t:
                     st.failures.append(f"gate/up of tile {t} found slot {gs} holding "
                                        f"{st.gather_slot.get(gs)}")
                     raise ProtocolError(st.failures[-1])
+                # g|u: the slot's previous tile must have finished writing it
                 prev = st.act_slot.get(as_)
-                if prev is not None and prev != t and st.dn_done.get(prev, 0) < p.ndn:
-                    st.failures.append(f"act slot {as_} overwritten while tile {prev} in use")
+                if prev is not None and prev != t and st.gu_done.get(prev, 0) < p.ngu:
+                    st.failures.append(f"act slot {as_} overwritten while tile {prev} writes it")
                     raise ProtocolError(st.failures[-1])
                 st.act_slot[as_] = t
             _nap(p)
+            # before h: the down items of the tile that used the h slot before are done
+            if q >= p.caph:
+                th = tile_of(q - p.caph)
+                _wait(st, lambda: st.dn_done.get(th, 0) >= p.ndn, f"h slot of tile {th}")
             with st.lock:
+                prev = st.h_slot.get(hs)
+                if prev is not None and prev != t and st.dn_done.get(prev, 0) < p.ndn:
+                    st.failures.append(f"h slot {hs} overwritten while tile {prev} in use")
+                    raise ProtocolError(st.failures[-1])
+                st.h_slot[hs] = t
                 if st.gather_slot.get(gs) != t:
                     st.failures.append(f"gather slot {gs} changed under gate/up of tile {t}")
                     raise ProtocolError(st.failures[-1])
                 st.gu_done[t] = st.gu_done.get(t, 0) + 1
         else:
             _wait(st, lambda: st.gu_done.get(t, 0) >= p.ngu, f"gu_done {t}")
-            as_ = (x, q % p.capa)
+            hs = (x, q % p.caph)
             with st.lock:
-                if st.act_slot.get(as_) != t:
-                    st.failures.append(f"down of tile {t} found slot {as_} holding "
-                                       f"{st.act_slot.get(as_)}")
+                if st.h_slot.get(hs) != t:
+                    st.failures.append(f"down of tile {t} found h slot {hs} holding "
+                                       f"{st.h_slot.get(hs)}")
                     raise ProtocolError(st.failures[-1])
             _nap(p)
             with st.lock:
-                if st.act_slot.get(as_) != t:
-                    st.failures.append(f"act slot {as_} changed under down of tile {t}")
+                if st.h_slot.get(hs) != t:
+                    st.failures.append(f"h slot {hs} changed under down of tile {t}")
                     raise ProtocolError(st.failures[-1])
                 st.dn_done[t] = st.dn_done.get(t, 0) + 1
 
@@ -271,11 +285,12 @@ def run(p: Params, seed: int = 0) -> State:
     return st
 
 
-def item_waits(ngu: int, ndn: int, lag: int, blocks: int):
+def item_waits(ngu: int, ndn: int, lag: int, blocks: int, caph: int = 3):
     """The waits of the GEMM items in item-number order, for the static check that every item
-    waits only on lower-numbered items: returns [(item, waited item or None)]. Gate/up of tile q
-    waits for the gather of tile q, which (for q >= capx or capa) waits for items of earlier
-    tiles; down of tile q waits for the gate/up items of tile q."""
+    waits only on lower-numbered items: returns [(item, waited item)]. Gate/up of tile q waits
+    for the gather of tile q, which (for q >= capx or capa) waits for items of earlier tiles,
+    and, before it stores h, for the down items of tile q - caph; down of tile q waits for the
+    gate/up items of tile q."""
     number = {}
     it = 0
     for q in range(lag):
@@ -293,4 +308,6 @@ def item_waits(ngu: int, ndn: int, lag: int, blocks: int):
     for (kind, q, k), n in number.items():
         if kind == "dn":
             out.append((n, max(number[("gu", q, j)] for j in range(ngu))))
+        elif q >= caph and ("dn", q - caph, 0) in number:
+            out.append((n, max(number[("dn", q - caph, j)] for j in range(ndn))))
     return out

@@ -66,18 +66,23 @@ def test_sizes_follow_host_bounds():
     assert s.rows_max == N * 4                                # N * min(K, E_loc)
     assert s.slots_bytes >= N * 8 * 7168 * 2                  # Z: [N*K][H] BF16
     assert s.xd_bytes >= s.rows_max * 7168 * 2
-    # the ring is split into 8 per-XCD shares; each holds 3 gather slots (X of 256 rows) and
-    # then as many activation slots (g|u and h of 256 rows) as fit
+    # the ring is split into 8 per-XCD shares; each holds 3 gather slots (X of 256 rows), 3 h
+    # slots (h of 256 rows) and then as many activation slots (g|u of 256 rows) as fit: at the
+    # DeepSeek-V3 shape 9 per XCD, more than the ~69 row tiles of the layer
     share = (256 << 20) // 8
     assert s.x_slot_bytes == 256 * 7168 * 2
-    assert s.slot_bytes == 256 * (2 * 2048 + 2048) * 2
-    assert s.ring_slots == 8 * ((share - 3 * s.x_slot_bytes) // s.slot_bytes) == 56
-    assert s.ring_min_bytes == 8 * (3 * s.x_slot_bytes + 2 * s.slot_bytes)
+    assert s.h_slot_bytes == 256 * 2048 * 2
+    assert s.slot_bytes == 256 * 2 * 2048 * 2
+    assert s.ring_slots == 8 * ((share - 3 * s.x_slot_bytes - 3 * s.h_slot_bytes)
+                                // s.slot_bytes) == 72
+    assert s.ring_min_bytes == 8 * (3 * s.x_slot_bytes + 3 * s.h_slot_bytes + 2 * s.slot_bytes)
     sm = mok.query_sizes(_d(dtype="mxfp8"))
     assert sm.rows_max == N * 4 + 4 * 31                      # per-expert padding to 32 rows
     assert sm.x_slot_bytes == 256 * (7168 + 7168 // 32)       # E4M3 codes + UE8M0 scales
-    assert sm.slot_bytes == 256 * (2 * 2048 * 2 + 2048 + 2048 // 32)
-    assert sm.ring_slots == 8 * ((share - 3 * sm.x_slot_bytes) // sm.slot_bytes)
+    assert sm.h_slot_bytes == 256 * (2048 + 2048 // 32)
+    assert sm.slot_bytes == 256 * 2 * 2048 * 2                # g|u stays BF16
+    assert sm.ring_slots == 8 * ((share - 3 * sm.x_slot_bytes - 3 * sm.h_slot_bytes)
+                                 // sm.slot_bytes)
     # null arguments are rejected before anything runs
     assert mok.lib().mok_schedule(ctypes.byref(_d()), None, None, None, None, None, None) == 1
 

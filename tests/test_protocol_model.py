@@ -1,8 +1,8 @@
 """The fused forward's hand-off protocol, run on the CPU model of tests/protocol_model.py with
 threads and random delays: no slot is overwritten while an item of its previous tile may still
-read it, every item runs once, every wait ends, and the ring record names each activation
-slot's last tile (per macrobatch). A planted mistake (the dispatch worker not waiting for its
-gather slot) is caught."""
+read or write it, every item runs once, every wait ends, and the ring record names each
+activation slot's last tile (per macrobatch). Planted mistakes (the dispatch worker not waiting
+for its gather slot; a gate/up item not waiting for its h slot) are caught."""
 import itertools
 
 import pytest
@@ -41,8 +41,9 @@ def test_protocol_runs_clean(capx, capa, comm, tiles, seed):
 
 def test_item_order_waits_only_on_earlier_items():
     for ngu, ndn, lag, capx, capa in [(3, 2, 1, 3, 2), (16, 28, 2, 3, 7), (4, 4, 2, 3, 6)]:
-        assert capa > lag and capx > lag
-        for item, waited in pm.item_waits(ngu, ndn, lag, blocks=12):
+        caph = 3
+        assert capa > lag and capx > lag and caph > lag
+        for item, waited in pm.item_waits(ngu, ndn, lag, blocks=12, caph=caph):
             assert waited < item
         # gate/up of tile q (numbered in block q - lag) waits, through its gather, for the
         # gate/up items of tile q - capx and the down items of tile q - capa: both in earlier
@@ -63,6 +64,27 @@ def test_model_catches_a_gather_slot_reused_too_early(monkeypatch):
         return real_wait(st, cond, what)
 
     monkeypatch.setattr(pm, "_wait", skip_gather_wait)
+    caught = 0
+    for seed in range(6):
+        p = pm.Params(capx=3, capa=5, comm=1, tiles=(17,), max_delay=0.002, timeout=5.0)
+        try:
+            pm.run(p, seed)
+        except pm.ProtocolError:
+            caught += 1
+    assert caught > 0
+
+
+def test_model_catches_an_h_slot_reused_too_early(monkeypatch):
+    """Plant a protocol mistake in the model: a gate/up item stores h without waiting for the
+    down items of the tile that used the h slot before."""
+    real_wait = pm._wait
+
+    def skip_h_wait(st, cond, what):
+        if what.startswith("h slot"):
+            return
+        return real_wait(st, cond, what)
+
+    monkeypatch.setattr(pm, "_wait", skip_h_wait)
     caught = 0
     for seed in range(6):
         p = pm.Params(capx=3, capa=5, comm=1, tiles=(17,), max_delay=0.002, timeout=5.0)
