@@ -160,8 +160,8 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
           ag = fmaxf(ag, fabsf(dgr[v]));
           au = fmaxf(au, fabsf(dur[v]));
         }
-        ag = fmaxf(ag, __shfl_xor(ag, 32, 64));
-        au = fmaxf(au, __shfl_xor(au, 32, 64));
+        ag = fmaxf(ag, __uint_as_float(xchg32(__float_as_uint(ag), lane)));
+        au = fmaxf(au, __uint_as_float(xchg32(__float_as_uint(au), lane)));
         const int eg = mx_block_exp(ag), eu = mx_block_exp(au);
         const float ig = exp2i(-eg), iu = exp2i(-eu);
         // Codes of rows 8t + 4h .. +3 as dword t; the two lanes of a column swap two dwords so
@@ -173,10 +173,10 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
           wu4[t] = e4m3x2(dur[4 * t] * iu, dur[4 * t + 1] * iu) | (e4m3x2(dur[4 * t + 2] * iu, dur[4 * t + 3] * iu) << 16);
         }
         const bool hi = (lane >> 5) != 0;
-        const uint32_t g0 = __shfl_xor(hi ? wg4[0] : wg4[2], 32, 64);
-        const uint32_t g1 = __shfl_xor(hi ? wg4[1] : wg4[3], 32, 64);
-        const uint32_t u0 = __shfl_xor(hi ? wu4[0] : wu4[2], 32, 64);
-        const uint32_t u1 = __shfl_xor(hi ? wu4[1] : wu4[3], 32, 64);
+        const uint32_t g0 = xchg32(hi ? wg4[0] : wg4[2], lane);
+        const uint32_t g1 = xchg32(hi ? wg4[1] : wg4[3], lane);
+        const uint32_t u0 = xchg32(hi ? wu4[0] : wu4[2], lane);
+        const uint32_t u1 = xchg32(hi ? wu4[1] : wu4[3], lane);
         const u32x4 og = hi ? u32x4{g0, wg4[2], g1, wg4[3]} : u32x4{wg4[0], g0, wg4[1], g1};
         const u32x4 ou = hi ? u32x4{u0, wu4[2], u1, wu4[3]} : u32x4{wu4[0], u0, wu4[1], u1};
         if (c < s.I && rbase < tq.padlim) {
@@ -190,14 +190,11 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         }
       }
     }
-    // dp partials: sum over the 32 columns of this half-wave (then the two wn waves' halves are
-    // added when the tile's partials leave)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float pv = part[v];
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) pv += __shfl_xor(pv, off, 64);
-      if ((lane & 31) == 0) s_dp[wn * 256 + rbase + acc_row(v, lane)] = pv;
+    // dp partials: sum over the 32 columns of this half-wave, by a reduce-scatter (a fixed
+    // order), then the two wn waves' halves are added when the tile's partials leave
+    {
+      const float pv = half_wave_row_reduce<false>(part, lane);
+      if ((lane & 1) == 0) s_dp[wn * 256 + rbase + acc_row(scatter_row(lane), lane)] = pv;
     }
     // (a wave's LDS accesses complete in order: no wait before reading dg | du back)
     __builtin_amdgcn_wave_barrier();

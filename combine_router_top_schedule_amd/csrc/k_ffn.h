@@ -20,34 +20,63 @@ struct FfnShape {
   int H, I;
 };
 
-// Reduce-scatter of |x| over the 32 lanes of a half-wave: lane l holds 16 values x[v] (one per
+// Cross-lane moves without LDS (gfx950): the value of lane l ^ 32 (a permlane32 swap), and a
+// DPP read of another lane of the same 16-lane row (CTRL: 0x128 row_ror:8 = lane ^ 8,
+// 0x141 row_half_mirror = lane ^ 7 within 8, 0x4E / 0xB1 quad_perm = lane ^ 2 / lane ^ 1).
+__device__ __forceinline__ uint32_t xchg32(uint32_t v, int lane) {
+  const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return lane < 32 ? s[1] : s[0];
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Reduce-scatter of x over the 32 lanes of a half-wave: lane l holds 16 values x[v] (one per
 // accumulator row v, its own column); on return it holds, for the row index
-// scatter_row(l) = 8 b4 + 4 b3 + 2 b2 + b1 (b = bits of l), the largest |x| over all 32 lanes
-// of its half-wave (lanes l and l ^ 1 hold the same row). Exchanges 8 + 4 + 2 + 1 + 1 values.
+// scatter_row(l) = 8 b4 + 4 b3 + 2 b2 + b1 (b = bits of l), the largest |x| (MAXABS) or the
+// sum of x over all 32 lanes of its half-wave, in a fixed order (lanes l and l ^ 1 hold the
+// same row and the same bits). Five halving steps, each with the
+// lane that differs in that step's bit: l ^ 16 (a permlane16 swap exchanges the two halves in
+// one move), l ^ 8, l ^ 7 (its bits 3 and 4 agree with l's, bit 2 differs), l ^ 2, l ^ 1 (DPP);
+// together they reach all 32 lanes.
 __device__ __forceinline__ int scatter_row(int lane) {
   return ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4 + ((lane >> 2) & 1) * 2 + ((lane >> 1) & 1);
 }
-__device__ __forceinline__ float half_wave_row_amax(const float (&x)[16], int lane) {
+template <bool MAXABS>
+__device__ __forceinline__ float half_wave_row_reduce(const float (&x)[16], int lane) {
+  auto op = [](float a, float b) { return MAXABS ? fmaxf(a, b) : a + b; };
   float m8[8], m4[4], m2[2];
   const bool b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float keep = fabsf(b4 ? x[k + 8] : x[k]), send = fabsf(b4 ? x[k] : x[k + 8]);
-    m8[k] = fmaxf(keep, __shfl_xor(send, 16, 64));
+    // lanes of the lower 16-lane row keep row k and get it from l ^ 16; the upper row keeps k + 8
+    const float lo = MAXABS ? fabsf(x[k]) : x[k], hi = MAXABS ? fabsf(x[k + 8]) : x[k + 8];
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi),
+                                                    false, false);
+    // (own value first, the partner's second, in every lane)
+    m8[k] = b4 ? op(__uint_as_float(r[1]), __uint_as_float(r[0]))
+               : op(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const float keep = b3 ? m8[k + 4] : m8[k], send = b3 ? m8[k] : m8[k + 4];
-    m4[k] = fmaxf(keep, __shfl_xor(send, 8, 64));
+    m4[k] = op(keep, dpp_f<0x128>(send));
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const float keep = b2 ? m4[k + 2] : m4[k], send = b2 ? m4[k] : m4[k + 2];
-    m2[k] = fmaxf(keep, __shfl_xor(send, 4, 64));
+    m2[k] = op(keep, dpp_f<0x141>(send));
   }
   const float keep = b1 ? m2[1] : m2[0], send = b1 ? m2[0] : m2[1];
-  const float m1 = fmaxf(keep, __shfl_xor(send, 2, 64));
-  return fmaxf(m1, __shfl_xor(m1, 1, 64));
+  const float m1 = op(keep, dpp_f<0x4E>(send));
+  // the pair's two lanes add in the same order (lower lane's value first) so both hold the same
+  // bits
+  const float other = dpp_f<0xB1>(m1);
+  return (lane & 1) ? op(other, m1) : op(m1, other);
+}
+__device__ __forceinline__ float half_wave_row_amax(const float (&x)[16], int lane) {
+  return half_wave_row_reduce<true>(x, lane);
 }
 
 // SwiGLU of the stored (BF16-rounded) g and u, h = g s(g) u with s(g) = 1 / (1 + e^-g) from the
