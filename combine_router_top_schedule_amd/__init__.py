@@ -49,7 +49,8 @@ class MokSizes(ctypes.Structure):
                 ("touched_offset", ctypes.c_int64), ("x_slot_bytes", ctypes.c_int64),
                 ("ring_min_bytes", ctypes.c_int64), ("tiles_offset", ctypes.c_int64),
                 ("tiles_max", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
-                ("trace_records", ctypes.c_int64), ("h_slot_bytes", ctypes.c_int64)]
+                ("trace_records", ctypes.c_int64), ("h_slot_bytes", ctypes.c_int64),
+                ("packed_bytes", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -58,7 +59,7 @@ _P = ctypes.c_void_p
 class MokWeights(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("wg", "wu", "wd", "wg_q", "wg_s", "wu_q", "wu_s", "wd_q",
                                   "wd_s", "wgt_q", "wgt_s", "wut_q", "wut_s", "wdt_q", "wdt_s",
-                                  "wg_t", "wu_t", "wd_t")]
+                                  "packed")]
 
 
 class MokTuneResult(ctypes.Structure):
@@ -100,8 +101,7 @@ _SIGS = {
                                      ctypes.POINTER(MokWeightGrads), _P, _P]),
     "mok_quantize_mx": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
                                        ctypes.c_int32, _P, _P, _P]),
-    "mok_transpose_bf16": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
-                                          _P]),
+    "mok_pack_bf16": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.POINTER(MokWeights), _P, _P]),
     "mok_device_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
     "mok_autotune": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
                                     _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
@@ -324,13 +324,11 @@ def mok_quantize_mx(src, transpose: bool, codes, scales, stream=None):
                                                     _ptr(codes), _ptr(scales), _stream(stream)))
 
 
-def mok_transpose_bf16(src, dst, stream=None):
-    """BF16 [batch][rows][cols] (or [rows][cols]) -> dst [batch][cols][rows]."""
-    _need_cuda(src, dst)
-    shape = tuple(src.shape)
-    batch, rows, cols = (1,) + shape if len(shape) == 2 else shape
-    _check("mok_transpose_bf16", lib().mok_transpose_bf16(batch, rows, cols, _ptr(src), _ptr(dst),
-                                                          _stream(stream)))
+def mok_pack_bf16(d: MokDesc, w: MokWeights, packed, stream=None):
+    """Pack the BF16 weights of `w` into `packed` (sizes.packed_bytes, 256-byte aligned)."""
+    _need_cuda(packed)
+    _check("mok_pack_bf16", lib().mok_pack_bf16(ctypes.byref(d), ctypes.byref(w), _ptr(packed),
+                                                _stream(stream)))
 
 
 def mok_autotune(d: MokDesc, x_seg, logits, w: MokWeights, out_seg, topk_idx, topk_p, saved,

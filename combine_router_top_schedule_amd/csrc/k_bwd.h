@@ -255,6 +255,7 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   const int ncols = min(kTileN, s.I - c0);
   Operand A = operand(make_rsrc(d + row0 * xrow, int64_t(nrows) * xrow), xrow);
   const int64_t wrow0 = int64_t(e) * s.I + c0;
+  // (MXFP8 stages B through LDS; BF16 reads the packed Wd^T plane straight into registers)
   Operand B = operand(make_rsrc(wdt + wrow0 * xrow, int64_t(ncols) * xrow), xrow);
   if (MX) {
     A.sstride = B.sstride = s.H / 32;
@@ -262,7 +263,11 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
     B.s0 = B.s1 = make_rsrc(wdt_s + wrow0 * (s.H / 32), int64_t(ncols) * (s.H / 32));
   }
   f32x16 acc[4][4];
-  gemm_tile<MX>(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
+  if constexpr (MX)
+    gemm_tile<MX>(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
+  else
+    gemm_tile_pb(sm, A, packed_b(wdt, wrow0, ncols, s.H), xrow / kStageRowBytes, acc, wm, wn,
+                 lane);
 
   // Epilogue. For each 32-row block i, every wave first copies the g, u and h values of its
   // 32 rows x 128 columns into its own LDS region with coalesced 16-byte loads (all issued
@@ -323,18 +328,22 @@ __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t 
   const int ncols = min(kTileN, s.H - c0);
   Operand A = operand(make_rsrc(dgu + row0 * arow, int64_t(nrows) * arow), arow);
   const int64_t wrow0 = int64_t(e) * s.H + c0;
-  Operand B = operand(make_rsrc(wgt + wrow0 * brow, int64_t(ncols) * brow), brow);
-  B.r1 = make_rsrc(wut + wrow0 * brow, int64_t(ncols) * brow);
-  B.ksplit = brow / kStageRowBytes;
-  if (MX) {
+  f32x16 acc[4][4];
+  if constexpr (MX) {
+    Operand B = operand(make_rsrc(wgt + wrow0 * brow, int64_t(ncols) * brow), brow);
+    B.r1 = make_rsrc(wut + wrow0 * brow, int64_t(ncols) * brow);
+    B.ksplit = brow / kStageRowBytes;
     A.sstride = 2 * s.I / 32;
     A.s0 = A.s1 = make_rsrc(dgu_s + row0 * A.sstride, int64_t(nrows) * A.sstride);
     B.sstride = s.I / 32;
     B.s0 = make_rsrc(wgt_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
     B.s1 = make_rsrc(wut_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
+    gemm_tile<MX>(sm, A, B, arow / kStageRowBytes, acc, wm, wn, lane);
+  } else {
+    // BF16: wgt is the packed [Wg^T | Wu^T] plane (K = 2I; wut unused), brow = I * 2 bytes
+    gemm_tile_pb(sm, A, packed_b(wgt, wrow0, ncols, 2 * s.I), arow / kStageRowBytes, acc, wm, wn,
+                 lane);
   }
-  f32x16 acc[4][4];
-  gemm_tile<MX>(sm, A, B, arow / kStageRowBytes, acc, wm, wn, lane);
   push_epilogue<kPushRec>(sm, acc, nrows, c0, s.H, 0, pt, row0);
 }
 

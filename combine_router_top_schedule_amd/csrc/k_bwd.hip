@@ -10,8 +10,9 @@
 // benchmark section; "Cursor Open-Sources Mixture-of-Kittens (MoK)", Technical Details) and
 // run backward as pull reverse-combine + push reverse-dispatch (same pages, pull dispatch).
 //
-// GEMM operands are staged K-contiguous. Weights are transposed once per call (BF16) or come
-// pre-quantised in the transposed blocking (MXFP8). Weight-gradient operands are transposed per
+// GEMM operands are staged K-contiguous. BF16 weights come packed in MFMA fragment order, Wd^T
+// and [Wg^T | Wu^T] included (made once per weight update, or per call into the workspace);
+// MXFP8 weights come pre-quantised in the transposed blocking. Weight-gradient operands are transposed per
 // expert into [feature][row] planes whose expert column ranges start at multiples of 128 and
 // are zero-padded, so the weight-gradient GEMM reduces over tokens in K-stages of 64 (BF16) or
 // 128 (E4M3) rows with no ragged edge. Every reduction has a fixed order.
@@ -22,46 +23,6 @@ namespace mok {
 namespace {
 
 // ---- transposes -------------------------------------------------------------------------
-
-// W [batch][R][C] -> WT [batch][C][R], BF16 (R, C multiples of 128): tiles of 64 rows x 128
-// columns, 16-byte loads along C into an LDS tile with a 260-byte pitch, 16-byte stores of 8
-// consecutive rows of one column.
-__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* src, uint16_t* dst, int batch,
-                                                     int R, int C) {
-  constexpr int kPitch = 130;
-  __shared__ __attribute__((aligned(16))) uint16_t t[64 * kPitch];
-  const int tid = threadIdx.x;
-  const int tr = R / 64, tc = C / 128;
-  const int64_t total = int64_t(batch) * tr * tc;
-  for (int64_t q = blockIdx.x; q < total; q += gridDim.x) {
-    const int bt = int(q / (int64_t(tr) * tc));
-    const int rem = int(q % (int64_t(tr) * tc));
-    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 128;
-    const uint16_t* sp = src + int64_t(bt) * R * C;
-    uint16_t* dp = dst + int64_t(bt) * R * C;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, r = idx >> 4, ch = idx & 15;
-      const u32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(sp + int64_t(r0 + r) * C + c0 + ch * 8));
-      uint32_t* w = reinterpret_cast<uint32_t*>(t + r * kPitch + ch * 8);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = v[k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, c = idx >> 3, rr = idx & 7;
-      u32x4 out;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        out[k] = uint32_t(t[(rr * 8 + 2 * k) * kPitch + c]) |
-                 (uint32_t(t[(rr * 8 + 2 * k + 1) * kPitch + c]) << 16);
-      *reinterpret_cast<u32x4*>(dp + int64_t(c0 + c) * R + r0 + rr * 8) = out;
-    }
-    __syncthreads();
-  }
-}
 
 // Gather-transpose for the weight-gradient operands: T[f][colpad_e + i] = value of feature f of
 // row off_e + i of expert e. Sources: a BF16 plane [rows][F] (with column offset), an MXFP8
@@ -452,7 +413,7 @@ struct BwdArgs {
   // a GEMM
   const uint8_t* d;        // D rows: BF16 [rows][H] or codes
   const uint8_t* d_s;      // MXFP8 scales [rows][H/32]
-  const uint8_t* wdt;      // Wd^T [El][I][H] (BF16 or codes)
+  const uint8_t* wdt;      // Wd^T: BF16 packed plane [El][I rows][H], or codes [El][I][H]
   const uint8_t* wdt_s;
   ActSource act;           // g|u and h of the forward (ring slot or replayed plane, per row)
   uint16_t* dgu;           // out: dg|du BF16 [rows][2I] (BF16 mode)
@@ -462,9 +423,9 @@ struct BwdArgs {
   // dx GEMM
   const uint8_t* dgu_a;    // dg|du as the dx GEMM reads it: BF16 or codes [rows][2I]
   const uint8_t* dgu_s;    // MXFP8 scales [rows][2I/32]
-  const uint8_t* wgt;      // Wg^T [El][H][I]
+  const uint8_t* wgt;      // BF16: packed [Wg^T | Wu^T] [El][H rows][2I]; MXFP8: Wg^T codes [El][H][I]
   const uint8_t* wgt_s;
-  const uint8_t* wut;      // Wu^T [El][H][I]
+  const uint8_t* wut;      // MXFP8: Wu^T codes [El][H][I] (BF16: unused)
   const uint8_t* wut_s;
   PushTarget push;         // dx rows: pair slots, or dX of a token's only local pair
   // weight gradients: up to three jobs dW[e] = Ta[:, cols of e] . Tb[:, cols of e]^T
@@ -592,13 +553,6 @@ int grid_cap(int64_t items, int cap) {
 
 }  // namespace
 
-hipError_t launch_transpose_w(const uint16_t* src, uint16_t* dst, int batch, int R, int C,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(k_transpose_w, dim3(grid_cap(int64_t(batch) * R * C / 8192, 8192)), dim3(256), 0, s,
-                     src, dst, batch, R, C);
-  return hipGetLastError();
-}
-
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) {
   static std::atomic<bool> attr_done[kMaxDevices];
   hipError_t err = once_per_device(attr_done, [] {
@@ -654,18 +608,10 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   //    (MXFP8: the gather quantises along H on the way, like the forward dispatch)
   //    (BF16: D is written by the (p D)^T gather-transpose below, which reads the same rows)
   if (mx && (err = launch_dispatch(L, b.saved, b.dout_seg, b.dq, s)) != hipSuccess) return err;
-  // 3. transposed BF16 weights for the backward GEMMs: the caller's (made once per weight
-  //    update), or made here into the workspace
-  const bool given_t = !mx && b.w.wg_t && b.w.wu_t && b.w.wd_t;
-  if (!mx && !given_t) {
-    if ((err = launch_transpose_w(static_cast<const uint16_t*>(b.w.wd), b.wdt, El, H, I, s)) != hipSuccess ||
-        (err = launch_transpose_w(static_cast<const uint16_t*>(b.w.wg), b.wgt, El, I, H, s)) != hipSuccess ||
-        (err = launch_transpose_w(static_cast<const uint16_t*>(b.w.wu), b.wut, El, I, H, s)) != hipSuccess)
-      return err;
-  }
-  const uint8_t* wdt_bf = reinterpret_cast<const uint8_t*>(given_t ? b.w.wd_t : b.wdt);
-  const uint8_t* wgt_bf = reinterpret_cast<const uint8_t*>(given_t ? b.w.wg_t : b.wgt);
-  const uint8_t* wut_bf = reinterpret_cast<const uint8_t*>(given_t ? b.w.wu_t : b.wut);
+  // 3. BF16 backward GEMMs read packed Wd^T and [Wg^T | Wu^T] (b.w.packed: the caller's, or
+  //    packed by the host entry point into the workspace)
+  const PackOffsets po = pack_offsets(El, H, I);
+  const uint8_t* packed = static_cast<const uint8_t*>(b.w.packed);
   // 4. weight-gradient operand planes that do not need dg|du: per-expert column ranges, X^T,
   //    (p D)^T and h^T (MXFP8: quantised along tokens as they are written)
   const uint16_t* const* xs = reinterpret_cast<const uint16_t* const*>(b.x_seg);
@@ -706,16 +652,16 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.s = FfnShape{H, I};
   a.d = mx ? b.dq : b.d;
   a.d_s = mx ? b.dq + L.rows_max * H : nullptr;
-  a.wdt = mx ? b.w.wdt_q : wdt_bf;
+  a.wdt = mx ? b.w.wdt_q : packed + po.wdt;
   a.wdt_s = mx ? b.w.wdt_s : nullptr;
   a.act = asrc;
   a.dgu = b.dgu;
   a.dp_part = b.dp_part;
   a.dgu_a = mx ? b.dguq : reinterpret_cast<const uint8_t*>(b.dgu);
   a.dgu_s = mx ? b.dguq + L.rows_max * 2 * I : nullptr;
-  a.wgt = mx ? b.w.wgt_q : wgt_bf;
+  a.wgt = mx ? b.w.wgt_q : packed + po.dx;
   a.wgt_s = mx ? b.w.wgt_s : nullptr;
-  a.wut = mx ? b.w.wut_q : wut_bf;
+  a.wut = mx ? b.w.wut_q : nullptr;
   a.wut_s = mx ? b.w.wut_s : nullptr;
   a.push = PushTarget{b.slots, b.push};
   a.ld = ld;

@@ -77,12 +77,7 @@ FfnStagedArgs staged_args(const Layout& L, const uint8_t* saved, const uint8_t* 
   }
   a.perm = reinterpret_cast<const int32_t*>(saved + L.sv_perm);
   a.s = FfnShape{L.H, L.I};
-  if (mx) {
-    a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
-  } else {
-    a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),
-                     static_cast<const uint8_t*>(w.wd), nullptr, nullptr, nullptr};
-  }
+  a.w = ffn_weights(L, w);
   ActPlanes xp = act_planes(const_cast<uint8_t*>(xd), L.rows_max, L.H, L.I, L.dtype, true);
   a.pl = act_planes(act, L.rows_max, L.H, L.I, L.dtype, false);
   a.pl.x = xp.x;

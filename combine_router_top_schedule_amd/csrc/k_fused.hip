@@ -600,9 +600,7 @@ hipError_t launch_layer_fwd_macro(const Layout& L, const mok_desc& d, int B,
   a.caph = L.ring_caph;
   a.capa = L.ring_capa;
   a.s = FfnShape{L.H, L.I};
-  if (mx) a.w = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s};
-  else a.w = FfnWeights{static_cast<const uint8_t*>(w.wg), static_cast<const uint8_t*>(w.wu),
-                        static_cast<const uint8_t*>(w.wd), nullptr, nullptr, nullptr};
+  a.w = ffn_weights(L, w);
   a.cnt = cnt;
   a.err = reinterpret_cast<int32_t*>(ws) + kWsError;
   a.tiles_max = L.tiles_max;

@@ -287,6 +287,115 @@ __device__ __forceinline__ void gemm_tile(GemmLds& sm, const Operand& A, const O
   }
 }
 
+// ---- B operand in fragment order (BF16) -----------------------------------------------------
+// A packed matrix with R rows (a multiple of 32) and reduction length K (a multiple of 16) is
+// stored as R/32 x K/16 fragments of 1 KB: fragment (n32, k16) at byte (n32 * K/16 + k16) * 1024,
+// where lane l's 16 bytes hold row 32 n32 + l % 32, elements 16 k16 + 8 (l / 32) .. +7 -- the
+// register contents of a v_mfma_f32_32x32x16_bf16 fragment. One load per lane then fills a
+// fragment from 1 KB of consecutive bytes (8 whole cache lines), where row-major rows would
+// touch 32 lines per load. The first r rows (r a multiple of 32) take the first r * K * 2 bytes,
+// as in a row-major matrix, so a row offset converts to a byte offset the same way.
+struct PackedB {
+  __amdgpu_buffer_rsrc_t r;   // from the tile's first row; rows past the valid ones read as 0
+  int k16s;                   // K / 16: fragments per 32-row block
+};
+
+__device__ __forceinline__ PackedB packed_b(const uint8_t* plane, int64_t row0, int nrows, int K) {
+  PackedB p;
+  p.r = make_rsrc(plane + row0 * K * 2, int64_t(nrows) * K * 2);
+  p.k16s = K / 16;
+  return p;
+}
+
+// Slice kk of stage kt: the wave's 4 B fragments (column blocks j of its 128 tile columns).
+__device__ __forceinline__ void load_b_packed(bf16x8 (&b)[4], const PackedB& B, int kt, int kk,
+                                              int wn, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 v = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   B.r, ((wn * 4 + j) * B.k16s + kt * 4 + kk) * 1024 + lane * 16, 0, 0));
+    b[j] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+__device__ __forceinline__ void load_a_frag(bf16x8 (&a)[4], const uint8_t* A, int kk, int wm,
+                                            int lane) {
+  const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a[i] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + i * 32 + (lane & 31), ch));
+}
+
+// The K loop of one BF16 output tile with a packed B operand. A is staged through LDS as in
+// gemm_tile; B fragments go from global memory straight into registers one stage ahead: once
+// the MFMAs of slice kk have read B(kt, kk), the same registers are loaded with B(kt+1, kk). That
+// halves the LDS traffic per stage (the DMA writes and fragment reads of B are gone), the
+// largest cost of the LDS-staged loop. The stage barrier waits only for the A stage; the 12 B
+// loads issued after it stay in flight. Slices run in the same order as gemm_tile, so the
+// result is bit-identical to it. On return no load is in flight and every LDS read of the stage
+// buffers has completed.
+__device__ __forceinline__ void gemm_tile_pb(GemmLds& sm, const Operand& A, const PackedB& B,
+                                             int ksteps, f32x16 (&acc)[4][4], int wm, int wn,
+                                             int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (ksteps <= 0) return;
+  const int w = wave_id();
+  const int last = ksteps - 1;
+  bf16x8 b[4][4];   // [slice][column block]
+  bf16x8 fa[2][4];
+  issue_stage<kLoadAgent>(A, sm.a[0], sm.as[0], 0, false, w);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) load_b_packed(b[kk], B, 0, kk, wn, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  load_a_frag(fa[0], sm.a[0], 0, wm, lane);
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt < last;
+    if (more) issue_stage<kLoadAgent>(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, false, w);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < 4) {
+        load_a_frag(fa[(kk + 1) & 1], sm.a[cur], kk + 1, wm, lane);
+      } else {
+        // vmcnt(12): the loads issued after A(kt+1) are B(kt+1) of slices 0-2, 4 each
+        __builtin_amdgcn_s_waitcnt(0x0F7C);
+        __syncthreads();
+        if (more) load_a_frag(fa[0], sm.a[cur ^ 1], 0, wm, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], b[kk][j], acc[i][j],
+                                                               0, 0, 0);
+      // (in the last stage a harmless reload of the same slice, so every stage issues the same
+      // loads and the wait count above holds)
+      load_b_packed(b[kk], B, more ? kt + 1 : kt, kk, wn, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 // ---- tile scheduling ------------------------------------------------------------------------
 // Logical workgroup id that gives the workgroups resident on one XCD (blockIdx % 8 on MI355X)
 // consecutive ids, so consecutive tiles -- which share operands -- land in one L2.

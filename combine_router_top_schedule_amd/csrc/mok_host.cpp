@@ -53,13 +53,7 @@ mok_status check_weights(const mok_desc* d, const mok_weights* w, bool backward)
   if (d->dtype == MOK_BF16) {
     if (!w->wg || !w->wu || !w->wd) return MOK_ERR_NULL;
     if (!aligned16(w->wg) || !aligned16(w->wu) || !aligned16(w->wd)) return MOK_ERR_ALIGN;
-    if (backward) {
-      // the transposed weights come as a set, or not at all
-      const int given = (w->wg_t != nullptr) + (w->wu_t != nullptr) + (w->wd_t != nullptr);
-      if (given != 0 && given != 3) return MOK_ERR_NULL;
-      if (given == 3 && (!aligned16(w->wg_t) || !aligned16(w->wu_t) || !aligned16(w->wd_t)))
-        return MOK_ERR_ALIGN;
-    }
+    if (w->packed && (reinterpret_cast<uintptr_t>(w->packed) & 255u)) return MOK_ERR_ALIGN;
   } else {
     if (!w->wg_q || !w->wg_s || !w->wu_q || !w->wu_s || !w->wd_q || !w->wd_s) return MOK_ERR_DTYPE;
     if (!aligned16(w->wg_q) || !aligned16(w->wu_q) || !aligned16(w->wd_q)) return MOK_ERR_ALIGN;
@@ -78,6 +72,19 @@ Layout layout_of(const mok_desc& d) {
 }
 
 mok_status hip_status(hipError_t e) { return e == hipSuccess ? MOK_OK : MOK_ERR_HIP; }
+
+// The weights as the kernels read them: BF16 with packed planes, the caller's (w.packed) or the
+// `planes` packed here by one launch into the workspace.
+mok_status with_packed(const Layout& L, const mok_weights& w, uint8_t* ws, int planes,
+                       hipStream_t s, mok_weights* out) {
+  *out = w;
+  if (L.dtype != MOK_BF16 || w.packed) return MOK_OK;
+  uint8_t* dst = ws + L.ws_pack;
+  const hipError_t e = launch_pack_bf16(L, w.wg, w.wu, w.wd, dst, planes, s);
+  if (e != hipSuccess) return MOK_ERR_HIP;
+  out->packed = dst;
+  return MOK_OK;
+}
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -147,6 +154,7 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   sizes->trace_offset = L.trace_max > 0 ? L.ws_trace : 0;
   sizes->trace_records = L.trace_max;
   sizes->h_slot_bytes = L.hsb;
+  sizes->packed_bytes = L.dtype == MOK_BF16 ? pack_offsets(L.El, L.H, L.I).bytes : 0;
   return MOK_OK;
 }
 
@@ -209,8 +217,11 @@ mok_status mok_expert_ffn(const mok_desc* desc, const void* saved_dev, const voi
   if (st != MOK_OK) return st;
   if (!aligned16(xd_dev) || !aligned16(act_dev) || !aligned16(slots_dev)) return MOK_ERR_ALIGN;
   const Layout L = layout_of(*desc);
+  mok_weights wk;
+  st = with_packed(L, *w, static_cast<uint8_t*>(ws_dev), kPackGu | kPackWd, as_stream(stream), &wk);
+  if (st != MOK_OK) return st;
   return hip_status(launch_ffn_staged(L, static_cast<const uint8_t*>(saved_dev),
-                                      static_cast<const uint8_t*>(xd_dev), *w,
+                                      static_cast<const uint8_t*>(xd_dev), wk,
                                       static_cast<uint8_t*>(act_dev),
                                       static_cast<uint16_t*>(slots_dev),
                                       static_cast<uint8_t*>(ws_dev), as_stream(stream)));
@@ -241,17 +252,20 @@ mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void
                                        transpose, codes_dev, scales_dev, as_stream(stream)));
 }
 
-mok_status mok_transpose_bf16(int32_t batch, int32_t rows, int32_t cols, const void* src_dev,
-                              void* dst_dev, void* stream) {
-  if (!src_dev || !dst_dev) return MOK_ERR_NULL;
-  if (batch < 1 || rows < 64 || cols < 128 || rows % 64 || cols % 128) return MOK_ERR_SHAPE;
-  if (!aligned16(src_dev) || !aligned16(dst_dev)) return MOK_ERR_ALIGN;
-  const int64_t bytes = int64_t(batch) * rows * cols * 2;
-  const uintptr_t a = reinterpret_cast<uintptr_t>(src_dev), b = reinterpret_cast<uintptr_t>(dst_dev);
-  if (a < b + bytes && b < a + bytes) return MOK_ERR_SHAPE;   // overlapping buffers
-  return hip_status(launch_transpose_w(static_cast<const uint16_t*>(src_dev),
-                                       static_cast<uint16_t*>(dst_dev), batch, rows, cols,
-                                       as_stream(stream)));
+mok_status mok_pack_bf16(const mok_desc* desc, const mok_weights* w, void* packed_dev,
+                         void* stream) {
+  mok_status st = check_desc(desc);
+  if (st != MOK_OK) return st;
+  if (!w || !packed_dev) return MOK_ERR_NULL;
+  if (desc->dtype != MOK_BF16) return MOK_ERR_DTYPE;
+  mok_weights src = *w;
+  src.packed = nullptr;
+  st = check_weights(desc, &src, false);
+  if (st != MOK_OK) return st;
+  if (reinterpret_cast<uintptr_t>(packed_dev) & 255u) return MOK_ERR_ALIGN;
+  const Layout L = layout_of(*desc);
+  return hip_status(launch_pack_bf16(L, w->wg, w->wu, w->wd, static_cast<uint8_t*>(packed_dev),
+                                     kPackAll, as_stream(stream)));
 }
 
 mok_status mok_device_status(const void* ws_dev, void* stream, mok_status* out) {
@@ -286,7 +300,10 @@ mok_status mok_layer_fwd(const mok_desc* desc, const void* const* x_seg_dev,
   if (fused_slots_per_xcd(L) < 2) return MOK_ERR_RING;
   const MacroBuffers mb{x_seg_dev, logits_dev, out_seg_dev, topk_idx_dev, topk_p_dev,
                         static_cast<uint8_t*>(saved_dev), static_cast<uint16_t*>(slots_dev)};
-  return hip_status(launch_layer_fwd_macro(L, *desc, 1, &mb, *w, static_cast<uint8_t*>(ring_dev),
+  mok_weights wk;
+  st = with_packed(L, *w, static_cast<uint8_t*>(ws_dev), kPackGu | kPackWd, as_stream(stream), &wk);
+  if (st != MOK_OK) return st;
+  return hip_status(launch_layer_fwd_macro(L, *desc, 1, &mb, wk, static_cast<uint8_t*>(ring_dev),
                                            static_cast<uint8_t*>(ws_dev), as_stream(stream)));
 }
 
@@ -331,7 +348,10 @@ mok_status mok_layer_fwd_macro(const mok_desc* desc, int32_t num_macro,
   }
   const Layout L = layout_of(*desc);
   if (fused_slots_per_xcd(L) < 2) return MOK_ERR_RING;
-  return hip_status(launch_layer_fwd_macro(L, *desc, num_macro, mb, *w,
+  mok_weights wk;
+  st = with_packed(L, *w, static_cast<uint8_t*>(ws_dev), kPackGu | kPackWd, as_stream(stream), &wk);
+  if (st != MOK_OK) return st;
+  return hip_status(launch_layer_fwd_macro(L, *desc, num_macro, mb, wk,
                                            static_cast<uint8_t*>(ring_dev),
                                            static_cast<uint8_t*>(ws_dev), as_stream(stream)));
 }
@@ -363,7 +383,9 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
   b.dx_seg = dx_seg_dev;
   b.topk_idx = topk_idx_dev;
   b.topk_p = topk_p_dev;
-  b.w = *w;
+  // the backward replays gate/up (packed gate/up plane) and reads Wd^T and [Wg^T | Wu^T]
+  st = with_packed(L, *w, ws, kPackGu | kPackWdt | kPackDx, as_stream(stream), &b.w);
+  if (st != MOK_OK) return st;
   b.g = *g;
   b.slots = static_cast<uint16_t*>(slots_dev);
   b.dp = dp_dev;
@@ -378,9 +400,6 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
   b.dgu = reinterpret_cast<uint16_t*>(ws + L.b_dgu);
   b.dguq = ws + L.b_dguq;
   b.dp_part = reinterpret_cast<float*>(ws + L.b_dp);
-  b.wdt = reinterpret_cast<uint16_t*>(ws + L.b_wdt);
-  b.wgt = reinterpret_cast<uint16_t*>(ws + L.b_wgt);
-  b.wut = reinterpret_cast<uint16_t*>(ws + L.b_wut);
   b.xt = reinterpret_cast<uint16_t*>(ws + L.b_xt);
   b.dt = reinterpret_cast<uint16_t*>(ws + L.b_dt);
   b.dgt = reinterpret_cast<uint16_t*>(ws + L.b_dgt);
@@ -421,6 +440,15 @@ extern "C" mok_status mok_autotune(const mok_desc* desc, const void* const* x_se
     if (c < cus / 2) cu_cand.push_back(c);
   if (cu_cand.empty()) cu_cand.push_back(kXcds);
   hipStream_t s = as_stream(stream);
+  if (!w || !ws_dev) return MOK_ERR_NULL;
+  if (!aligned16(ws_dev)) return MOK_ERR_ALIGN;
+  st = check_weights(desc, w, false);
+  if (st != MOK_OK) return st;
+  // BF16 weights without packed planes are packed once here (the pack region's offset is the
+  // same for every minibatch size), so that no timed call includes the packing
+  mok_weights wk;
+  st = with_packed(L0, *w, static_cast<uint8_t*>(ws_dev), kPackGu | kPackWd, s, &wk);
+  if (st != MOK_OK) return st;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
     if (e0) (void)hipEventDestroy(e0);
@@ -438,7 +466,7 @@ extern "C" mok_status mok_autotune(const mok_desc* desc, const void* const* x_se
       std::vector<float> times;
       for (int r = 0; r <= reps && out == MOK_OK; ++r) {
         if (hipEventRecord(e0, s) != hipSuccess) { out = MOK_ERR_HIP; break; }
-        out = mok_layer_fwd(&d, x_seg_dev, logits_dev, w, out_seg_dev, topk_idx_dev, topk_p_dev,
+        out = mok_layer_fwd(&d, x_seg_dev, logits_dev, &wk, out_seg_dev, topk_idx_dev, topk_p_dev,
                             saved_dev, ring_dev, slots_dev, ws_dev, stream);
         if (out != MOK_OK) break;
         if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) {

@@ -93,6 +93,24 @@ enum Bwd2Header : int {
 // gradient GEMM reduces in whole K-stages (64 BF16 or 128 E4M3 rows) with zero padding.
 constexpr int kPadRows = 128;
 
+// Packed BF16 weights: the B operands of the expert GEMMs in fragment order (PackedB in
+// k_gemm.h), four planes per set of local experts. Made once per weight update with
+// mok_pack_bf16, or by each call into its workspace.
+struct PackOffsets {
+  int64_t gu;     // [El][2I rows][H]: Wg and Wu rows in the gate/up tiles' order (64-row blocks
+                  // alternate Wg and Wu: packed row n is row (n/128)*64 + n%64 of Wg when
+                  // (n/64) is even, of Wu when it is odd)
+  int64_t wd;     // [El][H rows][I]: Wd (the down GEMM)
+  int64_t wdt;    // [El][I rows][H]: Wd^T (the a GEMM)
+  int64_t dx;     // [El][H rows][2I]: Wg^T then Wu^T along K (the dx GEMM)
+  int64_t bytes;
+};
+inline PackOffsets pack_offsets(int El, int H, int I) {
+  const int64_t m = int64_t(El) * H * I * 2;
+  return PackOffsets{0, 2 * m, 3 * m, 4 * m, 6 * m};
+}
+constexpr int kPackGu = 1, kPackWd = 2, kPackWdt = 4, kPackDx = 8, kPackAll = 15;
+
 struct Layout {
   // shapes
   int H, E, K, I, S, T, e0, El, M, dtype;
@@ -106,7 +124,7 @@ struct Layout {
   int64_t ring_share, xsb, hsb, asb;
   int ring_capx, ring_caph, ring_capa;
   // ws
-  int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_push, ws_trace, ws_bytes;
+  int64_t ws_state, ws_tiles, ws_counters, ws_dp, ws_push, ws_trace, ws_pack, ws_bytes;
   int64_t trace_max;   // phase-trace records (MOK_FLAG_TRACE; 0 without it)
   int topk_blocks;
   int64_t tiles_max, J_max;
@@ -116,7 +134,7 @@ struct Layout {
   int64_t xd_bytes, act_bytes, slots_bytes, wq_bytes;
   // backward workspace (after the forward ws): byte offsets from the ws start
   int64_t rp_max;
-  int64_t b_hdr2, b_xd, b_act, b_d, b_dq, b_dgu, b_dguq, b_dp, b_wdt, b_wgt, b_wut;
+  int64_t b_hdr2, b_xd, b_act, b_d, b_dq, b_dgu, b_dguq, b_dp;
   int64_t b_xt, b_dt, b_dgt, b_dut, b_ht, b_qxt, b_qdt, b_qdgt, b_qdut, b_qht;
   int64_t b_restore, b_replay, b_rsl, b_counts, b_actsrc, b_bytes;
 };
@@ -174,6 +192,10 @@ inline Layout make_layout(const mok_desc& d) {
   L.topk_blocks = int(cdiv(L.N, kTopkTokensPerBlock));
   off = 256;
   L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 2), 256);
+  // BF16 weights packed by the call itself when the caller gives none (after the router's
+  // words, so its offset does not depend on the minibatch size)
+  L.ws_pack = off;
+  off = align_up(off + (L.dtype == MOK_BF16 ? pack_offsets(L.El, L.H, L.I).bytes : 0), 256);
   L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
   L.ws_counters = off; off = align_up(off + 4 * (64 + (3 + kXcds) * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
@@ -204,9 +226,6 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_dgu = take(mx ? 0 : rm * 2 * I * 2);   // BF16 dg|du (MXFP8 writes codes only)
   L.b_dguq = take(mx ? rm * (2 * I + 2 * I / 32) : 0);
   L.b_dp = take(rm * (I / kTileN + 1) * 4);
-  L.b_wdt = take(mx ? 0 : int64_t(L.El) * H * I * 2);
-  L.b_wgt = take(mx ? 0 : int64_t(L.El) * H * I * 2);
-  L.b_wut = take(mx ? 0 : int64_t(L.El) * H * I * 2);
   // BF16 transposed planes (MXFP8 writes only the quantised planes below)
   L.b_xt = take(mx ? 0 : H * rp * 2);
   L.b_dt = take(mx ? 0 : H * rp * 2);
@@ -346,7 +365,6 @@ struct BwdBuffers {
   uint8_t *xd, *act, *d, *dq, *dguq;
   uint16_t* dgu;
   float* dp_part;
-  uint16_t *wdt, *wgt, *wut;
   uint16_t *xt, *dt, *dgt, *dut, *ht;
   uint8_t *q_xt, *q_dt, *q_dgt, *q_dut, *q_ht;
   uint8_t* ring;      // the forward's ring (null: replay every row)
@@ -354,9 +372,10 @@ struct BwdBuffers {
   PushRec* push;      // [rows_max] dx GEMM push records
 };
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
-// W [batch][R][C] -> [batch][C][R], BF16; R a multiple of 64, C a multiple of 128.
-hipError_t launch_transpose_w(const uint16_t* src, uint16_t* dst, int batch, int R, int C,
-                              hipStream_t s);
+// Packed BF16 weights (k_pack.hip): writes the planes selected by `planes` (kPack* bits) of
+// pack_offsets(El, H, I) at dst from the row-major weights wg, wu [El][I][H], wd [El][H][I].
+hipError_t launch_pack_bf16(const Layout& L, const void* wg, const void* wu, const void* wd,
+                            uint8_t* dst, int planes, hipStream_t s);
 
 // Fused forward (k_fused.hip): the ring is split into one share per XCD, each cut into tile
 // slots of 256 expert-ordered rows (X | g,u | h).

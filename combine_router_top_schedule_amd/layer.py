@@ -7,7 +7,7 @@ from typing import Optional
 import torch
 
 from . import (MOK_MXFP8, desc, mok_autotune, mok_combine, mok_dispatch, mok_expert_ffn,
-               mok_layer_bwd, mok_layer_fwd, mok_quantize_mx, mok_schedule, mok_transpose_bf16,
+               mok_layer_bwd, mok_layer_fwd, mok_pack_bf16, mok_quantize_mx, mok_schedule,
                query_sizes, seg_table, weights_struct)
 
 
@@ -42,27 +42,22 @@ class MokLayer:
         self._keep = []
 
     # ---- weights ---------------------------------------------------------------------------
-    def set_weights(self, wg, wu, wd, transposed: bool = True):
+    def set_weights(self, wg, wu, wd, packed: bool = True):
         """BF16 masters. In MXFP8 mode they are quantised here (forward blocking along each
         GEMM's reduction axis, and the transposed backward blocking). In BF16 mode, with
-        `transposed`, the backward's transposed copies are made here once (else the backward
-        transposes on every call)."""
+        `packed`, the GEMMs' packed weight planes are made here once (else every call packs
+        them into its workspace)."""
         d = self.d
         self._keep = [wg, wu, wd]
         E, I, H = d.num_local_experts, d.intermediate, d.hidden
         dev = self.device
         if not self.mx:
-            if not transposed:
-                self.w = weights_struct(wg, wu, wd)
-                return
-            wg_t = torch.empty((E, H, I), dtype=wg.dtype, device=dev)
-            wu_t = torch.empty_like(wg_t)
-            wd_t = torch.empty((E, I, H), dtype=wd.dtype, device=dev)
-            mok_transpose_bf16(wg, wg_t)
-            mok_transpose_bf16(wu, wu_t)
-            mok_transpose_bf16(wd, wd_t)
-            self._keep += [wg_t, wu_t, wd_t]
-            self.w = weights_struct(wg, wu, wd, wg_t=wg_t, wu_t=wu_t, wd_t=wd_t)
+            self.w = weights_struct(wg, wu, wd)
+            if packed:
+                buf = _bytes(query_sizes(d).packed_bytes, dev)
+                mok_pack_bf16(d, self.w, buf)
+                self._keep.append(buf)
+                self.w.packed = buf.data_ptr()
             return
 
         def q(src, rows, cols, transpose):

@@ -228,21 +228,49 @@ def test_backward_after_timed_out_forward_replays_every_row():
         assert torch.equal(a, b)
 
 
-def test_backward_with_caller_transposed_weights_equals_per_call_transposes():
-    """BF16: the backward reading transposed weights made once by mok_transpose_bf16 (the
-    layer's default) gives bit for bit the outputs of the backward that transposes the weights
-    into its workspace on every call; mok_transpose_bf16 equals torch's transpose exactly."""
+def _packed_reference(wg, wu, wd):
+    """The packed planes as the C header states them, built by rearranging the weights in torch:
+    in a plane of R rows and reduction length K, the 1 KB block (n32, k16) holds in lane l the
+    elements 16 k16 + 8 (l // 32) .. +7 of row 32 n32 + l % 32; planes in the order gate/up
+    (64-row blocks alternating Wg and Wu), Wd, Wd^T, [Wg^T | Wu^T]."""
+    E, I, H = wg.shape
+
+    def plane(W):
+        e, R, K = W.shape
+        t = W.reshape(e, R // 32, 32, K // 16, 2, 8).permute(0, 1, 3, 4, 2, 5)
+        return t.contiguous().reshape(-1)
+
+    gu = torch.stack([wg.reshape(E, I // 64, 64, H), wu.reshape(E, I // 64, 64, H)], dim=2)
+    dx = torch.cat([wg.transpose(1, 2), wu.transpose(1, 2)], dim=2)
+    return torch.cat([plane(gu.reshape(E, 2 * I, H)), plane(wd), plane(wd.transpose(1, 2)),
+                      plane(dx)])
+
+
+def test_packed_weights_match_the_stated_layout_and_per_call_packing():
+    """BF16: the planes mok_pack_bf16 writes (the layer's default) are exactly the layout the C
+    header states, element for element; and fused and staged forward + backward reading them
+    give bit for bit the outputs of calls that pack into their own workspace each time. I = 384
+    leaves a half column tile (128 rows of the packed Wd^T plane) at each expert's end."""
     cfg = datagen.CONFIGS["tiny"].replace(S=3, T=512, H=1024, E=16, K=4, I=384, e0=4, E_loc=4,
                                           x_std=1.0)
-    case = BwdCase(cfg)
-    assert case.layer.w.wg_t and case.layer.w.wu_t and case.layer.w.wd_t
-    case.run()
-    with_t = case.grads()
-    wd_t = torch.empty((cfg.E_loc, cfg.I, cfg.H), dtype=case.wd.dtype, device="cuda")
-    mok.mok_transpose_bf16(case.wd, wd_t)
-    assert torch.equal(wd_t, case.wd.transpose(1, 2).contiguous())
-    case.layer.set_weights(case.wg, case.wu, case.wd, transposed=False)
-    assert not case.layer.w.wg_t
-    case.run()
-    for a, b in zip(with_t, case.grads()):
-        assert torch.equal(a, b)
+    ring = 4 * mok.query_sizes(mok.desc_from_config(cfg)).ring_min_bytes
+    case = BwdCase(cfg, fused=True, ring_bytes=ring)
+    assert case.layer.w.packed
+    n = case.layer.sizes.packed_bytes
+    assert n == 6 * cfg.E_loc * cfg.H * cfg.I * 2
+    got = torch.empty(n // 2, dtype=torch.int16, device="cuda")
+    mok.mok_pack_bf16(case.d, case.layer.w, got)
+    assert torch.equal(got, _packed_reference(case.wg, case.wu, case.wd))
+    results = []
+    for packed in (True, False):
+        case.layer.set_weights(case.wg, case.wu, case.wd, packed=packed)
+        assert bool(case.layer.w.packed) == packed
+        for fused in (True, False):
+            case.out.zero_()
+            case.run(fused=fused)
+            results.append(case.grads() + [case.out.clone()])
+    fw, bw = case.oracle_backward()
+    _compare(case, fw, bw, max_rel_err, BF16_TOL)
+    for other in results[1:]:
+        for a, b in zip(results[0], other):
+            assert torch.equal(a, b)
