@@ -382,7 +382,8 @@ __device__ __forceinline__ void store_tile_f32(GemmLds& sm, const f32x16 (&acc)[
 
 // Weight-gradient tile: out[m0 + m][n0 + n] = sum over the expert's padded columns c of
 // Ta[m0 + m][c] Tb[n0 + n][c]; fp32 output [Fa][Fb] (fully overwritten). ld = row pitch of Ta
-// and Tb (elements; their MXFP8 scale rows have ld / 32 bytes).
+// and Tb (elements; their MXFP8 scale rows have ld / 32 bytes). BF16: Tb is packed in fragment
+// order with ld columns (K = the padded columns), read straight into registers.
 template <bool MX>
 __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const uint8_t* ta_s,
                                            const uint8_t* tb, const uint8_t* tb_s, int64_t ld,
@@ -404,7 +405,18 @@ __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const
       A.s0 = A.s1 = make_rsrc(ta_s + int64_t(m0) * (ld / 32) + c0 / 32, int64_t(ma) * (ld / 32));
       B.s0 = B.s1 = make_rsrc(tb_s + int64_t(n0) * (ld / 32) + c0 / 32, int64_t(nb) * (ld / 32));
     }
-    gemm_tile<MX>(sm, A, B, ncols * eb / kStageRowBytes, acc, wm, wn, lane);
+    if constexpr (MX) {
+      gemm_tile<MX>(sm, A, B, ncols * eb / kStageRowBytes, acc, wm, wn, lane);
+    } else {
+      // fragment (n32, k16) of the packed plane at (n32 * ld/16 + k16) KB; the resource covers
+      // the tile's nb rows over the expert's columns [c0, c0 + ncols)
+      const int k16s = int(ld / 16);
+      PackedB P;
+      P.r = make_rsrc(tb + (int64_t(n0 / 32) * k16s + c0 / 16) * 1024,
+                      (int64_t(nb / 32 - 1) * k16s + ncols / 16) * 1024);
+      P.k16s = k16s;
+      gemm_tile_pb(sm, A, P, ncols * eb / kStageRowBytes, acc, wm, wn, lane);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)

@@ -53,6 +53,9 @@ struct TransposeArgs {
   // decoded. (The plane fields are otherwise unused.)
   int from_act;
   ActSource act;
+  // BF16: store dst in MFMA fragment order (PackedB in k_gemm.h: rows = features, K = the
+  // padded columns), the layout the weight-gradient GEMMs read their B operand in
+  int packed;
 };
 
 // One tile = 64 padded columns (source rows) x 128 features. Source rows are read with 16-byte
@@ -203,6 +206,11 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
         *reinterpret_cast<uint2*>(a.qdst + int64_t(f0 + f) * cols + c0 + cc * 8) = codes;
         if ((cc & 3) == 0)
           a.qdst[int64_t(a.F) * a.ld + int64_t(f0 + f) * (cols / 32) + (c0 + cc * 8) / 32] = uint8_t(sc);
+      } else if (a.packed) {
+        // 8 columns of one feature are one lane's 16 bytes of fragment (feature/32, column/16)
+        const int fa = f0 + f, col = c0 + cc * 8;
+        const int64_t frag = int64_t(fa >> 5) * (cols >> 4) + (col >> 4);
+        *reinterpret_cast<u32x4*>(a.dst + (frag * 64 + (fa & 31) + 32 * ((col >> 3) & 1)) * 8) = out;
       } else {
         *reinterpret_cast<u32x4*>(a.dst + int64_t(f0 + f) * cols + c0 + cc * 8) = out;
       }
@@ -629,15 +637,17 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   asrc.code = b.actsrc;
   auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
                 int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst,
-                uint16_t* rows_out = nullptr, bool from_act = false) {
+                uint16_t* rows_out = nullptr, bool from_act = false, bool packed = false) {
     TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
-                    ld, F, L.K, L.T, El, rows_out, int(from_act), asrc};
+                    ld, F, L.K, L.T, El, rows_out, int(from_act), asrc, int(packed && !mx)};
     hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
   };
-  tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt);                         // X^T
+  // (X^T and h^T are the B operands of the weight-gradient GEMMs: BF16 stores them packed)
+  tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt, nullptr, false, true);   // X^T
   tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt,
      mx ? nullptr : reinterpret_cast<uint16_t*>(b.d));                              // (p D)^T (+ D)
-  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht, nullptr, true);  // h^T
+  tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht, nullptr, true,
+     true);                                                                         // h^T
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   BwdArgs a{};

@@ -72,8 +72,10 @@ __global__ __launch_bounds__(256) void k_router_wrt(const uint16_t* wr, uint16_t
   }
 }
 
-// Token rows from the segments -> X^T [H][Np] (zero-padded tokens). Tiles of 64 tokens x 128
-// features through LDS: 16-byte loads along H, 16-byte stores of 8 consecutive tokens.
+// Token rows from the segments -> X^T [H][Np] (zero-padded tokens), stored in MFMA fragment
+// order (PackedB in k_gemm.h; K = the tokens), the B operand of the dW_r GEMM. Tiles of 64
+// tokens x 128 features through LDS: 16-byte loads along H, 16-byte stores of 8 consecutive
+// tokens of one feature (one lane's share of fragment (feature/32, token/16)).
 __global__ __launch_bounds__(256) void k_router_xt(const uint16_t* const* x_seg, uint16_t* xt,
                                                    int64_t N, int T, int H, int64_t Np) {
   constexpr int kPitch = 130;
@@ -104,7 +106,10 @@ __global__ __launch_bounds__(256) void k_router_xt(const uint16_t* const* x_seg,
       for (int k = 0; k < 4; ++k)
         out[k] = uint32_t(t[(rr * 8 + 2 * k) * kPitch + c]) |
                  (uint32_t(t[(rr * 8 + 2 * k + 1) * kPitch + c]) << 16);
-      *reinterpret_cast<u32x4*>(xt + int64_t(f0 + c) * Np + n0 + rr * 8) = out;
+      const int fa = f0 + c;
+      const int64_t col = n0 + rr * 8;
+      const int64_t frag = int64_t(fa >> 5) * (Np >> 4) + (col >> 4);
+      *reinterpret_cast<u32x4*>(xt + (frag * 64 + (fa & 31) + 32 * ((col >> 3) & 1)) * 8) = out;
     }
     __syncthreads();
   }
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256) void k_router_xt(const uint16_t* const* x_seg,
 
 struct RouterBwdArgs {
   const uint16_t* dlt;     // [E][Np]
-  const uint16_t* xt;      // [H][Np]
+  const uint16_t* xt;      // [H][Np], fragment order
   float* dwr;              // [E][H]
   const uint16_t* dl16;    // [N][Ep]
   const uint16_t* wrt;     // [H][Ep]
