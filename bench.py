@@ -5,7 +5,9 @@ One step = mok_layer_fwd (router top-k, schedule table, pull dispatch through th
 SwiGLU expert GEMMs, weighted combine) followed by mok_layer_bwd (reverse combine, router-weight
 gradient fused into SwiGLU backward, dX, dW_gate, dW_up, dW_down) on the DeepSeek-V3-shaped
 local share: 64 source segments x 2,048 tokens, hidden 7168, 256 experts, top-8, expert
-intermediate 2048, experts 0-3 local, minibatch 2,368 rows, 256 MiB ring, BF16.
+intermediate 2048, experts 0-3 local, 256 MiB ring, BF16. The minibatch is the library's
+default, the smallest that fills two full waves of 256 x 256 tiles on every CU (8,192 rows on
+MI355X); --minibatch overrides it.
 
 Layer tokens/s = 2,048 source tokens per GPU (the unit of the "Mixture-of-Kittens (MoK)"
 benchmark section) / step time. Prints one JSON line (see the keys below).
@@ -241,9 +243,9 @@ def main() -> int:
     import combine_router_top_schedule_amd as mok
     from combine_router_top_schedule_amd.layer import MokLayer
 
-    cfg = datagen.CONFIGS[args.workload]
-    if args.minibatch:
-        cfg = cfg.replace(M=args.minibatch)
+    # minibatch: --minibatch, else 0 (the library's two-wave default; the test configs keep
+    # their own M to exercise the minibatch cut)
+    cfg = datagen.CONFIGS[args.workload].replace(M=args.minibatch)
     mx = cfg.dtype == "mxfp8"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
@@ -254,6 +256,8 @@ def main() -> int:
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     d = mok.desc_from_config(cfg)
     L = MokLayer(d, device=dev, staged=args.staged, fused=not args.staged)
+    M_used = int(L.sizes.minibatch)
+    cfg = cfg.replace(M=M_used)   # what every later descriptor and the oracle sample use
     buf = np.empty((cfg.N, cfg.H), dtype=np.uint16)
     x = up(datagen.x_all(cfg, buf))
     dout = up(datagen.dout_all(cfg, buf))
