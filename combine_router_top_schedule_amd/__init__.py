@@ -101,7 +101,8 @@ _SIGS = {
                                      ctypes.POINTER(MokWeightGrads), _P, _P]),
     "mok_quantize_mx": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
                                        ctypes.c_int32, _P, _P, _P]),
-    "mok_pack_bf16": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.POINTER(MokWeights), _P, _P]),
+    "mok_pack_weights": (ctypes.c_int, [ctypes.POINTER(MokDesc), ctypes.POINTER(MokWeights), _P,
+                                        _P]),
     "mok_device_status": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int)]),
     "mok_autotune": (ctypes.c_int, [ctypes.POINTER(MokDesc), _P, _P, ctypes.POINTER(MokWeights),
                                     _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
@@ -324,11 +325,12 @@ def mok_quantize_mx(src, transpose: bool, codes, scales, stream=None):
                                                     _ptr(codes), _ptr(scales), _stream(stream)))
 
 
-def mok_pack_bf16(d: MokDesc, w: MokWeights, packed, stream=None):
-    """Pack the BF16 weights of `w` into `packed` (sizes.packed_bytes, 256-byte aligned)."""
+def mok_pack_weights(d: MokDesc, w: MokWeights, packed, stream=None):
+    """Pack the weights of `w` (BF16 values or MXFP8 codes and scales) into `packed`
+    (sizes.packed_bytes, 256-byte aligned)."""
     _need_cuda(packed)
-    _check("mok_pack_bf16", lib().mok_pack_bf16(ctypes.byref(d), ctypes.byref(w), _ptr(packed),
-                                                _stream(stream)))
+    _check("mok_pack_weights", lib().mok_pack_weights(ctypes.byref(d), ctypes.byref(w),
+                                                      _ptr(packed), _stream(stream)))
 
 
 def mok_autotune(d: MokDesc, x_seg, logits, w: MokWeights, out_seg, topk_idx, topk_p, saved,

@@ -255,16 +255,15 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   const int ncols = min(kTileN, s.I - c0);
   Operand A = operand(make_rsrc(d + row0 * xrow, int64_t(nrows) * xrow), xrow);
   const int64_t wrow0 = int64_t(e) * s.I + c0;
-  // (MXFP8 stages B through LDS; BF16 reads the packed Wd^T plane straight into registers)
-  Operand B = operand(make_rsrc(wdt + wrow0 * xrow, int64_t(ncols) * xrow), xrow);
   if (MX) {
-    A.sstride = B.sstride = s.H / 32;
+    A.sstride = s.H / 32;
     A.s0 = A.s1 = make_rsrc(d_s + row0 * (s.H / 32), int64_t(nrows) * (s.H / 32));
-    B.s0 = B.s1 = make_rsrc(wdt_s + wrow0 * (s.H / 32), int64_t(ncols) * (s.H / 32));
   }
+  // B: the packed Wd^T plane (MXFP8: codes wdt, scales wdt_s)
   f32x16 acc[4][4];
   if constexpr (MX)
-    gemm_tile<MX>(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
+    gemm_tile_pb_mx(sm, A, packed_b_mx(wdt, wdt_s, wrow0, ncols, s.H), xrow / kStageRowBytes,
+                    acc, wm, wn, lane);
   else
     gemm_tile_pb(sm, A, packed_b(wdt, wrow0, ncols, s.H), xrow / kStageRowBytes, acc, wm, wn,
                  lane);
@@ -319,28 +318,22 @@ template <bool MX>
 __device__ __forceinline__ void dx_tile(GemmLds& sm, const FfnShape& s, int64_t row0, int nrows,
                                         int e, int c0, const uint8_t* dgu, const uint8_t* dgu_s,
                                         const uint8_t* wgt, const uint8_t* wgt_s,
-                                        const uint8_t* wut, const uint8_t* wut_s,
                                         const PushTarget& pt) {
   const int tid = tile_tid(), lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int eb = MX ? 1 : 2;
-  const int arow = 2 * s.I * eb, brow = s.I * eb;
+  const int arow = 2 * s.I * eb;
   const int ncols = min(kTileN, s.H - c0);
   Operand A = operand(make_rsrc(dgu + row0 * arow, int64_t(nrows) * arow), arow);
   const int64_t wrow0 = int64_t(e) * s.H + c0;
   f32x16 acc[4][4];
+  // B: the packed [Wg^T | Wu^T] plane (K = 2I; MXFP8: codes wgt, scales wgt_s)
   if constexpr (MX) {
-    Operand B = operand(make_rsrc(wgt + wrow0 * brow, int64_t(ncols) * brow), brow);
-    B.r1 = make_rsrc(wut + wrow0 * brow, int64_t(ncols) * brow);
-    B.ksplit = brow / kStageRowBytes;
     A.sstride = 2 * s.I / 32;
     A.s0 = A.s1 = make_rsrc(dgu_s + row0 * A.sstride, int64_t(nrows) * A.sstride);
-    B.sstride = s.I / 32;
-    B.s0 = make_rsrc(wgt_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
-    B.s1 = make_rsrc(wut_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
-    gemm_tile<MX>(sm, A, B, arow / kStageRowBytes, acc, wm, wn, lane);
+    gemm_tile_pb_mx(sm, A, packed_b_mx(wgt, wgt_s, wrow0, ncols, 2 * s.I), arow / kStageRowBytes,
+                    acc, wm, wn, lane);
   } else {
-    // BF16: wgt is the packed [Wg^T | Wu^T] plane (K = 2I; wut unused), brow = I * 2 bytes
     gemm_tile_pb(sm, A, packed_b(wgt, wrow0, ncols, 2 * s.I), arow / kStageRowBytes, acc, wm, wn,
                  lane);
   }
@@ -382,8 +375,9 @@ __device__ __forceinline__ void store_tile_f32(GemmLds& sm, const f32x16 (&acc)[
 
 // Weight-gradient tile: out[m0 + m][n0 + n] = sum over the expert's padded columns c of
 // Ta[m0 + m][c] Tb[n0 + n][c]; fp32 output [Fa][Fb] (fully overwritten). ld = row pitch of Ta
-// and Tb (elements; their MXFP8 scale rows have ld / 32 bytes). BF16: Tb is packed in fragment
-// order with ld columns (K = the padded columns), read straight into registers.
+// and Tb (elements; the MXFP8 scale rows of Ta have ld / 32 bytes). Tb is packed in fragment
+// order with ld columns (K = the padded columns; MXFP8: its scale plane at tb_s), read straight
+// into registers.
 template <bool MX>
 __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const uint8_t* ta_s,
                                            const uint8_t* tb, const uint8_t* tb_s, int64_t ld,
@@ -398,15 +392,20 @@ __device__ __forceinline__ void wgrad_tile(GemmLds& sm, const uint8_t* ta, const
   if (ncols > 0) {
     Operand A = operand(make_rsrc(ta + int64_t(m0) * stride + int64_t(c0) * eb, int64_t(ma) * stride),
                         int(stride));
-    Operand B = operand(make_rsrc(tb + int64_t(n0) * stride + int64_t(c0) * eb, int64_t(nb) * stride),
-                        int(stride));
     if (MX) {
-      A.sstride = B.sstride = int(ld / 32);
+      A.sstride = int(ld / 32);
       A.s0 = A.s1 = make_rsrc(ta_s + int64_t(m0) * (ld / 32) + c0 / 32, int64_t(ma) * (ld / 32));
-      B.s0 = B.s1 = make_rsrc(tb_s + int64_t(n0) * (ld / 32) + c0 / 32, int64_t(nb) * (ld / 32));
     }
     if constexpr (MX) {
-      gemm_tile<MX>(sm, A, B, ncols * eb / kStageRowBytes, acc, wm, wn, lane);
+      // packed codes: fragment (n32, k64) at (n32 * ld/64 + k64) * 2 KB; scales 64 bytes each
+      const int k64s = int(ld / 64);
+      const int64_t f0 = int64_t(n0 / 32) * k64s + c0 / 64;
+      const int64_t nf = int64_t(nb / 32 - 1) * k64s + ncols / 64;
+      PackedBMX P;
+      P.r = make_rsrc(tb + f0 * 2048, nf * 2048);
+      P.s = make_rsrc(tb_s + f0 * 64, nf * 64);
+      P.k64s = k64s;
+      gemm_tile_pb_mx(sm, A, P, ncols * eb / kStageRowBytes, acc, wm, wn, lane);
     } else {
       // fragment (n32, k16) of the packed plane at (n32 * ld/16 + k16) KB; the resource covers
       // the tile's nb rows over the expert's columns [c0, c0 + ncols)

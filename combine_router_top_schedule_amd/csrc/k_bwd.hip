@@ -53,7 +53,7 @@ struct TransposeArgs {
   // decoded. (The plane fields are otherwise unused.)
   int from_act;
   ActSource act;
-  // BF16: store dst in MFMA fragment order (PackedB in k_gemm.h: rows = features, K = the
+  // store in MFMA fragment order (PackedB / PackedBMX in k_gemm.h: rows = features, K = the
   // padded columns), the layout the weight-gradient GEMMs read their B operand in
   int packed;
 };
@@ -203,9 +203,21 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
         }
         uint32_t sc;
         const uint2 codes = mx_quant8_group4_f(fv, &sc);
-        *reinterpret_cast<uint2*>(a.qdst + int64_t(f0 + f) * cols + c0 + cc * 8) = codes;
-        if ((cc & 3) == 0)
-          a.qdst[int64_t(a.F) * a.ld + int64_t(f0 + f) * (cols / 32) + (c0 + cc * 8) / 32] = uint8_t(sc);
+        const int fa = f0 + f, col = c0 + cc * 8;
+        uint8_t* qs = a.qdst + int64_t(a.F) * a.ld;   // the scale plane
+        if (a.packed) {
+          // fragment (feature/32, column/64): half (column%64)/32, lane feature%32 + 32 *
+          // ((column%32)/16), byte column%16; the block's scale is byte feature%32 + 32 *
+          // ((column/32)%2) of the fragment's 64 scale bytes
+          const int64_t frag = int64_t(fa >> 5) * (cols >> 6) + (col >> 6);
+          const int q = col & 63;
+          *reinterpret_cast<uint2*>(a.qdst + (frag * 2 + (q >> 5)) * 1024 +
+                                    ((fa & 31) + 32 * ((q >> 4) & 1)) * 16 + (q & 15)) = codes;
+          if ((cc & 3) == 0) qs[frag * 64 + (fa & 31) + 32 * ((q >> 5) & 1)] = uint8_t(sc);
+        } else {
+          *reinterpret_cast<uint2*>(a.qdst + int64_t(fa) * cols + col) = codes;
+          if ((cc & 3) == 0) qs[int64_t(fa) * (cols / 32) + col / 32] = uint8_t(sc);
+        }
       } else if (a.packed) {
         // 8 columns of one feature are one lane's 16 bytes of fragment (feature/32, column/16)
         const int fa = f0 + f, col = c0 + cc * 8;
@@ -421,8 +433,8 @@ struct BwdArgs {
   // a GEMM
   const uint8_t* d;        // D rows: BF16 [rows][H] or codes
   const uint8_t* d_s;      // MXFP8 scales [rows][H/32]
-  const uint8_t* wdt;      // Wd^T: BF16 packed plane [El][I rows][H], or codes [El][I][H]
-  const uint8_t* wdt_s;
+  const uint8_t* wdt;      // packed Wd^T plane [El][I rows][H] (BF16 values or E4M3 codes)
+  const uint8_t* wdt_s;    // MXFP8: its scales
   ActSource act;           // g|u and h of the forward (ring slot or replayed plane, per row)
   uint16_t* dgu;           // out: dg|du BF16 [rows][2I] (BF16 mode)
   uint8_t* q_dgt;          // out (MXFP8): dg^T, du^T blocked along tokens, codes then scales
@@ -431,10 +443,8 @@ struct BwdArgs {
   // dx GEMM
   const uint8_t* dgu_a;    // dg|du as the dx GEMM reads it: BF16 or codes [rows][2I]
   const uint8_t* dgu_s;    // MXFP8 scales [rows][2I/32]
-  const uint8_t* wgt;      // BF16: packed [Wg^T | Wu^T] [El][H rows][2I]; MXFP8: Wg^T codes [El][H][I]
-  const uint8_t* wgt_s;
-  const uint8_t* wut;      // MXFP8: Wu^T codes [El][H][I] (BF16: unused)
-  const uint8_t* wut_s;
+  const uint8_t* wgt;      // packed [Wg^T | Wu^T] plane [El][H rows][2I]
+  const uint8_t* wgt_s;    // MXFP8: its scales
   PushTarget push;         // dx rows: pair slots, or dX of a token's only local pair
   // weight gradients: up to three jobs dW[e] = Ta[:, cols of e] . Tb[:, cols of e]^T
   WJob jobs[3];
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_gemms(BwdArgs a) {
                      const_cast<uint8_t*>(a.dgu_s), tq, a.dp_part);
         } else
           dx_tile<MX>(sm, a.s, tl.row0, tl.nrows, tl.e, nt * kTileN, a.dgu_a, a.dgu_s, a.wgt,
-                      a.wgt_s, a.wut, a.wut_s, a.push);
+                      a.wgt_s, a.push);
       } else {
         int j = 0, rem = t - n_p;
         for (; j < a.njobs; ++j) {
@@ -616,9 +626,9 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   //    (MXFP8: the gather quantises along H on the way, like the forward dispatch)
   //    (BF16: D is written by the (p D)^T gather-transpose below, which reads the same rows)
   if (mx && (err = launch_dispatch(L, b.saved, b.dout_seg, b.dq, s)) != hipSuccess) return err;
-  // 3. BF16 backward GEMMs read packed Wd^T and [Wg^T | Wu^T] (b.w.packed: the caller's, or
+  // 3. the backward GEMMs read packed Wd^T and [Wg^T | Wu^T] (b.w.packed: the caller's, or
   //    packed by the host entry point into the workspace)
-  const PackOffsets po = pack_offsets(El, H, I);
+  const PackOffsets po = pack_offsets(El, H, I, L.dtype);
   const uint8_t* packed = static_cast<const uint8_t*>(b.w.packed);
   // 4. weight-gradient operand planes that do not need dg|du: per-expert column ranges, X^T,
   //    (p D)^T and h^T (MXFP8: quantised along tokens as they are written)
@@ -639,10 +649,10 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
                 int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst,
                 uint16_t* rows_out = nullptr, bool from_act = false, bool packed = false) {
     TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
-                    ld, F, L.K, L.T, El, rows_out, int(from_act), asrc, int(packed && !mx)};
+                    ld, F, L.K, L.T, El, rows_out, int(from_act), asrc, int(packed)};
     hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
   };
-  // (X^T and h^T are the B operands of the weight-gradient GEMMs: BF16 stores them packed)
+  // (X^T and h^T are the B operands of the weight-gradient GEMMs: stored packed)
   tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt, nullptr, false, true);   // X^T
   tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt,
      mx ? nullptr : reinterpret_cast<uint16_t*>(b.d));                              // (p D)^T (+ D)
@@ -662,17 +672,15 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   a.s = FfnShape{H, I};
   a.d = mx ? b.dq : b.d;
   a.d_s = mx ? b.dq + L.rows_max * H : nullptr;
-  a.wdt = mx ? b.w.wdt_q : packed + po.wdt;
-  a.wdt_s = mx ? b.w.wdt_s : nullptr;
+  a.wdt = packed + po.wdt;
+  a.wdt_s = mx ? packed + po.wdt_s : nullptr;
   a.act = asrc;
   a.dgu = b.dgu;
   a.dp_part = b.dp_part;
   a.dgu_a = mx ? b.dguq : reinterpret_cast<const uint8_t*>(b.dgu);
   a.dgu_s = mx ? b.dguq + L.rows_max * 2 * I : nullptr;
-  a.wgt = mx ? b.w.wgt_q : packed + po.dx;
-  a.wgt_s = mx ? b.w.wgt_s : nullptr;
-  a.wut = mx ? b.w.wut_q : nullptr;
-  a.wut_s = mx ? b.w.wut_s : nullptr;
+  a.wgt = packed + po.dx;
+  a.wgt_s = mx ? packed + po.dx_s : nullptr;
   a.push = PushTarget{b.slots, b.push};
   a.ld = ld;
   a.El = El;

@@ -7,29 +7,20 @@
 
 namespace mok {
 
+// Packed expert weights (pack_offsets): BF16 values, or MXFP8 codes with their scale planes.
 struct FfnWeights {
-  const uint8_t* wg;    // E4M3 codes [El][I][H] (MXFP8)
-  const uint8_t* wu;
-  const uint8_t* wd;    // codes [El][H][I]
-  const uint8_t* wg_s;  // MXFP8 scales [El][I][H/32]
-  const uint8_t* wu_s;
-  const uint8_t* wd_s;  // [El][H][I/32]
-  const uint8_t* pgu;   // BF16: packed gate/up plane (pack_offsets: gu)
-  const uint8_t* pwd;   // BF16: packed Wd plane (pack_offsets: wd)
+  const uint8_t* pgu;     // gate/up plane
+  const uint8_t* pgu_s;   // MXFP8: its scales
+  const uint8_t* pwd;     // Wd plane
+  const uint8_t* pwd_s;   // MXFP8: its scales
 };
 
-// The FFN weights of a call: MXFP8 codes and scales, or the BF16 packed planes at w.packed.
+// The FFN weights of a call: the packed planes at w.packed.
 inline FfnWeights ffn_weights(const Layout& L, const mok_weights& w) {
-  FfnWeights f{};
-  if (L.dtype == MOK_MXFP8) {
-    f = FfnWeights{w.wg_q, w.wu_q, w.wd_q, w.wg_s, w.wu_s, w.wd_s, nullptr, nullptr};
-  } else {
-    const PackOffsets po = pack_offsets(L.El, L.H, L.I);
-    const uint8_t* pk = static_cast<const uint8_t*>(w.packed);
-    f.pgu = pk + po.gu;
-    f.pwd = pk + po.wd;
-  }
-  return f;
+  const PackOffsets po = pack_offsets(L.El, L.H, L.I, L.dtype);
+  const uint8_t* pk = static_cast<const uint8_t*>(w.packed);
+  const bool mx = L.dtype == MOK_MXFP8;
+  return FfnWeights{pk + po.gu, mx ? pk + po.gu_s : nullptr, pk + po.wd, mx ? pk + po.wd_s : nullptr};
 }
 
 struct FfnShape {
@@ -134,23 +125,16 @@ __device__ __forceinline__ bool gateup_tile(GemmLds& sm, const FfnShape& s, cons
   A.sstride = s.H / 32;
   A.r0 = A.r1 = make_rsrc(pl.x + prow0 * xrow, int64_t(nrows) * xrow);
   f32x16 acc[4][4];
+  // the packed gate/up plane holds the tile's 256 B rows in this order, from row 2 i0 of the
+  // expert's 2I rows
+  const int64_t brow0 = int64_t(e) * 2 * s.I + 2 * int64_t(i0);
   if constexpr (MX) {
-    Operand B;
-    B.ksplit = 0x7FFFFFFF;
-    B.interleave = 1;
-    B.stride = xrow;
-    B.sstride = s.H / 32;
-    const int64_t wrow0 = int64_t(e) * s.I + i0;
-    B.r0 = make_rsrc(w.wg + wrow0 * xrow, int64_t(128) * xrow);
-    B.r1 = make_rsrc(w.wu + wrow0 * xrow, int64_t(128) * xrow);
     A.s0 = A.s1 = make_rsrc(pl.xs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
-    B.s0 = make_rsrc(w.wg_s + wrow0 * B.sstride, int64_t(128) * B.sstride);
-    B.s1 = make_rsrc(w.wu_s + wrow0 * B.sstride, int64_t(128) * B.sstride);
-    gemm_tile<MX>(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
+    gemm_tile_pb_mx(sm, A, packed_b_mx(w.pgu, w.pgu_s, brow0, kTileN, s.H),
+                    xrow / kStageRowBytes, acc, wm, wn, lane);
   } else {
-    // the packed gate/up plane holds the tile's 256 B rows in this order, from row 2 i0
-    const PackedB B = packed_b(w.pgu + int64_t(e) * 2 * s.I * xrow, 2 * int64_t(i0), kTileN, s.H);
-    gemm_tile_pb(sm, A, B, xrow / kStageRowBytes, acc, wm, wn, lane);
+    gemm_tile_pb(sm, A, packed_b(w.pgu, brow0, kTileN, s.H), xrow / kStageRowBytes, acc, wm, wn,
+                 lane);
   }
 
   // SwiGLU epilogue. Column blocks (jg, jg+2) = (g, u) of h-column i0 + wn*64 + jg*32 + lane%32.
@@ -332,11 +316,9 @@ __device__ __forceinline__ void down_tile(GemmLds& sm, const FfnShape& s, const 
   const int32_t my_pair = MODE == kPushSlots && tid < nrows ? perm[row0 + tid] : 0;
   f32x16 acc[4][4];
   if constexpr (MX) {
-    Operand B = operand(make_rsrc(w.wd + wrow0 * hrow, int64_t(ncols) * hrow), hrow);
-    B.sstride = s.I / 32;
     A.s0 = A.s1 = make_rsrc(pl.hs + prow0 * A.sstride, int64_t(nrows) * A.sstride);
-    B.s0 = B.s1 = make_rsrc(w.wd_s + wrow0 * B.sstride, int64_t(ncols) * B.sstride);
-    gemm_tile<MX>(sm, A, B, hrow / kStageRowBytes, acc, wm, wn, lane);
+    gemm_tile_pb_mx(sm, A, packed_b_mx(w.pwd, w.pwd_s, wrow0, ncols, s.I), hrow / kStageRowBytes,
+                    acc, wm, wn, lane);
   } else {
     gemm_tile_pb(sm, A, packed_b(w.pwd, wrow0, ncols, s.I), hrow / kStageRowBytes, acc, wm, wn,
                  lane);

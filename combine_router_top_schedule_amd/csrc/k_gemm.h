@@ -396,6 +396,129 @@ __device__ __forceinline__ void gemm_tile_pb(GemmLds& sm, const Operand& A, cons
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+// ---- B operand in fragment order (MXFP8) ----------------------------------------------------
+// E4M3 codes of a packed matrix with R rows and reduction length K (a multiple of 64): R/32 x
+// K/64 fragments of 2 KB, fragment (n32, k64) at byte (n32 * K/64 + k64) * 2048, made of two
+// 1 KB halves: half 0 holds in lane l's 16 bytes the codes 64 k64 + 16 (l / 32) .. +15 of row
+// 32 n32 + l % 32, half 1 the codes 32 further -- together the lane's 32-byte operand of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (see load_frag). The UE8M0 scales follow the same blocks:
+// 64 bytes per fragment, byte l the scale of that row's 32-code block 2 k64 + l / 32, which is
+// the scale operand of lane l. The first r rows take the first r K code bytes and r K / 32 scale
+// bytes, as in a row-major matrix.
+struct PackedBMX {
+  __amdgpu_buffer_rsrc_t r;   // codes, from the tile's first fragment
+  __amdgpu_buffer_rsrc_t s;   // scales, from the tile's first fragment
+  int k64s;                   // K / 64: fragments per 32-row block
+};
+
+__device__ __forceinline__ PackedBMX packed_b_mx(const uint8_t* codes, const uint8_t* scales,
+                                                 int64_t row0, int nrows, int K) {
+  PackedBMX p;
+  p.r = make_rsrc(codes + row0 * K, int64_t(nrows) * K);
+  p.s = make_rsrc(scales + row0 * (K / 32), int64_t(nrows) * (K / 32));
+  p.k64s = K / 64;
+  return p;
+}
+
+// Slice kk of stage kt (64 codes per row): the wave's 4 B fragments and their scale bytes.
+__device__ __forceinline__ void load_b_packed_mx(i32x8 (&b)[4], int (&sb)[4], const PackedBMX& B,
+                                                 int kt, int kk, int wn, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = (wn * 4 + j) * B.k64s + kt * 2 + kk;
+    const u32x4 lo = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(B.r, f * 2048 + lane * 16, 0, 0));
+    const u32x4 hi = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(B.r, f * 2048 + 1024 + lane * 16, 0, 0));
+    b[j] = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                 int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+    sb[j] = int(__builtin_amdgcn_raw_buffer_load_b8(B.s, f * 64 + lane, 0, 0));
+  }
+}
+
+// A fragments of E4M3 slice kk from the LDS stage (as load_frag) and their scale bytes.
+__device__ __forceinline__ void load_a_frag_mx(i32x8 (&a)[4], int (&sa)[4], const uint8_t* A,
+                                               const uint32_t* As, int kk, int wm, int lane) {
+  const int h = lane >> 5;
+  const int blk = kk * 2 + h;
+  const int ch0 = kk * 4 + h, ch1 = kk * 4 + 2 + h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + (lane & 31);
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch0));
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(A + swz(ra, ch1));
+    a[i] = i32x8{int(a0[0]), int(a0[1]), int(a0[2]), int(a0[3]),
+                 int(a1[0]), int(a1[1]), int(a1[2]), int(a1[3])};
+    sa[i] = int((As[ra] >> (8 * blk)) & 0xFFu);
+  }
+}
+
+// The K loop of one MXFP8 output tile with a packed B operand: gemm_tile_pb's schedule with two
+// E4M3 slices per stage. A codes and scales go through LDS by DMA (9 loads per wave per stage);
+// B codes and scale bytes go straight into registers, one stage ahead (12 loads per slice).
+// The stage barrier waits for the A stage only: the 12 loads of B(kt+1) slice 0 stay in
+// flight. Bit-identical to gemm_tile<true>.
+__device__ __forceinline__ void gemm_tile_pb_mx(GemmLds& sm, const Operand& A, const PackedBMX& B,
+                                                int ksteps, f32x16 (&acc)[4][4], int wm, int wn,
+                                                int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (ksteps <= 0) return;
+  const int w = wave_id();
+  const int last = ksteps - 1;
+  i32x8 b[2][4];   // [slice][column block]
+  int sb[2][4];
+  i32x8 fa[2][4];
+  int sa[2][4];
+  issue_stage<kLoadAgent>(A, sm.a[0], sm.as[0], 0, true, w);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) load_b_packed_mx(b[kk], sb[kk], B, 0, kk, wn, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  load_a_frag_mx(fa[0], sa[0], sm.a[0], sm.as[0], 0, wm, lane);
+  for (int kt = 0; kt < ksteps; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt < last;
+    if (more) issue_stage<kLoadAgent>(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, true, w);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) {
+        load_a_frag_mx(fa[1], sa[1], sm.a[cur], sm.as[cur], 1, wm, lane);
+      } else {
+        // vmcnt(12): the loads issued after A(kt+1) are the 12 of B(kt+1) slice 0
+        __builtin_amdgcn_s_waitcnt(0x0F7C);
+        __syncthreads();
+        if (more) load_a_frag_mx(fa[0], sa[0], sm.a[cur ^ 1], sm.as[cur ^ 1], 0, wm, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[kk][i], b[kk][j], acc[i][j], 0, 0, 0, sa[kk][i], 0, sb[kk][j]);
+      // (in the last stage a harmless reload of the same slice, so the wait count holds)
+      load_b_packed_mx(b[kk], sb[kk], B, more ? kt + 1 : kt, kk, wn, lane);
+#pragma unroll
+      for (int q = 0; q < 12; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);   // global loads
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 // ---- tile scheduling ------------------------------------------------------------------------
 // Logical workgroup id that gives the workgroups resident on one XCD (blockIdx % 8 on MI355X)
 // consecutive ids, so consecutive tiles -- which share operands -- land in one L2.

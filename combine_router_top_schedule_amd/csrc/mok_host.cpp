@@ -50,10 +50,10 @@ mok_status check_desc(const mok_desc* d) {
 }
 
 mok_status check_weights(const mok_desc* d, const mok_weights* w, bool backward) {
+  if (w->packed && (reinterpret_cast<uintptr_t>(w->packed) & 255u)) return MOK_ERR_ALIGN;
   if (d->dtype == MOK_BF16) {
     if (!w->wg || !w->wu || !w->wd) return MOK_ERR_NULL;
     if (!aligned16(w->wg) || !aligned16(w->wu) || !aligned16(w->wd)) return MOK_ERR_ALIGN;
-    if (w->packed && (reinterpret_cast<uintptr_t>(w->packed) & 255u)) return MOK_ERR_ALIGN;
   } else {
     if (!w->wg_q || !w->wg_s || !w->wu_q || !w->wu_s || !w->wd_q || !w->wd_s) return MOK_ERR_DTYPE;
     if (!aligned16(w->wg_q) || !aligned16(w->wu_q) || !aligned16(w->wd_q)) return MOK_ERR_ALIGN;
@@ -73,14 +73,14 @@ Layout layout_of(const mok_desc& d) {
 
 mok_status hip_status(hipError_t e) { return e == hipSuccess ? MOK_OK : MOK_ERR_HIP; }
 
-// The weights as the kernels read them: BF16 with packed planes, the caller's (w.packed) or the
-// `planes` packed here by one launch into the workspace.
+// The weights as the kernels read them, with packed planes: the caller's (w.packed) or the
+// `planes` packed here into the workspace.
 mok_status with_packed(const Layout& L, const mok_weights& w, uint8_t* ws, int planes,
                        hipStream_t s, mok_weights* out) {
   *out = w;
-  if (L.dtype != MOK_BF16 || w.packed) return MOK_OK;
+  if (w.packed) return MOK_OK;
   uint8_t* dst = ws + L.ws_pack;
-  const hipError_t e = launch_pack_bf16(L, w.wg, w.wu, w.wd, dst, planes, s);
+  const hipError_t e = launch_pack_weights(L, w, dst, planes, s);
   if (e != hipSuccess) return MOK_ERR_HIP;
   out->packed = dst;
   return MOK_OK;
@@ -154,7 +154,7 @@ mok_status mok_query_sizes(const mok_desc* desc, mok_sizes* sizes) {
   sizes->trace_offset = L.trace_max > 0 ? L.ws_trace : 0;
   sizes->trace_records = L.trace_max;
   sizes->h_slot_bytes = L.hsb;
-  sizes->packed_bytes = L.dtype == MOK_BF16 ? pack_offsets(L.El, L.H, L.I).bytes : 0;
+  sizes->packed_bytes = pack_offsets(L.El, L.H, L.I, L.dtype).bytes;
   return MOK_OK;
 }
 
@@ -252,20 +252,19 @@ mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void
                                        transpose, codes_dev, scales_dev, as_stream(stream)));
 }
 
-mok_status mok_pack_bf16(const mok_desc* desc, const mok_weights* w, void* packed_dev,
-                         void* stream) {
+mok_status mok_pack_weights(const mok_desc* desc, const mok_weights* w, void* packed_dev,
+                            void* stream) {
   mok_status st = check_desc(desc);
   if (st != MOK_OK) return st;
   if (!w || !packed_dev) return MOK_ERR_NULL;
-  if (desc->dtype != MOK_BF16) return MOK_ERR_DTYPE;
   mok_weights src = *w;
   src.packed = nullptr;
-  st = check_weights(desc, &src, false);
+  st = check_weights(desc, &src, desc->dtype == MOK_MXFP8);
   if (st != MOK_OK) return st;
   if (reinterpret_cast<uintptr_t>(packed_dev) & 255u) return MOK_ERR_ALIGN;
   const Layout L = layout_of(*desc);
-  return hip_status(launch_pack_bf16(L, w->wg, w->wu, w->wd, static_cast<uint8_t*>(packed_dev),
-                                     kPackAll, as_stream(stream)));
+  return hip_status(launch_pack_weights(L, src, static_cast<uint8_t*>(packed_dev), kPackAll,
+                                        as_stream(stream)));
 }
 
 mok_status mok_device_status(const void* ws_dev, void* stream, mok_status* out) {

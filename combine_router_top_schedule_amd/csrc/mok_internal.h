@@ -93,9 +93,11 @@ enum Bwd2Header : int {
 // gradient GEMM reduces in whole K-stages (64 BF16 or 128 E4M3 rows) with zero padding.
 constexpr int kPadRows = 128;
 
-// Packed BF16 weights: the B operands of the expert GEMMs in fragment order (PackedB in
+// Packed weights: the B operands of the expert GEMMs in fragment order (PackedB, PackedBMX in
 // k_gemm.h), four planes per set of local experts. Made once per weight update with
-// mok_pack_bf16, or by each call into its workspace.
+// mok_pack_weights, or by each call into its workspace. BF16 planes hold 2-byte values; MXFP8
+// planes hold E4M3 codes, with their scale planes (one byte per 32 codes) after the four code
+// planes.
 struct PackOffsets {
   int64_t gu;     // [El][2I rows][H]: Wg and Wu rows in the gate/up tiles' order (64-row blocks
                   // alternate Wg and Wu: packed row n is row (n/128)*64 + n%64 of Wg when
@@ -103,11 +105,16 @@ struct PackOffsets {
   int64_t wd;     // [El][H rows][I]: Wd (the down GEMM)
   int64_t wdt;    // [El][I rows][H]: Wd^T (the a GEMM)
   int64_t dx;     // [El][H rows][2I]: Wg^T then Wu^T along K (the dx GEMM)
+  int64_t gu_s, wd_s, wdt_s, dx_s;   // MXFP8 scale planes (0 in BF16)
   int64_t bytes;
 };
-inline PackOffsets pack_offsets(int El, int H, int I) {
-  const int64_t m = int64_t(El) * H * I * 2;
-  return PackOffsets{0, 2 * m, 3 * m, 4 * m, 6 * m};
+inline PackOffsets pack_offsets(int El, int H, int I, int dtype) {
+  const int64_t m = int64_t(El) * H * I;   // elements of one H x I matrix per expert set
+  if (dtype == MOK_BF16) return PackOffsets{0, 4 * m, 6 * m, 8 * m, 0, 0, 0, 0, 12 * m};
+  const int64_t s0 = (6 * m + 255) / 256 * 256;
+  return PackOffsets{0,      2 * m,           3 * m,           4 * m,
+                     s0,     s0 + 2 * m / 32, s0 + 3 * m / 32, s0 + 4 * m / 32,
+                     s0 + 6 * m / 32};
 }
 constexpr int kPackGu = 1, kPackWd = 2, kPackWdt = 4, kPackDx = 8, kPackAll = 15;
 
@@ -192,10 +199,10 @@ inline Layout make_layout(const mok_desc& d) {
   L.topk_blocks = int(cdiv(L.N, kTopkTokensPerBlock));
   off = 256;
   L.ws_state = off; off = align_up(off + 4 * int64_t(L.topk_blocks) * (L.El + 2), 256);
-  // BF16 weights packed by the call itself when the caller gives none (after the router's
-  // words, so its offset does not depend on the minibatch size)
+  // weights packed by the call itself when the caller gives none (after the router's words, so
+  // its offset does not depend on the minibatch size)
   L.ws_pack = off;
-  off = align_up(off + (L.dtype == MOK_BF16 ? pack_offsets(L.El, L.H, L.I).bytes : 0), 256);
+  off = align_up(off + pack_offsets(L.El, L.H, L.I, L.dtype).bytes, 256);
   L.ws_tiles = off; off = align_up(off + 16 * L.tiles_max, 256);
   L.ws_counters = off; off = align_up(off + 4 * (64 + (3 + kXcds) * L.tiles_max), 256);
   L.ws_dp = off; off = align_up(off + 4 * L.rows_max * (L.I / kTileN), 256);
@@ -372,10 +379,12 @@ struct BwdBuffers {
   PushRec* push;      // [rows_max] dx GEMM push records
 };
 hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s);
-// Packed BF16 weights (k_pack.hip): writes the planes selected by `planes` (kPack* bits) of
-// pack_offsets(El, H, I) at dst from the row-major weights wg, wu [El][I][H], wd [El][H][I].
-hipError_t launch_pack_bf16(const Layout& L, const void* wg, const void* wu, const void* wd,
-                            uint8_t* dst, int planes, hipStream_t s);
+// Packed weights (k_pack.hip): writes the planes selected by `planes` (kPack* bits) of
+// pack_offsets(El, H, I, dtype) at dst: BF16 from the row-major weights wg, wu [El][I][H], wd
+// [El][H][I]; MXFP8 from the quantised codes and scales of mok_weights (forward and transposed
+// blockings).
+hipError_t launch_pack_weights(const Layout& L, const mok_weights& w, uint8_t* dst, int planes,
+                               hipStream_t s);
 
 // Fused forward (k_fused.hip): the ring is split into one share per XCD, each cut into tile
 // slots of 256 expert-ordered rows (X | g,u | h).

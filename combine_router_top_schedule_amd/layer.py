@@ -7,7 +7,7 @@ from typing import Optional
 import torch
 
 from . import (MOK_MXFP8, desc, mok_autotune, mok_combine, mok_dispatch, mok_expert_ffn,
-               mok_layer_bwd, mok_layer_fwd, mok_pack_bf16, mok_quantize_mx, mok_schedule,
+               mok_layer_bwd, mok_layer_fwd, mok_pack_weights, mok_quantize_mx, mok_schedule,
                query_sizes, seg_table, weights_struct)
 
 
@@ -44,39 +44,38 @@ class MokLayer:
     # ---- weights ---------------------------------------------------------------------------
     def set_weights(self, wg, wu, wd, packed: bool = True):
         """BF16 masters. In MXFP8 mode they are quantised here (forward blocking along each
-        GEMM's reduction axis, and the transposed backward blocking). In BF16 mode, with
-        `packed`, the GEMMs' packed weight planes are made here once (else every call packs
-        them into its workspace)."""
+        GEMM's reduction axis, and the transposed backward blocking). With `packed`, the GEMMs'
+        packed weight planes are made here once (else every call packs them into its
+        workspace)."""
         d = self.d
         self._keep = [wg, wu, wd]
         E, I, H = d.num_local_experts, d.intermediate, d.hidden
         dev = self.device
         if not self.mx:
             self.w = weights_struct(wg, wu, wd)
-            if packed:
-                buf = _bytes(query_sizes(d).packed_bytes, dev)
-                mok_pack_bf16(d, self.w, buf)
-                self._keep.append(buf)
-                self.w.packed = buf.data_ptr()
-            return
+        else:
+            def q(src, rows, cols, transpose):
+                orow, ocol = (cols, rows) if transpose else (rows, cols)
+                c = torch.empty((E, orow, ocol), dtype=torch.uint8, device=dev)
+                s = torch.empty((E, orow, ocol // 32), dtype=torch.uint8, device=dev)
+                mok_quantize_mx(src, transpose, c, s)
+                self._keep += [c, s]
+                return c, s
 
-        def q(src, rows, cols, transpose):
-            orow, ocol = (cols, rows) if transpose else (rows, cols)
-            c = torch.empty((E, orow, ocol), dtype=torch.uint8, device=dev)
-            s = torch.empty((E, orow, ocol // 32), dtype=torch.uint8, device=dev)
-            mok_quantize_mx(src, transpose, c, s)
-            self._keep += [c, s]
-            return c, s
-
-        wg_q, wg_s = q(wg, I, H, False)
-        wu_q, wu_s = q(wu, I, H, False)
-        wd_q, wd_s = q(wd, H, I, False)
-        wgt_q, wgt_s = q(wg, I, H, True)
-        wut_q, wut_s = q(wu, I, H, True)
-        wdt_q, wdt_s = q(wd, H, I, True)
-        self.w = weights_struct(wg, wu, wd, wg_q=wg_q, wg_s=wg_s, wu_q=wu_q, wu_s=wu_s,
-                                wd_q=wd_q, wd_s=wd_s, wgt_q=wgt_q, wgt_s=wgt_s, wut_q=wut_q,
-                                wut_s=wut_s, wdt_q=wdt_q, wdt_s=wdt_s)
+            wg_q, wg_s = q(wg, I, H, False)
+            wu_q, wu_s = q(wu, I, H, False)
+            wd_q, wd_s = q(wd, H, I, False)
+            wgt_q, wgt_s = q(wg, I, H, True)
+            wut_q, wut_s = q(wu, I, H, True)
+            wdt_q, wdt_s = q(wd, H, I, True)
+            self.w = weights_struct(wg, wu, wd, wg_q=wg_q, wg_s=wg_s, wu_q=wu_q, wu_s=wu_s,
+                                    wd_q=wd_q, wd_s=wd_s, wgt_q=wgt_q, wgt_s=wgt_s, wut_q=wut_q,
+                                    wut_s=wut_s, wdt_q=wdt_q, wdt_s=wdt_s)
+        if packed:
+            buf = _bytes(query_sizes(d).packed_bytes, dev)
+            mok_pack_weights(d, self.w, buf)
+            self._keep.append(buf)
+            self.w.packed = buf.data_ptr()
 
     # ---- segment pointer tables ---------------------------------------------------------------
     def segs(self, rows):

@@ -114,9 +114,8 @@ typedef struct {
 typedef struct {
   size_t saved_bytes;    /* schedule table; written by mok_schedule / mok_layer_fwd, read by
                             every later stage and by mok_layer_bwd                          */
-  size_t ws_bytes;       /* scratch of one call (counters, error word, tile tables, ...;
-                            BF16: also room to pack the weights when mok_weights.packed is
-                            NULL)                                                            */
+  size_t ws_bytes;       /* scratch of one call (counters, error word, tile tables, ...,
+                            and room to pack the weights when mok_weights.packed is NULL)   */
   size_t bwd_ws_bytes;   /* scratch of mok_layer_bwd (>= ws_bytes): replayed activations,
                             gathered dOut, dg|du, transposed weight-gradient operands        */
   size_t slots_bytes;    /* push/receive buffer Z: N*K rows of H BF16, indexed by pair id   */
@@ -149,12 +148,12 @@ typedef struct {
   int64_t trace_records;  /* capacity in records (0 without MOK_FLAG_TRACE)                 */
   int64_t h_slot_bytes;   /* bytes of one h slot of the ring (h of 256 rows: BF16, or MXFP8
                              codes and scales along I)                                      */
-  int64_t packed_bytes;   /* BF16: size of the packed weights mok_pack_bf16 writes (6 E_loc H I
-                             * 2 bytes; 0 in MXFP8 mode)                                     */
+  int64_t packed_bytes;   /* size of the packed weights mok_pack_weights writes (BF16: 12 E_loc
+                             H I bytes; MXFP8: 6 E_loc H I code bytes, then 6 E_loc H I / 32
+                             scale bytes)                                                   */
 } mok_sizes;
 
-/* Expert weights (device pointers). BF16 mode uses wg/wu/wd and, optionally, packed. MXFP8
- * mode uses E4M3 codes
+/* Expert weights (device pointers). BF16 mode uses wg/wu/wd; MXFP8 mode uses E4M3 codes
  * with UE8M0 scales per 32 elements along each GEMM's reduction axis, produced by
  * mok_quantize_mx:
  *   forward : wg_q/wg_s, wu_q/wu_s = Wg, Wu [E_loc][I][H] blocked along H;
@@ -168,9 +167,10 @@ typedef struct {
   const void* wd;
   const uint8_t *wg_q, *wg_s, *wu_q, *wu_s, *wd_q, *wd_s;
   const uint8_t *wgt_q, *wgt_s, *wut_q, *wut_s, *wdt_q, *wdt_s;
-  /* BF16, optional: the weights packed by mok_pack_bf16 (packed_bytes, 256-byte aligned),
-   * made once per weight update. Every BF16 expert GEMM reads its weight operand from these
-   * planes; when NULL, each call packs wg/wu/wd into its own workspace first (1 launch). */
+  /* Optional: the weights packed by mok_pack_weights (packed_bytes, 256-byte aligned), made
+   * once per weight update. Every expert GEMM reads its weight operand from these planes; when
+   * NULL, each call first packs the planes it needs from the fields above into its own
+   * workspace (one launch per plane). */
   const void* packed;
 } mok_weights;
 
@@ -361,18 +361,21 @@ mok_status mok_quantize_mx(int32_t batch, int32_t rows, int32_t cols, const void
                            int32_t transpose, uint8_t* codes_dev, uint8_t* scales_dev,
                            void* stream);
 
-/* BF16 weight packing, once per weight update: writes the weight operands of the four BF16
- * expert GEMMs into `packed_dev` (mok_sizes.packed_bytes, 256-byte aligned) in the order the
- * MFMA matrix cores read them, so that each GEMM loads its weight fragments with whole 1 KB
- * reads straight into registers instead of staging them through LDS. Four planes per set of
- * local experts: Wg and Wu interleaved for the gate/up GEMM, Wd for the down GEMM, Wd^T for
- * the a GEMM and [Wg^T | Wu^T] for the dx GEMM. Inside a plane of R rows and reduction length
- * K, 1 KB block (n32, k16) at offset (n32 K/16 + k16) KB holds in its 16-byte lane l the
- * elements 16 k16 + 8 (l/32) .. +7 of row 32 n32 + l%32. The layout is the library's own;
- * callers only pass the buffer back in mok_weights.packed. Needs wg, wu, wd of `w` (BF16
- * descriptor). Stream-ordered, no host sync. */
-mok_status mok_pack_bf16(const mok_desc* desc, const mok_weights* w, void* packed_dev,
-                         void* stream);
+/* Weight packing, once per weight update: writes the weight operands of the four expert GEMMs
+ * into `packed_dev` (mok_sizes.packed_bytes, 256-byte aligned) in the order the MFMA matrix
+ * cores read them, so that each GEMM loads its weight fragments with whole 1 KB reads straight
+ * into registers instead of staging them through LDS. Four planes per set of local experts: Wg
+ * and Wu interleaved for the gate/up GEMM, Wd for the down GEMM, Wd^T for the a GEMM and
+ * [Wg^T | Wu^T] for the dx GEMM. BF16 (from wg, wu, wd): in a plane of R rows and reduction
+ * length K, 1 KB block (n32, k16) at offset (n32 K/16 + k16) KB holds in its 16-byte lane l the
+ * elements 16 k16 + 8 (l/32) .. +7 of row 32 n32 + l%32. MXFP8 (from the codes and scales of
+ * both blockings): 2 KB block (n32, k64) holds in lane l of its first 1 KB the codes 64 k64 +
+ * 16 (l/32) .. +15 of row 32 n32 + l%32 and in its second 1 KB the 16 codes 32 further; the
+ * scale planes follow the code planes with 64 bytes per block, byte l the scale of that row's
+ * code block 2 k64 + l/32. The layout is the library's own; callers only pass the buffer back
+ * in mok_weights.packed. Stream-ordered, no host sync. */
+mok_status mok_pack_weights(const mok_desc* desc, const mok_weights* w, void* packed_dev,
+                            void* stream);
 
 /* One measured configuration of mok_autotune. */
 typedef struct {

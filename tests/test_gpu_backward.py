@@ -229,9 +229,9 @@ def test_backward_after_timed_out_forward_replays_every_row():
 
 
 def _packed_reference(wg, wu, wd):
-    """The packed planes as the C header states them, built by rearranging the weights in torch:
-    in a plane of R rows and reduction length K, the 1 KB block (n32, k16) holds in lane l the
-    elements 16 k16 + 8 (l // 32) .. +7 of row 32 n32 + l % 32; planes in the order gate/up
+    """The BF16 packed planes as the C header states them, built by rearranging the weights in
+    torch: in a plane of R rows and reduction length K, the 1 KB block (n32, k16) holds in lane l
+    the elements 16 k16 + 8 (l // 32) .. +7 of row 32 n32 + l % 32; planes in the order gate/up
     (64-row blocks alternating Wg and Wu), Wd, Wd^T, [Wg^T | Wu^T]."""
     E, I, H = wg.shape
 
@@ -246,21 +246,67 @@ def _packed_reference(wg, wu, wd):
                       plane(dx)])
 
 
-def test_packed_weights_match_the_stated_layout_and_per_call_packing():
-    """BF16: the planes mok_pack_bf16 writes (the layer's default) are exactly the layout the C
-    header states, element for element; and fused and staged forward + backward reading them
-    give bit for bit the outputs of calls that pack into their own workspace each time. I = 384
-    leaves a half column tile (128 rows of the packed Wd^T plane) at each expert's end."""
+def _packed_reference_mx(wg, wu, wd):
+    """The MXFP8 packed planes as the C header states them, from mok_quantize_mx's codes and
+    scales in both blockings: 2 KB block (n32, k64) holds in lane l of its first 1 KB the codes
+    64 k64 + 16 (l // 32) .. +15 of row 32 n32 + l % 32 and in its second 1 KB the 16 codes 32
+    further; then the scale planes, 64 bytes per block, byte l the scale of row 32 n32 + l % 32,
+    block 2 k64 + l // 32. Code planes first (aligned to 256 bytes), then the scale planes."""
+    E, I, H = wg.shape
+
+    def quant(src, transpose):
+        b, r, c = src.shape
+        orow, ocol = (c, r) if transpose else (r, c)
+        q = torch.empty((b, orow, ocol), dtype=torch.uint8, device=src.device)
+        sc = torch.empty((b, orow, ocol // 32), dtype=torch.uint8, device=src.device)
+        mok.mok_quantize_mx(src, transpose, q, sc)
+        return q, sc
+
+    (gq, gs), (uq, us), (dq, ds) = quant(wg, False), quant(wu, False), quant(wd, False)
+    (gtq, gts), (utq, uts), (dtq, dts) = quant(wg, True), quant(wu, True), quant(wd, True)
+
+    def codes(W):
+        e, R, K = W.shape
+        t = W.reshape(e, R // 32, 32, K // 64, 2, 2, 16).permute(0, 1, 3, 4, 5, 2, 6)
+        return t.contiguous().reshape(-1)
+
+    def scales(S):
+        e, R, KB = S.shape
+        t = S.reshape(e, R // 32, 32, KB // 2, 2).permute(0, 1, 3, 4, 2)
+        return t.contiguous().reshape(-1)
+
+    def inter(a, b, w):
+        return torch.stack([a.reshape(E, I // 64, 64, w), b.reshape(E, I // 64, 64, w)],
+                           dim=2).reshape(E, 2 * I, w)
+
+    c = torch.cat([codes(inter(gq, uq, H)), codes(dq), codes(dtq), codes(torch.cat([gtq, utq], 2))])
+    pad = torch.zeros((-c.numel()) % 256, dtype=torch.uint8, device=c.device)
+    sc = torch.cat([scales(inter(gs, us, H // 32)), scales(ds), scales(dts),
+                    scales(torch.cat([gts, uts], 2))])
+    return torch.cat([c, pad, sc])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+def test_packed_weights_match_the_stated_layout_and_per_call_packing(dtype):
+    """The planes mok_pack_weights writes (the layer's default) are exactly the layout the C
+    header states, byte for byte; and fused and staged forward + backward reading them give bit
+    for bit the outputs of calls that pack into their own workspace each time. I = 384 leaves a
+    half column tile (128 rows of the packed Wd^T plane) at each expert's end."""
     cfg = datagen.CONFIGS["tiny"].replace(S=3, T=512, H=1024, E=16, K=4, I=384, e0=4, E_loc=4,
-                                          x_std=1.0)
+                                          M=64, x_std=1.0, dtype=dtype)
     ring = 4 * mok.query_sizes(mok.desc_from_config(cfg)).ring_min_bytes
     case = BwdCase(cfg, fused=True, ring_bytes=ring)
     assert case.layer.w.packed
     n = case.layer.sizes.packed_bytes
-    assert n == 6 * cfg.E_loc * cfg.H * cfg.I * 2
-    got = torch.empty(n // 2, dtype=torch.int16, device="cuda")
-    mok.mok_pack_bf16(case.d, case.layer.w, got)
-    assert torch.equal(got, _packed_reference(case.wg, case.wu, case.wd))
+    m = cfg.E_loc * cfg.H * cfg.I
+    assert n == (12 * m if dtype == "bf16" else (6 * m + 255) // 256 * 256 + 6 * m // 32)
+    got = torch.empty(n, dtype=torch.uint8, device="cuda")
+    mok.mok_pack_weights(case.d, case.layer.w, got)
+    if dtype == "bf16":
+        ref = _packed_reference(case.wg, case.wu, case.wd).view(torch.uint8)
+    else:
+        ref = _packed_reference_mx(case.wg, case.wu, case.wd)
+    assert torch.equal(got, ref)
     results = []
     for packed in (True, False):
         case.layer.set_weights(case.wg, case.wu, case.wd, packed=packed)
@@ -270,7 +316,9 @@ def test_packed_weights_match_the_stated_layout_and_per_call_packing():
             case.run(fused=fused)
             results.append(case.grads() + [case.out.clone()])
     fw, bw = case.oracle_backward()
-    _compare(case, fw, bw, max_rel_err, BF16_TOL)
+    tol_fn, tol = (max_rel_err, BF16_TOL) if dtype == "bf16" else (frob_rel_err, MX_TOL)
+    errs = _compare(case, fw, bw, tol_fn, tol)
+    print(f"  {tol_fn.__name__} vs oracle: {errs}")
     for other in results[1:]:
         for a, b in zip(results[0], other):
             assert torch.equal(a, b)

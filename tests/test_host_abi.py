@@ -83,17 +83,20 @@ def test_sizes_follow_host_bounds():
     assert sm.slot_bytes == 256 * 2 * 2048 * 2                # g|u stays BF16
     assert sm.ring_slots == 8 * ((share - 3 * sm.x_slot_bytes - 3 * sm.h_slot_bytes)
                                  // sm.slot_bytes)
-    # packed BF16 weights: gate/up (2 E_loc I H), Wd, Wd^T, [Wg^T | Wu^T] (2 E_loc H I), BF16;
-    # the workspace has room to pack them per call; MXFP8 packs nothing
-    assert s.packed_bytes == 6 * 4 * 7168 * 2048 * 2
+    # packed weights: gate/up (2 E_loc I H), Wd, Wd^T, [Wg^T | Wu^T] (2 E_loc H I) values (BF16)
+    # or codes and scales (MXFP8); the workspace has room to pack them per call
+    m = 4 * 7168 * 2048
+    assert s.packed_bytes == 6 * m * 2
+    assert sm.packed_bytes == 6 * m + 6 * m // 32
     assert s.ws_bytes >= s.packed_bytes and s.bwd_ws_bytes >= s.ws_bytes
-    assert sm.packed_bytes == 0
+    assert sm.ws_bytes >= sm.packed_bytes
     # null arguments are rejected before anything runs
     assert mok.lib().mok_schedule(ctypes.byref(_d()), None, None, None, None, None, None) == 1
     w = mok.MokWeights()
-    assert mok.lib().mok_pack_bf16(ctypes.byref(_d()), ctypes.byref(w), None, None) == 1
-    assert mok.lib().mok_pack_bf16(ctypes.byref(_d(dtype="mxfp8")), ctypes.byref(w), 256,
-                                   None) != 0
+    assert mok.lib().mok_pack_weights(ctypes.byref(_d()), ctypes.byref(w), None, None) == 1
+    # MXFP8 needs the quantised codes and scales
+    assert mok.lib().mok_pack_weights(ctypes.byref(_d(dtype="mxfp8")), ctypes.byref(w), 256,
+                                      None) == 3
 
 
 def test_two_wave_floor_matches_pages_figure():
