@@ -133,11 +133,20 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
     __syncthreads();
     if (c0 + 32 < a.E) load_chunk(c0 + 32);
     const int ce = min(32, a.E - c0);
-    if (ce == 32) {
-#pragma unroll 8
-      for (int u = 0; u < 32; ++u) topk_insert<KM>(key, rank_key(s_l[buf][tid][u], c0 + u));
-    } else {
-      for (int u = 0; u < ce; ++u) topk_insert<KM>(key, rank_key(s_l[buf][tid][u], c0 + u));
+    // Only a candidate above the list's smallest key can enter it: one 64-bit compare per
+    // candidate builds the chunk's mask, and only those are inserted, in expert order (one the
+    // list has outgrown meanwhile passes through unchanged). A wave iterates as often as its
+    // busiest lane (a few times per chunk once the list has filled, against 32 insertions).
+    // The keys are unique, so the list is the one inserting every candidate gives.
+    const uint64_t kth = key[KM - 1];
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 32; ++u)
+      if (u < ce && rank_key(s_l[buf][tid][u], c0 + u) > kth) m |= 1u << u;
+    while (m) {
+      const int u = __builtin_ctz(m);
+      m &= m - 1;
+      topk_insert<KM>(key, rank_key(s_l[buf][tid][u], c0 + u));
     }
   }
   float v[KM];
