@@ -98,9 +98,10 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         const float g = bf2f(lg[lr * 128 + lc]);
         const float u = bf2f(lu[lr * 128 + lc]);
         const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
-        // the forward's h, recomputed from the stored g and u (through the forward's own helper:
-        // sharing sg with it here made the compiler spill inside the K loop)
-        const float hf = swiglu_bf(g, u);
+        // the forward's h, recomputed from the stored g and u: g and u are BF16 values, so
+        // swiglu_bf(g, u) is g * sigmoid_hw(g) * u with sigmoid_hw(g) = sg (the same expression);
+        // MXFP8 keeps the helper (sharing sg there made the compiler spill inside the K loop)
+        const float hf = MX ? swiglu_bf(g, u) : swiglu_of(g, sg, u);
         const float dh = pg * av;
         const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
         const float duv = dh * g * sg;
@@ -198,7 +199,14 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
     }
     // (a wave's LDS accesses complete in order: no wait before reading dg | du back)
     __builtin_amdgcn_wave_barrier();
-    // dg | du rows out with 16-byte stores (BF16) or 8-byte code stores (MXFP8), 16 lanes per row
+    // dg | du rows out with 16-byte stores (BF16) or 8-byte code stores (MXFP8), 16 lanes per row.
+    // BF16 stores go through a buffer resource over the tile's valid rows of this wave's columns
+    // (empty when they lie past I), which drops the rest: every wave issues exactly 16 stores, so
+    // the compiler's wait before the next block's staged g, u is for those loads alone.
+    __amdgpu_buffer_rsrc_t orsrc;
+    if (!MX)
+      orsrc = make_rsrc(dgu + row0 * 2 * s.I,
+                        colw < s.I ? int64_t(nrows) * 2 * s.I * 2 : int64_t(0));
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int rr = q * 4 + (lane >> 4), cc = (lane & 15) * 8;
@@ -206,6 +214,13 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
       const u32x4 gv = *reinterpret_cast<const u32x4*>(lg + rr * 128 + cc);
       const u32x4 uv = *reinterpret_cast<const u32x4*>(lu + rr * 128 + cc);
       const int64_t row = row0 + rbase + rr;
+      if (!MX) {
+        const int off = ((rbase + rr) * 2 * s.I + colw + cc) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, gv), orsrc, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, uv), orsrc, off + s.I * 2,
+                                               0, 0);
+        continue;
+      }
       if (!wr) continue;
       if (MX) {
         // low bytes of the 8 slots are the codes; the first slot of a 32-column block also
@@ -220,10 +235,6 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
           dgq_s[row * (2 * s.I / 32) + (colw + cc) / 32] = uint8_t(gv[0] >> 8);
           dgq_s[row * (2 * s.I / 32) + (s.I + colw + cc) / 32] = uint8_t(uv[0] >> 8);
         }
-      } else {
-        uint16_t* dst = dgu + row * 2 * s.I + colw + cc;
-        *reinterpret_cast<u32x4*>(dst) = gv;
-        *reinterpret_cast<u32x4*>(dst + s.I) = uv;
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -293,7 +304,7 @@ __device__ __forceinline__ void a_tile(GemmLds& sm, const FfnShape& s, int64_t r
   a_stage_load(st, s, row0, nrows, colw, wm * 128, act, lcode, lane);
 #define MOK_A_BLOCK(I_)                                                                          \
   {                                                                                              \
-    __builtin_amdgcn_s_waitcnt(0);                                                               \
+    if (MX) __builtin_amdgcn_s_waitcnt(0);                                                       \
     a_stage_store(st, lg, lu, lane);                                                             \
     if (I_ < 3) a_stage_load(st, s, row0, nrows, colw, wm * 128 + (I_ + 1) * 32, act,             \
                              lcode + (I_ + 1) * 32, lane);                                       \
