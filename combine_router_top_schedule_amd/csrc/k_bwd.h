@@ -99,9 +99,8 @@ __device__ __forceinline__ void a_epilogue_block(const f32x16 (&acc)[4][4], cons
         const float u = bf2f(lu[lr * 128 + lc]);
         const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-g));
         // the forward's h, recomputed from the stored g and u: g and u are BF16 values, so
-        // swiglu_bf(g, u) is g * sigmoid_hw(g) * u with sigmoid_hw(g) = sg (the same expression);
-        // MXFP8 keeps the helper (sharing sg there made the compiler spill inside the K loop)
-        const float hf = MX ? swiglu_bf(g, u) : swiglu_of(g, sg, u);
+        // swiglu_bf(g, u) is g * sigmoid_hw(g) * u with sigmoid_hw(g) = sg (the same expression)
+        const float hf = swiglu_of(g, sg, u);
         const float dh = pg * av;
         const float dgv = dh * u * sg * (1.f + g * (1.f - sg));
         const float duv = dh * g * sg;
