@@ -214,6 +214,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3", choices=["dsv3", "kimi", "kimi_mx_skew"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ring-mib", type=int, default=0,
+                    help="override the workload's ring size (MiB): how many row tiles stay resident")
     ap.add_argument("--minibatch", type=int, default=0,
                     help="override the workload's minibatch rows M (ring granularity)")
     ap.add_argument("--forward-only", action="store_true",
@@ -246,6 +248,8 @@ def main() -> int:
     # minibatch: --minibatch, else 0 (the library's two-wave default; the test configs keep
     # their own M to exercise the minibatch cut)
     cfg = datagen.CONFIGS[args.workload].replace(M=args.minibatch)
+    if args.ring_mib:
+        cfg = cfg.replace(ring_bytes=args.ring_mib << 20)
     mx = cfg.dtype == "mxfp8"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
@@ -356,7 +360,8 @@ def main() -> int:
     step_flop = (6.0 if args.forward_only else 18.0) * P * HI
     peak = PEAK_MXFP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     # the committed counter summaries cover the default DeepSeek-V3 BF16 run only
-    default_run = args.workload == "dsv3" and not args.minibatch and not args.forward_only
+    default_run = (args.workload == "dsv3" and not args.minibatch and not args.forward_only
+                   and not args.ring_mib)
     kernels = {}
     for name, t in kernel_ms.items():
         k = KERNELS[name]
