@@ -358,7 +358,10 @@ __device__ __forceinline__ void gemm_tile_pb(GemmLds& sm, const Operand& A, cons
   for (int kt = 0; kt < ksteps; ++kt) {
     const int cur = kt & 1;
     const bool more = kt < last;
-    if (more) issue_stage<kLoadAgent>(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, false, w);
+    // Issued in every stage (in the last one a harmless reload of the same stage): with a
+    // conditional issue the compiler counts the stage's loads as absent on the merged path and
+    // its waits for each B slice would also wait for 8 younger B loads.
+    issue_stage<kLoadAgent>(A, sm.a[cur ^ 1], sm.as[cur ^ 1], more ? kt + 1 : kt, false, w);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
@@ -453,11 +456,12 @@ __device__ __forceinline__ void load_a_frag_mx(i32x8 (&a)[4], int (&sa)[4], cons
   }
 }
 
-// The K loop of one MXFP8 output tile with a packed B operand: gemm_tile_pb's schedule with two
-// E4M3 slices per stage. A codes and scales go through LDS by DMA (9 loads per wave per stage);
-// B codes and scale bytes go straight into registers, one stage ahead (12 loads per slice).
-// The stage barrier waits for the A stage only: the 12 loads of B(kt+1) slice 0 stay in
-// flight. Bit-identical to gemm_tile<true>.
+// The K loop of one MXFP8 output tile with a packed B operand: two E4M3 slices per stage. A
+// codes and scales go through LDS by DMA (9 loads per wave per stage), issued into the
+// double buffer as soon as the mid-stage barrier frees it, so each A stage has a full stage of
+// matrix work to arrive; B codes and scale bytes go straight into registers, one stage ahead
+// (12 loads per slice). The barrier leaves the 12 loads of B(kt+1) slice 0 in flight.
+// Bit-identical to gemm_tile<true>.
 __device__ __forceinline__ void gemm_tile_pb_mx(GemmLds& sm, const Operand& A, const PackedBMX& B,
                                                 int ksteps, f32x16 (&acc)[4][4], int wm, int wn,
                                                 int lane) {
@@ -475,6 +479,7 @@ __device__ __forceinline__ void gemm_tile_pb_mx(GemmLds& sm, const Operand& A, c
   i32x8 fa[2][4];
   int sa[2][4];
   issue_stage<kLoadAgent>(A, sm.a[0], sm.as[0], 0, true, w);
+  issue_stage<kLoadAgent>(A, sm.a[1], sm.as[1], min(1, last), true, w);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) load_b_packed_mx(b[kk], sb[kk], B, 0, kk, wn, lane);
   __builtin_amdgcn_s_waitcnt(0);
@@ -483,16 +488,20 @@ __device__ __forceinline__ void gemm_tile_pb_mx(GemmLds& sm, const Operand& A, c
   for (int kt = 0; kt < ksteps; ++kt) {
     const int cur = kt & 1;
     const bool more = kt < last;
-    if (more) issue_stage<kLoadAgent>(A, sm.a[cur ^ 1], sm.as[cur ^ 1], kt + 1, true, w);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
       if (kk == 0) {
         load_a_frag_mx(fa[1], sa[1], sm.a[cur], sm.as[cur], 1, wm, lane);
       } else {
-        // vmcnt(12): the loads issued after A(kt+1) are the 12 of B(kt+1) slice 0
+        // vmcnt(12): everything but the 12 loads of B(kt+1) slice 0 has landed, A(kt+1) too
         __builtin_amdgcn_s_waitcnt(0x0F7C);
         __syncthreads();
+        // Stage kt's fragments are all in registers now, so its buffer takes A(kt+2): a whole
+        // stage of matrix work to cover the DMA, against one slice if it were issued at the
+        // start of stage kt+1. Issued in every stage (near the end a harmless reload of the
+        // last one) so that the compiler's waits for B count these 9 loads.
+        issue_stage<kLoadAgent>(A, sm.a[cur], sm.as[cur], min(kt + 2, last), true, w);
         if (more) load_a_frag_mx(fa[0], sa[0], sm.a[cur ^ 1], sm.as[cur ^ 1], 0, wm, lane);
       }
 #pragma unroll
