@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
 //  - the padded column layout of the per-expert transposed planes: expert e's rows go to
 //    columns [colpad[e], colpad[e] + count[e]), colpad[e] a multiple of kPadRows, the rest of its
 //    rounded-up range zero; hdr2[kB2RowsPad] = total padded columns;
-//  - zeroed work-queue counters of the two GEMM launches.
+//  - zeroed work-queue counters of the two GEMM launches, and a cleared error word.
 // El <= 64, so lane e owns expert e. The ring record is used only if it is whole: its slot
 // count matches this ring, and every recorded tile has a slot of this ring and lies inside its
 // expert's rows; otherwise every row is replayed (the result is the same either way).
@@ -252,8 +252,10 @@ __global__ __launch_bounds__(64) void k_bwd_plan(const int32_t* hdr, const int32
                                                  MTile* restore, int32_t* restore_slot,
                                                  MTile* replay, int32_t* counts, MTile* tiles,
                                                  int32_t* ntiles, int32_t* hdr2, int El,
-                                                 int64_t tiles_max) {
+                                                 int64_t tiles_max, int32_t* err) {
   const int lane = threadIdx.x;
+  // the backward's own error word (its workspace is not the forward's)
+  if (lane == 0) *err = 0;
   const uint64_t lt = (1ull << lane) - 1;
   // per-expert rows and tile counts, exclusive prefix over experts (lanes)
   const int off = lane < El ? hdr[kHdrOffsets + lane] : 0;
@@ -602,7 +604,8 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
                      int(b.ring != nullptr && L.ring_capa > 0), L.ring_capa, restore, rsl,
                      replay, counts,
                      reinterpret_cast<MTile*>(b.ws + L.ws_tiles),
-                     reinterpret_cast<int32_t*>(b.ws) + kWsNumTiles, b.hdr2, El, L.tiles_max);
+                     reinterpret_cast<int32_t*>(b.ws) + kWsNumTiles, b.hdr2, El, L.tiles_max,
+                     reinterpret_cast<int32_t*>(b.ws) + kWsError);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     StageArgs st{};

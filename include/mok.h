@@ -349,7 +349,7 @@ mok_status mok_layer_bwd(const mok_desc* desc, const void* const* dout_seg_dev,
                          const void* saved_dev, void* ring_dev, void* slots_dev,
                          void* const* dx_seg_dev, float* dp_dev, float* dlogits_dev,
                          const mok_weight_grads* g, void* ws_dev, void* stream);
-/* (mok_layer_bwd: ws_dev must hold bwd_ws_bytes.) */
+/* (mok_layer_bwd: ws_dev must hold bwd_ws_bytes; the call clears its error word first.) */
 
 /* MXFP8 quantiser (OCP MX v1.0: E4M3 codes, one UE8M0 scale per 32 elements; shared scale
  * 2^(floor(log2 amax) - 8), round to nearest even, saturate to +-448, amax 0 -> scale 0).

@@ -116,6 +116,8 @@ class BwdCase(Case):
                           self.dwd, self.bws)
         torch.cuda.synchronize()
         assert mok.mok_device_status(L.ws) == 0
+        # (the backward's workspace starts uninitialised: the call clears its error word)
+        assert mok.mok_device_status(self.bws) == 0
 
     def grads(self):
         """Copies of every backward output."""
@@ -175,6 +177,8 @@ class ArrayCase:
                           self.dwd, self.bws)
         torch.cuda.synchronize()
         assert mok.mok_device_status(L.ws) == 0
+        # (the backward's workspace starts uninitialised: the call clears its error word)
+        assert mok.mok_device_status(self.bws) == 0
         f64 = lambda t: t.cpu().numpy().astype(np.float64)
         return dict(out=bf16_to_f64(host_u16(self.out)), dx=bf16_to_f64(host_u16(self.dx)),
                     dwg=f64(self.dwg), dwu=f64(self.dwu), dwd=f64(self.dwd),

@@ -222,6 +222,7 @@ def test_backward_after_timed_out_forward_replays_every_row():
     mok.mok_layer_bwd(bad.d, bad.dout_seg, bad.x_seg, L.w, L.idx, L.p, L.saved, L.ring, L.slots,
                       bad.dx_seg, bad.dp, bad.dlogits, bad.dwg, bad.dwu, bad.dwd, bad.bws)
     torch.cuda.synchronize()
+    assert mok.mok_device_status(bad.bws) == 0
     good = BwdCase(cfg)
     good.run(fused=False)
     for a, b in zip(bad.grads(), good.grads()):
