@@ -73,6 +73,22 @@ __device__ __forceinline__ void topk_insert(uint64_t (&key)[KM], uint64_t k) {
   }
 }
 
+// Sorts KM unique keys into descending order: odd-even transposition, KM rounds of
+// compare-exchanges on neighbours (branch-free).
+template <int KM>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[KM]) {
+#pragma unroll
+  for (int r = 0; r < KM; ++r) {
+#pragma unroll
+    for (int j = r & 1; j + 1 < KM; j += 2) {
+      const uint64_t x = key[j], y = key[j + 1];
+      const bool c = y > x;
+      key[j] = c ? y : x;
+      key[j + 1] = c ? x : y;
+    }
+  }
+}
+
 // One thread per token: the block's 256 tokens stream their logits through LDS in chunks of
 // 32 experts (coalesced 128-byte row pieces in, conflict-free column reads out), and each
 // thread keeps its token's top-KM in registers. Two LDS chunk buffers: the loads of chunk
@@ -100,15 +116,21 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
   // unconditionally from a clamped (in-bounds) address and masked when stored, so all eight
   // rows' loads are in flight together.
   float4 val[8];
+  // (the branch on vec4 stays outside the row loop: inside it, the two paths were merged into
+  // four 4-byte loads per row)
   auto load_chunk = [&](int c0) {
     const int col = c0 + 4 * (tid & 7);
+    if (vec4) {
+      const int cc = min(col, a.E - 4);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int64_t n = min(n_base + (tid >> 3) + 32 * q, a.N - 1);
-      if (vec4) {
-        const int cc = min(col, a.E - 4);
+      for (int q = 0; q < 8; ++q) {
+        const int64_t n = min(n_base + (tid >> 3) + 32 * q, a.N - 1);
         val[q] = *reinterpret_cast<const float4*>(a.logits + n * a.E + cc);
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t n = min(n_base + (tid >> 3) + 32 * q, a.N - 1);
         val[q].x = a.logits[n * a.E + min(col, a.E - 1)];
         val[q].y = a.logits[n * a.E + min(col + 1, a.E - 1)];
         val[q].z = a.logits[n * a.E + min(col + 2, a.E - 1)];
@@ -133,6 +155,20 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
     __syncthreads();
     if (c0 + 32 < a.E) load_chunk(c0 + 32);
     const int ce = min(32, a.E - c0);
+    // The token's 32 logits of the chunk, read together (one LDS round trip, not one per
+    // candidate).
+    float lv[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) lv[u] = s_l[buf][tid][u];
+    // The first chunk starts the list as its first KM candidates, sorted by a compare-exchange
+    // network instead of KM insertions.
+    int u0 = 0;
+    if (c0 == 0 && ce >= KM) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) key[j] = rank_key(lv[j], j);
+      sort_desc<KM>(key);
+      u0 = KM;
+    }
     // Only a candidate above the list's smallest key can enter it: one 64-bit compare per
     // candidate builds the chunk's mask, and only those are inserted, in expert order (one the
     // list has outgrown meanwhile passes through unchanged). A wave iterates as often as its
@@ -141,8 +177,8 @@ __global__ __launch_bounds__(256) void k_topk_scan(RouterArgs a) {
     const uint64_t kth = key[KM - 1];
     uint32_t m = 0;
 #pragma unroll
-    for (int u = 0; u < 32; ++u)
-      if (u < ce && rank_key(s_l[buf][tid][u], c0 + u) > kth) m |= 1u << u;
+    for (int u = 0; u < 32; ++u) m |= uint32_t(rank_key(lv[u], c0 + u) > kth) << u;
+    m &= (ce >= 32 ? 0xFFFFFFFFu : (1u << ce) - 1u) & (0xFFFFFFFFu << u0);
     while (m) {
       const int u = __builtin_ctz(m);
       m &= m - 1;
