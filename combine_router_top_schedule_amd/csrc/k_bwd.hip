@@ -47,6 +47,11 @@ struct TransposeArgs {
   // Non-null (BF16 rows from segments): every source row is also copied, unscaled, to
   // rows_out[its expert-ordered row][F] (the dOut gather D of the backward, read once for both).
   uint16_t* rows_out;
+  // Non-null (rows from segments, MXFP8): every source row is also quantised along the features,
+  // as the dispatch gather does it (the same 32-element blocks and rule), to codes
+  // rows_q[row][F] and scales rows_qs[row][F / 32]: the MXFP8 D operand of the a GEMM.
+  uint8_t* rows_q;
+  uint8_t* rows_qs;
   // from_act: rows are h, recomputed from the g|u of the activations, read where each row
   // lives (ActSource); h is formed as the forward formed it and then taken as the down GEMM
   // used it: rounded to BF16, or (plane_s non-null) quantised to MXFP8 along the features and
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) w[k] = pack_bf2(hv[2 * k], hv[2 * k + 1]);
         }
-      } else if (src) {
+      } else if (src || a.rows_q) {
         if (mxp) {
           const uint64_t c64 = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(src + ch * 8));
           const uint2 c8 = make_uint2(uint32_t(c64), uint32_t(c64 >> 32));
@@ -161,11 +166,23 @@ __global__ __launch_bounds__(256) void k_transpose_rows(TransposeArgs a) {
             w[k] = pack_bf2(e4m3_value(uint8_t(cw >> sh)) * sc, e4m3_value(uint8_t(cw >> (sh + 8))) * sc);
           }
         } else {
-          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ch * 16));
+          const u32x4 v = src ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + ch * 16))
+                              : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int k = 0; k < 4; ++k) w[k] = v[k];
-          if (a.rows_out)
+          if (a.rows_out && src)
             *reinterpret_cast<u32x4*>(a.rows_out + int64_t(s_row[r]) * a.F + f0 + ch * 8) = v;
+          if (a.rows_q) {
+            // every lane takes part (the block amax is a 4-lane shuffle: lanes 4b .. 4b+3 of a
+            // row's 16 hold its b-th block of 32 features); rows without a source store nothing
+            uint32_t sc;
+            const uint2 cw = mx_quant8_group4(v, &sc);
+            if (src) {
+              const int64_t row = s_row[r];
+              *reinterpret_cast<uint2*>(a.rows_q + row * a.F + f0 + ch * 8) = cw;
+              if ((ch & 3) == 0) a.rows_qs[row * (a.F / 32) + (f0 + ch * 8) / 32] = uint8_t(sc);
+            }
+          }
           if (a.p && !a.qdst) {   // BF16 operand; MXFP8 applies the gate in fp32 below
             const float g = s_gate[r];
 #pragma unroll
@@ -625,10 +642,9 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   }
   if ((err = launch_ffn_gateup_list(L, b.saved, b.xd, b.w, b.act, replay, counts + 1, s)) != hipSuccess)
     return err;
-  // 2. pull reverse-combine: D[r] = dOut[n(r)] (BF16; quantised along H for the a GEMM)
-  //    (MXFP8: the gather quantises along H on the way, like the forward dispatch)
-  //    (BF16: D is written by the (p D)^T gather-transpose below, which reads the same rows)
-  if (mx && (err = launch_dispatch(L, b.saved, b.dout_seg, b.dq, s)) != hipSuccess) return err;
+  // 2. pull reverse-combine: D[r] = dOut[n(r)] (BF16; MXFP8 quantised along H for the a GEMM
+  //    as the forward dispatch quantises X), written by the (p D)^T gather-transpose below,
+  //    which reads the same rows
   // 3. the backward GEMMs read packed Wd^T and [Wg^T | Wu^T] (b.w.packed: the caller's, or
   //    packed by the host entry point into the workspace)
   const PackOffsets po = pack_offsets(El, H, I, L.dtype);
@@ -650,15 +666,19 @@ hipError_t launch_backward(const Layout& L, const BwdBuffers& b, hipStream_t s) 
   asrc.code = b.actsrc;
   auto tr = [&](const uint16_t* const* seg, const float* p, const uint8_t* plane, const uint8_t* plane_s,
                 int64_t stride, int col0, int F, uint16_t* dst, uint8_t* qdst,
-                uint16_t* rows_out = nullptr, bool from_act = false, bool packed = false) {
+                uint16_t* rows_out = nullptr, bool from_act = false, bool packed = false,
+                uint8_t* rows_q = nullptr) {
     TransposeArgs t{hdr, b.hdr2, perm, p, seg, plane, plane_s, stride, col0, dst, mx ? qdst : nullptr,
-                    ld, F, L.K, L.T, El, rows_out, int(from_act), asrc, int(packed)};
+                    ld, F, L.K, L.T, El, rows_out, rows_q,
+                    rows_q ? rows_q + L.rows_max * int64_t(F) : nullptr, int(from_act), asrc,
+                    int(packed)};
     hipLaunchKernelGGL(k_transpose_rows, dim3(grid_cap(ld / kTrCols * (F / kTrFeat), 8192)), dim3(256), 0, s, t);
   };
   // (X^T and h^T are the B operands of the weight-gradient GEMMs: stored packed)
   tr(xs, nullptr, nullptr, nullptr, 0, 0, H, b.xt, b.q_xt, nullptr, false, true);   // X^T
   tr(ds, b.topk_p, nullptr, nullptr, 0, 0, H, b.dt, b.q_dt,
-     mx ? nullptr : reinterpret_cast<uint16_t*>(b.d));                              // (p D)^T (+ D)
+     mx ? nullptr : reinterpret_cast<uint16_t*>(b.d), false, false,
+     mx ? b.dq : nullptr);                                                           // (p D)^T (+ D)
   tr(nullptr, nullptr, ap.h, mx ? ap.hs : nullptr, I, 0, I, b.ht, b.q_ht, nullptr, true,
      true);                                                                         // h^T
   if ((err = hipGetLastError()) != hipSuccess) return err;
