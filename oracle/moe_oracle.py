@@ -16,7 +16,7 @@ intermediate I, local experts [e0, e0+E_loc). A pair id is n*K + k. Weights are 
 the reduction axis contiguous: Wg, Wu [E_loc][I][H], Wd [E_loc][H][I]; so g = x Wg^T,
 u = x Wu^T, y = h Wd^T.
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 
 * gating is a softmax over the K selected logits (the tiny workload states it; no scaling);
 * top-k orders experts by descending logit, ties to the lower expert id, -0.0 == +0.0;
