@@ -99,10 +99,12 @@ __device__ __forceinline__ uint2 mx_quant8_group4(const u32x4& v, uint32_t* scod
 }
 
 // ---- agent-scope signalling ---------------------------------------------------------------
-// On MI355X every XCD has its own L2. An agent-scope release writes back the whole local L2
-// and an acquire invalidates it, so they are used once around a hand-off, never inside a
-// polling loop. Words that carry their own payload (scan states, counters) are accessed with
-// relaxed agent-scope atomics, which are coherent across XCDs without any cache maintenance.
+// On MI355X every XCD has its own L2. An agent-scope release would write back the whole local
+// L2 and an acquire invalidate it, so none is used: words that carry their own payload (scan
+// states, counters) are accessed with relaxed agent-scope atomics, which are coherent across
+// XCDs without any cache maintenance, and bulk data handed from one workgroup to another stays
+// inside one XCD (the producer's stores complete before it bumps a counter; the consumer reads
+// with loads that miss in its CU's L1).
 __device__ __forceinline__ uint32_t ld_relaxed_u(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -111,18 +113,6 @@ __device__ __forceinline__ void st_relaxed_u(uint32_t* p, uint32_t v) {
 }
 __device__ __forceinline__ int ld_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_acquire(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld_acquire_u(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_release_u(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int add_release(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int add_relaxed(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
