@@ -228,7 +228,8 @@ inline Layout make_layout(const mok_desc& d) {
   L.b_hdr2 = take(4 * kB2Words);
   L.b_xd = take(L.xd_bytes);
   L.b_act = take(L.act_bytes);
-  L.b_d = take(mx ? 0 : rm * H * 2);      // BF16 D (MXFP8 gathers straight into b_dq)
+  L.b_d = take(mx ? 0 : rm * H * 2);      // BF16 D (in MXFP8 the (p D)^T transpose writes
+                                          // the H-quantised D rows into b_dq instead)
   L.b_dq = take(mx ? rm * (H + H / 32) : 0);
   L.b_dgu = take(mx ? 0 : rm * 2 * I * 2);   // BF16 dg|du (MXFP8 writes codes only)
   L.b_dguq = take(mx ? rm * (2 * I + 2 * I / 32) : 0);

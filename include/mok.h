@@ -420,8 +420,7 @@ int32_t mok_device_cus(void);
  * MOK_TRACE_BWD_GEMM1   mok_layer_bwd's first GEMM launch: a = dOut Wd (with dp and SwiGLU
  *                       backward) and dW_down;
  * MOK_TRACE_BWD_GEMM2   its second: dx (pushed to the slots), dW_gate and dW_up;
- * MOK_TRACE_DISPATCH    the pull-dispatch gather kernel (mok_dispatch; in MXFP8 also the
- *                       backward's dOut gather);
+ * MOK_TRACE_DISPATCH    the pull-dispatch gather kernel of mok_dispatch;
  * MOK_TRACE_COMBINE     the merge kernel (mok_combine, and the merges of tokens with several
  *                       local pairs after the fused forward and in the backward).
  * Process-wide setting, not thread-safe; it changes no result. */
